@@ -1,0 +1,88 @@
+// dcr_internal.h -- plan layout shared by the host plan builder and the
+// gfx950 kernels of libdcr.so.  Not part of the public ABI.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "dcr.h"
+
+namespace dcr {
+
+constexpr uint32_t kChunkBytes = DCR_CHUNK_BYTES;   // canonical bytes per chunk
+constexpr uint32_t kVecBytes = 16;                  // one 128-bit access
+constexpr uint32_t kVecsPerChunk = kChunkBytes / kVecBytes;  // 4096
+constexpr uint32_t kThreads = 1024;                 // workgroup of encode / apply
+constexpr uint32_t kVecsPerThread = kVecsPerChunk / kThreads;  // 4
+constexpr uint32_t kMaxCachedPieces = 64;           // pieces of a chunk kept in LDS
+// largest payload of one chunk's records (mixed XOR + OW on BF16: two 4 KiB
+// bitmaps + 2 bytes per change + padding), rounded up to 16
+constexpr uint32_t kStageBytes = 73792;
+
+// status word of the decoupled look-back: 2 flag bits, then a packed value
+// (records << 36 | payload_bytes / 16)
+constexpr uint64_t kFlagAgg = 1, kFlagIncl = 2;
+constexpr int kValShift = 2;
+constexpr int kRecShift = 36;
+constexpr uint64_t kP16Mask = (uint64_t(1) << kRecShift) - 1;
+constexpr uint64_t kMaxTiles = uint64_t(1) << 25;   // 2 records per tile < 2^26
+
+// Device-side tensor descriptor.  48 bytes.
+struct DevTensor {
+    uint64_t numel;
+    uint64_t scale_bit_off;    // BLOCK_SCALED: bit offset of its scale tensor's flags
+    uint32_t w;
+    uint32_t route;
+    uint32_t n_chunks;
+    int32_t scale_tensor;
+    uint32_t scale_block;
+    uint32_t first_chunk;      // plan index of chunk 0
+    uint32_t pad[2];
+};
+static_assert(sizeof(DevTensor) == 48, "DevTensor");
+
+// One canonical chunk (one encode tile).  16 bytes.
+struct DevChunk {
+    uint32_t tensor;
+    uint32_t chunk_idx;
+    uint32_t first_piece;
+    uint32_t n_pieces;
+};
+static_assert(sizeof(DevChunk) == 16, "DevChunk");
+
+// A contiguous run of a chunk: canonical elements [canon_start, canon_start+len)
+// of the chunk are shard elements [shard_elem_off, +len) of shard `shard`.  16 bytes.
+struct DevPiece {
+    uint64_t shard_elem_off;
+    uint32_t shard;
+    uint16_t canon_start;      // first canonical element of the run within the chunk
+    uint16_t len_m1;           // run length - 1 (lengths 1 .. 65536)
+};
+static_assert(sizeof(DevPiece) == 16, "DevPiece");
+
+struct Plan {
+    std::vector<dcr_tensor_desc> tensors;
+    std::vector<uint64_t> shard_bytes;
+    std::vector<DevTensor> dt;
+    std::vector<DevChunk> chunks;
+    std::vector<DevPiece> pieces;
+    std::vector<uint32_t> scale_chunks;   // chunks of scale tensors that gate a BLOCK_SCALED one
+    uint64_t fingerprint = 0;
+    uint64_t canonical_bytes = 0;
+    uint64_t scale_bits = 0;              // total flag bits (multiple of 64)
+    uint64_t max_dir_bytes = 0, max_payload_bytes = 0;
+    // device table layout
+    uint64_t off_tensors = 0, off_chunks = 0, off_pieces = 0, off_scale_chunks = 0, table_bytes = 0;
+    // workspace layout
+    uint64_t ws_status = 0, ws_counter = 0, ws_old = 0, ws_new = 0, ws_scale = 0, ws_canon = 0,
+             ws_bytes = 0;
+    std::vector<uint8_t> blob;            // host image of the device tables
+    void* dev_tables = nullptr;           // bound by dcr_plan_upload
+};
+
+void set_error(const std::string& msg);
+
+}  // namespace dcr
+
+struct dcr_plan : dcr::Plan {};

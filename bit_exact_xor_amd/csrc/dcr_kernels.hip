@@ -1,0 +1,1014 @@
+// dcr_kernels.hip -- gfx950 kernels and device-side entry points of libdcr.so.
+//
+// encode (sender): one workgroup of 1024 threads per 64 KiB canonical chunk
+//   ("tile").  It gathers the chunk's old and new bytes from the trainer
+//   shards through the plan's pieces (the direct projection: ai-feeds summary
+//   "key modules" 1), 16 bytes per lane per load.  It compares stored bits as
+//   integers (tokendh blog "shard owner": +0/-0 differ) and routes each
+//   16-byte group to XOR or overwrite (ai-feeds "key modules" 2-3).  Change
+//   counts are scanned per workgroup; the tile's record count and payload size
+//   go through a device-wide decoupled look-back that yields the directory
+//   index and the payload offset.  The records are staged in LDS and written
+//   with 128-bit stores.
+// apply (receiver): one workgroup per directory entry.  It checks the entry
+//   and the record bytes before touching anything, stages the record in LDS,
+//   ranks the changes by a workgroup scan of the bitmap, and updates every
+//   touched 16-byte group of the canonical tensor with one 128-bit
+//   read-modify-write: XOR for masks, assignment for overwrites (ai-feeds
+//   "key modules" 4; humansand "Delta update algebra").  Dedup flags make a
+//   duplicate a no-op (tokendh "XOR or overwrite"); the retry ignores them and
+//   overwrites (tokendh "no backup copy").
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+
+#include "dcr_internal.h"
+
+namespace dcr {
+
+// ------------------------------------------------------------ device helpers
+
+__device__ __forceinline__ uint32_t dpad16(uint32_t x) { return (x + 15u) & ~15u; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint64_t ld_status(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_status(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x, uint32_t lane) {
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        uint64_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ uint64_t wave_sum(uint64_t x) {
+#pragma unroll
+    for (uint32_t d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
+// Exclusive workgroup scan of N packed 64-bit values; totals returned in tot.
+// Uses sh[2 * N * 16 + N] of LDS; ends with a barrier so sh may be reused.
+// The first wave scans the 16 wave totals, so that each thread reads back
+// just two values per scanned quantity.
+template <int N>
+__device__ __forceinline__ void block_excl_scan(uint64_t (&v)[N], uint64_t (&tot)[N], uint64_t* sh) {
+    constexpr uint32_t NW = kThreads / 64;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    uint64_t inc[N];
+#pragma unroll
+    for (int i = 0; i < N; i++) inc[i] = wave_incl_scan(v[i], lane);
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < N; i++) sh[i * NW + wave] = inc[i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const uint64_t t = lane < NW ? sh[i * NW + lane] : 0;
+            const uint64_t ti = wave_incl_scan(t, lane);
+            if (lane < NW) sh[N * NW + i * NW + lane] = ti - t;      // exclusive wave prefix
+            if (lane == NW - 1) sh[2 * N * NW + i] = ti;            // total
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        v[i] = sh[N * NW + i * NW + wave] + inc[i] - v[i];
+        tot[i] = sh[2 * N * NW + i];
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t field16(uint64_t packed, int k) {
+    return uint32_t(packed >> (16 * k)) & 0xFFFFu;
+}
+
+// Element e (a compile-time index after unrolling) of a 16-byte group of
+// W-byte elements held in 4 registers.
+template <int W>
+__device__ __forceinline__ uint32_t elem(const uint32_t (&q)[4], uint32_t e) {
+    if constexpr (W == 4) return q[e];
+    else if constexpr (W == 2) return (q[e >> 1] >> (16u * (e & 1u))) & 0xFFFFu;
+    else return (q[e >> 2] >> (8u * (e & 3u))) & 0xFFu;
+}
+// OR v into element e (compile-time index; the element's bits must be zero).
+template <int W>
+__device__ __forceinline__ void set_elem(uint32_t (&q)[4], uint32_t e, uint32_t v) {
+    if constexpr (W == 4) q[e] |= v;
+    else if constexpr (W == 2) q[e >> 1] |= (v & 0xFFFFu) << (16u * (e & 1u));
+    else q[e >> 2] |= (v & 0xFFu) << (8u * (e & 3u));
+}
+__device__ __forceinline__ uint32_t sgpr(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// chunk element -> index of the piece holding it (largest start <= e)
+__device__ __forceinline__ uint32_t find_piece(const DevPiece* pc, uint32_t n, uint32_t e) {
+    uint32_t lo = 0, hi = n;  // invariant: pc[lo].canon_start <= e
+    while (hi - lo > 1) {
+        uint32_t mid = (lo + hi) >> 1;
+        if (pc[mid].canon_start <= e) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------------ encode
+
+struct EncodeArgs {
+    const DevTensor* tensors;
+    const DevChunk* chunks;
+    const DevPiece* pieces;
+    const uint8_t* const* old_sh;
+    const uint8_t* const* new_sh;
+    const uint64_t* scale_flags;
+    uint64_t* status;
+    uint32_t* counter;      // [0] tile counter, [2..3] changed elements (u64)
+    uint8_t* dir;
+    uint8_t* payload;
+    uint64_t dir_cap;       // bytes
+    uint64_t payload_cap;   // bytes
+    uint32_t n_tiles;
+    uint32_t mode;
+};
+
+struct EncodeShared {
+    alignas(16) uint32_t pw[kVecsPerChunk][4];   // payload words of changed groups
+    alignas(16) uint32_t pres[1024];            // SPARSE presence bitmap (K <= 32768 bits)
+    DevPiece pieces[kMaxCachedPieces];
+    uint64_t scan[2 * 3 * (kThreads / 64) + 3];
+    uint64_t excl;
+    uint32_t next;
+};
+
+// Gather one 16-byte group (elements e0 .. e0+V-1 of the chunk) of old and
+// new.  Elements at or past n_c read as zero in both.
+template <int W>
+__device__ __forceinline__ void gather_group(const EncodeArgs& a, const DevPiece* pc, uint32_t np, uint32_t e0,
+                                             uint32_t n_c, uint32_t (&o)[4], uint32_t (&n)[4]) {
+    constexpr uint32_t V = 16 / W;
+#pragma unroll
+    for (int i = 0; i < 4; i++) o[i] = n[i] = 0;
+    if (e0 >= n_c) return;
+    uint32_t p = find_piece(pc, np, e0);
+    uint32_t pstart = pc[p].canon_start, pend = pstart + uint32_t(pc[p].len_m1) + 1;
+    if (e0 + V <= pend) {
+        const uint64_t off = (pc[p].shard_elem_off + (e0 - pstart)) * W;
+        const uint8_t* so = a.old_sh[pc[p].shard] + off;
+        const uint8_t* sn = a.new_sh[pc[p].shard] + off;
+        if (((reinterpret_cast<uintptr_t>(so) | reinterpret_cast<uintptr_t>(sn)) & 15u) == 0) {
+            uint4 vo = *reinterpret_cast<const uint4*>(so);
+            uint4 vn = *reinterpret_cast<const uint4*>(sn);
+            o[0] = vo.x; o[1] = vo.y; o[2] = vo.z; o[3] = vo.w;
+            n[0] = vn.x; n[1] = vn.y; n[2] = vn.z; n[3] = vn.w;
+            return;
+        }
+    }
+    // element by element (group crosses a piece border, is misaligned, or is
+    // the tail): shift each element into a 128-bit accumulator
+    uint64_t olo = 0, ohi = 0, nlo = 0, nhi = 0;
+    for (uint32_t i = 0; i < V; i++) {
+        const uint32_t e = e0 + i;
+        uint64_t vo = 0, vn = 0;
+        if (e < n_c) {
+            while (e >= pend) {
+                p++;
+                pstart = pc[p].canon_start;
+                pend = pstart + uint32_t(pc[p].len_m1) + 1;
+            }
+            const uint64_t off = (pc[p].shard_elem_off + (e - pstart)) * W;
+            const uint8_t* so = a.old_sh[pc[p].shard] + off;
+            const uint8_t* sn = a.new_sh[pc[p].shard] + off;
+            if constexpr (W == 1) { vo = *so; vn = *sn; }
+            else if constexpr (W == 2) { vo = *reinterpret_cast<const uint16_t*>(so); vn = *reinterpret_cast<const uint16_t*>(sn); }
+            else { vo = *reinterpret_cast<const uint32_t*>(so); vn = *reinterpret_cast<const uint32_t*>(sn); }
+        }
+        olo = (olo >> (8 * W)) | (ohi << (64 - 8 * W));
+        ohi = (ohi >> (8 * W)) | (vo << (64 - 8 * W));
+        nlo = (nlo >> (8 * W)) | (nhi << (64 - 8 * W));
+        nhi = (nhi >> (8 * W)) | (vn << (64 - 8 * W));
+    }
+    o[0] = uint32_t(olo); o[1] = uint32_t(olo >> 32); o[2] = uint32_t(ohi); o[3] = uint32_t(ohi >> 32);
+    n[0] = uint32_t(nlo); n[1] = uint32_t(nlo >> 32); n[2] = uint32_t(nhi); n[3] = uint32_t(nhi >> 32);
+}
+
+template <int W>
+__device__ __forceinline__ void encode_tile(const EncodeArgs& a, EncodeShared& S, uint32_t tile, const DevChunk ch,
+                                            const DevTensor td) {
+    constexpr uint32_t V = 16 / W;             // elements per 16-byte group
+    constexpr uint32_t E = kChunkBytes / W;    // elements per chunk
+    const uint32_t tid = threadIdx.x;
+    const uint64_t c0 = uint64_t(ch.chunk_idx) * E;
+    const uint32_t n_c = uint32_t(umin64(E, td.numel - c0));
+
+    // the chunk's pieces: LDS copy when few, else read in place
+    const DevPiece* pc = a.pieces + ch.first_piece;
+    bool fast = false;
+    if (ch.n_pieces == 1 && n_c == E) {
+        const DevPiece p0 = pc[0];
+        const uint8_t* so = a.old_sh[p0.shard] + p0.shard_elem_off * W;
+        const uint8_t* sn = a.new_sh[p0.shard] + p0.shard_elem_off * W;
+        fast = ((reinterpret_cast<uintptr_t>(so) | reinterpret_cast<uintptr_t>(sn)) & 15u) == 0;
+    }
+    if (!fast && ch.n_pieces <= kMaxCachedPieces) {
+        if (tid < ch.n_pieces) S.pieces[tid] = pc[tid];
+        __syncthreads();
+        pc = S.pieces;
+    }
+
+    // ---- load, compare, route
+    uint32_t meta[kVecsPerThread];    // changed bits | high-byte bits << 16 | kind << 31
+    uint64_t cnt[3] = {0, 0, 0};      // packed per-k counts: XOR K, OW K, XOR high bytes
+    auto digest = [&](uint32_t k, const uint32_t (&o)[4], const uint32_t (&n)[4]) {
+        const uint32_t g = tid + k * kThreads;
+        uint32_t b = 0, h = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < V; i++) {
+            const uint32_t d = elem<W>(o, i) ^ elem<W>(n, i);
+            b |= uint32_t(d != 0) << i;
+            if constexpr (W == 2) h |= uint32_t((d >> 8) != 0) << i;
+        }
+        uint32_t kd;
+        if (a.mode == DCR_MODE_RETRY || td.route == DCR_ROUTE_OVERWRITE) kd = DCR_KIND_OW;
+        else if (td.route == DCR_ROUTE_AFFINE_XOR || g * V >= n_c) kd = DCR_KIND_XOR;
+        else {
+            const uint64_t bit = td.scale_bit_off + (c0 + g * V) / td.scale_block;
+            kd = (a.scale_flags[bit >> 6] >> (bit & 63)) & 1u;   // 1 = scale changed -> OW
+        }
+        if (b) {
+            v4u q;
+            q.x = kd == DCR_KIND_XOR ? (o[0] ^ n[0]) : n[0];
+            q.y = kd == DCR_KIND_XOR ? (o[1] ^ n[1]) : n[1];
+            q.z = kd == DCR_KIND_XOR ? (o[2] ^ n[2]) : n[2];
+            q.w = kd == DCR_KIND_XOR ? (o[3] ^ n[3]) : n[3];
+            *reinterpret_cast<v4u*>(S.pw[g]) = q;
+        }
+        if (kd != DCR_KIND_XOR) h = 0;
+        meta[k] = b | (h << 16) | (kd << 31);
+        const uint64_t c = uint64_t(__popc(b)) << (16 * k);
+        cnt[0] |= kd == DCR_KIND_XOR ? c : 0;
+        cnt[1] |= kd == DCR_KIND_XOR ? 0 : c;
+        cnt[2] |= uint64_t(__popc(h)) << (16 * k);
+    };
+    if (fast) {
+        // one aligned piece covers the full chunk: straight 128-bit loads
+        const DevPiece p0 = pc[0];
+        const v4u* vo = reinterpret_cast<const v4u*>(a.old_sh[p0.shard] + p0.shard_elem_off * W) + tid;
+        const v4u* vn = reinterpret_cast<const v4u*>(a.new_sh[p0.shard] + p0.shard_elem_off * W) + tid;
+        v4u lo_[kVecsPerThread], ln_[kVecsPerThread];
+#pragma unroll
+        for (uint32_t k = 0; k < kVecsPerThread; k++) {
+            lo_[k] = __builtin_nontemporal_load(vo + k * kThreads);
+            ln_[k] = __builtin_nontemporal_load(vn + k * kThreads);
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < kVecsPerThread; k++) {
+            const uint32_t o[4] = {lo_[k].x, lo_[k].y, lo_[k].z, lo_[k].w};
+            const uint32_t n[4] = {ln_[k].x, ln_[k].y, ln_[k].z, ln_[k].w};
+            digest(k, o, n);
+        }
+    } else {
+#pragma unroll
+        for (uint32_t k = 0; k < kVecsPerThread; k++) {
+            uint32_t o[4], n[4];
+            gather_group<W>(a, pc, ch.n_pieces, (tid + k * kThreads) * V, n_c, o, n);
+            digest(k, o, n);
+        }
+    }
+    for (uint32_t q = tid; q < 1024; q += kThreads) S.pres[q] = 0;
+
+    // ---- counts -> change ranks and record sizes
+    uint64_t tot[3];
+    block_excl_scan<3>(cnt, tot, S.scan);   // (its barriers also publish S.pw / S.pres)
+    uint32_t Kx = 0, Ko = 0, Hx = 0;
+    uint32_t kbase[3][kVecsPerThread];      // per-k totals before k (uniform)
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        kbase[0][k] = Kx;
+        kbase[1][k] = Ko;
+        kbase[2][k] = Hx;
+        Kx += sgpr(field16(tot[0], k));
+        Ko += sgpr(field16(tot[1], k));
+        Hx += sgpr(field16(tot[2], k));
+    }
+    const uint32_t bm = dpad16((n_c + 7) / 8);
+    uint32_t mode_x = DCR_HI_NONE, size_x = 0, size_o = 0, Hfield_x = 0;
+    uint32_t off_pres = 0, off_hi_x = 0;
+    if (Kx) {
+        size_x = bm + dpad16(Kx);
+        off_hi_x = size_x;
+        if constexpr (W == 2) {
+            if (Hx) {
+                const uint32_t sparse = dpad16((Kx + 7) / 8) + dpad16(Hx);
+                if (sparse < dpad16(Kx)) {
+                    mode_x = DCR_HI_SPARSE;
+                    off_pres = size_x;
+                    off_hi_x = size_x + dpad16((Kx + 7) / 8);
+                    size_x += sparse;
+                    Hfield_x = Hx;
+                } else {
+                    mode_x = DCR_HI_DENSE;
+                    size_x += dpad16(Kx);
+                    Hfield_x = Kx;
+                }
+            }
+        }
+    }
+    if (Ko) size_o = bm + W * dpad16(Ko);
+    const uint32_t base_o = size_x;
+    const uint32_t tile_bytes = size_x + size_o;
+    const uint32_t nrec = (Kx ? 1u : 0u) + (Ko ? 1u : 0u);
+    const uint64_t agg = (uint64_t(nrec) << kRecShift) | (tile_bytes >> 4);
+
+    // publish the aggregate as early as possible
+    if (tid == 0) {
+        st_status(a.status + tile, (agg << kValShift) | (tile == 0 ? kFlagIncl : kFlagAgg));
+        if (Kx + Ko) atomicAdd(reinterpret_cast<unsigned long long*>(a.counter + 2), (unsigned long long)(Kx + Ko));
+    }
+
+    // ---- decoupled look-back (first wave): exclusive (records, payload/16)
+    if (tid < 64) {
+        const uint32_t lane = tid;
+        uint64_t excl = 0;
+        if (tile > 0) {
+            int64_t hi = int64_t(tile) - 1;
+            while (true) {
+                const int64_t idx = hi - int64_t(lane);
+                const uint64_t s = idx >= 0 ? ld_status(a.status + idx) : kFlagIncl;
+                const uint32_t flag = uint32_t(s & 3u);
+                const uint64_t incl_m = __ballot(flag == kFlagIncl);
+                const uint64_t zero_m = __ballot(flag == 0);
+                const uint32_t first = incl_m ? uint32_t(__ffsll((unsigned long long)incl_m) - 1) : 64u;
+                const uint64_t need = first >= 63 ? ~uint64_t(0) : ((uint64_t(2) << first) - 1);
+                if (zero_m & need) {
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                excl += wave_sum(lane <= first ? (s >> kValShift) : 0);
+                if (first < 64) break;
+                hi -= 64;
+            }
+            if (lane == 0) st_status(a.status + tile, ((excl + agg) << kValShift) | kFlagIncl);
+        }
+        if (lane == 0) S.excl = excl;
+    }
+    __syncthreads();
+
+    const uint64_t R = S.excl >> kRecShift;
+    const uint64_t P = (S.excl & kP16Mask) << 4;
+    const bool fits = (R + nrec) * DCR_DIRENT_BYTES <= a.dir_cap && P + tile_bytes <= a.payload_cap;
+    if (!fits || nrec == 0) return;   // uniform: nothing to write for this tile
+
+    // ---- write the records straight to the payload
+    uint8_t* out = a.payload + P;
+    const uint32_t pkx = dpad16(Kx), pko = dpad16(Ko);
+    // zero padding tails (each at most 15 bytes)
+    if (tid < 16) {
+        auto zpad = [&](uint32_t at, uint32_t from, uint32_t to) {
+            if (from + tid < to) out[at + from + tid] = 0;
+        };
+        if (Kx) {
+            zpad(bm, Kx, pkx);
+            if (mode_x == DCR_HI_SPARSE) zpad(off_hi_x, Hx, dpad16(Hx));
+            else if (mode_x == DCR_HI_DENSE) zpad(off_hi_x, Kx, pkx);
+        }
+        if (Ko) {
+            for (uint32_t pl = 0; pl < W; pl++) zpad(base_o + bm + pl * pko, Ko, pko);
+        }
+    }
+    const uint32_t hi_x_dense = sgpr(mode_x == DCR_HI_DENSE ? 1u : 0u);
+    const uint32_t hi_x_sparse = sgpr(mode_x == DCR_HI_SPARSE ? 1u : 0u);
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        const uint32_t g = tid + k * kThreads;
+        uint32_t b = meta[k] & 0xFFFFu;
+        const bool x = (meta[k] >> 31) == DCR_KIND_XOR;
+        // change bitmaps (LSB first) of both records, padding included
+        const uint32_t bx = x ? b : 0u, bo = x ? 0u : b;
+        uint32_t px = 0, po = 0;
+        if constexpr (W == 4) {      // nibble pairs: the odd lane's bits go to the even lane
+            px = __shfl_xor(bx, 1, 64);
+            po = __shfl_xor(bo, 1, 64);
+        }
+        if (g * V < bm * 8) {
+            if constexpr (W == 2) {
+                if (Kx) out[g] = uint8_t(bx);
+                if (Ko) out[base_o + g] = uint8_t(bo);
+            } else if constexpr (W == 1) {
+                if (Kx) reinterpret_cast<uint16_t*>(out)[g] = uint16_t(bx);
+                if (Ko) reinterpret_cast<uint16_t*>(out + base_o)[g] = uint16_t(bo);
+            } else {
+                if ((g & 1) == 0) {
+                    if (Kx) out[g / 2] = uint8_t(bx | (px << 4));
+                    if (Ko) out[base_o + g / 2] = uint8_t(bo | (po << 4));
+                }
+            }
+        }
+        if (!b) continue;
+        const v4u q = *reinterpret_cast<const v4u*>(S.pw[g]);
+        // byte planes of the group packed into 64-bit values
+        uint64_t pl0 = 0, pl1 = 0, ph = 0;
+        if constexpr (W == 1) {
+            pl0 = uint64_t(q.x) | (uint64_t(q.y) << 32);
+            pl1 = uint64_t(q.z) | (uint64_t(q.w) << 32);
+        } else if constexpr (W == 2) {
+            const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (uint32_t i = 0; i < 8; i++) {
+                const uint32_t e = (qq[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                pl0 |= uint64_t(e & 0xFFu) << (8 * i);
+                ph |= uint64_t(e >> 8) << (8 * i);
+            }
+        } else {
+            const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (uint32_t i = 0; i < 4; i++) {
+                pl0 |= uint64_t(qq[i] & 0xFFu) << (8 * i);
+                pl0 |= uint64_t((qq[i] >> 8) & 0xFFu) << (32 + 8 * i);
+                ph |= uint64_t((qq[i] >> 16) & 0xFFu) << (8 * i);
+                ph |= uint64_t(qq[i] >> 24) << (32 + 8 * i);
+            }
+        }
+        const uint32_t rb = x ? 0u : base_o;
+        const uint32_t pk = x ? pkx : pko;
+        uint8_t* lo = out + rb + bm;
+        uint32_t j = x ? kbase[0][k] + field16(cnt[0], k) : kbase[1][k] + field16(cnt[1], k);
+        uint32_t hr = kbase[2][k] + field16(cnt[2], k);
+#pragma nounroll
+        while (b) {
+            const uint32_t i = uint32_t(__ffs(b) - 1);
+            b &= b - 1;
+            if constexpr (W == 1) {
+                lo[j] = uint8_t((i < 8 ? pl0 : pl1) >> (8 * (i & 7)));
+            } else if constexpr (W == 2) {
+                lo[j] = uint8_t(pl0 >> (8 * i));
+                const uint8_t hb = uint8_t(ph >> (8 * i));
+                if (!x) {
+                    lo[pk + j] = hb;
+                } else if (hi_x_dense) {
+                    out[off_hi_x + j] = hb;
+                } else if (hi_x_sparse && hb) {
+                    atomicOr(&S.pres[j >> 5], 1u << (j & 31));
+                    out[off_hi_x + hr] = hb;
+                    hr++;
+                }
+            } else {
+                lo[j] = uint8_t(pl0 >> (8 * i));
+                lo[pk + j] = uint8_t(pl0 >> (32 + 8 * i));
+                lo[2 * pk + j] = uint8_t(ph >> (8 * i));
+                lo[3 * pk + j] = uint8_t(ph >> (32 + 8 * i));
+            }
+            j++;
+        }
+    }
+    if (tid < nrec) {
+        const bool x = Kx && tid == 0;
+        const uint32_t K = x ? Kx : Ko;
+        v4u e0, e1;
+        e0.x = ch.tensor;
+        e0.y = ch.chunk_idx;
+        e0.z = K;
+        const uint32_t hm = x ? mode_x : (W == 1 ? uint32_t(DCR_HI_NONE) : uint32_t(DCR_HI_DENSE));
+        e0.w = (x ? 0u : 1u) | (hm << 8) | (uint32_t(W) << 16);
+        const uint64_t off = P + (x ? 0u : base_o);
+        e1.x = uint32_t(off);
+        e1.y = uint32_t(off >> 32);
+        e1.z = x ? size_x : size_o;
+        e1.w = x ? Hfield_x : (W == 1 ? 0u : Ko);
+        v4u* de = reinterpret_cast<v4u*>(a.dir + (R + tid) * DCR_DIRENT_BYTES);
+        de[0] = e0;
+        de[1] = e1;
+    }
+    if (hi_x_sparse) {
+        __syncthreads();
+        const uint32_t nq = dpad16((Kx + 7) / 8) / 16;
+        for (uint32_t q = tid; q < nq; q += kThreads)
+            reinterpret_cast<v4u*>(out + off_pres)[q] = reinterpret_cast<const v4u*>(S.pres)[q];
+    }
+}
+
+// One workgroup per tile.  Tiles are claimed in increasing order from a
+// counter, so every tile a look-back waits on belongs to a workgroup that is
+// already running.
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_kernel(EncodeArgs a) {
+    __shared__ EncodeShared S;
+    if (threadIdx.x == 0) S.next = atomicAdd(a.counter, 1u);
+    __syncthreads();
+    const uint32_t tile = S.next;
+    if (tile >= a.n_tiles) return;
+    const DevChunk ch = a.chunks[tile];
+    const DevTensor td = a.tensors[ch.tensor];
+    if (td.w == 2) encode_tile<2>(a, S, tile, ch, td);
+    else if (td.w == 1) encode_tile<1>(a, S, tile, ch, td);
+    else encode_tile<4>(a, S, tile, ch, td);
+}
+
+// Per-element "scale bits changed" flags of the scale tensors that gate
+// block-scaled tensors.  One workgroup of 256 per scale chunk.
+__global__ __launch_bounds__(256) void scale_flags_kernel(const DevTensor* tensors, const DevChunk* chunks,
+                                                          const DevPiece* pieces, const uint32_t* scale_chunks,
+                                                          const uint8_t* const* old_sh, const uint8_t* const* new_sh,
+                                                          uint64_t* flags) {
+    const DevChunk ch = chunks[scale_chunks[blockIdx.x]];
+    const DevTensor td = tensors[ch.tensor];
+    constexpr uint32_t E = kChunkBytes / 4;
+    const uint64_t c0 = uint64_t(ch.chunk_idx) * E;
+    const uint32_t n_c = uint32_t(umin64(E, td.numel - c0));
+    const DevPiece* pc = pieces + ch.first_piece;
+    const uint32_t lane = threadIdx.x & 63u;
+    for (uint32_t e0 = (threadIdx.x & ~63u); e0 < n_c; e0 += 256) {
+        const uint32_t e = e0 + lane;
+        bool changed = false;
+        if (e < n_c) {
+            const uint32_t p = find_piece(pc, ch.n_pieces, e);
+            const uint64_t off = (pc[p].shard_elem_off + (e - pc[p].canon_start)) * 4;
+            changed = *reinterpret_cast<const uint32_t*>(old_sh[pc[p].shard] + off) !=
+                      *reinterpret_cast<const uint32_t*>(new_sh[pc[p].shard] + off);
+        }
+        const uint64_t m = __ballot(changed);
+        if (lane == 0) flags[(td.scale_bit_off + c0 + e0) >> 6] = m;
+    }
+}
+
+// Stream header and encode result from the last tile's inclusive prefix.
+__global__ void encode_finalize_kernel(const uint64_t* status, uint32_t n_tiles, const uint32_t* counter,
+                                       uint32_t mode, uint64_t base_v, uint64_t new_v, uint64_t fp,
+                                       uint64_t dir_cap, uint64_t payload_cap, uint8_t* header,
+                                       dcr_encode_result* res) {
+    if (threadIdx.x != 0) return;
+    const uint64_t v = n_tiles ? (ld_status(status + n_tiles - 1) >> kValShift) : 0;
+    const uint64_t nrec = v >> kRecShift, pbytes = (v & kP16Mask) << 4;
+    const bool fits = nrec * DCR_DIRENT_BYTES <= dir_cap && pbytes <= payload_cap;
+    uint4* h = reinterpret_cast<uint4*>(header);
+    h[0] = make_uint4(DCR_MAGIC, DCR_FORMAT_VERSION | (mode << 16), DCR_CHUNK_BYTES, 0u);
+    h[1] = make_uint4(uint32_t(base_v), uint32_t(base_v >> 32), uint32_t(new_v), uint32_t(new_v >> 32));
+    h[2] = make_uint4(uint32_t(fp), uint32_t(fp >> 32), uint32_t(nrec), uint32_t(nrec >> 32));
+    h[3] = make_uint4(uint32_t(pbytes), uint32_t(pbytes >> 32), 0u, 0u);
+    const uint64_t changed = *reinterpret_cast<const uint64_t*>(counter + 2);
+    uint4* r = reinterpret_cast<uint4*>(res);
+    r[0] = make_uint4(uint32_t(nrec), uint32_t(nrec >> 32), uint32_t(pbytes), uint32_t(pbytes >> 32));
+    r[1] = make_uint4(uint32_t(changed), uint32_t(changed >> 32), uint32_t(fits ? DCR_OK : DCR_E_CAPACITY), 0u);
+}
+
+__global__ void fill_u64_kernel(uint64_t* p, uint64_t n, uint64_t v) {
+    for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x)
+        p[i] = v;
+}
+
+// ------------------------------------------------------------------- apply
+
+struct ApplyArgs {
+    const DevTensor* tensors;
+    uint8_t* const* canon;
+    const uint8_t* dir;
+    const uint8_t* payload;
+    uint8_t* flags;
+    dcr_apply_result* result;
+    uint64_t payload_bytes;
+    uint64_t first;
+    uint32_t n_tensors;
+    uint32_t retry;          // 1: overwrite retry (ignore flags, OW records only)
+};
+
+struct ApplyShared {
+    alignas(16) uint8_t stage[kStageBytes];
+    uint32_t pres_pre[1024];        // SPARSE: set presence bits before each 32-bit word
+    uint64_t scan[2 * (kThreads / 64) + 1];
+    uint32_t ent[8];                // the directory entry
+    uint32_t state;                 // 0 invalid, 1 skip, 2 apply
+    uint32_t n_c;                   // elements of the record's chunk
+    uint32_t bad;                   // content check failed
+};
+
+__device__ __forceinline__ uint32_t rec_bytes(uint32_t n_c, uint32_t w, uint32_t kind, uint32_t K, uint32_t hm,
+                                              uint32_t H) {
+    uint32_t sz = dpad16((n_c + 7) / 8) + dpad16(K);
+    if (w == 2 && kind == DCR_KIND_XOR) {
+        if (hm == DCR_HI_SPARSE) sz += dpad16((K + 7) / 8) + dpad16(H);
+        else if (hm == DCR_HI_DENSE) sz += dpad16(K);
+    } else if (w == 2) sz += dpad16(K);
+    else if (w == 4) sz += 3 * dpad16(K);
+    return sz;
+}
+
+// Structural check of one directory entry (thread 0).
+__device__ __forceinline__ bool entry_ok(const ApplyArgs& a, const uint32_t (&e)[8], uint32_t& n_c_out) {
+    const uint32_t t = e[0], c = e[1], K = e[2];
+    const uint32_t kind = e[3] & 0xFF, hm = (e[3] >> 8) & 0xFF, w = (e[3] >> 16) & 0xFF, z = e[3] >> 24;
+    const uint64_t off = uint64_t(e[4]) | (uint64_t(e[5]) << 32);
+    const uint32_t sz = e[6], H = e[7];
+    if (t >= a.n_tensors || z != 0) return false;
+    const DevTensor td = a.tensors[t];
+    if (w != td.w || c >= td.n_chunks) return false;
+    const uint64_t E = kChunkBytes / w;
+    const uint32_t n_c = uint32_t(umin64(E, td.numel - uint64_t(c) * E));
+    if (K == 0 || K > n_c || kind > DCR_KIND_OW) return false;
+    if (a.retry && kind != DCR_KIND_OW) return false;
+    if (kind == DCR_KIND_XOR && w == 4) return false;
+    if (w == 1) {
+        if (hm != DCR_HI_NONE || H != 0) return false;
+    } else if (kind == DCR_KIND_OW) {
+        if (hm != DCR_HI_DENSE || H != K) return false;
+    } else if (hm == DCR_HI_NONE) {
+        if (H != 0) return false;
+    } else if (hm == DCR_HI_SPARSE) {
+        if (H == 0 || H > K || !(dpad16((K + 7) / 8) + dpad16(H) < dpad16(K))) return false;
+    } else if (hm == DCR_HI_DENSE) {
+        if (H != K) return false;
+    } else {
+        return false;
+    }
+    if (sz != rec_bytes(n_c, w, kind, K, hm, H)) return false;
+    if ((off & 15u) != 0 || off > a.payload_bytes || sz > a.payload_bytes - off) return false;
+    n_c_out = n_c;
+    return true;
+}
+
+template <int W>
+__device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uint32_t n_c) {
+    constexpr uint32_t V = 16 / W;
+    constexpr uint32_t E = kChunkBytes / W;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t t = S.ent[0], c = S.ent[1], K = S.ent[2];
+    const uint32_t kind = S.ent[3] & 0xFF, hm = (S.ent[3] >> 8) & 0xFF;
+    const uint64_t off = uint64_t(S.ent[4]) | (uint64_t(S.ent[5]) << 32);
+    const uint32_t sz = S.ent[6], H = S.ent[7];
+    const uint32_t bm = dpad16((n_c + 7) / 8);
+    const uint32_t lo = bm;
+    const uint32_t pres = lo + dpad16(K);
+    const uint32_t hi = hm == DCR_HI_SPARSE ? pres + dpad16((K + 7) / 8) : pres;
+
+    // stage the record
+    const uint4* src = reinterpret_cast<const uint4*>(a.payload + off);
+    for (uint32_t q = tid; q < sz / 16; q += kThreads) reinterpret_cast<uint4*>(S.stage)[q] = src[q];
+    if (tid == 0) S.bad = 0;
+    __syncthreads();
+
+    // bitmap bits per 16-byte group; nothing may be set at or past n_c
+    uint32_t bits[kVecsPerThread];
+    uint64_t cnt[1] = {0};
+    bool bad = false;
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        const uint32_t g = tid + k * kThreads;
+        uint32_t b = 0;
+        if (g * V < bm * 8) {   // the group's bits lie inside the padded bitmap
+            if constexpr (W == 2) b = S.stage[g];
+            else if constexpr (W == 1) b = reinterpret_cast<const uint16_t*>(S.stage)[g];
+            else b = (S.stage[g / 2] >> (4 * (g & 1))) & 0xFu;
+        }
+        const uint32_t first = g * V;
+        const uint32_t valid = first >= n_c ? 0u : (n_c - first >= V ? (1u << V) - 1u : (1u << (n_c - first)) - 1u);
+        if (b & ~valid) bad = true;
+        bits[k] = b & valid;
+        cnt[0] |= uint64_t(__popc(bits[k])) << (16 * k);
+    }
+    // SPARSE: presence bits, popcount H, nothing at or past K; word prefix counts
+    uint64_t pc1[1] = {0};
+    uint32_t pword = 0;
+    const uint32_t n_pw = dpad16((K + 7) / 8) / 4;
+    if (hm == DCR_HI_SPARSE && tid < n_pw) {
+        pword = reinterpret_cast<const uint32_t*>(S.stage + pres)[tid];
+        const uint32_t b0 = tid * 32;
+        const uint32_t vmask = b0 >= K ? 0u : (K - b0 >= 32 ? 0xFFFFFFFFu : ((1u << (K - b0)) - 1u));
+        if (pword & ~vmask) bad = true;
+        pc1[0] = __popc(pword);
+    }
+    uint64_t tot[1], ptot[1];
+    block_excl_scan<1>(cnt, tot, S.scan);
+    if (hm == DCR_HI_SPARSE) {
+        block_excl_scan<1>(pc1, ptot, S.scan);
+        if (tid < n_pw) S.pres_pre[tid] = uint32_t(pc1[0]);
+        if (tid == 0 && ptot[0] != H) bad = true;
+    }
+    uint32_t total = 0, base[kVecsPerThread];
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        base[k] = total + field16(cnt[0], k);
+        total += field16(tot[0], k);
+    }
+    if (tid == 0 && total != K) bad = true;
+    if (bad) atomicOr(&S.bad, 1u);
+    __syncthreads();
+    if (S.bad) return;   // refused before any write
+
+    // read-modify-write of every touched 16-byte group; the group's new words
+    // are assembled in two 64-bit values by a set-bit loop with dynamic shifts
+    uint8_t* dst = a.canon[t] + uint64_t(c) * E * W;
+    const uint32_t* pw32 = reinterpret_cast<const uint32_t*>(S.stage + pres);
+    const uint32_t pk = dpad16(K);
+    const bool is_xor = kind == DCR_KIND_XOR;
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        uint32_t b = bits[k];
+        if (!b) continue;
+        const uint32_t g = tid + k * kThreads;
+        uint64_t val0 = 0, val1 = 0, msk0 = 0, msk1 = 0;
+        uint32_t j = base[k];
+        const uint32_t bcopy = b;
+        while (b) {
+            const uint32_t i = uint32_t(__ffs(b) - 1);
+            b &= b - 1;
+            uint32_t v = S.stage[lo + j];
+            if constexpr (W == 2) {
+                if (!is_xor || hm == DCR_HI_DENSE) {
+                    v |= uint32_t(S.stage[hi + j]) << 8;
+                } else if (hm == DCR_HI_SPARSE) {
+                    const uint32_t pwj = pw32[j >> 5];
+                    if ((pwj >> (j & 31)) & 1u) {
+                        const uint32_t rank = S.pres_pre[j >> 5] + __popc(pwj & ((1u << (j & 31)) - 1u));
+                        v |= uint32_t(S.stage[hi + rank]) << 8;
+                    }
+                }
+            } else if constexpr (W == 4) {
+                v |= uint32_t(S.stage[lo + pk + j]) << 8;
+                v |= uint32_t(S.stage[lo + 2 * pk + j]) << 16;
+                v |= uint32_t(S.stage[lo + 3 * pk + j]) << 24;
+            }
+            constexpr uint32_t EB = 8 * W;                   // element bits
+            constexpr uint64_t EM = (W == 4) ? 0xFFFFFFFFull : ((1ull << EB) - 1);
+            const uint32_t bitpos = i * EB;                  // 0 .. 127
+            const uint32_t sh = bitpos & 63;
+            if (bitpos < 64) { val0 |= uint64_t(v) << sh; msk0 |= EM << sh; }
+            else { val1 |= uint64_t(v) << sh; msk1 |= EM << sh; }
+            j++;
+        }
+        uint8_t* gp = dst + uint64_t(g) * 16;
+        if ((g + 1) * V <= n_c) {
+            v4u w4 = *reinterpret_cast<const v4u*>(gp);
+            uint64_t q0 = uint64_t(w4.x) | (uint64_t(w4.y) << 32);
+            uint64_t q1 = uint64_t(w4.z) | (uint64_t(w4.w) << 32);
+            q0 = is_xor ? (q0 ^ val0) : ((q0 & ~msk0) | val0);
+            q1 = is_xor ? (q1 ^ val1) : ((q1 & ~msk1) | val1);
+            v4u r4;
+            r4.x = uint32_t(q0); r4.y = uint32_t(q0 >> 32); r4.z = uint32_t(q1); r4.w = uint32_t(q1 >> 32);
+            *reinterpret_cast<v4u*>(gp) = r4;
+        } else {
+            // tail group of a tensor: element accesses only inside the tensor
+            uint32_t bb = bcopy;
+            while (bb) {
+                const uint32_t i = uint32_t(__ffs(bb) - 1);
+                bb &= bb - 1;
+                if (g * V + i >= n_c) break;
+                const uint32_t bitpos = i * 8 * W;
+                const uint32_t v = uint32_t(((bitpos < 64) ? val0 : val1) >> (bitpos & 63));
+                if constexpr (W == 1) { gp[i] = is_xor ? uint8_t(gp[i] ^ v) : uint8_t(v); }
+                else if constexpr (W == 2) {
+                    uint16_t* p = reinterpret_cast<uint16_t*>(gp) + i;
+                    *p = is_xor ? uint16_t(*p ^ v) : uint16_t(v);
+                } else {
+                    uint32_t* p = reinterpret_cast<uint32_t*>(gp) + i;
+                    *p = is_xor ? (*p ^ v) : v;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        if (!a.retry) {
+            __threadfence();
+            a.flags[r] = 1;
+        }
+        atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_applied), 1ull);
+    }
+}
+
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void apply_kernel(ApplyArgs a) {
+    __shared__ ApplyShared S;
+    const uint64_t r = a.first + blockIdx.x;
+    uint32_t n_c = 0;
+    if (threadIdx.x == 0) {
+        const uint4* de = reinterpret_cast<const uint4*>(a.dir + r * DCR_DIRENT_BYTES);
+        const uint4 e0 = de[0], e1 = de[1];
+        uint32_t e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+        for (int i = 0; i < 8; i++) S.ent[i] = e[i];
+        uint32_t st;
+        if (!entry_ok(a, e, n_c)) st = 0;
+        else if (!a.retry && a.flags[r]) st = 1;
+        else st = 2;
+        S.state = st;
+        S.n_c = n_c;
+    }
+    __syncthreads();
+    const uint32_t st = S.state;
+    n_c = S.n_c;
+    if (st == 1) {
+        if (threadIdx.x == 0) atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_skipped), 1ull);
+        return;
+    }
+    if (st == 2) {
+        const uint32_t w = (S.ent[3] >> 16) & 0xFF;
+        if (w == 2) apply_record<2>(a, S, r, n_c);
+        else if (w == 1) apply_record<1>(a, S, r, n_c);
+        else apply_record<4>(a, S, r, n_c);
+        if (!S.bad) return;
+    }
+    if (threadIdx.x == 0) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_invalid), 1ull);
+        atomicMin(reinterpret_cast<unsigned long long*>(&a.result->first_invalid), (unsigned long long)r);
+    }
+}
+
+__global__ void apply_init_kernel(dcr_apply_result* res) {
+    if (threadIdx.x == 0) {
+        uint4* r = reinterpret_cast<uint4*>(res);
+        r[0] = make_uint4(0, 0, 0, 0);
+        r[1] = make_uint4(0, 0, 0xFFFFFFFFu, 0xFFFFFFFFu);
+    }
+}
+
+// ------------------------------------------------------------- host side
+
+static int32_t fail(int32_t rc, const std::string& m) {
+    set_error(m);
+    return rc;
+}
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static int32_t hip_check(hipError_t e, const char* what) {
+    if (e == hipSuccess) return DCR_OK;
+    return fail(DCR_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class T>
+static const T* tab(const Plan& p, uint64_t off) {
+    return reinterpret_cast<const T*>(static_cast<const uint8_t*>(p.dev_tables) + off);
+}
+
+static int32_t copy_ptrs(void* dst, const void* const* src, uint64_t n, hipStream_t s) {
+    if (!n) return DCR_OK;
+    return hip_check(hipMemcpyAsync(dst, src, n * sizeof(void*), hipMemcpyHostToDevice, s), "pointer table copy");
+}
+
+static int32_t check_header(const Plan& p, const dcr_stream_header* h, uint64_t expected_base) {
+    if (!h) return fail(DCR_E_INVAL, "header is NULL");
+    if (h->magic != DCR_MAGIC || h->format_version != DCR_FORMAT_VERSION || h->chunk_bytes != DCR_CHUNK_BYTES ||
+        h->reserved0 != 0 || h->reserved1 != 0)
+        return fail(DCR_E_FORMAT, "stream header: bad magic / version / chunk size");
+    if (h->stream_kind > DCR_MODE_RETRY) return fail(DCR_E_FORMAT, "stream header: bad stream kind");
+    if (h->plan_fingerprint != p.fingerprint) return fail(DCR_E_FORMAT, "stream header: plan fingerprint mismatch");
+    if (h->base_version != expected_base) return fail(DCR_E_VERSION, "stream base_version != expected base version");
+    return DCR_OK;
+}
+
+static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_stream_header* hdr,
+                            const void* dir, const void* payload, uint8_t* flags, uint64_t first, uint64_t n,
+                            dcr_apply_result* res, void* ws, uint64_t ws_bytes, hipStream_t s, bool retry) {
+    const Plan& p = *plan;
+    const uint32_t nT = uint32_t(p.tensors.size());
+    if ((n && !dir) || (n && !payload) || !res || !ws) return fail(DCR_E_INVAL, "NULL device buffer");
+    if (!al16(dir) || !al16(payload) || !al16(res) || !al16(ws)) return fail(DCR_E_INVAL, "buffer not 16-byte aligned");
+    if (!retry && n && !flags) return fail(DCR_E_INVAL, "applied_flags is NULL");
+    if (ws_bytes < p.ws_bytes) return fail(DCR_E_CAPACITY, "workspace too small");
+    if (n > 0x7FFFFFFFull) return fail(DCR_E_INVAL, "too many records in one call");
+    if (nT && !canon) return fail(DCR_E_INVAL, "canon is NULL");
+    for (uint32_t t = 0; t < nT; t++) {
+        if (p.tensors[t].numel && !canon[t]) return fail(DCR_E_INVAL, "canonical tensor " + std::to_string(t) + " is NULL");
+        if (!al16(canon[t])) return fail(DCR_E_INVAL, "canonical tensor " + std::to_string(t) + " not 16-byte aligned");
+    }
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    int32_t rc = copy_ptrs(wsb + p.ws_canon, reinterpret_cast<const void* const*>(canon), nT, s);
+    if (rc) return rc;
+    hipLaunchKernelGGL(apply_init_kernel, dim3(1), dim3(64), 0, s, res);
+    if (n) {
+        ApplyArgs a;
+        a.tensors = tab<DevTensor>(p, p.off_tensors);
+        a.canon = reinterpret_cast<uint8_t* const*>(wsb + p.ws_canon);
+        a.dir = static_cast<const uint8_t*>(dir);
+        a.payload = static_cast<const uint8_t*>(payload);
+        a.flags = flags;
+        a.result = res;
+        a.payload_bytes = hdr->payload_bytes;
+        a.first = first;
+        a.n_tensors = nT;
+        a.retry = retry ? 1u : 0u;
+        hipLaunchKernelGGL(apply_kernel, dim3(uint32_t(n)), dim3(kThreads), 0, s, a);
+    }
+    return hip_check(hipGetLastError(), "apply launch");
+}
+
+}  // namespace dcr
+
+extern "C" {
+
+int32_t dcr_plan_upload(dcr_plan* plan, void* dev_tables, uint64_t bytes, void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan || !dev_tables) return fail(DCR_E_INVAL, "NULL argument");
+    if (!al16(dev_tables)) return fail(DCR_E_INVAL, "dev_tables not 16-byte aligned");
+    if (bytes < plan->table_bytes) return fail(DCR_E_CAPACITY, "dev_tables too small");
+    int32_t rc = hip_check(hipMemcpyAsync(dev_tables, plan->blob.data(), plan->table_bytes, hipMemcpyHostToDevice,
+                                          static_cast<hipStream_t>(stream)),
+                           "plan upload");
+    if (rc) return rc;
+    plan->dev_tables = dev_tables;
+    return DCR_OK;
+}
+
+int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards, uint32_t mode,
+                   uint64_t base_version, uint64_t new_version, void* header_dev, void* dir_dev, uint64_t dir_cap,
+                   void* payload_dev, uint64_t payload_cap, dcr_encode_result* result_dev, void* workspace_dev,
+                   uint64_t ws_bytes, void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
+    const Plan& p = *plan;
+    if (!p.dev_tables) return fail(DCR_E_INVAL, "plan not uploaded");
+    if (mode > DCR_MODE_RETRY) return fail(DCR_E_INVAL, "bad mode");
+    if (!header_dev || !result_dev || !workspace_dev) return fail(DCR_E_INVAL, "NULL device buffer");
+    if ((dir_cap && !dir_dev) || (payload_cap && !payload_dev)) return fail(DCR_E_INVAL, "NULL device buffer");
+    if (!al16(header_dev) || !al16(dir_dev) || !al16(payload_dev) || !al16(result_dev) || !al16(workspace_dev))
+        return fail(DCR_E_INVAL, "buffer not 16-byte aligned");
+    if (ws_bytes < p.ws_bytes) return fail(DCR_E_CAPACITY, "workspace too small");
+    const uint32_t nS = uint32_t(p.shard_bytes.size());
+    if (nS && (!old_shards || !new_shards)) return fail(DCR_E_INVAL, "shard arrays are NULL");
+    for (uint32_t s = 0; s < nS; s++) {
+        if (p.shard_bytes[s] && (!old_shards[s] || !new_shards[s]))
+            return fail(DCR_E_INVAL, "shard " + std::to_string(s) + " is NULL");
+        if (!al16(old_shards[s]) || !al16(new_shards[s]))
+            return fail(DCR_E_INVAL, "shard " + std::to_string(s) + " not 16-byte aligned");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace_dev);
+    int32_t rc = copy_ptrs(ws + p.ws_old, old_shards, nS, s);
+    if (!rc) rc = copy_ptrs(ws + p.ws_new, new_shards, nS, s);
+    if (rc) return rc;
+    const uint32_t n_tiles = uint32_t(p.chunks.size());
+    // look-back status words and counters start at zero
+    const uint64_t n_zero = (p.ws_old) / 8;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(uint32_t(std::min<uint64_t>((n_zero + 255) / 256, 4096))), dim3(256), 0,
+                       s, reinterpret_cast<uint64_t*>(ws), n_zero, 0ull);
+    const auto* tensors = tab<DevTensor>(p, p.off_tensors);
+    const auto* chunks = tab<DevChunk>(p, p.off_chunks);
+    const auto* pieces = tab<DevPiece>(p, p.off_pieces);
+    const auto* old_sh = reinterpret_cast<const uint8_t* const*>(ws + p.ws_old);
+    const auto* new_sh = reinterpret_cast<const uint8_t* const*>(ws + p.ws_new);
+    auto* scale_flags = reinterpret_cast<uint64_t*>(ws + p.ws_scale);
+    if (mode == DCR_MODE_DELTA && !p.scale_chunks.empty())
+        hipLaunchKernelGGL(scale_flags_kernel, dim3(uint32_t(p.scale_chunks.size())), dim3(256), 0, s, tensors,
+                           chunks, pieces, tab<uint32_t>(p, p.off_scale_chunks), old_sh, new_sh, scale_flags);
+    uint32_t* counter = reinterpret_cast<uint32_t*>(ws + p.ws_counter);
+    if (n_tiles) {
+        EncodeArgs a;
+        a.tensors = tensors;
+        a.chunks = chunks;
+        a.pieces = pieces;
+        a.old_sh = old_sh;
+        a.new_sh = new_sh;
+        a.scale_flags = scale_flags;
+        a.status = reinterpret_cast<uint64_t*>(ws + p.ws_status);
+        a.counter = counter;
+        a.dir = static_cast<uint8_t*>(dir_dev);
+        a.payload = static_cast<uint8_t*>(payload_dev);
+        a.dir_cap = dir_cap;
+        a.payload_cap = payload_cap;
+        a.n_tiles = n_tiles;
+        a.mode = mode;
+        hipLaunchKernelGGL(encode_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
+    }
+    hipLaunchKernelGGL(encode_finalize_kernel, dim3(1), dim3(64), 0, s,
+                       reinterpret_cast<const uint64_t*>(ws + p.ws_status), n_tiles, counter, mode, base_version,
+                       new_version, p.fingerprint, dir_cap, payload_cap, static_cast<uint8_t*>(header_dev),
+                       result_dev);
+    return hip_check(hipGetLastError(), "encode launch");
+}
+
+int32_t dcr_apply(const dcr_plan* plan, void* const* canon, const dcr_stream_header* header, const void* dir_dev,
+                  const void* payload_dev, uint8_t* applied_flags_dev, uint64_t first_record, uint64_t n_records,
+                  uint64_t expected_base_version, dcr_apply_result* result_dev, void* workspace_dev,
+                  uint64_t ws_bytes, void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
+    if (!plan->dev_tables) return fail(DCR_E_INVAL, "plan not uploaded");
+    int32_t rc = check_header(*plan, header, expected_base_version);
+    if (rc) return rc;
+    if (first_record > header->n_records || n_records > header->n_records - first_record)
+        return fail(DCR_E_INVAL, "record range outside the stream");
+    return launch_apply(plan, canon, header, dir_dev, payload_dev, applied_flags_dev, first_record, n_records,
+                        result_dev, workspace_dev, ws_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+int32_t dcr_apply_overwrite_retry(const dcr_plan* plan, void* const* canon, const dcr_stream_header* header,
+                                  const void* dir_dev, const void* payload_dev, uint64_t expected_base_version,
+                                  dcr_apply_result* result_dev, void* workspace_dev, uint64_t ws_bytes,
+                                  void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
+    if (!plan->dev_tables) return fail(DCR_E_INVAL, "plan not uploaded");
+    int32_t rc = check_header(*plan, header, expected_base_version);
+    if (rc) return rc;
+    if (header->stream_kind != DCR_MODE_RETRY) return fail(DCR_E_FORMAT, "not a RETRY stream");
+    return launch_apply(plan, canon, header, dir_dev, payload_dev, nullptr, 0, header->n_records, result_dev,
+                        workspace_dev, ws_bytes, static_cast<hipStream_t>(stream), true);
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// synth.hip -- GPU side of the seeded synthetic input generator (untimed).
+//
+// Implements the same definition as bit_exact_xor_amd/synth.py, element for
+// element: the i-th output of a SplitMix64 sequence (Steele, Lea, Flood,
+// "Fast splittable pseudorandom number generators", OOPSLA 2014) keyed per
+// generated region, turned into BF16 N(0, 0.02) weights (Irwin-Hall sum of
+// four 16-bit lanes, one fp32 multiply, round-to-nearest-even to BF16), uint8
+// codes or fp32 scales, and the changed element of a new version.  Holds
+// nothing of the delta method itself.  Built into its own library,
+// libdcr_synth.so.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+__device__ __forceinline__ uint64_t hash_at(uint64_t key, uint64_t i) { return mix64(key + (i + 1) * kGamma); }
+
+__device__ __forceinline__ uint16_t bf16_old(uint64_t key_old, uint64_t i, uint32_t scale_bits) {
+    const uint64_t h = hash_at(key_old, i);
+    const int32_t s = int32_t((h & 0xFFFF) + ((h >> 16) & 0xFFFF) + ((h >> 32) & 0xFFFF) + (h >> 48));
+    const float x = float(s - 131070) * __uint_as_float(scale_bits);   // exact convert, one rounded multiply
+    const uint32_t b = __float_as_uint(x);
+    return uint16_t((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ uint16_t bf16_step(uint16_t old, bool up) {
+    const uint32_t o = old, mag = o & 0x7FFFu;
+    if (mag == 0) return uint16_t(o | 1u);
+    return uint16_t((up && mag < 0x7F7Fu) ? o + 1u : o - 1u);
+}
+
+struct Region {
+    uint64_t elem_off;   // first element in the shard
+    uint64_t n;          // elements
+    uint64_t key_old, key_chg;
+    uint64_t thr;        // change iff low 32 bits of the change hash < thr
+    uint64_t row_len;    // GEN_BF16_HOT: elements per row
+    uint64_t hot_off;    // GEN_BF16_HOT: first index into the hot-row list
+    uint32_t kind;       // 0 BF16, 1 U8, 2 F32 scale, 3 BF16 with hot rows
+    uint32_t n_hot;      // GEN_BF16_HOT: hot rows (sorted)
+};
+
+__device__ __forceinline__ bool is_hot(const uint32_t* hot, uint32_t n, uint64_t row) {
+    uint32_t lo = 0, hi = n;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (hot[mid] < row) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo < n && hot[lo] == row;
+}
+
+// One thread per element of one region; version 0 = old, 1 = new.
+__global__ void gen_kernel(uint8_t* shard, Region r, const uint32_t* hot, uint32_t version, uint32_t scale_bits) {
+    const uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x;
+    if (i >= r.n) return;
+    const uint64_t e = r.elem_off + i;
+    if (r.kind == 0 || r.kind == 3) {
+        const uint16_t old = bf16_old(r.key_old, i, scale_bits);
+        uint16_t v = old;
+        if (version) {
+            const uint64_t h = hash_at(r.key_chg, i);
+            bool changed = (h & 0xFFFFFFFFull) < r.thr;
+            if (r.kind == 3 && r.n_hot) changed = changed || is_hot(hot + r.hot_off, r.n_hot, i / r.row_len);
+            if (changed) v = bf16_step(old, ((h >> 32) & 1u) != 0);
+        }
+        reinterpret_cast<uint16_t*>(shard)[e] = v;
+    } else if (r.kind == 1) {
+        const uint8_t old = uint8_t(hash_at(r.key_old, i) & 0xFF);
+        uint8_t v = old;
+        if (version) {
+            const uint64_t h = hash_at(r.key_chg, i);
+            if ((h & 0xFFFFFFFFull) < r.thr) {
+                const uint32_t sh = uint32_t((h >> 33) & 1u) * 4u;
+                const uint32_t nib = (old >> sh) & 0xFu;
+                const uint32_t nn = (nib + 1u + uint32_t((h >> 34) % 15u)) & 0xFu;
+                v = uint8_t((old & ~(0xFu << sh)) | (nn << sh));
+            }
+        }
+        shard[e] = v;
+    } else {
+        const uint32_t old = 0x3B000000u + uint32_t(hash_at(r.key_old, i) & 0x00FFFFFFull);
+        uint32_t v = old;
+        if (version) {
+            const uint64_t h = hash_at(r.key_chg, i);
+            if ((h & 0xFFFFFFFFull) < r.thr) v = old ^ (1u + uint32_t((h >> 40) & 0x3FFu));
+        }
+        reinterpret_cast<uint32_t*>(shard)[e] = v;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Fill elements [elem_off, elem_off + n) of `shard` (device memory) with one
+// generated region.  `hot` is a device array of sorted hot-row indices (or
+// NULL).  Returns 0 or a HIP error code.
+int32_t dcr_synth_fill(void* shard, uint64_t elem_off, uint64_t n, uint32_t kind, uint64_t key_old,
+                       uint64_t key_chg, uint64_t thr, uint64_t row_len, const uint32_t* hot, uint64_t hot_off,
+                       uint32_t n_hot, uint32_t version, uint32_t scale_bits, void* stream) {
+    if (n == 0) return 0;
+    Region r{elem_off, n, key_old, key_chg, thr, row_len ? row_len : 1, hot_off, kind, n_hot};
+    const uint64_t blocks = (n + 255) / 256;
+    if (blocks > 0x7FFFFFFFull) return int32_t(hipErrorInvalidValue);
+    hipLaunchKernelGGL(gen_kernel, dim3(uint32_t(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint8_t*>(shard), r, hot, version, scale_bits);
+    return int32_t(hipGetLastError());
+}
+
+}  // extern "C"

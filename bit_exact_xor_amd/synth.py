@@ -641,3 +641,58 @@ def _assemble_random(recipes, shards, n_tensors):
         else:
             raise ValueError(how)
     return out
+
+
+# ---------------------------------------------------------- GPU generation
+
+_synth_lib = None
+
+
+def _load_synth():
+    """libdcr_synth.so: the same generator definition on the GPU (untimed input setup)."""
+    global _synth_lib
+    if _synth_lib is None:
+        import ctypes
+        import os
+        p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdcr_synth.so")
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with `python -m bit_exact_xor_amd.build`")
+        lib = ctypes.CDLL(p)
+        U64, U32, P = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
+        lib.dcr_synth_fill.restype = ctypes.c_int32
+        lib.dcr_synth_fill.argtypes = [P, U64, U64, U32, U64, U64, U64, U64, P, U64, U32, U32, U32, P]
+        _synth_lib = lib
+    return _synth_lib
+
+
+def alloc_shards(lay: Layout, device="cuda", align=256):
+    """One device buffer per version holding every shard at an aligned offset."""
+    import torch
+    offs, total = [], 0
+    for s in range(lay.n_shards):
+        offs.append(total)
+        total += (lay.shard_bytes(s) + align - 1) // align * align
+    buf = torch.empty(max(total, align), dtype=torch.uint8, device=device)
+    return buf, [buf[o:o + lay.shard_bytes(s)] for s, o in enumerate(offs)]
+
+
+def fill_shards_gpu(lay: Layout, shards, version: int, stream=None):
+    """Generate every region of the layout into device shards (version 0 / 1)."""
+    import torch
+    lib = _load_synth()
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    hot_lists = [r.hot_rows for r in lay.regions if r.hot_rows is not None and len(r.hot_rows)]
+    hot_dev = None
+    if hot_lists:
+        hot_dev = torch.from_numpy(np.concatenate(hot_lists).astype(np.uint32).view(np.int32)).to(shards[0].device)
+    hot_off = 0
+    for r in lay.regions:
+        n_hot = 0 if r.hot_rows is None else len(r.hot_rows)
+        rc = lib.dcr_synth_fill(shards[r.shard].data_ptr(), r.elem_off, r.n, r.kind, r.key_old, r.key_chg,
+                                r.thr, r.row_len, hot_dev.data_ptr() if n_hot else None, hot_off, n_hot,
+                                version, SCALE_BITS, stream or None)
+        if rc:
+            raise RuntimeError(f"dcr_synth_fill failed: {rc}")
+        hot_off += n_hot
+    return hot_dev  # keep alive until the fills have run

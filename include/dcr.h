@@ -1,0 +1,255 @@
+/*
+ * dcr.h -- C-ABI of the MI355X (gfx950) bit-exact delta encode / apply library.
+ *
+ * The library implements the data-parallel core of bit-exact delta-compressed
+ * refit as described on the NeMo-DCR pages:
+ *   - the owner of each training shard compares new against the last committed
+ *     weights on their stored bits, not as float values, so +0/-0 and other
+ *     sign flips are changes (ai-feeds summary "Method / input and change
+ *     detection"; tokendh blog "shard owner");
+ *   - changed elements are projected by a fixed affine map from the shard's
+ *     local index to canonical checkpoint coordinates (ai-feeds summary "key
+ *     modules" 1; ai.info abstract); non-affine ones (fused QKV, shared
+ *     scales) become overwrite records (ai-feeds "key modules" 2; tokendh
+ *     "shard owner");
+ *   - affine changes travel as XOR masks, the rest as overwrites, in one delta
+ *     stream (ai-feeds "key modules" 2-3; tokendh "XOR or overwrite"); the
+ *     delta algebra is mask = old ^ new, new = old ^ mask on a flat bit buffer
+ *     (humansand "weight teleportation" page, "Delta update algebra");
+ *   - the receiver applies the records in place with per-record dedup flags,
+ *     since a XOR applied twice undoes itself (tokendh "XOR or overwrite"), and
+ *     a retry re-applies the whole change set as overwrites, which is
+ *     idempotent (tokendh "no backup copy"; ai.info abstract).
+ *
+ * Record format (the pages fix none; this is the library's own): per 64 KiB
+ * chunk of each canonical tensor, at most one XOR and one overwrite record,
+ * each = change bitmap | low byte plane | upper planes, every section
+ * zero-padded to 16 bytes; XOR records on 2-byte elements elide zero high
+ * bytes with a presence bitmap when that is strictly smaller (SPARSE), keep
+ * all high bytes otherwise (DENSE) or none when all are zero (NONE).  A
+ * 64-byte stream header and 32-byte directory entries describe the stream.
+ *
+ * Conventions
+ *   - All integers little-endian.  All status codes: 0 = DCR_OK, < 0 = error.
+ *   - Host-detectable errors are returned synchronously; the message is in
+ *     dcr_last_error() (thread-local).  Device-detected conditions (capacity,
+ *     invalid records) are reported in result structs in device memory.
+ *   - Memory: the caller owns ALL device memory (shards, canonical tensors,
+ *     directory, payload, flags, workspace, plan tables).  The library
+ *     allocates host memory only (the plan) and never calls hipMalloc.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  All device
+ *     work is enqueued on it; the library never synchronises it.  Host arrays
+ *     of device pointers passed to a call are copied during the call.
+ *   - Alignment: every shard, canonical tensor, directory, payload, result and
+ *     workspace pointer must be 16-byte aligned (DCR_E_INVAL otherwise).
+ *   - Concurrency: a plan is immutable after upload and may be shared; calls
+ *     that run concurrently need separate workspaces.
+ */
+#ifndef DCR_H
+#define DCR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ constants */
+enum {
+    DCR_OK = 0,
+    DCR_E_INVAL = -1,     /* bad argument / descriptor / alignment            */
+    DCR_E_COVERAGE = -2,  /* canonical elements not covered exactly once      */
+    DCR_E_FORMAT = -3,    /* stream header does not match (magic, plan, kind) */
+    DCR_E_VERSION = -4,   /* stream base_version != expected base version     */
+    DCR_E_CAPACITY = -5,  /* a caller buffer is too small                     */
+    DCR_E_HIP = -6,       /* a HIP runtime call failed                        */
+    DCR_E_NOMEM = -7      /* host allocation failed                           */
+};
+enum { DCR_ROUTE_AFFINE_XOR = 0, DCR_ROUTE_OVERWRITE = 1, DCR_ROUTE_BLOCK_SCALED = 2 };
+enum { DCR_MODE_DELTA = 0, DCR_MODE_RETRY = 1 };
+enum { DCR_KIND_XOR = 0, DCR_KIND_OW = 1 };
+enum { DCR_HI_NONE = 0, DCR_HI_SPARSE = 1, DCR_HI_DENSE = 2 };
+#define DCR_MAGIC 0x31524344u          /* "DCR1" */
+#define DCR_FORMAT_VERSION 1u
+#define DCR_CHUNK_BYTES 65536u
+#define DCR_HEADER_BYTES 64u
+#define DCR_DIRENT_BYTES 32u
+
+/* ---------------------------------------------------------------- types */
+
+/* One canonical (checkpoint) tensor.  24 bytes.
+ *   numel        elements
+ *   elem_bytes   1, 2 or 4 (XOR-carrying routes: 1 or 2 only)
+ *   route        DCR_ROUTE_*: AFFINE_XOR -> XOR records; OVERWRITE -> overwrite
+ *                records; BLOCK_SCALED -> an element is an overwrite iff the
+ *                fp32 bits of its block's scale changed, else XOR
+ *   scale_tensor BLOCK_SCALED: id of its fp32 OVERWRITE scale tensor, which
+ *                has ceil(numel / scale_block) elements; else -1
+ *   scale_block  BLOCK_SCALED: elements per scale, a multiple of 16/elem_bytes;
+ *                else 0 */
+typedef struct {
+    uint64_t numel;
+    uint32_t elem_bytes;
+    uint32_t route;
+    int32_t scale_tensor;
+    uint32_t scale_block;
+} dcr_tensor_desc;
+
+/* One affine segment of the direct projection: for every multi-index x with
+ * 0 <= x_d < extent[d] (d < ndim, 1 <= ndim <= 4), canonical element
+ *   canon_off + sum_d x_d * canon_stride[d]   of tensor tensor_id
+ * is stored at element
+ *   shard_off + sum_d x_d * shard_stride[d]   of shard shard_id,
+ * in element units of the tensor's width.  128 bytes.  Every canonical
+ * element must be covered exactly once over all segments. */
+typedef struct {
+    uint32_t tensor_id, shard_id, ndim, reserved;
+    uint64_t shard_off, canon_off;
+    uint64_t extent[4];
+    int64_t shard_stride[4];
+    int64_t canon_stride[4];
+} dcr_segment;
+
+typedef struct dcr_plan dcr_plan; /* opaque; host-owned */
+
+typedef struct {
+    uint64_t n_tensors, n_shards, n_chunks, n_pieces;
+    uint64_t table_bytes;       /* device bytes dcr_plan_upload needs            */
+    uint64_t workspace_bytes;   /* device workspace bytes encode / apply need    */
+    uint64_t max_dir_bytes;     /* directory bytes of the largest possible stream */
+    uint64_t max_payload_bytes; /* payload bytes of the largest possible stream   */
+    uint64_t fingerprint;       /* FNV-1a-64 of the serialised tensor table       */
+    uint64_t canonical_bytes;   /* sum of numel * elem_bytes                      */
+} dcr_plan_info;
+
+/* Stream header, 64 bytes (the first bytes of every stream). */
+typedef struct {
+    uint32_t magic;             /* DCR_MAGIC */
+    uint16_t format_version;    /* DCR_FORMAT_VERSION */
+    uint16_t stream_kind;       /* DCR_MODE_DELTA or DCR_MODE_RETRY */
+    uint32_t chunk_bytes;       /* 65536 */
+    uint32_t reserved0;
+    uint64_t base_version;
+    uint64_t new_version;
+    uint64_t plan_fingerprint;
+    uint64_t n_records;
+    uint64_t payload_bytes;
+    uint64_t reserved1;
+} dcr_stream_header;
+
+/* Written by dcr_encode in device memory.  32 bytes. */
+typedef struct {
+    uint64_t n_records;         /* records of the stream (also when it did not fit) */
+    uint64_t payload_bytes;     /* payload bytes of the stream (also when it did not fit) */
+    uint64_t n_changed;         /* elements whose stored bits differ */
+    int32_t status;             /* DCR_OK, or DCR_E_CAPACITY if dir_cap / payload_cap
+                                   was too small: grow the buffers and encode again */
+    uint32_t reserved;
+} dcr_encode_result;
+
+/* Written by dcr_apply / dcr_apply_overwrite_retry in device memory.  32 bytes. */
+typedef struct {
+    uint64_t n_applied;         /* records applied by this call */
+    uint64_t n_skipped;         /* records skipped because their flag was set */
+    uint64_t n_invalid;         /* records refused (malformed entry or payload); untouched */
+    uint64_t first_invalid;     /* lowest refused record index, or UINT64_MAX */
+} dcr_apply_result;
+
+/* --------------------------------------------------------------- calls */
+
+/* Build a plan from the canonical tensor table, the shard sizes (bytes) and
+ * the affine segments (see dcr_segment).  Checks every descriptor, that every
+ * segment stays inside its tensor and shard (DCR_E_INVAL) and that every
+ * canonical element is covered exactly once (DCR_E_COVERAGE; the ownership
+ * invariant: one owner per element, replicas are not listed).  Expands the
+ * segments into contiguous runs, cuts them at 64 KiB canonical chunk borders
+ * and builds the chunk and piece tables the kernels read.  On success *out
+ * owns host memory; free it with dcr_plan_destroy. */
+int32_t dcr_plan_build(const dcr_tensor_desc* tensors, uint32_t n_tensors,
+                       const uint64_t* shard_bytes, uint32_t n_shards,
+                       const dcr_segment* segments, uint64_t n_segments,
+                       dcr_plan** out);
+
+/* Sizes and fingerprint of a plan. */
+int32_t dcr_plan_query(const dcr_plan* plan, dcr_plan_info* out);
+
+/* Copy the plan's tables to caller-owned device memory `dev_tables` (at least
+ * table_bytes, 16-byte aligned) on `stream`, and bind the plan to it.  The
+ * memory must stay allocated and unmodified while the plan is used.  The host
+ * copy source is owned by the plan, which must outlive the copy. */
+int32_t dcr_plan_upload(dcr_plan* plan, void* dev_tables, uint64_t bytes, void* stream);
+
+void dcr_plan_destroy(dcr_plan* plan);
+
+/* Encode one refit step (sender side).
+ *   old_shards / new_shards  host arrays of n_shards device pointers: the
+ *                  trainer shards of the committed base and of the new step
+ *   mode           DCR_MODE_DELTA: XOR / overwrite records by route;
+ *                  DCR_MODE_RETRY: one overwrite record per changed chunk
+ *                  carrying the new stored bits of every changed element
+ *   base_version, new_version  written to the header (version binding)
+ *   header_dev     64 bytes of device memory for the stream header
+ *   dir_dev, dir_cap           directory buffer and its size in bytes
+ *   payload_dev, payload_cap   payload buffer and its size in bytes
+ *   result_dev     a dcr_encode_result in device memory
+ *   workspace_dev, ws_bytes    at least workspace_bytes of device memory
+ * Records are written in (tensor, chunk, kind) order with contiguous 16-byte
+ * aligned payload offsets.  If a buffer is too small, result->status becomes
+ * DCR_E_CAPACITY with the required totals; the buffers then hold no usable
+ * stream.  Read the result after synchronising the stream. */
+int32_t dcr_encode(const dcr_plan* plan,
+                   const void* const* old_shards, const void* const* new_shards,
+                   uint32_t mode, uint64_t base_version, uint64_t new_version,
+                   void* header_dev, void* dir_dev, uint64_t dir_cap,
+                   void* payload_dev, uint64_t payload_cap,
+                   dcr_encode_result* result_dev,
+                   void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* Apply records [first_record, first_record + n_records) of a stream in place
+ * (receiver side).
+ *   canon          host array of n_tensors device pointers, one per canonical
+ *                  tensor (numel * elem_bytes bytes, 16-byte aligned)
+ *   header         the stream header, in HOST memory; its magic, format, chunk
+ *                  size and plan fingerprint must match (DCR_E_FORMAT) and its
+ *                  base_version must equal expected_base_version (DCR_E_VERSION)
+ *   dir_dev, payload_dev  the stream's directory and payload in device memory
+ *   applied_flags_dev     one byte per record of the stream, zeroed by the
+ *                  caller once per stream: a record whose flag is set is
+ *                  skipped, an applied record gets its flag set (dedup)
+ * Each record is checked on the device before it is touched (tensor, chunk,
+ * sizes, modes, bounds, bitmap popcount); a malformed record is refused,
+ * counted in result_dev and leaves memory untouched.  XOR and overwrite
+ * records of one chunk must not mark elements of the same 16-byte group. */
+int32_t dcr_apply(const dcr_plan* plan, void* const* canon,
+                  const dcr_stream_header* header,
+                  const void* dir_dev, const void* payload_dev,
+                  uint8_t* applied_flags_dev,
+                  uint64_t first_record, uint64_t n_records,
+                  uint64_t expected_base_version,
+                  dcr_apply_result* result_dev,
+                  void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* Re-apply every record of a RETRY stream (header stream_kind must be
+ * DCR_MODE_RETRY, every record an overwrite) as an overwrite, ignoring and
+ * not touching dedup flags.  Overwrites are idempotent, so any partial, torn
+ * or duplicated earlier apply ends at the new bits. */
+int32_t dcr_apply_overwrite_retry(const dcr_plan* plan, void* const* canon,
+                                  const dcr_stream_header* header,
+                                  const void* dir_dev, const void* payload_dev,
+                                  uint64_t expected_base_version,
+                                  dcr_apply_result* result_dev,
+                                  void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* Message of the last error on this thread ("" if none). */
+const char* dcr_last_error(void);
+
+/* Format constants as this library defines them, for cross-checks:
+ * out[0..7] = magic, format version, chunk bytes, header bytes, dirent bytes,
+ * sizeof(dcr_tensor_desc), sizeof(dcr_segment), sizeof(dcr_stream_header).
+ * Returns the number written (at most n). */
+uint32_t dcr_format_constants(uint32_t* out, uint32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DCR_H */

@@ -1,0 +1,82 @@
+"""Helpers that drive libdcr.so on the GPU for the parity tests."""
+import numpy as np
+import torch
+
+from bit_exact_xor_amd import dcr, synth
+
+
+def shard_bytes(lay):
+    return [lay.shard_bytes(s) for s in range(lay.n_shards)]
+
+
+class Gpu:
+    """A layout's plan, shards and workspace on the GPU."""
+
+    def __init__(self, lay, olds=None, news=None, gen_gpu=False, device="cuda"):
+        self.lay = lay
+        self.device = device
+        self.plan = dcr.dcr_plan_build(lay.tensors, shard_bytes(lay), lay.segments)
+        dcr.dcr_plan_upload(self.plan, device)
+        self.old_buf, self.olds = synth.alloc_shards(lay, device)
+        self.new_buf, self.news = synth.alloc_shards(lay, device)
+        if gen_gpu:
+            self._hot0 = synth.fill_shards_gpu(lay, self.olds, 0)
+            self._hot1 = synth.fill_shards_gpu(lay, self.news, 1)
+        else:
+            olds = olds if olds is not None else lay.shards_host(0)
+            news = news if news is not None else lay.shards_host(1)
+            for dst, src in zip(self.olds, olds):
+                if dst.numel():
+                    dst.copy_(torch.from_numpy(np.ascontiguousarray(src).view(np.uint8).reshape(-1)))
+            for dst, src in zip(self.news, news):
+                if dst.numel():
+                    dst.copy_(torch.from_numpy(np.ascontiguousarray(src).view(np.uint8).reshape(-1)))
+        self.ws = dcr.workspace(self.plan, device)
+        torch.cuda.synchronize()
+
+    def encode(self, mode=0, base=7, new=8, dir_bytes=None, payload_bytes=None):
+        sb = dcr.StreamBuffers(self.plan, self.device, dir_bytes, payload_bytes)
+        dcr.dcr_encode(self.plan, self.olds, self.news, mode, base, new, sb.header, sb.dir, sb.payload,
+                       sb.result, self.ws)
+        torch.cuda.synchronize()
+        return sb
+
+    def stream_host(self, sb):
+        """(header, directory, payload) bytes as numpy, trimmed to the stream."""
+        r = sb.result_host()
+        assert int(r["status"]) == 0, r
+        n, pb = int(r["n_records"]), int(r["payload_bytes"])
+        return (sb.header.cpu().numpy(), sb.dir[: n * 32].cpu().numpy(), sb.payload[:pb].cpu().numpy())
+
+    def canon_alloc(self, init=None, align=256):
+        """Canonical tensors in one device buffer, each 256-byte aligned."""
+        T = self.lay.tensors
+        offs, total = [], 0
+        for t in range(len(T)):
+            offs.append(total)
+            total += (int(T[t]["numel"]) * int(T[t]["elem_bytes"]) + align - 1) // align * align
+        buf = torch.zeros(max(total, align), dtype=torch.uint8, device=self.device)
+        views = [buf[o:o + int(T[t]["numel"]) * int(T[t]["elem_bytes"])] for t, o in enumerate(offs)]
+        if init is not None:
+            for v, x in zip(views, init):
+                if v.numel():
+                    v.copy_(torch.from_numpy(np.ascontiguousarray(x).view(np.uint8).reshape(-1)))
+        return buf, views
+
+    def apply(self, canon, hdr, sb, flags, first=0, n=None, base=7):
+        nrec = int(hdr[40:48].view("<u8")[0])
+        n = nrec - first if n is None else n
+        res = torch.zeros(32, dtype=torch.uint8, device=self.device)
+        dcr.dcr_apply(self.plan, canon, hdr, sb.dir, sb.payload, flags, first, n, base, res, self.ws)
+        torch.cuda.synchronize()
+        return dcr.apply_result(res)
+
+    def retry(self, canon, hdr, sb, base=7):
+        res = torch.zeros(32, dtype=torch.uint8, device=self.device)
+        dcr.dcr_apply_overwrite_retry(self.plan, canon, hdr, sb.dir, sb.payload, base, res, self.ws)
+        torch.cuda.synchronize()
+        return dcr.apply_result(res)
+
+
+def host(views):
+    return [v.cpu().numpy() for v in views]

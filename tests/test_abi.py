@@ -1,0 +1,97 @@
+"""Host-side checks of libdcr.so (no GPU): symbols, constants, plan building."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from bit_exact_xor_amd import dcr, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "dcr.h")).read()
+    return sorted(set(re.findall(r"\b(dcr_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dcr.load_library()
+    names = declared_symbols()
+    assert {"dcr_plan_build", "dcr_encode", "dcr_apply", "dcr_apply_overwrite_retry"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", dcr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (dcr_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_format_constants_agree_with_oracle():
+    from oracle import oracle as O
+    c = dcr.format_constants()
+    assert c == [0x31524344, 1, O.CHUNK_BYTES, O.HEADER_BYTES, O.DIRENT_BYTES,
+                 O.ORC_TENSOR.itemsize, O.ORC_SEGMENT.itemsize, 64]
+    assert dcr.TENSOR_DESC == O.ORC_TENSOR or dcr.TENSOR_DESC.descr == O.ORC_TENSOR.descr
+    assert dcr.SEGMENT.itemsize == O.ORC_SEGMENT.itemsize
+
+
+def test_plan_fingerprint_matches_oracle(orc):
+    for seed in range(5):
+        lay = synth.random_layout(seed)
+        p = dcr.dcr_plan_build(lay.tensors, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
+        assert p.info.fingerprint == orc.fingerprint(lay.tensors)
+        assert p.info.canonical_bytes == lay.total_bytes()
+
+
+def test_plan_pieces_llama_tp4():
+    lay = synth.llama_layout(hidden=256, layers=2, ffn=640, n_q=8, n_kv=4, head_dim=32, vocab=1000, tp=4)
+    p = dcr.dcr_plan_build(lay.tensors, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
+    n_chunks = sum(-(-int(t["numel"]) * 2 // 65536) for t in lay.tensors)
+    assert p.info.n_chunks == n_chunks
+    assert p.info.n_pieces > n_chunks  # row-parallel o / down tensors split chunks into runs
+
+
+def test_plan_rejects_bad_layouts():
+    T = np.zeros(1, dtype=synth.TENSOR_DT)
+    T[0] = (100, 2, 0, -1, 0)
+    S = np.zeros(2, dtype=synth.SEGMENT_DT)
+    for i in range(2):
+        S[i]["ndim"] = 1
+        S[i]["shard_stride"][0] = 1
+        S[i]["canon_stride"][0] = 1
+    S[0]["extent"][0], S[1]["extent"][0] = 60, 40
+    S[1]["shard_off"], S[1]["canon_off"] = 60, 60
+    dcr.dcr_plan_build(T, [200], S)                     # exact cover
+    S2 = S.copy(); S2[1]["canon_off"] = 59                # overlap + gap
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_plan_build(T, [200], S2)
+    assert e.value.code == dcr.DCR_E_COVERAGE
+    S2 = S.copy(); S2[1]["extent"][0] = 39                # gap at the end
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_plan_build(T, [200], S2)
+    assert e.value.code == dcr.DCR_E_COVERAGE
+    S2 = S.copy(); S2[1]["shard_off"] = 170               # shard overrun
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_plan_build(T, [200], S2)
+    assert e.value.code == dcr.DCR_E_INVAL
+    T2 = T.copy(); T2[0]["elem_bytes"] = 4                # XOR route on 4-byte elements
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_plan_build(T2, [400], S)
+    assert e.value.code == dcr.DCR_E_INVAL
+    T3 = T.copy(); T3[0]["route"] = 2                     # block-scaled without scales
+    with pytest.raises(dcr.DcrError):
+        dcr.dcr_plan_build(T3, [200], S)
+
+
+def test_plan_accepts_degenerate_tensors():
+    T = np.zeros(3, dtype=synth.TENSOR_DT)
+    T[0] = (0, 2, 0, -1, 0)
+    T[1] = (1, 1, 1, -1, 0)
+    T[2] = (7, 2, 0, -1, 0)
+    S = np.zeros(2, dtype=synth.SEGMENT_DT)
+    S[0] = (1, 0, 1, 0, 0, 0, [1, 1, 1, 1], [1, 0, 0, 0], [1, 0, 0, 0])
+    S[1] = (2, 1, 1, 0, 0, 0, [7, 1, 1, 1], [1, 0, 0, 0], [1, 0, 0, 0])
+    p = dcr.dcr_plan_build(T, [1, 14], S)
+    assert p.info.n_chunks == 2

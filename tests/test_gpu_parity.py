@@ -1,0 +1,254 @@
+"""GPU parity: libdcr.so (gfx950 kernels) against the CPU oracle.
+
+Stream bytes (header, directory, payload) must equal the oracle's byte for
+byte, and patched weights must equal the oracle's (= the new weights) bit for
+bit.  Every test prints the case it runs before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from bit_exact_xor_amd import dcr, synth
+from tests import fmt, pins
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gh():
+    from tests import gpu_harness
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dcr.load_library()
+    return gpu_harness
+
+
+def oracle_stream(orc, lay, olds, news, mode=0):
+    rc, h, d, p = orc.encode(lay.tensors, lay.segments, olds, news, mode=mode, base_version=7, new_version=8)
+    assert rc == 0
+    return h, d, p
+
+
+def assert_same_stream(got, exp, what=""):
+    gh_, gd, gp = got
+    eh, ed, ep = exp
+    assert np.array_equal(gh_, eh), f"{what}: header differs"
+    assert gd.shape == ed.shape, f"{what}: directory size {gd.shape} vs {ed.shape}"
+    if not np.array_equal(gd, ed):
+        bad = np.nonzero((gd.reshape(-1, 32) != ed.reshape(-1, 32)).any(1))[0]
+        r = int(bad[0])
+        raise AssertionError(f"{what}: directory entry {r} differs: gpu {fmt.dirents(gd[r*32:r*32+32])} "
+                             f"oracle {fmt.dirents(ed[r*32:r*32+32])}")
+    assert gp.shape == ep.shape, f"{what}: payload size {gp.shape} vs {ep.shape}"
+    if not np.array_equal(gp, ep):
+        i = int(np.nonzero(gp != ep)[0][0])
+        ents = fmt.dirents(ed)
+        rec = [e for e in ents if e["off"] <= i < e["off"] + e["size"]]
+        raise AssertionError(f"{what}: payload byte {i} differs (gpu {gp[i]} oracle {ep[i]}) in {rec}")
+
+
+SEEDS = list(range(40))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_layout_parity(gh, orc, seed):
+    """Random layouts: 1/2/4-byte elements, all routes, split / transposed
+    shards, ragged tails, empty tensors."""
+    say("random layout", seed)
+    lay = synth.random_layout(seed)
+    olds, news, co, cn = pins.canon_lists(lay)
+    g = gh.Gpu(lay, olds, news)
+    for mode in (0, 1):
+        sb = g.encode(mode)
+        assert_same_stream(g.stream_host(sb), oracle_stream(orc, lay, olds, news, mode), f"seed {seed} mode {mode}")
+    sb = g.encode(0)
+    hdr, d, p = g.stream_host(sb)
+    n = len(d) // 32
+    buf, canon = g.canon_alloc(co)
+    flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+    r = g.apply(canon, hdr, sb, flags)
+    assert int(r["n_applied"]) == n and int(r["n_invalid"]) == 0
+    got = gh.host(canon)
+    for t in range(lay.n_tensors):
+        assert np.array_equal(got[t], cn[t]), (seed, t)
+    assert bool((flags[:n] == 1).all()) if n else True
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dedup_involution_retry(gh, orc, seed):
+    """Duplicates are skipped; a XOR stream applied twice restores old; the
+    overwrite retry heals half-applied, torn and duplicated states."""
+    say("dedup / involution / retry", seed)
+    lay = synth.random_layout(600 + seed)
+    olds, news, co, cn = pins.canon_lists(lay)
+    g = gh.Gpu(lay, olds, news)
+    sb = g.encode(0)
+    hdr, d, p = g.stream_host(sb)
+    n = len(d) // 32
+    buf, canon = g.canon_alloc(co)
+    flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+    g.apply(canon, hdr, sb, flags, 0, n // 2)                 # killed at 50 %
+    r = g.apply(canon, hdr, sb, flags)                        # resume: first half skipped
+    assert int(r["n_skipped"]) == n // 2 and int(r["n_applied"]) == n - n // 2
+    got = gh.host(canon)
+    for t in range(lay.n_tensors):
+        assert np.array_equal(got[t], cn[t])
+    # XOR-only twice restores old
+    xor_only = all(e["kind"] == 0 for e in fmt.dirents(d))
+    if xor_only and n:
+        flags.zero_()
+        g.apply(canon, hdr, sb, flags)
+        got = gh.host(canon)
+        for t in range(lay.n_tensors):
+            assert np.array_equal(got[t], co[t])
+    # retry from several prior states built by the oracle on the host
+    rsb = g.encode(1)
+    rh, rd, rp = g.stream_host(rsb)
+    states = [[x.copy() for x in co]]
+    W = [x.copy() for x in co]
+    f = np.zeros(max(n, 1), np.uint8)
+    orc.apply(lay.tensors, W, hdr, d, p, f, 0, n // 2, expected_base_version=7)
+    states.append(W)
+    if n:
+        W = [x.copy() for x in co]
+        orc.apply_record_part(lay.tensors, W, d, p, n // 2, 0, max(fmt.dirents(d)[n // 2]["K"] // 2, 1))
+        states.append(W)
+        W = [x.copy() for x in co]
+        f = np.zeros(n, np.uint8)
+        orc.apply(lay.tensors, W, hdr, d, p, f, expected_base_version=7)
+        f[::2] = 0
+        orc.apply(lay.tensors, W, hdr, d, p, f, expected_base_version=7)
+        states.append(W)
+    for si, st in enumerate(states):
+        buf, canon = g.canon_alloc(st)
+        g.retry(canon, rh, rsb)
+        once = gh.host(canon)
+        g.retry(canon, rh, rsb)
+        twice = gh.host(canon)
+        for t in range(lay.n_tensors):
+            assert np.array_equal(once[t], cn[t]), (si, t)
+            assert np.array_equal(twice[t], cn[t]), (si, t)
+
+
+def test_config1_parity(gh, orc):
+    """Config 1: one 4096x4096 BF16 tensor, 1 % changed + 64 forced +-0 flips."""
+    say("config 1")
+    lay = synth.config1_layout()
+    old, new, _lr, pos = synth.config1_values(lay, lr=synth.CFG1_LR)
+    g = gh.Gpu(lay, [old], [new])
+    sb = g.encode(0)
+    got = g.stream_host(sb)
+    exp = oracle_stream(orc, lay, [old], [new])
+    assert_same_stream(got, exp, "config 1")
+    assert int(sb.result_host()["n_changed"]) == int(np.count_nonzero(old != new))
+    buf, canon = g.canon_alloc([old])
+    flags = torch.zeros(len(got[1]) // 32, dtype=torch.uint8, device="cuda")
+    g.apply(canon, got[0], sb, flags)
+    assert np.array_equal(canon[0].cpu().numpy().view(np.uint16), new)
+    for mode in (1,):
+        assert_same_stream(g.stream_host(g.encode(mode)), oracle_stream(orc, lay, [old], [new], mode), "cfg1 retry")
+
+
+def test_llama_small_gpu_generated(gh, orc):
+    """Scaled-down TP=4 Llama layout with shards generated on the GPU: the
+    GPU generator reproduces the numpy one, and the streams match."""
+    say("llama small, gpu-generated shards")
+    lay = synth.llama_layout(hidden=256, layers=2, ffn=640, n_q=8, n_kv=4, head_dim=32, vocab=1000, tp=4,
+                             rate=0.03)
+    g = gh.Gpu(lay, gen_gpu=True)
+    olds, news = lay.shards_host(0), lay.shards_host(1)
+    for s in range(lay.n_shards):
+        assert np.array_equal(g.olds[s].cpu().numpy(), olds[s].view(np.uint8)), s
+        assert np.array_equal(g.news[s].cpu().numpy(), news[s].view(np.uint8)), s
+    for mode in (0, 1):
+        assert_same_stream(g.stream_host(g.encode(mode)), oracle_stream(orc, lay, olds, news, mode),
+                           f"llama small mode {mode}")
+
+
+def test_determinism(gh):
+    """Ten encodes of the same input give identical bytes (look-back order
+    varies from run to run; the stream may not)."""
+    say("determinism")
+    lay = synth.llama_layout(hidden=256, layers=2, ffn=640, n_q=8, n_kv=4, head_dim=32, vocab=1000, tp=4,
+                             rate=0.05)
+    g = gh.Gpu(lay, gen_gpu=True)
+    ref = g.stream_host(g.encode(0))
+    for _ in range(10):
+        got = g.stream_host(g.encode(0))
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b)
+
+
+def test_capacity_overflow(gh, orc):
+    """Too-small buffers: status DCR_E_CAPACITY with the required sizes."""
+    say("capacity overflow")
+    lay = synth.random_layout(3, rate=0.2)
+    olds, news, co, cn = pins.canon_lists(lay)
+    h, d, p = oracle_stream(orc, lay, olds, news)
+    g = gh.Gpu(lay, olds, news)
+    for dcap, pcap in ((len(d) - 32, len(p)), (len(d), len(p) - 16), (32, 16)):
+        sb = g.encode(0, dir_bytes=dcap, payload_bytes=pcap)
+        r = sb.result_host()
+        assert int(r["status"]) == dcr.DCR_E_CAPACITY
+        assert int(r["n_records"]) * 32 == len(d) and int(r["payload_bytes"]) == len(p)
+
+
+def test_header_checks(gh):
+    """Wrong base version, plan fingerprint or stream kind are refused on the host."""
+    say("header checks")
+    lay = synth.random_layout(5, rate=0.2)
+    g = gh.Gpu(lay)
+    sb = g.encode(0)
+    hdr, d, p = g.stream_host(sb)
+    olds, news, co, cn = pins.canon_lists(lay)
+    buf, canon = g.canon_alloc(co)
+    flags = torch.zeros(max(len(d) // 32, 1), dtype=torch.uint8, device="cuda")
+    with pytest.raises(dcr.DcrError) as e:
+        g.apply(canon, hdr, sb, flags, base=6)
+    assert e.value.code == dcr.DCR_E_VERSION
+    bad = hdr.copy(); bad[32] ^= 1
+    with pytest.raises(dcr.DcrError) as e:
+        g.apply(canon, bad, sb, flags)
+    assert e.value.code == dcr.DCR_E_FORMAT
+    with pytest.raises(dcr.DcrError) as e:
+        g.retry(canon, hdr, sb)            # a DELTA stream is not a RETRY stream
+    assert e.value.code == dcr.DCR_E_FORMAT
+    got = gh.host(canon)
+    for t in range(lay.n_tensors):
+        assert np.array_equal(got[t], co[t])   # nothing was touched
+
+
+def test_corrupt_records_refused(gh):
+    """A record whose bitmap popcount or fields are wrong is refused on the
+    device and its chunk left untouched; the other records still apply."""
+    say("corrupt records")
+    lay = synth.config1_layout(512, 512)
+    old, new, _lr, _pos = synth.config1_values(lay, lr=synth.CFG1_LR)
+    g = gh.Gpu(lay, [old], [new])
+    sb = g.encode(0)
+    hdr, d, p = g.stream_host(sb)
+    ents = fmt.dirents(d)
+    assert len(ents) >= 4
+    # flip one bitmap bit of record 1 and the K of record 2
+    sb.payload[ents[1]["off"]] ^= 0x01
+    dd = sb.dir.clone()
+    dd[2 * 32 + 8] ^= 0x01
+    sb.dir.copy_(dd)
+    buf, canon = g.canon_alloc([old])
+    flags = torch.zeros(len(ents), dtype=torch.uint8, device="cuda")
+    r = g.apply(canon, hdr, sb, flags)
+    assert int(r["n_invalid"]) == 2 and int(r["first_invalid"]) == 1
+    assert int(r["n_applied"]) == len(ents) - 2
+    w = canon[0].cpu().numpy().view(np.uint16)
+    E = 32768
+    for i, e in enumerate(ents):
+        sl = slice(e["c"] * E, (e["c"] + 1) * E)
+        exp = old[sl] if i in (1, 2) else new[sl]
+        assert np.array_equal(w[sl], exp), i
+    assert flags[1].item() == 0 and flags[2].item() == 0 and flags[0].item() == 1
