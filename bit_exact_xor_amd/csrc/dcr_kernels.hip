@@ -109,6 +109,7 @@ __device__ __forceinline__ void set_elem(uint32_t (&q)[4], uint32_t e, uint32_t 
 }
 __device__ __forceinline__ uint32_t sgpr(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) v4u* gv4p;   // global (not flat) 128-bit loads
 
 // chunk element -> index of the piece holding it (largest start <= e)
 __device__ __forceinline__ uint32_t find_piece(const DevPiece* pc, uint32_t n, uint32_t e) {
@@ -261,8 +262,8 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, EncodeShared& S
     if (fast) {
         // one aligned piece covers the full chunk: straight 128-bit loads
         const DevPiece p0 = pc[0];
-        const v4u* vo = reinterpret_cast<const v4u*>(a.old_sh[p0.shard] + p0.shard_elem_off * W) + tid;
-        const v4u* vn = reinterpret_cast<const v4u*>(a.new_sh[p0.shard] + p0.shard_elem_off * W) + tid;
+        gv4p vo = (gv4p)(a.old_sh[p0.shard] + p0.shard_elem_off * W) + tid;
+        gv4p vn = (gv4p)(a.new_sh[p0.shard] + p0.shard_elem_off * W) + tid;
         v4u lo_[kVecsPerThread], ln_[kVecsPerThread];
 #pragma unroll
         for (uint32_t k = 0; k < kVecsPerThread; k++) {
@@ -773,10 +774,10 @@ __device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uin
     }
     __syncthreads();
     if (tid == 0) {
-        if (!a.retry) {
-            __threadfence();
-            a.flags[r] = 1;
-        }
+        // The flag becomes visible with the record's writes at kernel
+        // completion (stream order); no cross-agent ordering is promised
+        // while the kernel runs, so no device-wide fence is paid per record.
+        if (!a.retry) a.flags[r] = 1;
         atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_applied), 1ull);
     }
 }
