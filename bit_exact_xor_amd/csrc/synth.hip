@@ -43,7 +43,10 @@ struct Region {
     uint64_t thr;        // change iff low 32 bits of the change hash < thr
     uint64_t row_len;    // GEN_BF16_HOT: elements per row
     uint64_t hot_off;    // GEN_BF16_HOT: first index into the hot-row list
-    uint32_t kind;       // 0 BF16, 1 U8, 2 F32 scale, 3 BF16 with hot rows
+    uint64_t key_blk;    // GEN_BF16_HOT: change key of the coupled scale region
+    uint64_t thr_blk;
+    uint32_t blk;        // elements per coupled block (0: none)
+    uint32_t kind;       // 0 BF16, 1 U8, 2 F32 scale, 3 BF16 with hot rows / coupled blocks
     uint32_t n_hot;      // GEN_BF16_HOT: hot rows (sorted)
 };
 
@@ -69,6 +72,7 @@ __global__ void gen_kernel(uint8_t* shard, Region r, const uint32_t* hot, uint32
             const uint64_t h = hash_at(r.key_chg, i);
             bool changed = (h & 0xFFFFFFFFull) < r.thr;
             if (r.kind == 3 && r.n_hot) changed = changed || is_hot(hot + r.hot_off, r.n_hot, i / r.row_len);
+            if (r.kind == 3 && r.blk) changed = changed || (hash_at(r.key_blk, i / r.blk) & 0xFFFFFFFFull) < r.thr_blk;
             if (changed) v = bf16_step(old, ((h >> 32) & 1u) != 0);
         }
         reinterpret_cast<uint16_t*>(shard)[e] = v;
@@ -105,9 +109,10 @@ extern "C" {
 // NULL).  Returns 0 or a HIP error code.
 int32_t dcr_synth_fill(void* shard, uint64_t elem_off, uint64_t n, uint32_t kind, uint64_t key_old,
                        uint64_t key_chg, uint64_t thr, uint64_t row_len, const uint32_t* hot, uint64_t hot_off,
-                       uint32_t n_hot, uint32_t version, uint32_t scale_bits, void* stream) {
+                       uint32_t n_hot, uint64_t key_blk, uint64_t thr_blk, uint32_t blk, uint32_t version,
+                       uint32_t scale_bits, void* stream) {
     if (n == 0) return 0;
-    Region r{elem_off, n, key_old, key_chg, thr, row_len ? row_len : 1, hot_off, kind, n_hot};
+    Region r{elem_off, n, key_old, key_chg, thr, row_len ? row_len : 1, hot_off, key_blk, thr_blk, blk, kind, n_hot};
     const uint64_t blocks = (n + 255) / 256;
     if (blocks > 0x7FFFFFFFull) return int32_t(hipErrorInvalidValue);
     hipLaunchKernelGGL(gen_kernel, dim3(uint32_t(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),

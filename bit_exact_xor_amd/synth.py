@@ -43,7 +43,8 @@ SCALE_BITS = int(SCALE_F32.view(np.uint32))
 GEN_BF16 = 0      # BF16 N(0,0.02), +-1 ulp changes
 GEN_U8 = 1        # uint8 nibble codes, one-nibble changes
 GEN_F32SCALE = 2  # fp32 positive scales, changes flagged per element
-GEN_BF16_HOT = 3  # like GEN_BF16, but rows listed hot change with certainty
+GEN_BF16_HOT = 3  # like GEN_BF16, plus: listed hot rows change with certainty, and
+                  # whole blocks change when their (coupled) scale changes
 
 # neutral descriptions of the plan inputs (each side packs its own struct)
 TENSOR_DT = np.dtype([("numel", "<u8"), ("elem_bytes", "<u4"), ("route", "<u4"),
@@ -116,7 +117,8 @@ def change_mask(key_chg: int, start: int, n: int, thr: int):
 
 
 def gen_region(kind: int, key_old: int, key_chg: int, thr: int, start: int, n: int,
-               version: int, row_len: int = 0, hot_rows: np.ndarray | None = None) -> np.ndarray:
+               version: int, row_len: int = 0, hot_rows: np.ndarray | None = None,
+               key_blk: int = 0, thr_blk: int = 0, blk: int = 0) -> np.ndarray:
     """Contents of elements start..start+n-1 of one region, version 0 (old) or 1 (new)."""
     if kind in (GEN_BF16, GEN_BF16_HOT):
         old = bf16_old(key_old, start, n)
@@ -126,6 +128,10 @@ def gen_region(kind: int, key_old: int, key_chg: int, thr: int, start: int, n: i
         if kind == GEN_BF16_HOT and hot_rows is not None and len(hot_rows):
             rows = (np.arange(start, start + n, dtype=np.int64) // row_len)
             changed = changed | np.isin(rows, hot_rows)
+        if kind == GEN_BF16_HOT and blk:
+            b0, b1 = start // blk, (start + n - 1) // blk
+            bch, _u, _h = change_mask(key_blk, b0, b1 - b0 + 1, thr_blk)
+            changed = changed | bch[np.arange(start, start + n, dtype=np.int64) // blk - b0]
         return np.where(changed, bf16_step(old, up), old).astype(np.uint16)
     if kind == GEN_U8:
         old = (hashes(key_old, start, n) & np.uint64(0xFF)).astype(np.uint8)
@@ -162,6 +168,9 @@ class Region:
     thr: int
     row_len: int = 0
     hot_rows: np.ndarray | None = None
+    key_blk: int = 0       # GEN_BF16_HOT: change key of the coupled scale region
+    thr_blk: int = 0
+    blk: int = 0           # elements per coupled block (0: none)
 
 
 @dataclasses.dataclass
@@ -202,7 +211,8 @@ class Layout:
             if r.shard != s:
                 continue
             out[r.elem_off:r.elem_off + r.n] = gen_region(
-                r.kind, r.key_old, r.key_chg, r.thr, 0, r.n, version, r.row_len, r.hot_rows)
+                r.kind, r.key_old, r.key_chg, r.thr, 0, r.n, version, r.row_len, r.hot_rows,
+                r.key_blk, r.thr_blk, r.blk)
         return out
 
     def shards_host(self, version: int) -> list:
@@ -233,11 +243,14 @@ class _Builder:
         cs = list(canon_stride) + [0] * (4 - nd)
         self.segs.append((t, s, nd, 0, shard_off, canon_off, ext, ss, cs))
 
-    def region(self, shard, elem_off, n, kind, thr, row_len=0, hot_rows=None):
+    def region(self, shard, elem_off, n, kind, thr, row_len=0, hot_rows=None, key_chg=None,
+               key_blk=0, thr_blk=0, blk=0):
         sid = self._stream
         self._stream += 1
+        kc = derive_key(self.seed, sid, 1) if key_chg is None else key_chg
         self.regions.append(Region(shard, elem_off, n, kind, derive_key(self.seed, sid, 0),
-                                   derive_key(self.seed, sid, 1), int(thr), row_len, hot_rows))
+                                   kc, int(thr), row_len, hot_rows, key_blk, int(thr_blk), blk))
+        return self.regions[-1]
 
     def build(self, assemble=None, meta=None) -> Layout:
         T = np.zeros(len(self.tensors), dtype=TENSOR_DT)
@@ -660,7 +673,8 @@ def _load_synth():
         lib = ctypes.CDLL(p)
         U64, U32, P = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
         lib.dcr_synth_fill.restype = ctypes.c_int32
-        lib.dcr_synth_fill.argtypes = [P, U64, U64, U32, U64, U64, U64, U64, P, U64, U32, U32, U32, P]
+        lib.dcr_synth_fill.argtypes = [P, U64, U64, U32, U64, U64, U64, U64, P, U64, U32, U64, U64, U32,
+                                       U32, U32, P]
         _synth_lib = lib
     return _synth_lib
 
@@ -691,8 +705,199 @@ def fill_shards_gpu(lay: Layout, shards, version: int, stream=None):
         n_hot = 0 if r.hot_rows is None else len(r.hot_rows)
         rc = lib.dcr_synth_fill(shards[r.shard].data_ptr(), r.elem_off, r.n, r.kind, r.key_old, r.key_chg,
                                 r.thr, r.row_len, hot_dev.data_ptr() if n_hot else None, hot_off, n_hot,
-                                version, SCALE_BITS, stream or None)
+                                r.key_blk, r.thr_blk, r.blk, version, SCALE_BITS, stream or None)
         if rc:
             raise RuntimeError(f"dcr_synth_fill failed: {rc}")
         hot_off += n_hot
     return hot_dev  # keep alive until the fills have run
+
+
+# ------------------------------------------------- configs 3 / 4 (MoE)
+
+def _uniforms(key: int, n: int) -> np.ndarray:
+    return (hashes(key, 0, n) >> np.uint64(11)).astype(np.float64) / float(1 << 53)
+
+
+def beta_2_60_rates(seed: int, numels: np.ndarray, mean: float) -> np.ndarray:
+    """One Beta(2, 60) draw per tensor (the 2nd smallest of 61 uniforms), then
+    rescaled so that the numel-weighted mean is `mean`; clamped to [0, 1]."""
+    n = len(numels)
+    u = _uniforms(derive_key(seed, 7777, 0), 61 * n).reshape(n, 61)
+    r = np.sort(u, axis=1)[:, 1]
+    w = numels.astype(np.float64)
+    r = r * mean * w.sum() / (r * w).sum()
+    return np.minimum(r, 1.0)
+
+
+def _hot_rows(seed: int, stream: int, rows: int, frac: float) -> np.ndarray:
+    """frac of the rows (at least one): the first ranks of a seeded permutation
+    of the row ids (the most-hit ids under a Zipf(1.1) popularity law)."""
+    k = max(1, int(np.ceil(frac * rows)))
+    order = np.argsort(hashes(derive_key(seed, 9000 + stream, 0), 0, rows), kind="stable")
+    return np.sort(order[:k]).astype(np.uint32)
+
+
+def moe_layout(hidden=2048, layers=48, n_exp=128, moe_ffn=768, n_q=32, n_kv=4, head_dim=128,
+               vocab=151936, ep=8, rate=0.03, variant="beta", seed=0xDC202603, name="cfg3",
+               hot_frac=0.01, scale_block=128, ow_share=0.05) -> Layout:
+    """Qwen3-30B-A3B-shaped MoE checkpoint, experts sharded EP=ep.
+
+    Trainer shards: each rank holds its n_exp/ep experts of every layer as
+    stacked tensors gate [E_r, moe_ffn, hidden], up [E_r, moe_ffn, hidden],
+    down [E_r, hidden, moe_ffn]; every non-expert tensor is stored whole and
+    owned by rank 0 (identity projection).  Canonical tensors are per expert.
+
+    variant "beta": per canonical tensor a change rate drawn from Beta(2,60),
+    rescaled to a `rate` (numel-weighted) mean; +-1 ulp changes.
+    variant "hot": `rate` overall with hot rows (hot_frac of the rows of
+    every 2-D tensor change at 100 %) and block-scaled experts: each expert
+    tensor gets an fp32 scale tensor of one scale per `scale_block` elements;
+    a changed scale changes its whole block (OW route), for `ow_share` of all
+    changes; the remaining changes are uniform.
+    """
+    assert n_exp % ep == 0 and n_q * head_dim >= hidden // 2
+    b = _Builder(name, seed)
+    e_r = n_exp // ep
+    q_out, kv_out = n_q * head_dim, n_kv * head_dim
+    hot = variant == "hot"
+    recipe = []
+    # ---- canonical tensors (id order = record order)
+    specs = []   # (name, rows, cols, kind, extra)
+    specs.append(("model.embed_tokens.weight", vocab, hidden, "whole", None))
+    for L in range(layers):
+        p = f"model.layers.{L}."
+        specs += [(p + "input_layernorm.weight", 1, hidden, "whole", None),
+                  (p + "self_attn.q_proj.weight", q_out, hidden, "whole", None),
+                  (p + "self_attn.k_proj.weight", kv_out, hidden, "whole", None),
+                  (p + "self_attn.v_proj.weight", kv_out, hidden, "whole", None),
+                  (p + "self_attn.o_proj.weight", hidden, q_out, "whole", None),
+                  (p + "self_attn.q_norm.weight", 1, head_dim, "whole", None),
+                  (p + "self_attn.k_norm.weight", 1, head_dim, "whole", None),
+                  (p + "post_attention_layernorm.weight", 1, hidden, "whole", None),
+                  (p + "mlp.gate.weight", n_exp, hidden, "whole", None)]
+        for e in range(n_exp):
+            for proj, rows, cols in (("gate_proj", moe_ffn, hidden), ("up_proj", moe_ffn, hidden),
+                                     ("down_proj", hidden, moe_ffn)):
+                specs.append((p + f"mlp.experts.{e}.{proj}.weight", rows, cols, "expert", (L, e, proj)))
+    specs.append(("model.norm.weight", 1, hidden, "whole", None))
+    specs.append(("lm_head.weight", vocab, hidden, "whole", None))
+    numels = np.array([r * c for _, r, c, _, _ in specs], dtype=np.int64)
+
+    if hot:
+        expert_numel = sum(n for (_, _, _, k, _), n in zip(specs, numels) if k == "expert")
+        total = numels.sum()
+        p_blk = ow_share * rate * total / expert_numel            # scale-block hit probability
+        hot_elems = sum(n * hot_frac for (_, r, _, _, _), n in zip(specs, numels) if r > 1)
+        base = (rate * total - hot_elems - p_blk * expert_numel) / (total - hot_elems - p_blk * expert_numel)
+        rates = np.full(len(specs), max(base, 0.0))
+        thr_blk = rate_thr(p_blk)
+    else:
+        rates = beta_2_60_rates(seed, numels, rate)
+        thr_blk = 0
+
+    # ---- shards: stacked expert shards per (layer, rank, proj); others whole
+    tid = {}
+    stack_shard = {}
+    scale_stack = {}
+    for i, (nm, rows, cols, kind, extra) in enumerate(specs):
+        route = ROUTE_BLOCK_SCALED if (hot and kind == "expert") else ROUTE_AFFINE_XOR
+        t = b.tensor(nm, rows * cols, 2, route, -1, 0)
+        tid[nm] = t
+        if hot and kind == "expert":
+            ns = (rows * cols + scale_block - 1) // scale_block
+            st = b.tensor(nm + "_scale", ns, 4, ROUTE_OVERWRITE)
+            b.tensors[t] = (rows * cols, 2, route, st, scale_block)
+        if kind == "whole":
+            s = b.shard(rows * cols, 2)
+            b.seg(t, s, 0, 0, [rows * cols], [1], [1])
+            hr = _hot_rows(seed, t, rows, hot_frac) if (hot and rows > 1) else None
+            b.region(s, 0, rows * cols, GEN_BF16_HOT if hot else GEN_BF16, rate_thr(rates[i]),
+                     row_len=cols, hot_rows=hr)
+            recipe.append((t, "whole", [s]))
+        else:
+            L, e, proj = extra
+            r_ = e // e_r
+            j = e % e_r
+            key = (L, r_, proj)
+            if key not in stack_shard:
+                stack_shard[key] = b.shard(e_r * rows * cols, 2)
+                if hot:
+                    scale_stack[key] = b.shard(e_r * ((rows * cols + scale_block - 1) // scale_block), 4)
+            s = stack_shard[key]
+            b.seg(t, s, j * rows * cols, 0, [rows * cols], [1], [1])
+            recipe.append((t, "stack_sel", (s, j, rows, cols)))
+            if hot:
+                ns = (rows * cols + scale_block - 1) // scale_block
+                kblk = derive_key(seed, 50000 + t, 1)
+                hr = _hot_rows(seed, t, rows, hot_frac)
+                b.region(s, j * rows * cols, rows * cols, GEN_BF16_HOT, rate_thr(rates[i]), row_len=cols,
+                         hot_rows=hr, key_blk=kblk, thr_blk=thr_blk, blk=scale_block)
+                ss = scale_stack[key]
+                st = b.tensors[t][3]
+                b.seg(st, ss, j * ns, 0, [ns], [1], [1])
+                b.region(ss, j * ns, ns, GEN_F32SCALE, thr_blk, key_chg=kblk)
+                recipe.append((st, "stack_sel", (ss, j, 1, ns)))
+            else:
+                b.region(s, j * rows * cols, rows * cols, GEN_BF16, rate_thr(rates[i]))
+
+    def assemble(shards):
+        return _assemble(recipe, shards, len(b.tensors))
+
+    return b.build(assemble=assemble, meta={"seed": seed, "rate": rate, "variant": variant, "ep": ep,
+                                            "rates": rates})
+
+
+def config3_layout(**kw) -> Layout:
+    return moe_layout(rate=0.03, variant="beta", seed=0xDC202603, name="cfg3", **kw)
+
+
+def config4_layout(**kw) -> Layout:
+    return moe_layout(rate=0.05, variant="hot", seed=0xDC202604, name="cfg4", **kw)
+
+
+def sub_layout(lay: Layout, tensor_ids):
+    """The inputs of a subset of tensors as a small layout of their own: each
+    segment reads a private mini-shard holding just the shard range it
+    touches, generated on the CPU from the same regions.  Returns
+    (tensors, segments, old mini-shards, new mini-shards); tensor ids are
+    renumbered in the given order (scale links follow when both are kept)."""
+    tensor_ids = list(tensor_ids)
+    remap = {t: i for i, t in enumerate(tensor_ids)}
+    T = lay.tensors[tensor_ids].copy()
+    for i, t in enumerate(tensor_ids):
+        st = int(lay.tensors[t]["scale_tensor"])
+        if st >= 0:
+            assert st in remap, "keep a block-scaled tensor's scale tensor in the subset"
+            T[i]["scale_tensor"] = remap[st]
+    segs, olds, news = [], [], []
+    for g in lay.segments:
+        t = int(g["tensor_id"])
+        if t not in remap:
+            continue
+        nd = int(g["ndim"])
+        ext = [int(x) for x in g["extent"][:nd]]
+        ss = [int(x) for x in g["shard_stride"][:nd]]
+        lo = int(g["shard_off"]) + sum(min(0, (e - 1) * s) for e, s in zip(ext, ss))
+        hi = int(g["shard_off"]) + sum(max(0, (e - 1) * s) for e, s in zip(ext, ss)) + 1
+        s = int(g["shard_id"])
+        w = lay.shard_w[s]
+        dt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[w]
+        mo, mn = np.zeros(hi - lo, dtype=dt), np.zeros(hi - lo, dtype=dt)
+        for r in lay.regions:
+            if r.shard != s:
+                continue
+            a, b_ = max(lo, r.elem_off), min(hi, r.elem_off + r.n)
+            if a >= b_:
+                continue
+            for v, out in ((0, mo), (1, mn)):
+                out[a - lo:b_ - lo] = gen_region(r.kind, r.key_old, r.key_chg, r.thr, a - r.elem_off, b_ - a,
+                                                 v, r.row_len, r.hot_rows, r.key_blk, r.thr_blk, r.blk)
+        g2 = g.copy()
+        g2["tensor_id"] = remap[t]
+        g2["shard_id"] = len(olds)
+        g2["shard_off"] = int(g["shard_off"]) - lo
+        segs.append(g2)
+        olds.append(mo)
+        news.append(mn)
+    S = np.array(segs, dtype=SEGMENT_DT) if segs else np.zeros(0, dtype=SEGMENT_DT)
+    return T, S, olds, news

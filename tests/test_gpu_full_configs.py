@@ -1,0 +1,152 @@
+"""Full-size GPU runs of the Llama-8B TP=4, Qwen3-30B-A3B EP=8 (3 %, Beta(2,60)
+rates) and block-scaled 5 % hot-row MoE workloads.
+
+At these sizes the oracle cannot run the whole model in seconds, so:
+  * sampled parity: the GPU's records of a sample of tensors equal, byte for
+    byte, the oracle's records for those tensors (oracle inputs regenerated on
+    the CPU from the seeded generator);
+  * properties on the whole model: records count exactly the elements whose
+    stored bits differ; apply turns the old canonical tensors into the new
+    ones; after a kill at 50 % of the records the overwrite retry heals all.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from bit_exact_xor_amd import dcr, synth
+from tests import fmt
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def typed(lay, shards):
+    """Element-typed views of byte shards (what the layout's assembly expects)."""
+    return [x.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[lay.shard_w[s]]) for s, x in enumerate(shards)]
+
+
+def run_full(orc, lay, sample_names):
+    assert torch.cuda.is_available()
+    say(lay.name, "plan")
+    T = lay.tensors
+    plan = dcr.dcr_plan_build(T, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
+    dcr.dcr_plan_upload(plan, "cuda")
+    say(lay.name, "inputs", f"{plan.info.canonical_bytes / 1e9:.1f} GB canonical")
+    ob, olds = synth.alloc_shards(lay, "cuda")
+    nb, news = synth.alloc_shards(lay, "cuda")
+    synth.fill_shards_gpu(lay, olds, 0)
+    synth.fill_shards_gpu(lay, news, 1)
+    ws = dcr.workspace(plan, "cuda")
+    cb = int(plan.info.canonical_bytes)
+    sb = dcr.StreamBuffers(plan, "cuda", dir_bytes=2 * 32 * int(plan.info.n_chunks),
+                           payload_bytes=int(cb * 0.2) + (1 << 20))
+    torch.cuda.synchronize()
+    say(lay.name, "encode")
+    dcr.dcr_encode(plan, olds, news, 0, 3, 4, sb.header, sb.dir, sb.payload, sb.result, ws)
+    torch.cuda.synchronize()
+    r = sb.result_host()
+    assert int(r["status"]) == 0, r
+    n_rec, pbytes = int(r["n_records"]), int(r["payload_bytes"])
+    # property: records count exactly the differing stored elements
+    diff = 0
+    for s in range(lay.n_shards):
+        w = lay.shard_w[s]
+        a = olds[s].view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[w])
+        b = news[s].view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[w])
+        diff += int((a != b).sum())
+    assert int(r["n_changed"]) == diff
+    say(lay.name, f"{n_rec} records, {pbytes / 1e9:.2f} GB payload, {diff} changed")
+
+    # sampled parity against the oracle
+    name_to_t = {n: i for i, n in enumerate(lay.tensor_names)}
+    sample = [name_to_t[n] for n in sample_names]
+    for t in list(sample):
+        st = int(T[t]["scale_tensor"])
+        if st >= 0 and st not in sample:
+            sample.append(st)
+    sample.sort()
+    Ts, Ss, so, sn = synth.sub_layout(lay, sample)
+    rc, h, d, p = orc.encode(Ts, Ss, so, sn, base_version=3, new_version=4)
+    assert rc == 0
+    gd = sb.dir[: n_rec * 32].cpu().numpy()
+    ents = fmt.dirents(gd)
+    remap = {t: i for i, t in enumerate(sample)}
+    mine = [e for e in ents if e["t"] in remap]
+    theirs = fmt.dirents(d)
+    assert len(mine) == len(theirs) and len(theirs) > 0
+    for e, o in zip(mine, theirs):
+        assert (remap[e["t"]], e["c"], e["K"], e["kind"], e["hi_mode"], e["w"], e["size"], e["H"]) == \
+               (o["t"], o["c"], o["K"], o["kind"], o["hi_mode"], o["w"], o["size"], o["H"])
+        got = sb.payload[e["off"]:e["off"] + e["size"]].cpu().numpy()
+        assert np.array_equal(got, p[o["off"]:o["off"] + o["size"]]), (lay.tensor_names[e["t"]], e["c"])
+    say(lay.name, f"sampled parity: {len(theirs)} records of {len(sample)} tensors identical")
+
+    # apply / kill at 50 % / retry, on canonical tensors
+    co = lay.assemble(typed(lay, olds))
+    sizes = [int(T[t]["numel"]) * int(T[t]["elem_bytes"]) for t in range(len(T))]
+    offs = np.concatenate([[0], np.cumsum([(s + 255) // 256 * 256 for s in sizes])]).astype(np.int64)
+    cbuf = torch.empty(int(offs[-1]), dtype=torch.uint8, device="cuda")
+    canon = [cbuf[int(offs[t]):int(offs[t]) + sizes[t]] for t in range(len(T))]
+    for t in range(len(T)):
+        canon[t].copy_(co[t].reshape(-1).view(torch.uint8))
+    del co
+    cn = lay.assemble(typed(lay, news))
+    hdr = sb.header.cpu().numpy()
+    flags = torch.zeros(max(n_rec, 1), dtype=torch.uint8, device="cuda")
+    res = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    say(lay.name, "apply")
+    dcr.dcr_apply(plan, canon, hdr, sb.dir, sb.payload, flags, 0, n_rec, 3, res, ws)
+    torch.cuda.synchronize()
+    ar = dcr.apply_result(res)
+    assert int(ar["n_applied"]) == n_rec and int(ar["n_invalid"]) == 0
+    for t in range(len(T)):
+        assert torch.equal(canon[t], cn[t].reshape(-1).view(torch.uint8)), lay.tensor_names[t]
+    # back to old by re-copying, apply the first half (a kill), retry all
+    co = lay.assemble(typed(lay, olds))
+    for t in range(len(T)):
+        canon[t].copy_(co[t].reshape(-1).view(torch.uint8))
+    del co
+    flags.zero_()
+    dcr.dcr_apply(plan, canon, hdr, sb.dir, sb.payload, flags, 0, n_rec // 2, 3, res, ws)
+    del sb
+    rsb = dcr.StreamBuffers(plan, "cuda", dir_bytes=32 * int(plan.info.n_chunks),
+                            payload_bytes=int(cb * 0.2) + (1 << 20))
+    say(lay.name, "retry")
+    dcr.dcr_encode(plan, olds, news, 1, 3, 4, rsb.header, rsb.dir, rsb.payload, rsb.result, ws)
+    torch.cuda.synchronize()
+    assert int(rsb.result_host()["status"]) == 0
+    dcr.dcr_apply_overwrite_retry(plan, canon, rsb.header.cpu().numpy(), rsb.dir, rsb.payload, 3, res, ws)
+    torch.cuda.synchronize()
+    for t in range(len(T)):
+        assert torch.equal(canon[t], cn[t].reshape(-1).view(torch.uint8)), lay.tensor_names[t]
+    say(lay.name, "apply, kill at 50 % and retry: all tensors equal new")
+    del cbuf, canon, cn, ob, nb, olds, news, rsb
+    torch.cuda.empty_cache()
+
+
+def test_full_llama8b_tp4(orc):
+    lay = synth.llama_layout()
+    run_full(orc, lay, ["model.layers.0.input_layernorm.weight", "model.layers.0.self_attn.q_proj.weight",
+                        "model.layers.0.self_attn.k_proj.weight", "model.layers.0.self_attn.o_proj.weight",
+                        "model.layers.31.mlp.down_proj.weight", "model.norm.weight"])
+
+
+def test_full_qwen30b_ep8_beta(orc):
+    lay = synth.config3_layout()
+    run_full(orc, lay, ["model.layers.0.self_attn.q_proj.weight", "model.layers.0.self_attn.o_proj.weight",
+                        "model.layers.0.mlp.gate.weight", "model.layers.0.self_attn.q_norm.weight",
+                        "model.layers.0.mlp.experts.0.gate_proj.weight",
+                        "model.layers.47.mlp.experts.127.down_proj.weight", "model.norm.weight"])
+
+
+def test_full_qwen30b_hot_block_scaled(orc):
+    lay = synth.config4_layout()
+    run_full(orc, lay, ["model.layers.0.self_attn.q_proj.weight", "model.layers.0.mlp.gate.weight",
+                        "model.layers.0.mlp.experts.0.gate_proj.weight",
+                        "model.layers.0.mlp.experts.5.down_proj.weight",
+                        "model.layers.47.mlp.experts.127.up_proj.weight", "model.norm.weight"])
