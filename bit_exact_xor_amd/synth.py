@@ -901,3 +901,47 @@ def sub_layout(lay: Layout, tensor_ids):
         news.append(mn)
     S = np.array(segs, dtype=SEGMENT_DT) if segs else np.zeros(0, dtype=SEGMENT_DT)
     return T, S, olds, news
+
+
+# ------------------------------------------------ config 5 (receiver share)
+
+def config5_layout(n_bf16=6812, bf16_shape=(7168, 2048), n_u8=5450, u8_shape=(7168, 1024),
+                   rate_bf16=0.03, rate_u8=0.00085, seed=0xDC202605) -> Layout:
+    """One GPU's receiver share of a 1T-parameter model: n_bf16 BF16 tensors
+    (100 B parameters, 200 GB) and n_u8 uint8 NVFP4-packed tensors (40 GB),
+    each stored whole (identity projection, shard i = tensor i)."""
+    b = _Builder("cfg5", seed)
+    recipe = []
+    for i in range(n_bf16):
+        n = bf16_shape[0] * bf16_shape[1]
+        t = b.tensor(f"bf16.{i}", n, 2)
+        s = b.shard(n, 2)
+        b.seg(t, s, 0, 0, [n], [1], [1])
+        b.region(s, 0, n, GEN_BF16, rate_thr(rate_bf16))
+        recipe.append((t, "whole", [s]))
+    for i in range(n_u8):
+        n = u8_shape[0] * u8_shape[1]
+        t = b.tensor(f"nvfp4.{i}", n, 1)
+        s = b.shard(n, 1)
+        b.seg(t, s, 0, 0, [n], [1], [1])
+        b.region(s, 0, n, GEN_U8, rate_thr(rate_u8))
+        recipe.append((t, "whole", [s]))
+
+    def assemble(shards):
+        return _assemble(recipe, shards, len(b.tensors))
+
+    return b.build(assemble=assemble, meta={"seed": seed})
+
+
+def window_layout(lay: Layout, a: int, b_: int) -> Layout:
+    """Tensors [a, b_) of an identity layout (shard i = tensor i) as a layout of
+    their own, with shard and tensor ids renumbered from 0."""
+    T = lay.tensors[a:b_].copy()
+    S = lay.segments[a:b_].copy()
+    S["tensor_id"] = np.arange(b_ - a)
+    S["shard_id"] = np.arange(b_ - a)
+    regions = []
+    for r in lay.regions[a:b_]:
+        regions.append(dataclasses.replace(r, shard=r.shard - a))
+    return Layout(f"{lay.name}[{a}:{b_}]", lay.tensor_names[a:b_], T, S, lay.shard_elems[a:b_],
+                  lay.shard_w[a:b_], regions, None, {})
