@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
     ap.add_argument("--cpu-reps", type=int, default=4, help="oracle steps timed on the sample")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain device copy of this many GiB, 3 times (counter calibration)")
+    ap.add_argument("--pmc-report", metavar="DIR",
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs found under DIR and exit")
     return ap.parse_args()
 
 
@@ -52,6 +56,9 @@ def log(*a):
 
 def main():
     args = parse()
+    if args.pmc_report:
+        print(pmc_report(args.pmc_report))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: --gpus {args.gpus}: this build runs the hot path on one GPU only "
               "(no cross-GPU sharding or collectives); run with --gpus 1", file=sys.stderr)
@@ -66,6 +73,16 @@ def main():
     dcr.load_library()
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        n = int(args.copy_probe * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 4 * n, "reps": 3}), flush=True)
+        return
 
     # ---------------------------------------------------------------- setup
     t0 = time.time()
@@ -197,7 +214,7 @@ def main():
     roof = {"bound": "hbm", "kernel": {"encode": "encode_kernel", "encode_retry": "encode_kernel",
                                        "apply": "apply_kernel", "retry": "apply_kernel"}[dom],
             "op": dom, "achieved": per_op[dom]["alg_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": per_op[dom]["hbm_frac"], "traffic": None}
+            "frac": per_op[dom]["hbm_frac"], "traffic": measured_traffic(dom)}
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
@@ -294,6 +311,98 @@ def cpu_baseline(lay, delta, hdr_dev, reps):
                      f"median of {reps}",
            "step_s": round(step_s, 3)}
     return cpu, {"tensors": len(T), "records": len(oents), "identical": bool(same)}
+
+
+# ------------------------------------------------------------ HBM traffic
+#
+# rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (one counter per run) give
+# KiB per dispatch.  Each counter is scaled by what it reads for a plain
+# device copy of known size (bench.py --copy-probe).  The scaled bytes per
+# launch are kept in a summary under profiles/ together with the SHA-256 of the
+# kernel source they were measured on; the bench reports them only while the
+# source is unchanged, else null.
+
+KERNEL_SRC = os.path.join(ROOT, "bit_exact_xor_amd", "csrc", "dcr_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_apply_llama8b_tp4_hbm_traffic.md")
+TRAFFIC_TAG = "traffic-json:"
+
+
+def _src_sha256():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(op):
+    """HBM bytes per launch of op's kernel from the committed counter summary,
+    or None when that summary is missing or the kernel source has changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            line = next(ln for ln in f if ln.strip().startswith(TRAFFIC_TAG))
+    except (OSError, StopIteration):
+        return None
+    rec = json.loads(line.strip()[len(TRAFFIC_TAG):])
+    if rec.get("source_sha256") != _src_sha256():
+        return None
+    return rec["bytes_per_launch"].get(op)
+
+
+def _pmc_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def pmc_report(d):
+    """Markdown summary of four rocprofv3 --pmc runs under d: pmc_FETCH_SIZE and
+    pmc_WRITE_SIZE of bench.py, pmc_copy_FETCH_SIZE and pmc_copy_WRITE_SIZE of
+    bench.py --copy-probe (3 copies of a known size)."""
+    import glob
+
+    def rows(sub):
+        (path,) = glob.glob(os.path.join(d, sub, "*_counter_collection.csv"))
+        return _pmc_rows(path)
+
+    def per_kernel(rs, key):
+        out = {}
+        for r in rs:
+            if key in r["Kernel_Name"]:
+                out.setdefault(int(r["Dispatch_Id"]), 0.0)
+                out[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+        return [out[k] for k in sorted(out)]
+
+    factors = {}
+    copy_bytes = None
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = per_kernel(rows(f"pmc_copy_{c}"), "copyBuffer")
+        kib = float(np.mean(v))
+        log_path = os.path.join(d, f"pmc_copy_{c}.log")
+        with open(log_path) as f:
+            probe = json.loads(next(ln for ln in f if ln.startswith("{\"copy_probe_bytes\"")))
+        copy_bytes = probe["copy_probe_bytes"]
+        factors[c] = copy_bytes / (kib * 1024.0)
+    # dispatch order per step in bench.py: encode DELTA, encode RETRY (first step),
+    # then encode DELTA, apply, encode RETRY, retry; kernels alternate
+    ops = {"encode": ("encode_kernel", 0), "encode_retry": ("encode_kernel", 1),
+           "apply": ("apply_kernel(", 0), "retry": ("apply_kernel(", 1)}
+    table, per_launch = [], {}
+    for op, (k, parity) in ops.items():
+        got = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = per_kernel(rows(f"pmc_{c}"), k)[parity::2]
+            got[c] = (len(v), float(np.mean(v)))
+        fb = got["FETCH_SIZE"][1] * 1024 * factors["FETCH_SIZE"]
+        wb = got["WRITE_SIZE"][1] * 1024 * factors["WRITE_SIZE"]
+        per_launch[op] = int(round(fb + wb))
+        table.append(f"| {op} | `{k.rstrip('(')}` | {got['FETCH_SIZE'][0]} | {got['FETCH_SIZE'][1]:.0f} | "
+                     f"{got['WRITE_SIZE'][1]:.0f} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | {(fb + wb) / 1e9:.3f} |")
+    out = [f"Copy calibration ({copy_bytes / 2**30:.0f} GiB device copy read and written): "
+           f"FETCH_SIZE x {factors['FETCH_SIZE']:.4f}, WRITE_SIZE x {factors['WRITE_SIZE']:.4f}.", "",
+           "| op | kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | written GB | HBM GB / launch |",
+           "|---|---|---|---|---|---|---|---|", *table, "",
+           TRAFFIC_TAG + " " + json.dumps({"source_sha256": _src_sha256(), "bytes_per_launch": per_launch,
+                                            "factors": factors})]
+    return "\n".join(out)
 
 
 def fmt_dirents(d):
