@@ -27,6 +27,11 @@ constexpr int kValShift = 2;
 constexpr int kRecShift = 36;
 constexpr uint64_t kP16Mask = (uint64_t(1) << kRecShift) - 1;
 constexpr uint64_t kMaxTiles = uint64_t(1) << 25;   // 2 records per tile < 2^26
+constexpr uint32_t kFixTiles = 256;                 // tiles per workgroup of the encode fix-up
+// encode counters (uint32 words at ws_counter): [0] tile claim, [1] fix-up
+// block claim, [2..3] changed elements, [4..5] stream total
+// (records << 36 | payload / 16)
+constexpr uint32_t kCtrTile = 0, kCtrFix = 1, kCtrChanged = 2, kCtrTotal = 4;
 
 // Device-side tensor descriptor.  48 bytes.
 struct DevTensor {
@@ -68,15 +73,16 @@ struct Plan {
     std::vector<DevChunk> chunks;
     std::vector<DevPiece> pieces;
     std::vector<uint32_t> scale_chunks;   // chunks of scale tensors that gate a BLOCK_SCALED one
+    std::vector<uint64_t> slots;          // per chunk: staging slot offset (prefix of worst cases)
     uint64_t fingerprint = 0;
     uint64_t canonical_bytes = 0;
     uint64_t scale_bits = 0;              // total flag bits (multiple of 64)
     uint64_t max_dir_bytes = 0, max_payload_bytes = 0;
     // device table layout
-    uint64_t off_tensors = 0, off_chunks = 0, off_pieces = 0, off_scale_chunks = 0, table_bytes = 0;
+    uint64_t off_tensors = 0, off_chunks = 0, off_pieces = 0, off_scale_chunks = 0, off_slots = 0, table_bytes = 0;
     // workspace layout
-    uint64_t ws_status = 0, ws_counter = 0, ws_old = 0, ws_new = 0, ws_scale = 0, ws_canon = 0,
-             ws_bytes = 0;
+    uint64_t ws_status = 0, ws_fix = 0, ws_counter = 0, ws_old = 0, ws_new = 0, ws_scale = 0, ws_canon = 0,
+             ws_agg = 0, ws_info = 0, ws_bytes = 0;
     std::vector<uint8_t> blob;            // host image of the device tables
     void* dev_tables = nullptr;           // bound by dcr_plan_upload
 };

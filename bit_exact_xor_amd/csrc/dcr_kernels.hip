@@ -108,6 +108,21 @@ __device__ __forceinline__ void set_elem(uint32_t (&q)[4], uint32_t e, uint32_t 
     else q[e >> 2] |= (v & 0xFFu) << (8u * (e & 3u));
 }
 __device__ __forceinline__ uint32_t sgpr(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+// A workgroup-uniform struct loaded from memory, moved word by word into
+// scalar registers (the loads themselves cannot be scalar once the kernel has
+// written memory, and vector copies would occupy VGPRs for the whole tile).
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* p) {
+    static_assert(sizeof(T) % 4 == 0, "uniform_load");
+    const T v = *p;
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (uint32_t i = 0; i < sizeof(T) / 4; i++) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+    T r;
+    __builtin_memcpy(&r, w, sizeof(T));
+    return r;
+}
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) v4u* gv4p;   // global (not flat) 128-bit loads
 
@@ -132,13 +147,18 @@ struct EncodeArgs {
     const uint8_t* const* new_sh;
     const uint64_t* scale_flags;
     uint64_t* status;
-    uint32_t* counter;      // [0] tile counter, [2..3] changed elements (u64)
+    uint32_t* counter;      // encode counters (kCtr*)
+    uint64_t* tile_agg;     // per tile: records << 36 | payload / 16
+    uint64_t* tile_info;    // per tile: Kx | Ko << 17 | Hx << 34
+    const uint64_t* slots;  // per tile: staging slot offset
+    uint8_t* stage;         // staging area (staged launches)
     uint8_t* dir;
     uint8_t* payload;
     uint64_t dir_cap;       // bytes
     uint64_t payload_cap;   // bytes
     uint32_t n_tiles;
     uint32_t mode;
+    uint32_t staged;        // 1: every tile writes to its slot, nobody waits
 };
 
 struct EncodeShared {
@@ -149,6 +169,89 @@ struct EncodeShared {
     uint64_t excl;
     uint32_t next;
 };
+
+// Sizes and high-byte mode of a chunk's records (the record layout of the
+// format): bitmap, low plane, then for 2-byte XOR records a sparse (presence
+// bitmap + nonzero high bytes) or dense high plane, whichever is smaller
+// (dense on a tie); overwrite records carry all W byte planes.
+struct RecLayout {
+    uint32_t size_x, size_o;     // bytes of the XOR / overwrite record (0: none)
+    uint32_t mode_x, h_x;        // XOR record: hi_mode and its H field
+    uint32_t off_pres, off_hi_x; // XOR record: presence bitmap / high plane offsets
+};
+
+__device__ __forceinline__ RecLayout rec_layout(uint32_t w, uint32_t n_c, uint32_t Kx, uint32_t Ko, uint32_t Hx) {
+    RecLayout L{0, 0, DCR_HI_NONE, 0, 0, 0};
+    const uint32_t bm = dpad16((n_c + 7) / 8);
+    if (Kx) {
+        L.size_x = bm + dpad16(Kx);
+        L.off_hi_x = L.size_x;
+        if (w == 2 && Hx) {
+            const uint32_t sparse = dpad16((Kx + 7) / 8) + dpad16(Hx);
+            if (sparse < dpad16(Kx)) {
+                L.mode_x = DCR_HI_SPARSE;
+                L.off_pres = L.size_x;
+                L.off_hi_x = L.size_x + dpad16((Kx + 7) / 8);
+                L.size_x += sparse;
+                L.h_x = Hx;
+            } else {
+                L.mode_x = DCR_HI_DENSE;
+                L.size_x += dpad16(Kx);
+                L.h_x = Kx;
+            }
+        }
+    }
+    if (Ko) L.size_o = bm + w * dpad16(Ko);
+    return L;
+}
+
+// Directory entry `which` (0 = first record of the tile) of a tile whose
+// records start at payload offset P.
+__device__ __forceinline__ void put_dirent(uint8_t* dir, uint64_t index, uint32_t which, uint32_t tensor,
+                                           uint32_t chunk, uint32_t w, const RecLayout& L, uint32_t Kx,
+                                           uint32_t Ko, uint64_t P) {
+    const bool x = Kx && which == 0;
+    v4u e0, e1;
+    e0.x = tensor;
+    e0.y = chunk;
+    e0.z = x ? Kx : Ko;
+    const uint32_t hm = x ? L.mode_x : (w == 1 ? uint32_t(DCR_HI_NONE) : uint32_t(DCR_HI_DENSE));
+    e0.w = (x ? 0u : 1u) | (hm << 8) | (w << 16);
+    const uint64_t off = P + (x ? 0u : L.size_x);
+    e1.x = uint32_t(off);
+    e1.y = uint32_t(off >> 32);
+    e1.z = x ? L.size_x : L.size_o;
+    e1.w = x ? L.h_x : (w == 1 ? 0u : Ko);
+    v4u* de = reinterpret_cast<v4u*>(dir + index * DCR_DIRENT_BYTES);
+    de[0] = e0;
+    de[1] = e1;
+}
+
+// Decoupled look-back, run by one full wave: the exclusive sum of the values
+// of entries [0, idx) of `status`.  Waits until each entry it needs holds at
+// least an aggregate; every entry below idx belongs to a workgroup that has
+// already started (ids are claimed in order), so the wait ends.
+__device__ __forceinline__ uint64_t look_back(const uint64_t* status, uint32_t idx, uint32_t lane) {
+    uint64_t excl = 0;
+    int64_t hi = int64_t(idx) - 1;
+    while (hi >= 0) {
+        const int64_t i = hi - int64_t(lane);
+        const uint64_t st = i >= 0 ? ld_status(status + i) : kFlagIncl;
+        const uint32_t flag = uint32_t(st & 3u);
+        const uint64_t incl_m = __ballot(flag == kFlagIncl);
+        const uint64_t zero_m = __ballot(flag == 0);
+        const uint32_t first = incl_m ? uint32_t(__ffsll((unsigned long long)incl_m) - 1) : 64u;
+        const uint64_t need = first >= 63 ? ~uint64_t(0) : ((uint64_t(2) << first) - 1);
+        if (zero_m & need) {
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        excl += wave_sum(lane <= first ? (st >> kValShift) : 0);
+        if (first < 64) break;
+        hi -= 64;
+    }
+    return excl;
+}
 
 // Gather one 16-byte group (elements e0 .. e0+V-1 of the chunk) of old and
 // new.  Elements at or past n_c read as zero in both.
@@ -301,75 +404,43 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, EncodeShared& S
         Hx += sgpr(field16(tot[2], k));
     }
     const uint32_t bm = dpad16((n_c + 7) / 8);
-    uint32_t mode_x = DCR_HI_NONE, size_x = 0, size_o = 0, Hfield_x = 0;
-    uint32_t off_pres = 0, off_hi_x = 0;
-    if (Kx) {
-        size_x = bm + dpad16(Kx);
-        off_hi_x = size_x;
-        if constexpr (W == 2) {
-            if (Hx) {
-                const uint32_t sparse = dpad16((Kx + 7) / 8) + dpad16(Hx);
-                if (sparse < dpad16(Kx)) {
-                    mode_x = DCR_HI_SPARSE;
-                    off_pres = size_x;
-                    off_hi_x = size_x + dpad16((Kx + 7) / 8);
-                    size_x += sparse;
-                    Hfield_x = Hx;
-                } else {
-                    mode_x = DCR_HI_DENSE;
-                    size_x += dpad16(Kx);
-                    Hfield_x = Kx;
-                }
-            }
-        }
-    }
-    if (Ko) size_o = bm + W * dpad16(Ko);
+    const RecLayout L = rec_layout(W, n_c, Kx, Ko, Hx);
+    const uint32_t mode_x = L.mode_x, size_x = L.size_x, off_pres = L.off_pres, off_hi_x = L.off_hi_x;
     const uint32_t base_o = size_x;
-    const uint32_t tile_bytes = size_x + size_o;
+    const uint32_t tile_bytes = size_x + L.size_o;
     const uint32_t nrec = (Kx ? 1u : 0u) + (Ko ? 1u : 0u);
     const uint64_t agg = (uint64_t(nrec) << kRecShift) | (tile_bytes >> 4);
 
-    // publish the aggregate as early as possible
+    // sizes for the fix-up pass; staged: records go to the tile's slot (the
+    // fix-up moves them into place); else publish the aggregate and look back
     if (tid == 0) {
-        st_status(a.status + tile, (agg << kValShift) | (tile == 0 ? kFlagIncl : kFlagAgg));
-        if (Kx + Ko) atomicAdd(reinterpret_cast<unsigned long long*>(a.counter + 2), (unsigned long long)(Kx + Ko));
+        if (!a.staged) st_status(a.status + tile, (agg << kValShift) | (tile == 0 ? kFlagIncl : kFlagAgg));
+        a.tile_agg[tile] = agg;
+        a.tile_info[tile] = uint64_t(Kx) | (uint64_t(Ko) << 17) | (uint64_t(Hx) << 34);
     }
-
-    // ---- decoupled look-back (first wave): exclusive (records, payload/16)
-    if (tid < 64) {
-        const uint32_t lane = tid;
-        uint64_t excl = 0;
-        if (tile > 0) {
-            int64_t hi = int64_t(tile) - 1;
-            while (true) {
-                const int64_t idx = hi - int64_t(lane);
-                const uint64_t s = idx >= 0 ? ld_status(a.status + idx) : kFlagIncl;
-                const uint32_t flag = uint32_t(s & 3u);
-                const uint64_t incl_m = __ballot(flag == kFlagIncl);
-                const uint64_t zero_m = __ballot(flag == 0);
-                const uint32_t first = incl_m ? uint32_t(__ffsll((unsigned long long)incl_m) - 1) : 64u;
-                const uint64_t need = first >= 63 ? ~uint64_t(0) : ((uint64_t(2) << first) - 1);
-                if (zero_m & need) {
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                excl += wave_sum(lane <= first ? (s >> kValShift) : 0);
-                if (first < 64) break;
-                hi -= 64;
+    if (nrec == 0) return;   // uniform; an empty tile's aggregate is all it owes
+    uint8_t* out;
+    uint64_t R = 0, P = 0;
+    if (a.staged) {
+        out = a.stage + a.slots[tile];
+    } else {
+        // ---- decoupled look-back (first wave): exclusive (records, payload/16)
+        if (tid < 64) {
+            const uint64_t excl = look_back(a.status, tile, tid);
+            if (tid == 0) {
+                if (tile > 0) st_status(a.status + tile, ((excl + agg) << kValShift) | kFlagIncl);
+                S.excl = excl;
             }
-            if (lane == 0) st_status(a.status + tile, ((excl + agg) << kValShift) | kFlagIncl);
         }
-        if (lane == 0) S.excl = excl;
+        __syncthreads();
+        R = S.excl >> kRecShift;
+        P = (S.excl & kP16Mask) << 4;
+        const bool fits = (R + nrec) * DCR_DIRENT_BYTES <= a.dir_cap && P + tile_bytes <= a.payload_cap;
+        if (!fits) return;   // uniform
+        out = a.payload + P;
     }
-    __syncthreads();
 
-    const uint64_t R = S.excl >> kRecShift;
-    const uint64_t P = (S.excl & kP16Mask) << 4;
-    const bool fits = (R + nrec) * DCR_DIRENT_BYTES <= a.dir_cap && P + tile_bytes <= a.payload_cap;
-    if (!fits || nrec == 0) return;   // uniform: nothing to write for this tile
-
-    // ---- write the records straight to the payload
-    uint8_t* out = a.payload + P;
+    // ---- write the records (in place or to the staging area)
     const uint32_t pkx = dpad16(Kx), pko = dpad16(Ko);
     // zero padding tails (each at most 15 bytes)
     if (tid < 16) {
@@ -470,24 +541,7 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, EncodeShared& S
             j++;
         }
     }
-    if (tid < nrec) {
-        const bool x = Kx && tid == 0;
-        const uint32_t K = x ? Kx : Ko;
-        v4u e0, e1;
-        e0.x = ch.tensor;
-        e0.y = ch.chunk_idx;
-        e0.z = K;
-        const uint32_t hm = x ? mode_x : (W == 1 ? uint32_t(DCR_HI_NONE) : uint32_t(DCR_HI_DENSE));
-        e0.w = (x ? 0u : 1u) | (hm << 8) | (uint32_t(W) << 16);
-        const uint64_t off = P + (x ? 0u : base_o);
-        e1.x = uint32_t(off);
-        e1.y = uint32_t(off >> 32);
-        e1.z = x ? size_x : size_o;
-        e1.w = x ? Hfield_x : (W == 1 ? 0u : Ko);
-        v4u* de = reinterpret_cast<v4u*>(a.dir + (R + tid) * DCR_DIRENT_BYTES);
-        de[0] = e0;
-        de[1] = e1;
-    }
+    if (!a.staged && tid < nrec) put_dirent(a.dir, R + tid, tid, ch.tensor, ch.chunk_idx, W, L, Kx, Ko, P);
     if (hi_x_sparse) {
         __syncthreads();
         const uint32_t nq = dpad16((Kx + 7) / 8) / 16;
@@ -496,20 +550,135 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, EncodeShared& S
     }
 }
 
-// One workgroup per tile.  Tiles are claimed in increasing order from a
-// counter, so every tile a look-back waits on belongs to a workgroup that is
-// already running.
+// One workgroup per tile.  Unstaged, tiles are claimed in increasing order
+// from a counter, so every tile a look-back waits on belongs to a workgroup
+// that is already running; staged, nothing waits and the tile is the
+// workgroup id.
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_kernel(EncodeArgs a) {
     __shared__ EncodeShared S;
-    if (threadIdx.x == 0) S.next = atomicAdd(a.counter, 1u);
-    __syncthreads();
-    const uint32_t tile = S.next;
+    uint32_t tile = blockIdx.x;
+    if (!a.staged) {
+        if (threadIdx.x == 0) S.next = atomicAdd(a.counter + kCtrTile, 1u);
+        __syncthreads();
+        tile = sgpr(S.next);
+    }
     if (tile >= a.n_tiles) return;
-    const DevChunk ch = a.chunks[tile];
-    const DevTensor td = a.tensors[ch.tensor];
+    const DevChunk ch = uniform_load(a.chunks + tile);
+    const DevTensor td = uniform_load(a.tensors + ch.tensor);
     if (td.w == 2) encode_tile<2>(a, S, tile, ch, td);
     else if (td.w == 1) encode_tile<1>(a, S, tile, ch, td);
     else encode_tile<4>(a, S, tile, ch, td);
+}
+
+// Encode fix-up: one workgroup of 256 threads per kFixTiles consecutive
+// tiles.  Scans the tiles' aggregates (records, payload/16) into exclusive
+// prefixes (a short decoupled look-back across fix-up blocks), sums the
+// changed elements, and in a staged launch moves every tile's records from
+// its slot to their place in the payload and writes their directory
+// entries.  The last block stores the stream totals.
+struct FixArgs {
+    const DevTensor* tensors;
+    const DevChunk* chunks;
+    const uint64_t* tile_agg;
+    const uint64_t* tile_info;
+    const uint64_t* slots;
+    uint64_t* fix_status;
+    uint32_t* counter;
+    const uint8_t* stage;
+    uint8_t* dir;
+    uint8_t* payload;
+    uint64_t dir_cap;
+    uint64_t payload_cap;
+    uint32_t n_tiles;
+    uint32_t n_blocks;
+    uint32_t staged;
+};
+
+__global__ __launch_bounds__(256) void encode_fixup_kernel(FixArgs a) {
+    constexpr uint32_t NW = kFixTiles / 64;
+    __shared__ uint64_t wtot[NW], wchg[NW];
+    __shared__ uint64_t excl_of[kFixTiles];
+    __shared__ uint32_t list[kFixTiles];
+    __shared__ uint32_t wcnt[NW];
+    __shared__ uint64_t bexcl;
+    __shared__ uint32_t blk_s;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    if (tid == 0) blk_s = atomicAdd(a.counter + kCtrFix, 1u);
+    __syncthreads();
+    const uint32_t blk = sgpr(blk_s);
+    const uint32_t t = blk * kFixTiles + tid;
+    const bool in = t < a.n_tiles;
+    const uint64_t v = in ? a.tile_agg[t] : 0;
+    const uint64_t info = in ? a.tile_info[t] : 0;
+    const uint64_t inc = wave_incl_scan(v, lane);
+    const uint64_t chg = wave_sum((info & 0x1FFFFu) + ((info >> 17) & 0x1FFFFu));
+    const bool staged = a.staged && v != 0;
+    const uint64_t sm = __ballot(staged);
+    if (lane == 63) wtot[wave] = inc;
+    if (lane == 0) {
+        wcnt[wave] = uint32_t(__popcll(sm));
+        wchg[wave] = chg;
+    }
+    __syncthreads();
+    uint64_t wpre = 0, total = 0;
+    uint32_t lpre = 0, nlist = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < NW; w++) {
+        wpre += w < wave ? wtot[w] : 0;
+        total += wtot[w];
+        lpre += w < wave ? wcnt[w] : 0;
+        nlist += wcnt[w];
+    }
+    if (tid < 64) {
+        if (tid == 0) st_status(a.fix_status + blk, (total << kValShift) | (blk == 0 ? kFlagIncl : kFlagAgg));
+        const uint64_t ex = look_back(a.fix_status, blk, tid);
+        if (tid == 0) {
+            if (blk > 0) st_status(a.fix_status + blk, ((ex + total) << kValShift) | kFlagIncl);
+            bexcl = ex;
+            uint64_t c = 0;
+            for (uint32_t w = 0; w < NW; w++) c += wchg[w];
+            if (c) atomicAdd(reinterpret_cast<unsigned long long*>(a.counter + kCtrChanged), (unsigned long long)c);
+            if (blk == a.n_blocks - 1) *reinterpret_cast<uint64_t*>(a.counter + kCtrTotal) = ex + total;
+        }
+    }
+    __syncthreads();
+    excl_of[tid] = bexcl + wpre + inc - v;
+    if (staged) list[lpre + uint32_t(__popcll(sm & ((uint64_t(1) << lane) - 1)))] = tid;
+    __syncthreads();
+    // one wave per staged tile
+    for (uint32_t i = wave; i < nlist; i += NW) {
+        const uint32_t lt = sgpr(list[i]);
+        const uint32_t tile = blk * kFixTiles + lt;
+        const uint64_t ex = excl_of[lt];
+        const uint64_t R = ex >> kRecShift, P = (ex & kP16Mask) << 4;
+        const uint64_t ag = a.tile_agg[tile];
+        const uint32_t nrec = uint32_t(ag >> kRecShift);
+        const uint64_t bytes = (ag & kP16Mask) << 4;
+        if ((R + nrec) * DCR_DIRENT_BYTES > a.dir_cap || P + bytes > a.payload_cap) continue;
+        const v4u* src = reinterpret_cast<const v4u*>(a.stage + a.slots[tile]);
+        v4u* dst = reinterpret_cast<v4u*>(a.payload + P);
+        const uint32_t nv = uint32_t(bytes >> 4);
+        uint32_t j = lane;
+        for (; j + 192 < nv; j += 256) {
+            const v4u q0 = src[j], q1 = src[j + 64], q2 = src[j + 128], q3 = src[j + 192];
+            dst[j] = q0;
+            dst[j + 64] = q1;
+            dst[j + 128] = q2;
+            dst[j + 192] = q3;
+        }
+        for (; j < nv; j += 64) dst[j] = src[j];
+        if (lane < nrec) {
+            const DevChunk ch = a.chunks[tile];
+            const DevTensor td = a.tensors[ch.tensor];
+            const uint64_t tinfo = a.tile_info[tile];
+            const uint32_t Kx = uint32_t(tinfo & 0x1FFFFu), Ko = uint32_t((tinfo >> 17) & 0x1FFFFu);
+            const uint32_t Hx = uint32_t((tinfo >> 34) & 0x1FFFFu);
+            const uint64_t E = kChunkBytes / td.w;
+            const uint32_t n_c = uint32_t(umin64(E, td.numel - uint64_t(ch.chunk_idx) * E));
+            const RecLayout L = rec_layout(td.w, n_c, Kx, Ko, Hx);
+            put_dirent(a.dir, R + lane, lane, ch.tensor, ch.chunk_idx, td.w, L, Kx, Ko, P);
+        }
+    }
 }
 
 // Per-element "scale bits changed" flags of the scale tensors that gate
@@ -539,13 +708,12 @@ __global__ __launch_bounds__(256) void scale_flags_kernel(const DevTensor* tenso
     }
 }
 
-// Stream header and encode result from the last tile's inclusive prefix.
-__global__ void encode_finalize_kernel(const uint64_t* status, uint32_t n_tiles, const uint32_t* counter,
-                                       uint32_t mode, uint64_t base_v, uint64_t new_v, uint64_t fp,
-                                       uint64_t dir_cap, uint64_t payload_cap, uint8_t* header,
+// Stream header and encode result from the totals the fix-up stored.
+__global__ void encode_finalize_kernel(const uint32_t* counter, uint32_t mode, uint64_t base_v, uint64_t new_v,
+                                       uint64_t fp, uint64_t dir_cap, uint64_t payload_cap, uint8_t* header,
                                        dcr_encode_result* res) {
     if (threadIdx.x != 0) return;
-    const uint64_t v = n_tiles ? (ld_status(status + n_tiles - 1) >> kValShift) : 0;
+    const uint64_t v = *reinterpret_cast<const uint64_t*>(counter + kCtrTotal);
     const uint64_t nrec = v >> kRecShift, pbytes = (v & kP16Mask) << 4;
     const bool fits = nrec * DCR_DIRENT_BYTES <= dir_cap && pbytes <= payload_cap;
     uint4* h = reinterpret_cast<uint4*>(header);
@@ -553,7 +721,7 @@ __global__ void encode_finalize_kernel(const uint64_t* status, uint32_t n_tiles,
     h[1] = make_uint4(uint32_t(base_v), uint32_t(base_v >> 32), uint32_t(new_v), uint32_t(new_v >> 32));
     h[2] = make_uint4(uint32_t(fp), uint32_t(fp >> 32), uint32_t(nrec), uint32_t(nrec >> 32));
     h[3] = make_uint4(uint32_t(pbytes), uint32_t(pbytes >> 32), 0u, 0u);
-    const uint64_t changed = *reinterpret_cast<const uint64_t*>(counter + 2);
+    const uint64_t changed = *reinterpret_cast<const uint64_t*>(counter + kCtrChanged);
     uint4* r = reinterpret_cast<uint4*>(res);
     r[0] = make_uint4(uint32_t(nrec), uint32_t(nrec >> 32), uint32_t(pbytes), uint32_t(pbytes >> 32));
     r[1] = make_uint4(uint32_t(changed), uint32_t(changed >> 32), uint32_t(fits ? DCR_OK : DCR_E_CAPACITY), 0u);
@@ -833,6 +1001,13 @@ static int32_t fail(int32_t rc, const std::string& m) {
     return rc;
 }
 static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// benchmark hook: events recorded around the main kernel of each call
+static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+static void mark(bool start, hipStream_t s) {
+    hipEvent_t e = start ? g_ev_start : g_ev_stop;
+    if (g_ev_start && g_ev_stop) (void)hipEventRecord(e, s);
+}
 static int32_t hip_check(hipError_t e, const char* what) {
     if (e == hipSuccess) return DCR_OK;
     return fail(DCR_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -890,7 +1065,9 @@ static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_
         a.first = first;
         a.n_tensors = nT;
         a.retry = retry ? 1u : 0u;
+        mark(true, s);
         hipLaunchKernelGGL(apply_kernel, dim3(uint32_t(n)), dim3(kThreads), 0, s, a);
+        mark(false, s);
     }
     return hip_check(hipGetLastError(), "apply launch");
 }
@@ -898,6 +1075,11 @@ static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_
 }  // namespace dcr
 
 extern "C" {
+
+void dcr_set_kernel_events(void* start, void* stop) {
+    dcr::g_ev_start = static_cast<hipEvent_t>(start);
+    dcr::g_ev_stop = static_cast<hipEvent_t>(stop);
+}
 
 int32_t dcr_plan_upload(dcr_plan* plan, void* dev_tables, uint64_t bytes, void* stream) {
     using namespace dcr;
@@ -956,6 +1138,10 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
         hipLaunchKernelGGL(scale_flags_kernel, dim3(uint32_t(p.scale_chunks.size())), dim3(256), 0, s, tensors,
                            chunks, pieces, tab<uint32_t>(p, p.off_scale_chunks), old_sh, new_sh, scale_flags);
     uint32_t* counter = reinterpret_cast<uint32_t*>(ws + p.ws_counter);
+    // bytes past the plan's workspace: staging area, used when it holds every
+    // chunk's slot (max_payload_bytes)
+    uint8_t* stage = ws + p.ws_bytes;
+    const uint32_t staged = ws_bytes - p.ws_bytes >= p.max_payload_bytes ? 1u : 0u;
     if (n_tiles) {
         EncodeArgs a;
         a.tensors = tensors;
@@ -966,18 +1152,40 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
         a.scale_flags = scale_flags;
         a.status = reinterpret_cast<uint64_t*>(ws + p.ws_status);
         a.counter = counter;
+        a.tile_agg = reinterpret_cast<uint64_t*>(ws + p.ws_agg);
+        a.tile_info = reinterpret_cast<uint64_t*>(ws + p.ws_info);
+        a.slots = tab<uint64_t>(p, p.off_slots);
+        a.stage = stage;
         a.dir = static_cast<uint8_t*>(dir_dev);
         a.payload = static_cast<uint8_t*>(payload_dev);
+        a.staged = staged;
         a.dir_cap = dir_cap;
         a.payload_cap = payload_cap;
         a.n_tiles = n_tiles;
         a.mode = mode;
+        mark(true, s);
         hipLaunchKernelGGL(encode_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
+        mark(false, s);
+        FixArgs f;
+        f.tensors = tensors;
+        f.chunks = chunks;
+        f.tile_agg = a.tile_agg;
+        f.tile_info = a.tile_info;
+        f.slots = a.slots;
+        f.fix_status = reinterpret_cast<uint64_t*>(ws + p.ws_fix);
+        f.counter = counter;
+        f.stage = stage;
+        f.dir = a.dir;
+        f.payload = a.payload;
+        f.dir_cap = dir_cap;
+        f.payload_cap = payload_cap;
+        f.n_tiles = n_tiles;
+        f.n_blocks = (n_tiles + kFixTiles - 1) / kFixTiles;
+        f.staged = staged;
+        hipLaunchKernelGGL(encode_fixup_kernel, dim3(f.n_blocks), dim3(kFixTiles), 0, s, f);
     }
-    hipLaunchKernelGGL(encode_finalize_kernel, dim3(1), dim3(64), 0, s,
-                       reinterpret_cast<const uint64_t*>(ws + p.ws_status), n_tiles, counter, mode, base_version,
-                       new_version, p.fingerprint, dir_cap, payload_cap, static_cast<uint8_t*>(header_dev),
-                       result_dev);
+    hipLaunchKernelGGL(encode_finalize_kernel, dim3(1), dim3(64), 0, s, counter, mode, base_version, new_version,
+                       p.fingerprint, dir_cap, payload_cap, static_cast<uint8_t*>(header_dev), result_dev);
     return hip_check(hipGetLastError(), "encode launch");
 }
 

@@ -226,7 +226,9 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
                 worst = std::max(worst, 2 * nb + w * (n_c + 30));         // XOR + OW records
                 ents = 2;
             }
-            P.max_payload_bytes += worst;
+            // the chunk's staging slot: its worst case, 16-byte aligned
+            P.slots.push_back(P.max_payload_bytes);
+            P.max_payload_bytes += pad16(worst);
             P.max_dir_bytes += ents * DCR_DIRENT_BYTES;
         }
         P.canonical_bytes += d.numel * w;
@@ -250,7 +252,8 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     P.off_chunks = pad256(P.off_tensors + P.dt.size() * sizeof(DevTensor));
     P.off_pieces = pad256(P.off_chunks + P.chunks.size() * sizeof(DevChunk));
     P.off_scale_chunks = pad256(P.off_pieces + P.pieces.size() * sizeof(DevPiece));
-    P.table_bytes = pad256(P.off_scale_chunks + P.scale_chunks.size() * sizeof(uint32_t) + 4);
+    P.off_slots = pad256(P.off_scale_chunks + P.scale_chunks.size() * sizeof(uint32_t) + 4);
+    P.table_bytes = pad256(P.off_slots + P.slots.size() * sizeof(uint64_t));
     P.blob.assign(P.table_bytes, 0);
     if (!P.dt.empty()) std::memcpy(P.blob.data() + P.off_tensors, P.dt.data(), P.dt.size() * sizeof(DevTensor));
     if (!P.chunks.empty())
@@ -260,16 +263,25 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     if (!P.scale_chunks.empty())
         std::memcpy(P.blob.data() + P.off_scale_chunks, P.scale_chunks.data(),
                     P.scale_chunks.size() * sizeof(uint32_t));
+    if (!P.slots.empty())
+        std::memcpy(P.blob.data() + P.off_slots, P.slots.data(), P.slots.size() * sizeof(uint64_t));
 
-    // workspace: look-back status | tile counter + scratch | shard pointers |
-    // scale flags | canonical pointers
+    // workspace: tile look-back status | fix-up look-back status | counters |
+    // shard pointers | scale flags | canonical pointers | per-tile aggregates |
+    // per-tile change counts.  Everything before the shard pointers is zeroed
+    // at the start of an encode.  Bytes past ws_bytes are the optional
+    // staging area of encode (used when it holds every chunk's slot).
+    const uint64_t n_tiles = P.chunks.size();
     P.ws_status = 0;
-    P.ws_counter = pad256(P.chunks.size() * 8);
+    P.ws_fix = pad256(n_tiles * 8);
+    P.ws_counter = pad256(P.ws_fix + (n_tiles + kFixTiles - 1) / kFixTiles * 8);
     P.ws_old = P.ws_counter + 256;
     P.ws_new = pad256(P.ws_old + uint64_t(nS) * 8);
     P.ws_scale = pad256(P.ws_new + uint64_t(nS) * 8);
     P.ws_canon = pad256(P.ws_scale + P.scale_bits / 8);
-    P.ws_bytes = pad256(P.ws_canon + uint64_t(nT) * 8);
+    P.ws_agg = pad256(P.ws_canon + uint64_t(nT) * 8);
+    P.ws_info = pad256(P.ws_agg + n_tiles * 8);
+    P.ws_bytes = pad256(P.ws_info + n_tiles * 8);
     return DCR_OK;
 }
 

@@ -82,6 +82,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dcr_apply_overwrite_retry.argtypes = [P, P, P, P, P, U64, P, P, U64, P]
     lib.dcr_last_error.restype = ctypes.c_char_p
     lib.dcr_last_error.argtypes = []
+    lib.dcr_set_kernel_events.restype = None
+    lib.dcr_set_kernel_events.argtypes = [P, P]
     lib.dcr_format_constants.restype = U32
     lib.dcr_format_constants.argtypes = [P, U32]
     if path is None:
@@ -188,6 +190,16 @@ def dcr_apply_overwrite_retry(plan: Plan, canon, header: np.ndarray, dir_buf, pa
     _check(rc, "dcr_apply_overwrite_retry")
 
 
+def dcr_set_kernel_events(start=None, stop=None) -> None:
+    """Record start / stop (torch.cuda.Event, created, or raw hipEvent_t) around
+    the main kernel of the following calls on this thread; None, None: off."""
+    def h(e):
+        if e is None:
+            return None
+        return int(e.cuda_event) if hasattr(e, "cuda_event") else int(e)
+    load_library().dcr_set_kernel_events(h(start), h(stop))
+
+
 def format_constants():
     out = (ctypes.c_uint32 * 8)()
     n = load_library().dcr_format_constants(out, 8)
@@ -226,9 +238,11 @@ class StreamBuffers:
         return int(self.result_host()["payload_bytes"])
 
 
-def workspace(plan: Plan, device="cuda"):
+def workspace(plan: Plan, device="cuda", stage_bytes: int = 0):
+    """Workspace of the plan's size plus an optional encode staging area."""
     import torch
-    return torch.zeros(max(int(plan.info.workspace_bytes), 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(int(plan.info.workspace_bytes) + int(stage_bytes), 256), dtype=torch.uint8,
+                       device=device)
 
 
 def apply_result(t) -> np.void:

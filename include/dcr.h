@@ -117,7 +117,9 @@ typedef struct {
     uint64_t table_bytes;       /* device bytes dcr_plan_upload needs            */
     uint64_t workspace_bytes;   /* device workspace bytes encode / apply need    */
     uint64_t max_dir_bytes;     /* directory bytes of the largest possible stream */
-    uint64_t max_payload_bytes; /* payload bytes of the largest possible stream   */
+    uint64_t max_payload_bytes; /* payload bytes of the largest possible stream
+                                   (each chunk's worst case, 16-aligned); also
+                                   the size of encode's staging area          */
     uint64_t fingerprint;       /* FNV-1a-64 of the serialised tensor table       */
     uint64_t canonical_bytes;   /* sum of numel * elem_bytes                      */
 } dcr_plan_info;
@@ -192,7 +194,14 @@ void dcr_plan_destroy(dcr_plan* plan);
  *   dir_dev, dir_cap           directory buffer and its size in bytes
  *   payload_dev, payload_cap   payload buffer and its size in bytes
  *   result_dev     a dcr_encode_result in device memory
- *   workspace_dev, ws_bytes    at least workspace_bytes of device memory
+ *   workspace_dev, ws_bytes    at least workspace_bytes of device memory.
+ *                  With at least workspace_bytes + max_payload_bytes, the
+ *                  excess is a staging area: each chunk writes its records to
+ *                  a slot of its own at once and a second pass moves them into
+ *                  place, so no chunk waits for another.  With less, each
+ *                  chunk waits until every earlier chunk has published its
+ *                  sizes (decoupled look-back) and writes in place.  Both give
+ *                  the same stream.
  * Records are written in (tensor, chunk, kind) order with contiguous 16-byte
  * aligned payload offsets.  If a buffer is too small, result->status becomes
  * DCR_E_CAPACITY with the required totals; the buffers then hold no usable
@@ -239,6 +248,14 @@ int32_t dcr_apply_overwrite_retry(const dcr_plan* plan, void* const* canon,
                                   uint64_t expected_base_version,
                                   dcr_apply_result* result_dev,
                                   void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* Benchmark hook.  While set (both non-NULL), every encode, apply or retry
+ * call made on this host thread records `start` on its stream just before its
+ * main kernel (the encode tile kernel, or the apply kernel) and `stop` just
+ * after it, so that hipEventElapsedTime gives that kernel's duration alone.
+ * The events are hipEvent_t handles the caller created; NULL, NULL turns the
+ * hook off.  Never fails. */
+void dcr_set_kernel_events(void* start, void* stop);
 
 /* Message of the last error on this thread ("" if none). */
 const char* dcr_last_error(void);

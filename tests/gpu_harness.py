@@ -34,10 +34,12 @@ class Gpu:
         self.ws = dcr.workspace(self.plan, device)
         torch.cuda.synchronize()
 
-    def encode(self, mode=0, base=7, new=8, dir_bytes=None, payload_bytes=None):
+    def encode(self, mode=0, base=7, new=8, dir_bytes=None, payload_bytes=None, stage=0):
+        """stage: bytes of encode staging area past the plan's workspace."""
         sb = dcr.StreamBuffers(self.plan, self.device, dir_bytes, payload_bytes)
+        ws = self.ws if not stage else dcr.workspace(self.plan, self.device, stage)
         dcr.dcr_encode(self.plan, self.olds, self.news, mode, base, new, sb.header, sb.dir, sb.payload,
-                       sb.result, self.ws)
+                       sb.result, ws)
         torch.cuda.synchronize()
         return sb
 

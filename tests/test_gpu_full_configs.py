@@ -30,6 +30,17 @@ def typed(lay, shards):
     return [x.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[lay.shard_w[s]]) for s, x in enumerate(shards)]
 
 
+def staged_workspace(plan, sb):
+    """The benchmark's launch configuration: a staging area holding every
+    chunk's slot (none when device memory is short: in-order look-back)."""
+    free, _ = torch.cuda.mem_get_info()
+    stage = int(plan.info.max_payload_bytes)
+    if stage > int(free) - (4 << 30):
+        stage = 0
+    say("staging area", f"{stage / 1e9:.2f} GB")
+    return dcr.workspace(plan, "cuda", stage)
+
+
 def run_full(orc, lay, sample_names):
     assert torch.cuda.is_available()
     say(lay.name, "plan")
@@ -47,8 +58,10 @@ def run_full(orc, lay, sample_names):
                            payload_bytes=int(cb * 0.2) + (1 << 20))
     torch.cuda.synchronize()
     say(lay.name, "encode")
-    dcr.dcr_encode(plan, olds, news, 0, 3, 4, sb.header, sb.dir, sb.payload, sb.result, ws)
+    wss = staged_workspace(plan, sb)
+    dcr.dcr_encode(plan, olds, news, 0, 3, 4, sb.header, sb.dir, sb.payload, sb.result, wss)
     torch.cuda.synchronize()
+    del wss
     r = sb.result_host()
     assert int(r["status"]) == 0, r
     n_rec, pbytes = int(r["n_records"]), int(r["payload_bytes"])
@@ -117,8 +130,10 @@ def run_full(orc, lay, sample_names):
     rsb = dcr.StreamBuffers(plan, "cuda", dir_bytes=32 * int(plan.info.n_chunks),
                             payload_bytes=int(cb * 0.2) + (1 << 20))
     say(lay.name, "retry")
-    dcr.dcr_encode(plan, olds, news, 1, 3, 4, rsb.header, rsb.dir, rsb.payload, rsb.result, ws)
+    wss = staged_workspace(plan, rsb)
+    dcr.dcr_encode(plan, olds, news, 1, 3, 4, rsb.header, rsb.dir, rsb.payload, rsb.result, wss)
     torch.cuda.synchronize()
+    del wss
     assert int(rsb.result_host()["status"]) == 0
     dcr.dcr_apply_overwrite_retry(plan, canon, rsb.header.cpu().numpy(), rsb.dir, rsb.payload, 3, res, ws)
     torch.cuda.synchronize()

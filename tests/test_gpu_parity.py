@@ -56,6 +56,13 @@ def assert_same_stream(got, exp, what=""):
 SEEDS = list(range(40))
 
 
+def stage_sizes(g):
+    """Staging areas: none, too small (both run in-order look-back), and one
+    holding every chunk's slot (no chunk waits)."""
+    full = int(g.plan.info.max_payload_bytes)
+    return (0, full // 2, full)
+
+
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_layout_parity(gh, orc, seed):
     """Random layouts: 1/2/4-byte elements, all routes, split / transposed
@@ -65,8 +72,10 @@ def test_random_layout_parity(gh, orc, seed):
     olds, news, co, cn = pins.canon_lists(lay)
     g = gh.Gpu(lay, olds, news)
     for mode in (0, 1):
-        sb = g.encode(mode)
-        assert_same_stream(g.stream_host(sb), oracle_stream(orc, lay, olds, news, mode), f"seed {seed} mode {mode}")
+        exp = oracle_stream(orc, lay, olds, news, mode)
+        for stage in stage_sizes(g):
+            sb = g.encode(mode, stage=stage)
+            assert_same_stream(g.stream_host(sb), exp, f"seed {seed} mode {mode} stage {stage}")
     sb = g.encode(0)
     hdr, d, p = g.stream_host(sb)
     n = len(d) // 32
@@ -142,10 +151,11 @@ def test_config1_parity(gh, orc):
     lay = synth.config1_layout()
     old, new, _lr, pos = synth.config1_values(lay, lr=synth.CFG1_LR)
     g = gh.Gpu(lay, [old], [new])
+    exp = oracle_stream(orc, lay, [old], [new])
+    for stage in stage_sizes(g):
+        assert_same_stream(g.stream_host(g.encode(0, stage=stage)), exp, f"config 1 stage {stage}")
     sb = g.encode(0)
     got = g.stream_host(sb)
-    exp = oracle_stream(orc, lay, [old], [new])
-    assert_same_stream(got, exp, "config 1")
     assert int(sb.result_host()["n_changed"]) == int(np.count_nonzero(old != new))
     buf, canon = g.canon_alloc([old])
     flags = torch.zeros(len(got[1]) // 32, dtype=torch.uint8, device="cuda")
@@ -167,8 +177,9 @@ def test_llama_small_gpu_generated(gh, orc):
         assert np.array_equal(g.olds[s].cpu().numpy(), olds[s].view(np.uint8)), s
         assert np.array_equal(g.news[s].cpu().numpy(), news[s].view(np.uint8)), s
     for mode in (0, 1):
-        assert_same_stream(g.stream_host(g.encode(mode)), oracle_stream(orc, lay, olds, news, mode),
-                           f"llama small mode {mode}")
+        exp = oracle_stream(orc, lay, olds, news, mode)
+        for stage in stage_sizes(g):
+            assert_same_stream(g.stream_host(g.encode(mode, stage=stage)), exp, f"llama small mode {mode} {stage}")
 
 
 def test_determinism(gh):
@@ -179,8 +190,8 @@ def test_determinism(gh):
                              rate=0.05)
     g = gh.Gpu(lay, gen_gpu=True)
     ref = g.stream_host(g.encode(0))
-    for _ in range(10):
-        got = g.stream_host(g.encode(0))
+    for i in range(10):
+        got = g.stream_host(g.encode(0, stage=stage_sizes(g)[i % 3]))
         for a, b in zip(got, ref):
             assert np.array_equal(a, b)
 
@@ -193,10 +204,11 @@ def test_capacity_overflow(gh, orc):
     h, d, p = oracle_stream(orc, lay, olds, news)
     g = gh.Gpu(lay, olds, news)
     for dcap, pcap in ((len(d) - 32, len(p)), (len(d), len(p) - 16), (32, 16)):
-        sb = g.encode(0, dir_bytes=dcap, payload_bytes=pcap)
-        r = sb.result_host()
-        assert int(r["status"]) == dcr.DCR_E_CAPACITY
-        assert int(r["n_records"]) * 32 == len(d) and int(r["payload_bytes"]) == len(p)
+        for stage in stage_sizes(g):
+            sb = g.encode(0, dir_bytes=dcap, payload_bytes=pcap, stage=stage)
+            r = sb.result_host()
+            assert int(r["status"]) == dcr.DCR_E_CAPACITY
+            assert int(r["n_records"]) * 32 == len(d) and int(r["payload_bytes"]) == len(p)
 
 
 def test_header_checks(gh):
