@@ -158,13 +158,16 @@ struct EncodeArgs {
     uint64_t payload_cap;   // bytes
     uint32_t n_tiles;
     uint32_t mode;
-    uint32_t staged;        // 1: every tile writes to its slot, nobody waits
 };
 
 struct EncodeShared {
     alignas(16) uint32_t pw[kVecsPerChunk][4];   // payload words of changed groups
-    alignas(16) uint32_t pres[1024];            // SPARSE presence bitmap (K <= 32768 bits)
+    alignas(16) uint8_t win[kWinBytes];         // output window of the record writer
     DevPiece pieces[kMaxCachedPieces];
+    uint32_t pstart[kMaxCachedPieces];      // first chunk element of each piece
+    uint32_t pend[kMaxCachedPieces];        // one past its last
+    uint64_t pold[kMaxCachedPieces];        // old / new address of the piece's first element
+    uint64_t pnew[kMaxCachedPieces];
     uint64_t scan[2 * 3 * (kThreads / 64) + 3];
     uint64_t excl;
     uint32_t next;
@@ -254,13 +257,13 @@ __device__ __forceinline__ uint64_t look_back(const uint64_t* status, uint32_t i
 }
 
 // Gather one 16-byte group (elements e0 .. e0+V-1 of the chunk) of old and
-// new.  Elements at or past n_c read as zero in both.
+// new from the pieces pc[0..np).  Elements at or past n_c read as zero.
 template <int W>
 __device__ __forceinline__ void gather_group(const EncodeArgs& a, const DevPiece* pc, uint32_t np, uint32_t e0,
-                                             uint32_t n_c, uint32_t (&o)[4], uint32_t (&n)[4]) {
+                                             uint32_t n_c, v4u& vo, v4u& vn) {
     constexpr uint32_t V = 16 / W;
-#pragma unroll
-    for (int i = 0; i < 4; i++) o[i] = n[i] = 0;
+    vo = v4u{0, 0, 0, 0};
+    vn = v4u{0, 0, 0, 0};
     if (e0 >= n_c) return;
     uint32_t p = find_piece(pc, np, e0);
     uint32_t pstart = pc[p].canon_start, pend = pstart + uint32_t(pc[p].len_m1) + 1;
@@ -269,10 +272,8 @@ __device__ __forceinline__ void gather_group(const EncodeArgs& a, const DevPiece
         const uint8_t* so = a.old_sh[pc[p].shard] + off;
         const uint8_t* sn = a.new_sh[pc[p].shard] + off;
         if (((reinterpret_cast<uintptr_t>(so) | reinterpret_cast<uintptr_t>(sn)) & 15u) == 0) {
-            uint4 vo = *reinterpret_cast<const uint4*>(so);
-            uint4 vn = *reinterpret_cast<const uint4*>(sn);
-            o[0] = vo.x; o[1] = vo.y; o[2] = vo.z; o[3] = vo.w;
-            n[0] = vn.x; n[1] = vn.y; n[2] = vn.z; n[3] = vn.w;
+            vo = *reinterpret_cast<const v4u*>(so);
+            vn = *reinterpret_cast<const v4u*>(sn);
             return;
         }
     }
@@ -281,7 +282,7 @@ __device__ __forceinline__ void gather_group(const EncodeArgs& a, const DevPiece
     uint64_t olo = 0, ohi = 0, nlo = 0, nhi = 0;
     for (uint32_t i = 0; i < V; i++) {
         const uint32_t e = e0 + i;
-        uint64_t vo = 0, vn = 0;
+        uint64_t xo = 0, xn = 0;
         if (e < n_c) {
             while (e >= pend) {
                 p++;
@@ -291,173 +292,265 @@ __device__ __forceinline__ void gather_group(const EncodeArgs& a, const DevPiece
             const uint64_t off = (pc[p].shard_elem_off + (e - pstart)) * W;
             const uint8_t* so = a.old_sh[pc[p].shard] + off;
             const uint8_t* sn = a.new_sh[pc[p].shard] + off;
-            if constexpr (W == 1) { vo = *so; vn = *sn; }
-            else if constexpr (W == 2) { vo = *reinterpret_cast<const uint16_t*>(so); vn = *reinterpret_cast<const uint16_t*>(sn); }
-            else { vo = *reinterpret_cast<const uint32_t*>(so); vn = *reinterpret_cast<const uint32_t*>(sn); }
+            if constexpr (W == 1) { xo = *so; xn = *sn; }
+            else if constexpr (W == 2) { xo = *reinterpret_cast<const uint16_t*>(so); xn = *reinterpret_cast<const uint16_t*>(sn); }
+            else { xo = *reinterpret_cast<const uint32_t*>(so); xn = *reinterpret_cast<const uint32_t*>(sn); }
         }
         olo = (olo >> (8 * W)) | (ohi << (64 - 8 * W));
-        ohi = (ohi >> (8 * W)) | (vo << (64 - 8 * W));
+        ohi = (ohi >> (8 * W)) | (xo << (64 - 8 * W));
         nlo = (nlo >> (8 * W)) | (nhi << (64 - 8 * W));
-        nhi = (nhi >> (8 * W)) | (vn << (64 - 8 * W));
+        nhi = (nhi >> (8 * W)) | (xn << (64 - 8 * W));
     }
-    o[0] = uint32_t(olo); o[1] = uint32_t(olo >> 32); o[2] = uint32_t(ohi); o[3] = uint32_t(ohi >> 32);
-    n[0] = uint32_t(nlo); n[1] = uint32_t(nlo >> 32); n[2] = uint32_t(nhi); n[3] = uint32_t(nhi >> 32);
+    vo = v4u{uint32_t(olo), uint32_t(olo >> 32), uint32_t(ohi), uint32_t(ohi >> 32)};
+    vn = v4u{uint32_t(nlo), uint32_t(nlo >> 32), uint32_t(nhi), uint32_t(nhi >> 32)};
 }
 
-template <int W>
-__device__ __forceinline__ void encode_tile(const EncodeArgs& a, EncodeShared& S, uint32_t tile, const DevChunk ch,
-                                            const DevTensor td) {
-    constexpr uint32_t V = 16 / W;             // elements per 16-byte group
-    constexpr uint32_t E = kChunkBytes / W;    // elements per chunk
-    const uint32_t tid = threadIdx.x;
-    const uint64_t c0 = uint64_t(ch.chunk_idx) * E;
-    const uint32_t n_c = uint32_t(umin64(E, td.numel - c0));
+// What a workgroup needs to know of its tile (uniform: scalar registers).
+struct TileCtx {
+    uint64_t c0;             // first canonical element of the chunk
+    uint64_t fast_old;       // fast tiles: address of the chunk's old / new bytes
+    uint64_t fast_new;
+    uint64_t scale_bit_off;
+    uint64_t numel;
+    uint32_t tile, tensor, chunk_idx, first_piece, n_pieces, n_c, w, route, scale_block, fast;
+};
 
-    // the chunk's pieces: LDS copy when few, else read in place
-    const DevPiece* pc = a.pieces + ch.first_piece;
-    bool fast = false;
-    if (ch.n_pieces == 1 && n_c == E) {
-        const DevPiece p0 = pc[0];
-        const uint8_t* so = a.old_sh[p0.shard] + p0.shard_elem_off * W;
-        const uint8_t* sn = a.new_sh[p0.shard] + p0.shard_elem_off * W;
-        fast = ((reinterpret_cast<uintptr_t>(so) | reinterpret_cast<uintptr_t>(sn)) & 15u) == 0;
+// A fast tile is one aligned piece covering a full chunk: 128-bit loads
+// straight from the shard.
+__device__ __forceinline__ TileCtx tile_ctx(const EncodeArgs& a, uint32_t tile) {
+    TileCtx c;
+    const DevChunk ch = uniform_load(a.chunks + tile);
+    const DevTensor td = uniform_load(a.tensors + ch.tensor);
+    const uint64_t E = kChunkBytes / td.w;
+    c.tile = tile;
+    c.tensor = ch.tensor;
+    c.chunk_idx = ch.chunk_idx;
+    c.first_piece = ch.first_piece;
+    c.n_pieces = ch.n_pieces;
+    c.c0 = uint64_t(ch.chunk_idx) * E;
+    c.n_c = uint32_t(umin64(E, td.numel - c.c0));
+    c.w = td.w;
+    c.route = td.route;
+    c.scale_block = td.scale_block;
+    c.scale_bit_off = td.scale_bit_off;
+    c.numel = td.numel;
+    c.fast = 0;
+    c.fast_old = c.fast_new = 0;
+    if (ch.n_pieces == 1 && c.n_c == E) {
+        const DevPiece p0 = uniform_load(a.pieces + ch.first_piece);
+        const uint64_t so = uniform_load(reinterpret_cast<const uint64_t*>(a.old_sh) + p0.shard);
+        const uint64_t sn = uniform_load(reinterpret_cast<const uint64_t*>(a.new_sh) + p0.shard);
+        c.fast_old = so + p0.shard_elem_off * td.w;
+        c.fast_new = sn + p0.shard_elem_off * td.w;
+        c.fast = ((c.fast_old | c.fast_new) & 15u) == 0 ? 1u : 0u;
     }
-    if (!fast && ch.n_pieces <= kMaxCachedPieces) {
-        if (tid < ch.n_pieces) S.pieces[tid] = pc[tid];
-        __syncthreads();
-        pc = S.pieces;
-    }
+    return c;
+}
 
-    // ---- load, compare, route
-    uint32_t meta[kVecsPerThread];    // changed bits | high-byte bits << 16 | kind << 31
-    uint64_t cnt[3] = {0, 0, 0};      // packed per-k counts: XOR K, OW K, XOR high bytes
-    auto digest = [&](uint32_t k, const uint32_t (&o)[4], const uint32_t (&n)[4]) {
-        const uint32_t g = tid + k * kThreads;
-        uint32_t b = 0, h = 0;
+// Issue the 128-bit loads of a fast tile (the registers fill later).
+__device__ __forceinline__ void load_fast(const TileCtx& c, v4u (&lo)[kVecsPerThread], v4u (&ln)[kVecsPerThread]) {
+    gv4p vo = reinterpret_cast<gv4p>(c.fast_old) + threadIdx.x;
+    gv4p vn = reinterpret_cast<gv4p>(c.fast_new) + threadIdx.x;
 #pragma unroll
-        for (uint32_t i = 0; i < V; i++) {
-            const uint32_t d = elem<W>(o, i) ^ elem<W>(n, i);
-            b |= uint32_t(d != 0) << i;
-            if constexpr (W == 2) h |= uint32_t((d >> 8) != 0) << i;
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        lo[k] = __builtin_nontemporal_load(vo + k * kThreads);
+        ln[k] = __builtin_nontemporal_load(vn + k * kThreads);
+    }
+}
+
+// Gather a tile that spans several pieces (the direct projection).  With few
+// pieces, each piece's old / new addresses are resolved once into LDS; every
+// group then finds its piece there, all aligned in-piece groups are loaded at
+// once, and only groups that straddle pieces are gathered element by element.
+template <int W>
+__device__ __forceinline__ void gather_tile(const EncodeArgs& a, EncodeShared& S, const TileCtx& c,
+                                            v4u (&lo)[kVecsPerThread], v4u (&ln)[kVecsPerThread]) {
+    constexpr uint32_t V = 16 / W;
+    const uint32_t tid = threadIdx.x;
+    const DevPiece* gp = a.pieces + c.first_piece;
+    if (c.n_pieces > kMaxCachedPieces) {
+#pragma unroll
+        for (uint32_t k = 0; k < kVecsPerThread; k++)
+            gather_group<W>(a, gp, c.n_pieces, (tid + k * kThreads) * V, c.n_c, lo[k], ln[k]);
+        return;
+    }
+    if (tid < c.n_pieces) {
+        const DevPiece p = gp[tid];
+        S.pieces[tid] = p;
+        S.pstart[tid] = p.canon_start;
+        S.pend[tid] = uint32_t(p.canon_start) + uint32_t(p.len_m1) + 1;
+        S.pold[tid] = reinterpret_cast<uint64_t>(a.old_sh[p.shard] + p.shard_elem_off * W);
+        S.pnew[tid] = reinterpret_cast<uint64_t>(a.new_sh[p.shard] + p.shard_elem_off * W);
+    }
+    __syncthreads();
+    const uint32_t np = c.n_pieces;
+    uint32_t direct = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        const uint32_t e0 = (tid + k * kThreads) * V;
+        lo[k] = v4u{0, 0, 0, 0};
+        ln[k] = v4u{0, 0, 0, 0};
+        if (e0 < c.n_c) {
+            uint32_t l = 0, h = np;
+            while (h - l > 1) {
+                const uint32_t mid = (l + h) >> 1;
+                if (S.pstart[mid] <= e0) l = mid;
+                else h = mid;
+            }
+            const uint64_t ao = S.pold[l] + uint64_t(e0 - S.pstart[l]) * W;
+            const uint64_t an = S.pnew[l] + uint64_t(e0 - S.pstart[l]) * W;
+            if (e0 + V <= S.pend[l] && ((ao | an) & 15u) == 0) {
+                lo[k] = __builtin_nontemporal_load(reinterpret_cast<gv4p>(ao));
+                ln[k] = __builtin_nontemporal_load(reinterpret_cast<gv4p>(an));
+                direct |= 1u << k;
+            }
         }
-        uint32_t kd;
-        if (a.mode == DCR_MODE_RETRY || td.route == DCR_ROUTE_OVERWRITE) kd = DCR_KIND_OW;
-        else if (td.route == DCR_ROUTE_AFFINE_XOR || g * V >= n_c) kd = DCR_KIND_XOR;
-        else {
-            const uint64_t bit = td.scale_bit_off + (c0 + g * V) / td.scale_block;
-            kd = (a.scale_flags[bit >> 6] >> (bit & 63)) & 1u;   // 1 = scale changed -> OW
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++)
+        if (!((direct >> k) & 1u)) gather_group<W>(a, S.pieces, np, (tid + k * kThreads) * V, c.n_c, lo[k], ln[k]);
+}
+
+// Per-k routing bits of this thread's groups (1 = overwrite record).  A
+// block-scaled group goes to the overwrite record iff the fp32 scale of its
+// block changed (a group never straddles blocks: scale_block is a multiple
+// of the group's element count).  Computed before the tile's loads are issued.
+template <int W>
+__device__ __forceinline__ uint32_t ow_mask(const EncodeArgs& a, const TileCtx& c) {
+    constexpr uint32_t V = 16 / W;
+    if (a.mode == DCR_MODE_RETRY || c.route == DCR_ROUTE_OVERWRITE) return (1u << kVecsPerThread) - 1;
+    if (c.route != DCR_ROUTE_BLOCK_SCALED) return 0;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t sbg = c.scale_block / V;               // groups per block
+    const uint64_t gi = c.c0 / V + tid;                   // this thread's first group in the tensor
+    uint64_t q = gi / sbg, r = gi % sbg;
+    const uint64_t sq = kThreads / sbg, sr = kThreads % sbg;
+    uint32_t m = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        if ((tid + k * kThreads) * V < c.n_c) {
+            const uint64_t bit = c.scale_bit_off + q;
+            m |= uint32_t((a.scale_flags[bit >> 6] >> (bit & 63)) & 1u) << k;
         }
+        q += sq;
+        r += sr;
+        if (r >= sbg) {
+            r -= sbg;
+            q++;
+        }
+    }
+    return m;
+}
+
+// Changed-element bits of a 16-byte group of W-byte elements (d = old ^ new,
+// four 32-bit words); for W = 2 also the bits of elements whose high byte
+// changed.  Integer arithmetic only: x != 0 for an n-bit field x is
+// (x + 2^n - 1) >> n.
+template <int W>
+__device__ __forceinline__ uint32_t changed_bits(const uint32_t (&d)[4], uint32_t& hi_bits) {
+    uint32_t b = 0, h = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < 4; i++) {
+        const uint32_t x = d[i];
+        if constexpr (W == 4) {
+            b |= uint32_t(x != 0) << i;
+        } else if constexpr (W == 2) {
+            b |= (((x & 0xFFFFu) + 0xFFFFu) >> 16) << (2 * i);
+            b |= (((x >> 16) + 0xFFFFu) >> 16) << (2 * i + 1);
+            h |= ((((x >> 8) & 0xFFu) + 0xFFu) >> 8) << (2 * i);
+            h |= (((x >> 24) + 0xFFu) >> 8) << (2 * i + 1);
+        } else {
+            // high bit of each byte set iff the byte is nonzero
+            const uint32_t t = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+            b |= ((t >> 7) & 1u) << (4 * i);
+            b |= ((t >> 15) & 1u) << (4 * i + 1);
+            b |= ((t >> 23) & 1u) << (4 * i + 2);
+            b |= ((t >> 31) & 1u) << (4 * i + 3);
+        }
+    }
+    hi_bits = h;
+    return b;
+}
+
+// Compare stored bits and route each 16-byte group: meta[k] = changed bits |
+// high-byte bits << 16 | kind << 31; cnt = per-k counts packed 16 bits per k
+// (XOR K, overwrite K, XOR high bytes); the group's payload words (XOR mask or
+// new bits) go to S.pw.
+template <int W>
+__device__ __forceinline__ void digest_tile(EncodeShared& S, uint32_t owm, const v4u (&lo)[kVecsPerThread],
+                                            const v4u (&ln)[kVecsPerThread], uint32_t (&meta)[kVecsPerThread],
+                                            uint64_t (&cnt)[3]) {
+    const uint32_t tid = threadIdx.x;
+    cnt[0] = cnt[1] = cnt[2] = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        const uint32_t g = tid + k * kThreads;
+        const uint32_t d[4] = {lo[k].x ^ ln[k].x, lo[k].y ^ ln[k].y, lo[k].z ^ ln[k].z, lo[k].w ^ ln[k].w};
+        uint32_t h;
+        const uint32_t b = changed_bits<W>(d, h);
+        const uint32_t kd = (owm >> k) & 1u;
         if (b) {
-            v4u q;
-            q.x = kd == DCR_KIND_XOR ? (o[0] ^ n[0]) : n[0];
-            q.y = kd == DCR_KIND_XOR ? (o[1] ^ n[1]) : n[1];
-            q.z = kd == DCR_KIND_XOR ? (o[2] ^ n[2]) : n[2];
-            q.w = kd == DCR_KIND_XOR ? (o[3] ^ n[3]) : n[3];
+            const v4u q = kd == DCR_KIND_XOR ? v4u{d[0], d[1], d[2], d[3]} : ln[k];
             *reinterpret_cast<v4u*>(S.pw[g]) = q;
         }
         if (kd != DCR_KIND_XOR) h = 0;
         meta[k] = b | (h << 16) | (kd << 31);
-        const uint64_t c = uint64_t(__popc(b)) << (16 * k);
-        cnt[0] |= kd == DCR_KIND_XOR ? c : 0;
-        cnt[1] |= kd == DCR_KIND_XOR ? 0 : c;
+        const uint64_t cc = uint64_t(__popc(b)) << (16 * k);
+        cnt[0] |= kd == DCR_KIND_XOR ? cc : 0;
+        cnt[1] |= kd == DCR_KIND_XOR ? 0 : cc;
         cnt[2] |= uint64_t(__popc(h)) << (16 * k);
-    };
-    if (fast) {
-        // one aligned piece covers the full chunk: straight 128-bit loads
-        const DevPiece p0 = pc[0];
-        gv4p vo = (gv4p)(a.old_sh[p0.shard] + p0.shard_elem_off * W) + tid;
-        gv4p vn = (gv4p)(a.new_sh[p0.shard] + p0.shard_elem_off * W) + tid;
-        v4u lo_[kVecsPerThread], ln_[kVecsPerThread];
-#pragma unroll
-        for (uint32_t k = 0; k < kVecsPerThread; k++) {
-            lo_[k] = __builtin_nontemporal_load(vo + k * kThreads);
-            ln_[k] = __builtin_nontemporal_load(vn + k * kThreads);
-        }
-#pragma unroll
-        for (uint32_t k = 0; k < kVecsPerThread; k++) {
-            const uint32_t o[4] = {lo_[k].x, lo_[k].y, lo_[k].z, lo_[k].w};
-            const uint32_t n[4] = {ln_[k].x, ln_[k].y, ln_[k].z, ln_[k].w};
-            digest(k, o, n);
-        }
-    } else {
-#pragma unroll
-        for (uint32_t k = 0; k < kVecsPerThread; k++) {
-            uint32_t o[4], n[4];
-            gather_group<W>(a, pc, ch.n_pieces, (tid + k * kThreads) * V, n_c, o, n);
-            digest(k, o, n);
-        }
     }
-    for (uint32_t q = tid; q < 1024; q += kThreads) S.pres[q] = 0;
+}
 
-    // ---- counts -> change ranks and record sizes
+// Tile totals and, per k, the totals of all lower k (uniform).
+struct TileSums {
+    uint32_t Kx, Ko, Hx;
+    uint32_t kb[3][kVecsPerThread];
+};
+
+// Workgroup scan of the packed counts: cnt becomes each thread's exclusive
+// prefix; its barriers also publish S.pw.
+__device__ __forceinline__ TileSums scan_tile(EncodeShared& S, uint64_t (&cnt)[3]) {
     uint64_t tot[3];
-    block_excl_scan<3>(cnt, tot, S.scan);   // (its barriers also publish S.pw / S.pres)
-    uint32_t Kx = 0, Ko = 0, Hx = 0;
-    uint32_t kbase[3][kVecsPerThread];      // per-k totals before k (uniform)
+    block_excl_scan<3>(cnt, tot, S.scan);
+    TileSums t;
+    t.Kx = t.Ko = t.Hx = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kVecsPerThread; k++) {
-        kbase[0][k] = Kx;
-        kbase[1][k] = Ko;
-        kbase[2][k] = Hx;
-        Kx += sgpr(field16(tot[0], k));
-        Ko += sgpr(field16(tot[1], k));
-        Hx += sgpr(field16(tot[2], k));
+        t.kb[0][k] = t.Kx;
+        t.kb[1][k] = t.Ko;
+        t.kb[2][k] = t.Hx;
+        t.Kx += sgpr(field16(tot[0], k));
+        t.Ko += sgpr(field16(tot[1], k));
+        t.Hx += sgpr(field16(tot[2], k));
     }
-    const uint32_t bm = dpad16((n_c + 7) / 8);
-    const RecLayout L = rec_layout(W, n_c, Kx, Ko, Hx);
-    const uint32_t mode_x = L.mode_x, size_x = L.size_x, off_pres = L.off_pres, off_hi_x = L.off_hi_x;
-    const uint32_t base_o = size_x;
-    const uint32_t tile_bytes = size_x + L.size_o;
-    const uint32_t nrec = (Kx ? 1u : 0u) + (Ko ? 1u : 0u);
-    const uint64_t agg = (uint64_t(nrec) << kRecShift) | (tile_bytes >> 4);
+    return t;
+}
 
-    // sizes for the fix-up pass; staged: records go to the tile's slot (the
-    // fix-up moves them into place); else publish the aggregate and look back
-    if (tid == 0) {
-        if (!a.staged) st_status(a.status + tile, (agg << kValShift) | (tile == 0 ? kFlagIncl : kFlagAgg));
-        a.tile_agg[tile] = agg;
-        a.tile_info[tile] = uint64_t(Kx) | (uint64_t(Ko) << 17) | (uint64_t(Hx) << 34);
-    }
-    if (nrec == 0) return;   // uniform; an empty tile's aggregate is all it owes
-    uint8_t* out;
-    uint64_t R = 0, P = 0;
-    if (a.staged) {
-        out = a.stage + a.slots[tile];
-    } else {
-        // ---- decoupled look-back (first wave): exclusive (records, payload/16)
-        if (tid < 64) {
-            const uint64_t excl = look_back(a.status, tile, tid);
-            if (tid == 0) {
-                if (tile > 0) st_status(a.status + tile, ((excl + agg) << kValShift) | kFlagIncl);
-                S.excl = excl;
-            }
-        }
-        __syncthreads();
-        R = S.excl >> kRecShift;
-        P = (S.excl & kP16Mask) << 4;
-        const bool fits = (R + nrec) * DCR_DIRENT_BYTES <= a.dir_cap && P + tile_bytes <= a.payload_cap;
-        if (!fits) return;   // uniform
-        out = a.payload + P;
-    }
-
-    // ---- write the records (in place or to the staging area)
+// One output window [w0, w0 + kWinBytes) of a tile's records: each thread
+// puts the bitmap bits of its groups and the plane bytes of its changed
+// elements that fall in the window into LDS (zeroed first: the zero padding),
+// then the window leaves as 128-bit stores.  ONE: the records fit in one
+// window (no range checks).
+template <int W, bool ONE>
+__device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint32_t w0, uint32_t total,
+                                             uint32_t bm, const uint32_t (&meta)[kVecsPerThread],
+                                             const uint64_t (&cnt)[3], const TileSums& t, const RecLayout& L) {
+    constexpr uint32_t V = 16 / W;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t Kx = t.Kx, Ko = t.Ko;
+    const uint32_t base_o = L.size_x;
     const uint32_t pkx = dpad16(Kx), pko = dpad16(Ko);
-    // zero padding tails (each at most 15 bytes)
-    if (tid < 16) {
-        auto zpad = [&](uint32_t at, uint32_t from, uint32_t to) {
-            if (from + tid < to) out[at + from + tid] = 0;
-        };
-        if (Kx) {
-            zpad(bm, Kx, pkx);
-            if (mode_x == DCR_HI_SPARSE) zpad(off_hi_x, Hx, dpad16(Hx));
-            else if (mode_x == DCR_HI_DENSE) zpad(off_hi_x, Kx, pkx);
-        }
-        if (Ko) {
-            for (uint32_t pl = 0; pl < W; pl++) zpad(base_o + bm + pl * pko, Ko, pko);
-        }
-    }
-    const uint32_t hi_x_dense = sgpr(mode_x == DCR_HI_DENSE ? 1u : 0u);
-    const uint32_t hi_x_sparse = sgpr(mode_x == DCR_HI_SPARSE ? 1u : 0u);
+    const uint32_t hi_x_dense = sgpr(L.mode_x == DCR_HI_DENSE ? 1u : 0u);
+    const uint32_t hi_x_sparse = sgpr(L.mode_x == DCR_HI_SPARSE ? 1u : 0u);
+    const uint32_t w1 = w0 + kWinBytes;
+    uint8_t* win = S.win;
+    for (uint32_t q = tid; q < kWinBytes / 16; q += kThreads) reinterpret_cast<v4u*>(win)[q] = v4u{0, 0, 0, 0};
+    __syncthreads();
+    auto inwin = [&](uint32_t pos) { return ONE || (pos >= w0 && pos < w1); };
+    auto put = [&](uint32_t pos, uint32_t v) {
+        if (inwin(pos)) win[pos - w0] = uint8_t(v);
+    };
 #pragma unroll
     for (uint32_t k = 0; k < kVecsPerThread; k++) {
         const uint32_t g = tid + k * kThreads;
@@ -472,19 +565,33 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, EncodeShared& S
         }
         if (g * V < bm * 8) {
             if constexpr (W == 2) {
-                if (Kx) out[g] = uint8_t(bx);
-                if (Ko) out[base_o + g] = uint8_t(bo);
+                if (Kx) put(g, bx);
+                if (Ko) put(base_o + g, bo);
             } else if constexpr (W == 1) {
-                if (Kx) reinterpret_cast<uint16_t*>(out)[g] = uint16_t(bx);
-                if (Ko) reinterpret_cast<uint16_t*>(out + base_o)[g] = uint16_t(bo);
+                if (Kx) { put(2 * g, bx); put(2 * g + 1, bx >> 8); }
+                if (Ko) { put(base_o + 2 * g, bo); put(base_o + 2 * g + 1, bo >> 8); }
             } else {
                 if ((g & 1) == 0) {
-                    if (Kx) out[g / 2] = uint8_t(bx | (px << 4));
-                    if (Ko) out[base_o + g / 2] = uint8_t(bo | (po << 4));
+                    if (Kx) put(g / 2, bx | (px << 4));
+                    if (Ko) put(base_o + g / 2, bo | (po << 4));
                 }
             }
         }
         if (!b) continue;
+        const uint32_t rb = x ? 0u : base_o;
+        const uint32_t pk = x ? pkx : pko;
+        const uint32_t lo = rb + bm;
+        uint32_t j = x ? t.kb[0][k] + field16(cnt[0], k) : t.kb[1][k] + field16(cnt[1], k);
+        uint32_t hr = t.kb[2][k] + field16(cnt[2], k);
+        if (!ONE) {
+            // every byte of this group lies in [lo + j, end): skip the group
+            // when that range misses the window
+            const uint32_t nb = uint32_t(__popc(b));
+            uint32_t end = lo + (W - 1) * pk + j + nb;
+            if (W == 2 && x)
+                end = hi_x_sparse ? L.off_hi_x + hr + nb : (hi_x_dense ? L.off_hi_x + j + nb : lo + j + nb);
+            if (lo + j >= w1 || end <= w0) continue;
+        }
         const v4u q = *reinterpret_cast<const v4u*>(S.pw[g]);
         // byte planes of the group packed into 64-bit values
         uint64_t pl0 = 0, pl1 = 0, ph = 0;
@@ -509,65 +616,165 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, EncodeShared& S
                 ph |= uint64_t(qq[i] >> 24) << (32 + 8 * i);
             }
         }
-        const uint32_t rb = x ? 0u : base_o;
-        const uint32_t pk = x ? pkx : pko;
-        uint8_t* lo = out + rb + bm;
-        uint32_t j = x ? kbase[0][k] + field16(cnt[0], k) : kbase[1][k] + field16(cnt[1], k);
-        uint32_t hr = kbase[2][k] + field16(cnt[2], k);
 #pragma nounroll
         while (b) {
             const uint32_t i = uint32_t(__ffs(b) - 1);
             b &= b - 1;
             if constexpr (W == 1) {
-                lo[j] = uint8_t((i < 8 ? pl0 : pl1) >> (8 * (i & 7)));
+                put(lo + j, uint32_t((i < 8 ? pl0 : pl1) >> (8 * (i & 7))));
             } else if constexpr (W == 2) {
-                lo[j] = uint8_t(pl0 >> (8 * i));
-                const uint8_t hb = uint8_t(ph >> (8 * i));
+                put(lo + j, uint32_t(pl0 >> (8 * i)));
+                const uint32_t hb = uint32_t(ph >> (8 * i)) & 0xFFu;
                 if (!x) {
-                    lo[pk + j] = hb;
+                    put(lo + pk + j, hb);
                 } else if (hi_x_dense) {
-                    out[off_hi_x + j] = hb;
+                    put(L.off_hi_x + j, hb);
                 } else if (hi_x_sparse && hb) {
-                    atomicOr(&S.pres[j >> 5], 1u << (j & 31));
-                    out[off_hi_x + hr] = hb;
+                    // presence bit j (LSB first) and the byte itself
+                    const uint32_t pp = L.off_pres + (j >> 3);
+                    if (inwin(pp)) atomicOr(reinterpret_cast<uint32_t*>(win) + ((pp - w0) >> 2), 1u << (j & 31));
+                    put(L.off_hi_x + hr, hb);
                     hr++;
                 }
             } else {
-                lo[j] = uint8_t(pl0 >> (8 * i));
-                lo[pk + j] = uint8_t(pl0 >> (32 + 8 * i));
-                lo[2 * pk + j] = uint8_t(ph >> (8 * i));
-                lo[3 * pk + j] = uint8_t(ph >> (32 + 8 * i));
+                put(lo + j, uint32_t(pl0 >> (8 * i)));
+                put(lo + pk + j, uint32_t(pl0 >> (32 + 8 * i)));
+                put(lo + 2 * pk + j, uint32_t(ph >> (8 * i)));
+                put(lo + 3 * pk + j, uint32_t(ph >> (32 + 8 * i)));
             }
             j++;
         }
     }
-    if (!a.staged && tid < nrec) put_dirent(a.dir, R + tid, tid, ch.tensor, ch.chunk_idx, W, L, Kx, Ko, P);
-    if (hi_x_sparse) {
+    __syncthreads();
+    const uint32_t n = ONE ? total : uint32_t(umin64(kWinBytes, total - w0));
+    for (uint32_t q = tid; q < n / 16; q += kThreads)
+        reinterpret_cast<v4u*>(out + w0)[q] = reinterpret_cast<const v4u*>(win)[q];
+}
+
+// Write a tile's records (XOR record, then overwrite record) at out: change
+// bitmaps (LSB first), byte planes of the changed elements in element order,
+// zero padding to 16 bytes, assembled in LDS one window at a time.
+template <int W>
+__device__ __forceinline__ void write_tile(EncodeShared& S, uint8_t* out, uint32_t n_c,
+                                           const uint32_t (&meta)[kVecsPerThread], const uint64_t (&cnt)[3],
+                                           const TileSums& t, const RecLayout& L) {
+    const uint32_t bm = dpad16((n_c + 7) / 8);
+    const uint32_t total = L.size_x + L.size_o;
+    if (total <= kWinBytes) {
+        write_window<W, true>(S, out, 0, total, bm, meta, cnt, t, L);
+        return;
+    }
+#pragma nounroll
+    for (uint32_t w0 = 0; w0 < total; w0 += kWinBytes) {
+        // keep the per-group values inside the loop (recomputed per window)
+        uint32_t m[kVecsPerThread];
+        uint64_t cc[3];
+#pragma unroll
+        for (uint32_t k = 0; k < kVecsPerThread; k++) m[k] = __builtin_amdgcn_readfirstlane(0) + meta[k];
+        cc[0] = cnt[0];
+        cc[1] = cnt[1];
+        cc[2] = cnt[2];
+        asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(cc[0]), "+v"(cc[1]), "+v"(cc[2]));
+        write_window<W, false>(S, out, w0, total, bm, m, cc, t, L);
         __syncthreads();
-        const uint32_t nq = dpad16((Kx + 7) / 8) / 16;
-        for (uint32_t q = tid; q < nq; q += kThreads)
-            reinterpret_cast<v4u*>(out + off_pres)[q] = reinterpret_cast<const v4u*>(S.pres)[q];
     }
 }
 
-// One workgroup per tile.  Unstaged, tiles are claimed in increasing order
-// from a counter, so every tile a look-back waits on belongs to a workgroup
-// that is already running; staged, nothing waits and the tile is the
-// workgroup id.
+__device__ __forceinline__ uint64_t tile_aggregate(const TileSums& t, const RecLayout& L) {
+    const uint32_t nrec = (t.Kx ? 1u : 0u) + (t.Ko ? 1u : 0u);
+    return (uint64_t(nrec) << kRecShift) | ((L.size_x + L.size_o) >> 4);
+}
+__device__ __forceinline__ uint64_t tile_counts(const TileSums& t) {
+    return uint64_t(t.Kx) | (uint64_t(t.Ko) << 17) | (uint64_t(t.Hx) << 34);
+}
+
+// In-order encode of one tile of W-byte elements (no staging area): publish
+// the aggregate, look back for the exclusive prefix, write the records and
+// directory entries in place.
+template <int W>
+__device__ __forceinline__ void inorder_tile(const EncodeArgs& a, EncodeShared& S, const TileCtx& c) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t owm = ow_mask<W>(a, c);
+    v4u lo[kVecsPerThread], ln[kVecsPerThread];
+    if (c.fast) load_fast(c, lo, ln);
+    else gather_tile<W>(a, S, c, lo, ln);
+    uint32_t meta[kVecsPerThread];
+    uint64_t cnt[3];
+    digest_tile<W>(S, owm, lo, ln, meta, cnt);
+    const TileSums t = scan_tile(S, cnt);
+    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx);
+    const uint64_t agg = tile_aggregate(t, L);
+    const uint32_t nrec = uint32_t(agg >> kRecShift);
+    const uint32_t tile = c.tile;
+    if (tid == 0) {
+        st_status(a.status + tile, (agg << kValShift) | (tile == 0 ? kFlagIncl : kFlagAgg));
+        a.tile_agg[tile] = agg;
+        a.tile_info[tile] = tile_counts(t);
+    }
+    if (nrec == 0) return;   // uniform; an empty tile's aggregate is all it owes
+    if (tid < 64) {
+        const uint64_t excl = look_back(a.status, tile, tid);
+        if (tid == 0) {
+            if (tile > 0) st_status(a.status + tile, ((excl + agg) << kValShift) | kFlagIncl);
+            S.excl = excl;
+        }
+    }
+    __syncthreads();
+    const uint64_t R = S.excl >> kRecShift;
+    const uint64_t P = (S.excl & kP16Mask) << 4;
+    const uint64_t bytes = (agg & kP16Mask) << 4;
+    if ((R + nrec) * DCR_DIRENT_BYTES > a.dir_cap || P + bytes > a.payload_cap) return;   // uniform
+    write_tile<W>(S, a.payload + P, c.n_c, meta, cnt, t, L);
+    if (tid < nrec) put_dirent(a.dir, R + tid, tid, c.tensor, c.chunk_idx, W, L, t.Kx, t.Ko, P);
+}
+
+// In-order encode (no staging area): one workgroup per tile, tiles claimed
+// in increasing order from a counter, so every tile a look-back waits on
+// belongs to a workgroup that is already running.
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_kernel(EncodeArgs a) {
     __shared__ EncodeShared S;
-    uint32_t tile = blockIdx.x;
-    if (!a.staged) {
-        if (threadIdx.x == 0) S.next = atomicAdd(a.counter + kCtrTile, 1u);
-        __syncthreads();
-        tile = sgpr(S.next);
-    }
+    if (threadIdx.x == 0) S.next = atomicAdd(a.counter + kCtrTile, 1u);
+    __syncthreads();
+    const uint32_t tile = sgpr(S.next);
     if (tile >= a.n_tiles) return;
-    const DevChunk ch = uniform_load(a.chunks + tile);
-    const DevTensor td = uniform_load(a.tensors + ch.tensor);
-    if (td.w == 2) encode_tile<2>(a, S, tile, ch, td);
-    else if (td.w == 1) encode_tile<1>(a, S, tile, ch, td);
-    else encode_tile<4>(a, S, tile, ch, td);
+    const TileCtx c = tile_ctx(a, tile);
+    if (c.w == 2) inorder_tile<2>(a, S, c);
+    else if (c.w == 1) inorder_tile<1>(a, S, c);
+    else inorder_tile<4>(a, S, c);
+}
+
+// Staged encode of one tile of W-byte elements: write the records to the
+// tile's slot of the staging area; nothing waits on another workgroup.
+template <int W>
+__device__ __forceinline__ void staged_tile(const EncodeArgs& a, EncodeShared& S, const TileCtx& c) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t owm = ow_mask<W>(a, c);
+    v4u lo[kVecsPerThread], ln[kVecsPerThread];
+    if (c.fast) load_fast(c, lo, ln);
+    else gather_tile<W>(a, S, c, lo, ln);
+    uint32_t meta[kVecsPerThread];
+    uint64_t cnt[3];
+    digest_tile<W>(S, owm, lo, ln, meta, cnt);
+    const TileSums t = scan_tile(S, cnt);
+    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx);
+    const uint64_t agg = tile_aggregate(t, L);
+    if (tid == 0) {
+        a.tile_agg[c.tile] = agg;
+        a.tile_info[c.tile] = tile_counts(t);
+    }
+    if (agg) write_tile<W>(S, a.stage + a.slots[c.tile], c.n_c, meta, cnt, t, L);
+}
+
+// Staged encode (the staging area holds every chunk's slot): one workgroup
+// per tile, the tile is the workgroup id.
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_staged_kernel(
+    EncodeArgs a) {
+    __shared__ EncodeShared S;
+    if (blockIdx.x >= a.n_tiles) return;
+    const TileCtx c = tile_ctx(a, blockIdx.x);
+    if (c.w == 2) staged_tile<2>(a, S, c);
+    else if (c.w == 1) staged_tile<1>(a, S, c);
+    else staged_tile<4>(a, S, c);
 }
 
 // Encode fix-up: one workgroup of 256 threads per kFixTiles consecutive
@@ -1158,13 +1365,15 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
         a.stage = stage;
         a.dir = static_cast<uint8_t*>(dir_dev);
         a.payload = static_cast<uint8_t*>(payload_dev);
-        a.staged = staged;
         a.dir_cap = dir_cap;
         a.payload_cap = payload_cap;
         a.n_tiles = n_tiles;
         a.mode = mode;
         mark(true, s);
-        hipLaunchKernelGGL(encode_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
+        if (staged)
+            hipLaunchKernelGGL(encode_staged_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(encode_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
         mark(false, s);
         FixArgs f;
         f.tensors = tensors;
