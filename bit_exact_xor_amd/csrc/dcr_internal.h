@@ -48,13 +48,18 @@ struct DevTensor {
 };
 static_assert(sizeof(DevTensor) == 48, "DevTensor");
 
-// One canonical chunk (one encode tile).  16 bytes.
+// One canonical chunk (one encode tile).  16 bytes.  n_pieces carries flags
+// in its top byte (kChunkDirect).
 struct DevChunk {
     uint32_t tensor;
     uint32_t chunk_idx;
     uint32_t first_piece;
     uint32_t n_pieces;
 };
+constexpr uint32_t kPiecesMask = 0xFFFFFFu;
+// every 16-byte group of the chunk lies inside one piece at a 16-byte aligned
+// shard offset, and the chunk has at most kMaxCachedPieces pieces
+constexpr uint32_t kChunkDirect = 1u << 24;
 static_assert(sizeof(DevChunk) == 16, "DevChunk");
 
 // A contiguous run of a chunk: canonical elements [canon_start, canon_start+len)
@@ -75,12 +80,15 @@ struct Plan {
     std::vector<DevPiece> pieces;
     std::vector<uint32_t> scale_chunks;   // chunks of scale tensors that gate a BLOCK_SCALED one
     std::vector<uint64_t> slots;          // per chunk: staging slot offset (prefix of worst cases)
+    std::vector<uint32_t> slow;           // chunks without kChunkDirect
+    std::vector<uint32_t> direct[3];      // direct chunks of 1-, 2-, 4-byte elements
     uint64_t fingerprint = 0;
     uint64_t canonical_bytes = 0;
     uint64_t scale_bits = 0;              // total flag bits (multiple of 64)
     uint64_t max_dir_bytes = 0, max_payload_bytes = 0;
     // device table layout
-    uint64_t off_tensors = 0, off_chunks = 0, off_pieces = 0, off_scale_chunks = 0, off_slots = 0, table_bytes = 0;
+    uint64_t off_tensors = 0, off_chunks = 0, off_pieces = 0, off_scale_chunks = 0, off_slots = 0, off_slow = 0,
+             off_direct[3] = {0, 0, 0}, table_bytes = 0;
     // workspace layout
     uint64_t ws_status = 0, ws_fix = 0, ws_counter = 0, ws_old = 0, ws_new = 0, ws_scale = 0, ws_canon = 0,
              ws_agg = 0, ws_info = 0, ws_bytes = 0;

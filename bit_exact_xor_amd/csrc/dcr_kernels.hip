@@ -312,7 +312,7 @@ struct TileCtx {
     uint64_t fast_new;
     uint64_t scale_bit_off;
     uint64_t numel;
-    uint32_t tile, tensor, chunk_idx, first_piece, n_pieces, n_c, w, route, scale_block, fast;
+    uint32_t tile, tensor, chunk_idx, first_piece, n_pieces, n_c, w, route, scale_block, fast, direct;
 };
 
 // A fast tile is one aligned piece covering a full chunk: 128-bit loads
@@ -326,7 +326,8 @@ __device__ __forceinline__ TileCtx tile_ctx(const EncodeArgs& a, uint32_t tile) 
     c.tensor = ch.tensor;
     c.chunk_idx = ch.chunk_idx;
     c.first_piece = ch.first_piece;
-    c.n_pieces = ch.n_pieces;
+    c.n_pieces = ch.n_pieces & kPiecesMask;
+    c.direct = (ch.n_pieces & kChunkDirect) ? 1u : 0u;
     c.c0 = uint64_t(ch.chunk_idx) * E;
     c.n_c = uint32_t(umin64(E, td.numel - c.c0));
     c.w = td.w;
@@ -336,7 +337,7 @@ __device__ __forceinline__ TileCtx tile_ctx(const EncodeArgs& a, uint32_t tile) 
     c.numel = td.numel;
     c.fast = 0;
     c.fast_old = c.fast_new = 0;
-    if (ch.n_pieces == 1 && c.n_c == E) {
+    if (c.n_pieces == 1 && c.n_c == E) {
         const DevPiece p0 = uniform_load(a.pieces + ch.first_piece);
         const uint64_t so = uniform_load(reinterpret_cast<const uint64_t*>(a.old_sh) + p0.shard);
         const uint64_t sn = uniform_load(reinterpret_cast<const uint64_t*>(a.new_sh) + p0.shard);
@@ -765,16 +766,82 @@ __device__ __forceinline__ void staged_tile(const EncodeArgs& a, EncodeShared& S
     if (agg) write_tile<W>(S, a.stage + a.slots[c.tile], c.n_c, meta, cnt, t, L);
 }
 
-// Staged encode (the staging area holds every chunk's slot): one workgroup
-// per tile, the tile is the workgroup id.
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_staged_kernel(
-    EncodeArgs a) {
+// Staged encode of the tiles that are not direct (pieces that split
+// 16-byte groups, misaligned or many pieces, ragged tails): one workgroup
+// per listed tile.
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_slow_kernel(
+    EncodeArgs a, const uint32_t* tiles, uint32_t n) {
     __shared__ EncodeShared S;
-    if (blockIdx.x >= a.n_tiles) return;
-    const TileCtx c = tile_ctx(a, blockIdx.x);
+    if (blockIdx.x >= n) return;
+    const TileCtx c = tile_ctx(a, tiles[blockIdx.x]);
     if (c.w == 2) staged_tile<2>(a, S, c);
     else if (c.w == 1) staged_tile<1>(a, S, c);
     else staged_tile<4>(a, S, c);
+}
+
+// Issue the loads of a direct tile: straight 128-bit loads for a fast tile;
+// otherwise each group finds its piece in an LDS copy of the piece table
+// (every group is inside one piece and aligned).  Ends with a barrier when it
+// used the LDS table.
+__device__ __forceinline__ void prefetch_direct(const EncodeArgs& a, EncodeShared& S, const TileCtx& c,
+                                                v4u (&o)[kVecsPerThread], v4u (&n)[kVecsPerThread]) {
+    if (c.fast) {
+        load_fast(c, o, n);
+        return;
+    }
+    const uint32_t tid = threadIdx.x;
+    const uint32_t w = c.w, V = 16u / w, np = c.n_pieces;
+    if (tid < np) {
+        const DevPiece p = a.pieces[c.first_piece + tid];
+        S.pstart[tid] = p.canon_start;
+        S.pold[tid] = reinterpret_cast<uint64_t>(a.old_sh[p.shard]) + p.shard_elem_off * w;
+        S.pnew[tid] = reinterpret_cast<uint64_t>(a.new_sh[p.shard]) + p.shard_elem_off * w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) {
+        const uint32_t e0 = (tid + k * kThreads) * V;
+        o[k] = v4u{0, 0, 0, 0};
+        n[k] = v4u{0, 0, 0, 0};
+        if (e0 < c.n_c) {
+            uint32_t l = 0, h = np;
+            while (h - l > 1) {
+                const uint32_t mid = (l + h) >> 1;
+                if (S.pstart[mid] <= e0) l = mid;
+                else h = mid;
+            }
+            const uint64_t off = uint64_t(e0 - S.pstart[l]) * w;
+            o[k] = __builtin_nontemporal_load(reinterpret_cast<gv4p>(S.pold[l] + off));
+            n[k] = __builtin_nontemporal_load(reinterpret_cast<gv4p>(S.pnew[l] + off));
+        }
+    }
+    __syncthreads();   // the LDS piece table is free again
+}
+
+// Staged encode of the direct tiles of W-byte elements (the staging area
+// holds every chunk's slot): one workgroup per list entry; nothing waits on
+// another workgroup.
+template <int W>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_direct_kernel(
+    EncodeArgs a, const uint32_t* list, uint32_t n_list) {
+    __shared__ EncodeShared S;
+    if (blockIdx.x >= n_list) return;
+    const uint32_t tid = threadIdx.x;
+    const TileCtx c = tile_ctx(a, list[blockIdx.x]);
+    const uint32_t owm = ow_mask<W>(a, c);
+    v4u o[kVecsPerThread], n[kVecsPerThread];
+    prefetch_direct(a, S, c, o, n);
+    uint32_t meta[kVecsPerThread];
+    uint64_t cnt[3];
+    digest_tile<W>(S, owm, o, n, meta, cnt);
+    const TileSums t = scan_tile(S, cnt);
+    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx);
+    const uint64_t agg = tile_aggregate(t, L);
+    if (tid == 0) {
+        a.tile_agg[c.tile] = agg;
+        a.tile_info[c.tile] = tile_counts(t);
+    }
+    if (agg) write_tile<W>(S, a.stage + a.slots[c.tile], c.n_c, meta, cnt, t, L);
 }
 
 // Encode fix-up: one workgroup of 256 threads per kFixTiles consecutive
@@ -905,7 +972,7 @@ __global__ __launch_bounds__(256) void scale_flags_kernel(const DevTensor* tenso
         const uint32_t e = e0 + lane;
         bool changed = false;
         if (e < n_c) {
-            const uint32_t p = find_piece(pc, ch.n_pieces, e);
+            const uint32_t p = find_piece(pc, ch.n_pieces & kPiecesMask, e);
             const uint64_t off = (pc[p].shard_elem_off + (e - pc[p].canon_start)) * 4;
             changed = *reinterpret_cast<const uint32_t*>(old_sh[pc[p].shard] + off) !=
                       *reinterpret_cast<const uint32_t*>(new_sh[pc[p].shard] + off);
@@ -1370,11 +1437,24 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
         a.n_tiles = n_tiles;
         a.mode = mode;
         mark(true, s);
-        if (staged)
-            hipLaunchKernelGGL(encode_staged_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
-        else
+        if (staged) {
+            // direct tiles per element width, then the others (in any order:
+            // every tile has its own slot)
+            for (int i = 0; i < 3; i++) {
+                const uint32_t n = uint32_t(p.direct[i].size());
+                if (!n) continue;
+                const uint32_t* list = tab<uint32_t>(p, p.off_direct[i]);
+                if (i == 0) hipLaunchKernelGGL(encode_direct_kernel<1>, dim3(n), dim3(kThreads), 0, s, a, list, n);
+                else if (i == 1) hipLaunchKernelGGL(encode_direct_kernel<2>, dim3(n), dim3(kThreads), 0, s, a, list, n);
+                else hipLaunchKernelGGL(encode_direct_kernel<4>, dim3(n), dim3(kThreads), 0, s, a, list, n);
+            }
+        } else {
             hipLaunchKernelGGL(encode_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
+        }
         mark(false, s);
+        if (staged && !p.slow.empty())
+            hipLaunchKernelGGL(encode_slow_kernel, dim3(uint32_t(p.slow.size())), dim3(kThreads), 0, s, a,
+                               tab<uint32_t>(p, p.off_slow), uint32_t(p.slow.size()));
         FixArgs f;
         f.tensors = tensors;
         f.chunks = chunks;

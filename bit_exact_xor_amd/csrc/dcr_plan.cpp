@@ -217,6 +217,20 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
                 ch.n_pieces++;
             }
             if (P.pieces.size() > 0xFFFFFFFFull) return fail(DCR_E_INVAL, "plan has too many pieces");
+            // direct: each 16-byte group sits inside one piece at a 16-byte
+            // aligned shard offset (shard bases are 16-byte aligned)
+            const uint32_t V = 16 / w;
+            bool direct = (c1 - c0) % V == 0 && ch.n_pieces <= kMaxCachedPieces;
+            for (uint32_t i = 0; direct && i < ch.n_pieces; i++) {
+                const DevPiece& pp = P.pieces[ch.first_piece + i];
+                direct = pp.canon_start % V == 0 && (uint32_t(pp.len_m1) + 1) % V == 0 && pp.shard_elem_off % V == 0;
+            }
+            if (direct) {
+                ch.n_pieces |= kChunkDirect;
+                P.direct[w == 1 ? 0 : (w == 2 ? 1 : 2)].push_back(uint32_t(P.chunks.size()));
+            } else {
+                P.slow.push_back(uint32_t(P.chunks.size()));
+            }
             P.chunks.push_back(ch);
             // worst-case stream sizes (DELTA or RETRY, whichever is larger)
             const uint64_t n_c = c1 - c0, nb = pad16((n_c + 7) / 8);
@@ -253,7 +267,13 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     P.off_pieces = pad256(P.off_chunks + P.chunks.size() * sizeof(DevChunk));
     P.off_scale_chunks = pad256(P.off_pieces + P.pieces.size() * sizeof(DevPiece));
     P.off_slots = pad256(P.off_scale_chunks + P.scale_chunks.size() * sizeof(uint32_t) + 4);
-    P.table_bytes = pad256(P.off_slots + P.slots.size() * sizeof(uint64_t));
+    P.off_slow = pad256(P.off_slots + P.slots.size() * sizeof(uint64_t));
+    uint64_t end = pad256(P.off_slow + P.slow.size() * sizeof(uint32_t) + 4);
+    for (int i = 0; i < 3; i++) {
+        P.off_direct[i] = end;
+        end = pad256(end + P.direct[i].size() * sizeof(uint32_t) + 4);
+    }
+    P.table_bytes = end;
     P.blob.assign(P.table_bytes, 0);
     if (!P.dt.empty()) std::memcpy(P.blob.data() + P.off_tensors, P.dt.data(), P.dt.size() * sizeof(DevTensor));
     if (!P.chunks.empty())
@@ -265,6 +285,11 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
                     P.scale_chunks.size() * sizeof(uint32_t));
     if (!P.slots.empty())
         std::memcpy(P.blob.data() + P.off_slots, P.slots.data(), P.slots.size() * sizeof(uint64_t));
+    if (!P.slow.empty())
+        std::memcpy(P.blob.data() + P.off_slow, P.slow.data(), P.slow.size() * sizeof(uint32_t));
+    for (int i = 0; i < 3; i++)
+        if (!P.direct[i].empty())
+            std::memcpy(P.blob.data() + P.off_direct[i], P.direct[i].data(), P.direct[i].size() * sizeof(uint32_t));
 
     // workspace: tile look-back status | fix-up look-back status | counters |
     // shard pointers | scale flags | canonical pointers | per-tile aggregates |
