@@ -33,6 +33,11 @@ constexpr uint32_t kFixTiles = 256;                 // tiles per workgroup of th
 // block claim, [2..3] changed elements, [4..5] stream total
 // (records << 36 | payload / 16)
 constexpr uint32_t kCtrTile = 0, kCtrFix = 1, kCtrChanged = 2, kCtrTotal = 4;
+// apply counters (uint32 words at ws_counter): [8] records deferred to the
+// large-record kernel
+constexpr uint32_t kCtrBig = 8;
+constexpr uint32_t kSmallThreads = 256;             // workgroup of the small-record apply
+constexpr uint32_t kSmallStage = 16384;             // its LDS stage (records up to this size)
 
 // Device-side tensor descriptor.  48 bytes.
 struct DevTensor {
@@ -91,7 +96,7 @@ struct Plan {
              off_direct[3] = {0, 0, 0}, table_bytes = 0;
     // workspace layout
     uint64_t ws_status = 0, ws_fix = 0, ws_counter = 0, ws_old = 0, ws_new = 0, ws_scale = 0, ws_canon = 0,
-             ws_agg = 0, ws_info = 0, ws_bytes = 0;
+             ws_agg = 0, ws_info = 0, ws_big = 0, big_cap = 0, ws_bytes = 0;
     std::vector<uint8_t> blob;            // host image of the device tables
     void* dev_tables = nullptr;           // bound by dcr_plan_upload
 };

@@ -1015,6 +1015,8 @@ struct ApplyArgs {
     const uint8_t* payload;
     uint8_t* flags;
     dcr_apply_result* result;
+    uint32_t* big_list;      // records (relative to first) deferred to the large-record kernel
+    uint32_t* big_count;
     uint64_t payload_bytes;
     uint64_t first;
     uint32_t n_tensors;
@@ -1220,13 +1222,13 @@ __device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uin
         // completion (stream order); no cross-agent ordering is promised
         // while the kernel runs, so no device-wide fence is paid per record.
         if (!a.retry) a.flags[r] = 1;
-        atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_applied), 1ull);
     }
 }
 
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void apply_kernel(ApplyArgs a) {
-    __shared__ ApplyShared S;
-    const uint64_t r = a.first + blockIdx.x;
+// One record with the large-record path: state already decided by the
+// caller (entry checked, dedup flag read).  Counts only refusals and skips;
+// the applied count is derived at the end.
+__device__ __forceinline__ void apply_one(const ApplyArgs& a, ApplyShared& S, uint64_t r) {
     uint32_t n_c = 0;
     if (threadIdx.x == 0) {
         const uint4* de = reinterpret_cast<const uint4*>(a.dir + r * DCR_DIRENT_BYTES);
@@ -1260,12 +1262,253 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     }
 }
 
-__global__ void apply_init_kernel(dcr_apply_result* res) {
+// Large-record apply, one workgroup per record of [first, first + n).
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void apply_kernel(ApplyArgs a) {
+    __shared__ ApplyShared S;
+    apply_one(a, S, a.first + blockIdx.x);
+}
+
+// Large-record apply over the records the small-record kernel deferred: a
+// persistent grid looping over the list.
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void apply_big_kernel(ApplyArgs a) {
+    __shared__ ApplyShared S;
+    const uint32_t n = *a.big_count;
+    for (uint32_t i = blockIdx.x; i < n; i += gridDim.x) {
+        apply_one(a, S, a.first + a.big_list[i]);
+        __syncthreads();
+    }
+}
+
+// Small-record apply: a workgroup of kSmallThreads per record, the record
+// staged in a kSmallStage LDS buffer, so that many records per compute unit
+// are in flight.  Thread t owns the 16 consecutive 16-byte groups starting
+// at group 16t (its bitmap bits are contiguous, so one scan of per-thread
+// change counts ranks every change).  Records that do not fit go to the
+// large-record kernel.
+struct SmallShared {
+    alignas(16) uint8_t stage[kSmallStage];
+    uint32_t pres_pre[kSmallThreads];   // SPARSE: set presence bits before each 32-bit word
+    uint64_t scan[kSmallThreads / 64];
+    uint32_t ent[8];
+    uint32_t state;                     // 0 invalid, 1 skip, 2 apply, 3 deferred
+    uint32_t n_c;
+    uint32_t bad;
+};
+
+// Exclusive scan of one value per thread over a kSmallThreads workgroup.
+__device__ __forceinline__ uint64_t small_excl_scan(uint64_t v, uint64_t& total, uint64_t* sh) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    const uint64_t inc = wave_incl_scan(v, lane);
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    uint64_t pre = 0, tot = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kSmallThreads / 64; w++) {
+        pre += w < wave ? sh[w] : 0;
+        tot += sh[w];
+    }
+    __syncthreads();
+    total = tot;
+    return pre + inc - v;
+}
+
+template <int W>
+__device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t r, uint32_t n_c) {
+    constexpr uint32_t V = 16 / W;                        // elements (= bitmap bits) per group
+    constexpr uint32_t E = kChunkBytes / W;
+    constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;  // groups per thread (16)
+    constexpr uint32_t BB = GT * V / 8;                   // bitmap bytes per thread (8, 16 or 32)
+    constexpr uint32_t NW = BB / 4;                       // ... in 32-bit words
+    constexpr uint32_t GPW = 32 / V;                      // groups per bitmap word
+    constexpr uint32_t GM = (V == 16) ? 0xFFFFu : ((1u << V) - 1u);
+    const uint32_t tid = threadIdx.x;
+    const uint32_t t = S.ent[0], c = S.ent[1], K = S.ent[2];
+    const uint32_t kind = S.ent[3] & 0xFF, hm = (S.ent[3] >> 8) & 0xFF;
+    const uint64_t off = uint64_t(S.ent[4]) | (uint64_t(S.ent[5]) << 32);
+    const uint32_t sz = S.ent[6], H = S.ent[7];
+    const uint32_t bm = dpad16((n_c + 7) / 8);
+    const uint32_t lo = bm;
+    const uint32_t pres = lo + dpad16(K);
+    const uint32_t hi = hm == DCR_HI_SPARSE ? pres + dpad16((K + 7) / 8) : pres;
+
+    // stage the record
+    const uint4* src = reinterpret_cast<const uint4*>(a.payload + off);
+    for (uint32_t q = tid; q < sz / 16; q += kSmallThreads) reinterpret_cast<uint4*>(S.stage)[q] = src[q];
+    if (tid == 0) S.bad = 0;
+    __syncthreads();
+
+    // this thread's bitmap words (bytes at or past bm are other sections: 0);
+    // nothing may be set at or past n_c
+    uint32_t bw[NW];
+    uint32_t cnt = 0;
+    bool bad = false;
+    const uint32_t b0 = tid * BB;
+#pragma unroll
+    for (uint32_t i = 0; i < NW; i++) {
+        const uint32_t byte = b0 + 4 * i;
+        uint32_t x = byte < bm ? reinterpret_cast<const uint32_t*>(S.stage)[byte / 4] : 0u;
+        const uint32_t e0 = byte * 8;
+        const uint32_t valid = e0 >= n_c ? 0u : (n_c - e0 >= 32 ? 0xFFFFFFFFu : ((1u << (n_c - e0)) - 1u));
+        if (x & ~valid) bad = true;
+        x &= valid;
+        bw[i] = x;
+        cnt += __popc(x);
+    }
+    // SPARSE: presence words (one per thread), their prefix counts and H
+    const uint32_t n_pw = dpad16((K + 7) / 8) / 4;
+    uint32_t pword = 0;
+    if (hm == DCR_HI_SPARSE && tid < n_pw) {
+        pword = reinterpret_cast<const uint32_t*>(S.stage + pres)[tid];
+        const uint32_t pb = tid * 32;
+        const uint32_t vmask = pb >= K ? 0u : (K - pb >= 32 ? 0xFFFFFFFFu : ((1u << (K - pb)) - 1u));
+        if (pword & ~vmask) bad = true;
+    }
+    uint64_t total;
+    uint32_t j = uint32_t(small_excl_scan(cnt, total, S.scan));
+    if (hm == DCR_HI_SPARSE) {
+        uint64_t ptot;
+        const uint32_t pp = uint32_t(small_excl_scan(__popc(pword), ptot, S.scan));
+        if (tid < n_pw) S.pres_pre[tid] = pp;
+        if (tid == 0 && ptot != H) bad = true;
+    }
+    if (tid == 0 && total != K) bad = true;
+    if (bad) atomicOr(&S.bad, 1u);
+    __syncthreads();
+    if (S.bad) return;   // refused before any write
+
+    // read-modify-write of every touched 16-byte group, in element order
+    uint8_t* dst = a.canon[t] + uint64_t(c) * E * W;
+    const uint32_t* pw32 = reinterpret_cast<const uint32_t*>(S.stage + pres);
+    const uint32_t pk = dpad16(K);
+    const bool is_xor = kind == DCR_KIND_XOR;
+#pragma unroll
+    for (uint32_t wi = 0; wi < NW; wi++) {
+        uint32_t wv = bw[wi];
+        while (wv) {
+            const uint32_t gi = uint32_t(__ffs(wv) - 1) / V;
+            uint32_t b = (wv >> (gi * V)) & GM;
+            wv &= ~(GM << (gi * V));
+            const uint32_t g = tid * GT + wi * GPW + gi;
+            uint64_t val0 = 0, val1 = 0, msk0 = 0, msk1 = 0;
+            const uint32_t bcopy = b;
+            while (b) {
+                const uint32_t i = uint32_t(__ffs(b) - 1);
+                b &= b - 1;
+                uint32_t v = S.stage[lo + j];
+                if constexpr (W == 2) {
+                    if (!is_xor || hm == DCR_HI_DENSE) {
+                        v |= uint32_t(S.stage[hi + j]) << 8;
+                    } else if (hm == DCR_HI_SPARSE) {
+                        const uint32_t pwj = pw32[j >> 5];
+                        if ((pwj >> (j & 31)) & 1u) {
+                            const uint32_t rank = S.pres_pre[j >> 5] + __popc(pwj & ((1u << (j & 31)) - 1u));
+                            v |= uint32_t(S.stage[hi + rank]) << 8;
+                        }
+                    }
+                } else if constexpr (W == 4) {
+                    v |= uint32_t(S.stage[lo + pk + j]) << 8;
+                    v |= uint32_t(S.stage[lo + 2 * pk + j]) << 16;
+                    v |= uint32_t(S.stage[lo + 3 * pk + j]) << 24;
+                }
+                constexpr uint32_t EB = 8 * W;
+                constexpr uint64_t EM = (W == 4) ? 0xFFFFFFFFull : ((1ull << EB) - 1);
+                const uint32_t bitpos = i * EB;
+                const uint32_t sh = bitpos & 63;
+                if (bitpos < 64) { val0 |= uint64_t(v) << sh; msk0 |= EM << sh; }
+                else { val1 |= uint64_t(v) << sh; msk1 |= EM << sh; }
+                j++;
+            }
+            uint8_t* gp = dst + uint64_t(g) * 16;
+            if ((g + 1) * V <= n_c) {
+                v4u w4 = *reinterpret_cast<const v4u*>(gp);
+                uint64_t q0 = uint64_t(w4.x) | (uint64_t(w4.y) << 32);
+                uint64_t q1 = uint64_t(w4.z) | (uint64_t(w4.w) << 32);
+                q0 = is_xor ? (q0 ^ val0) : ((q0 & ~msk0) | val0);
+                q1 = is_xor ? (q1 ^ val1) : ((q1 & ~msk1) | val1);
+                v4u r4;
+                r4.x = uint32_t(q0); r4.y = uint32_t(q0 >> 32); r4.z = uint32_t(q1); r4.w = uint32_t(q1 >> 32);
+                *reinterpret_cast<v4u*>(gp) = r4;
+            } else {
+                // tail group of a tensor: element accesses only inside the tensor
+                uint32_t bb = bcopy;
+                while (bb) {
+                    const uint32_t i = uint32_t(__ffs(bb) - 1);
+                    bb &= bb - 1;
+                    if (g * V + i >= n_c) break;
+                    const uint32_t bitpos = i * 8 * W;
+                    const uint32_t v = uint32_t(((bitpos < 64) ? val0 : val1) >> (bitpos & 63));
+                    if constexpr (W == 1) { gp[i] = is_xor ? uint8_t(gp[i] ^ v) : uint8_t(v); }
+                    else if constexpr (W == 2) {
+                        uint16_t* p = reinterpret_cast<uint16_t*>(gp) + i;
+                        *p = is_xor ? uint16_t(*p ^ v) : uint16_t(v);
+                    } else {
+                        uint32_t* p = reinterpret_cast<uint32_t*>(gp) + i;
+                        *p = is_xor ? (*p ^ v) : v;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0 && !a.retry) a.flags[r] = 1;   // visible with the writes at kernel completion
+}
+
+__global__ __launch_bounds__(kSmallThreads) void apply_small_kernel(ApplyArgs a) {
+    __shared__ SmallShared S;
+    const uint64_t r = a.first + blockIdx.x;
+    uint32_t n_c = 0;
+    if (threadIdx.x == 0) {
+        const uint4* de = reinterpret_cast<const uint4*>(a.dir + r * DCR_DIRENT_BYTES);
+        const uint4 e0 = de[0], e1 = de[1];
+        uint32_t e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+        for (int i = 0; i < 8; i++) S.ent[i] = e[i];
+        uint32_t st;
+        if (!entry_ok(a, e, n_c)) {
+            st = 0;
+        } else if (!a.retry && a.flags[r]) {
+            st = 1;
+        } else {
+            const uint32_t K = e[2], hm = (e[3] >> 8) & 0xFF;
+            const bool fits = e[6] <= kSmallStage && (hm != DCR_HI_SPARSE || dpad16((K + 7) / 8) / 4 <= kSmallThreads);
+            st = fits ? 2 : 3;
+            if (!fits) a.big_list[atomicAdd(a.big_count, 1u)] = uint32_t(r - a.first);
+        }
+        S.state = st;
+        S.n_c = n_c;
+    }
+    __syncthreads();
+    const uint32_t st = S.state;
+    n_c = S.n_c;
+    if (st == 3) return;
+    if (st == 1) {
+        if (threadIdx.x == 0) atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_skipped), 1ull);
+        return;
+    }
+    if (st == 2) {
+        const uint32_t w = (S.ent[3] >> 16) & 0xFF;
+        if (w == 2) apply_small_record<2>(a, S, r, n_c);
+        else if (w == 1) apply_small_record<1>(a, S, r, n_c);
+        else apply_small_record<4>(a, S, r, n_c);
+        if (!S.bad) return;
+    }
+    if (threadIdx.x == 0) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_invalid), 1ull);
+        atomicMin(reinterpret_cast<unsigned long long*>(&a.result->first_invalid), (unsigned long long)r);
+    }
+}
+
+__global__ void apply_init_kernel(dcr_apply_result* res, uint32_t* big_count) {
     if (threadIdx.x == 0) {
         uint4* r = reinterpret_cast<uint4*>(res);
         r[0] = make_uint4(0, 0, 0, 0);
         r[1] = make_uint4(0, 0, 0xFFFFFFFFu, 0xFFFFFFFFu);
+        *big_count = 0;
     }
+}
+
+// Every record of the call ends applied, skipped or refused.
+__global__ void apply_finalize_kernel(dcr_apply_result* res, uint64_t n) {
+    if (threadIdx.x == 0) res->n_applied = n - res->n_skipped - res->n_invalid;
 }
 
 // ------------------------------------------------------------- host side
@@ -1275,6 +1518,19 @@ static int32_t fail(int32_t rc, const std::string& m) {
     return rc;
 }
 static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// compute units of the current device
+static uint32_t cu_count() {
+    static uint32_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = uint32_t(n);
+    }
+    return cached[dev];
+}
 
 // benchmark hook: events recorded around the main kernel of each call
 static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
@@ -1326,7 +1582,8 @@ static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     int32_t rc = copy_ptrs(wsb + p.ws_canon, reinterpret_cast<const void* const*>(canon), nT, s);
     if (rc) return rc;
-    hipLaunchKernelGGL(apply_init_kernel, dim3(1), dim3(64), 0, s, res);
+    uint32_t* big_count = reinterpret_cast<uint32_t*>(wsb + p.ws_counter) + kCtrBig;
+    hipLaunchKernelGGL(apply_init_kernel, dim3(1), dim3(64), 0, s, res, big_count);
     if (n) {
         ApplyArgs a;
         a.tensors = tab<DevTensor>(p, p.off_tensors);
@@ -1335,14 +1592,24 @@ static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_
         a.payload = static_cast<const uint8_t*>(payload);
         a.flags = flags;
         a.result = res;
+        a.big_list = reinterpret_cast<uint32_t*>(wsb + p.ws_big);
+        a.big_count = big_count;
         a.payload_bytes = hdr->payload_bytes;
         a.first = first;
         a.n_tensors = nT;
         a.retry = retry ? 1u : 0u;
         mark(true, s);
-        hipLaunchKernelGGL(apply_kernel, dim3(uint32_t(n)), dim3(kThreads), 0, s, a);
+        if (n <= p.big_cap) {
+            // small records with many per compute unit; the rest deferred
+            hipLaunchKernelGGL(apply_small_kernel, dim3(uint32_t(n)), dim3(kSmallThreads), 0, s, a);
+            hipLaunchKernelGGL(apply_big_kernel, dim3(uint32_t(std::min<uint64_t>(n, 2 * cu_count()))), dim3(kThreads),
+                               0, s, a);
+        } else {
+            hipLaunchKernelGGL(apply_kernel, dim3(uint32_t(n)), dim3(kThreads), 0, s, a);
+        }
         mark(false, s);
     }
+    hipLaunchKernelGGL(apply_finalize_kernel, dim3(1), dim3(64), 0, s, res, n);
     return hip_check(hipGetLastError(), "apply launch");
 }
 

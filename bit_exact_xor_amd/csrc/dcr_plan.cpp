@@ -293,8 +293,9 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
 
     // workspace: tile look-back status | fix-up look-back status | counters |
     // shard pointers | scale flags | canonical pointers | per-tile aggregates |
-    // per-tile change counts.  Everything before the shard pointers is zeroed
-    // at the start of an encode.  Bytes past ws_bytes are the optional
+    // per-tile change counts | apply's list of deferred large records.
+    // Everything before the shard pointers is zeroed at the start of an
+    // encode.  Bytes past ws_bytes are the optional
     // staging area of encode (used when it holds every chunk's slot).
     const uint64_t n_tiles = P.chunks.size();
     P.ws_status = 0;
@@ -306,7 +307,9 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     P.ws_canon = pad256(P.ws_scale + P.scale_bits / 8);
     P.ws_agg = pad256(P.ws_canon + uint64_t(nT) * 8);
     P.ws_info = pad256(P.ws_agg + n_tiles * 8);
-    P.ws_bytes = pad256(P.ws_info + n_tiles * 8);
+    P.big_cap = P.max_dir_bytes / DCR_DIRENT_BYTES;
+    P.ws_big = pad256(P.ws_info + n_tiles * 8);
+    P.ws_bytes = pad256(P.ws_big + P.big_cap * 4);
     return DCR_OK;
 }
 

@@ -74,6 +74,9 @@ def build_stream(lay, plan_full, mode, dir_buf, payload, t_old, t_new):
 
 
 def test_receiver_share_1t(orc):
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()          # memory cached by earlier tests
     free, total = torch.cuda.mem_get_info()
     lay = synth.config5_layout()
     need = lay.total_bytes() + 2 * 8 * 10**9 + 26 * 10**9
