@@ -219,8 +219,8 @@ def main():
     ret_bytes = 32 * rn_rec + rp_bytes + 2 * LINE * touched
     alg = {"encode": enc_bytes, "apply": app_bytes, "encode_retry": renc_bytes, "retry": ret_bytes}
     per_op = {}
-    kname = {"encode": "encode_staged_kernel", "encode_retry": "encode_staged_kernel", "apply": "apply_kernel",
-             "retry": "apply_kernel"}
+    kname = {"encode": "encode_direct_kernel", "encode_retry": "encode_direct_kernel", "apply": "apply_small_kernel",
+             "retry": "apply_small_kernel"}
     for op in ops:
         gbps = alg[op] / (op_ms[op] * 1e-3) / 1e9
         kgbps = alg[op] / (kern_ms[op] * 1e-3) / 1e9
@@ -402,8 +402,8 @@ def pmc_report(d):
         factors[c] = copy_bytes / (kib * 1024.0)
     # dispatch order per step in bench.py: encode DELTA, encode RETRY (first step),
     # then encode DELTA, apply, encode RETRY, retry; kernels alternate
-    ops = {"encode": ("encode_staged_kernel", 0), "encode_retry": ("encode_staged_kernel", 1),
-           "apply": ("apply_kernel(", 0), "retry": ("apply_kernel(", 1)}
+    ops = {"encode": ("encode_direct_kernel", 0), "encode_retry": ("encode_direct_kernel", 1),
+           "apply": ("apply_small_kernel", 0), "retry": ("apply_small_kernel", 1)}
     table, per_launch = [], {}
     for op, (k, parity) in ops.items():
         got = {}
