@@ -49,6 +49,8 @@ def parse():
                     help="only run a plain device copy of this many GiB, 3 times (counter calibration)")
     ap.add_argument("--pmc-report", metavar="DIR",
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs found under DIR and exit")
+    ap.add_argument("--pmc-dump", metavar="DIR",
+                    help="per-kernel averages of every counter in the rocprofv3 runs under DIR/pmc_*; exit")
     return ap.parse_args()
 
 
@@ -60,6 +62,9 @@ def main():
     args = parse()
     if args.pmc_report:
         print(pmc_report(args.pmc_report))
+        return
+    if args.pmc_dump:
+        print(pmc_dump(args.pmc_dump))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: --gpus {args.gpus}: this build runs the hot path on one GPU only "
@@ -430,6 +435,36 @@ def pmc_report(d):
            TRAFFIC_TAG + " " + json.dumps({"source_sha256": _src_sha256(), "bytes_per_launch": per_launch,
                                             "factors": factors})]
     return "\n".join(out)
+
+
+def pmc_dump(d):
+    """Markdown table: per main kernel and op (dispatches alternate DELTA /
+    RETRY, apply / retry), the per-dispatch average of every counter found in
+    the runs DIR/pmc_*/bench_counter_collection.csv."""
+    import glob
+    ops = [("encode", "encode_direct_kernel", 0), ("encode_retry", "encode_direct_kernel", 1),
+           ("apply", "apply_small_kernel", 0), ("retry", "apply_small_kernel", 1),
+           ("fix-up (DELTA)", "encode_fixup_kernel", 0)]
+    vals = {}
+    counters = []
+    for path in sorted(glob.glob(os.path.join(d, "pmc_*", "bench_counter_collection.csv"))):
+        per = {}
+        for r in _pmc_rows(path):
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]), r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (kn, disp, cn), v in per.items():
+            if cn not in counters:
+                counters.append(cn)
+            vals.setdefault((kn, cn), []).append((disp, v))
+    lines = ["| counter | " + " | ".join(o for o, _, _ in ops) + " |", "|---|" + "---|" * len(ops)]
+    for cn in counters:
+        row = []
+        for _, k, par in ops:
+            xs = sorted(v for (kn, c), v in vals.items() if k in kn and c == cn for v in v)
+            xs = [v for _, v in sorted(xs)][par::2]
+            row.append(f"{np.mean(xs):.4g}" if xs else "-")
+        lines.append(f"| `{cn}` | " + " | ".join(row) + " |")
+    return "\n".join(lines)
 
 
 def fmt_dirents(d):

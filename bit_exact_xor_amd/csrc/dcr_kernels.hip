@@ -1343,10 +1343,28 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     uint32_t cnt = 0;
     bool bad = false;
     const uint32_t b0 = tid * BB;
+    // the thread's bitmap slice as whole 64- / 128-bit LDS reads (word reads
+    // at this stride would collide on the banks)
+    uint32_t raw[NW];
+    if constexpr (NW == 2) {
+        const uint2 v = b0 < bm ? *reinterpret_cast<const uint2*>(S.stage + b0) : make_uint2(0, 0);
+        raw[0] = v.x;
+        raw[1] = v.y;
+    } else {
+#pragma unroll
+        for (uint32_t h = 0; h < NW / 4; h++) {
+            const uint4 v = b0 + 16 * h < bm ? *reinterpret_cast<const uint4*>(S.stage + b0 + 16 * h)
+                                             : make_uint4(0, 0, 0, 0);
+            raw[4 * h] = v.x;
+            raw[4 * h + 1] = v.y;
+            raw[4 * h + 2] = v.z;
+            raw[4 * h + 3] = v.w;
+        }
+    }
 #pragma unroll
     for (uint32_t i = 0; i < NW; i++) {
         const uint32_t byte = b0 + 4 * i;
-        uint32_t x = byte < bm ? reinterpret_cast<const uint32_t*>(S.stage)[byte / 4] : 0u;
+        uint32_t x = raw[i];
         const uint32_t e0 = byte * 8;
         const uint32_t valid = e0 >= n_c ? 0u : (n_c - e0 >= 32 ? 0xFFFFFFFFu : ((1u << (n_c - e0)) - 1u));
         if (x & ~valid) bad = true;
