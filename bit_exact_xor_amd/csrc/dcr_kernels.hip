@@ -30,6 +30,14 @@ namespace dcr {
 // ------------------------------------------------------------ device helpers
 
 __device__ __forceinline__ uint32_t dpad16(uint32_t x) { return (x + 15u) & ~15u; }
+
+// The thread index, opaque to the compiler: values derived from it are
+// recomputed where they are used instead of being kept live in registers.
+__device__ __forceinline__ uint32_t opaque_tid() {
+    uint32_t t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
 __device__ __forceinline__ uint64_t ld_status(const uint64_t* p) {
@@ -443,23 +451,39 @@ __device__ __forceinline__ uint32_t ow_mask(const EncodeArgs& a, const TileCtx& 
     return m;
 }
 
+// 1 in each 16-bit half of the result iff that half of d is nonzero (one
+// packed 16-bit integer minimum against 1).
+__device__ __forceinline__ uint32_t nz16(uint32_t d) {
+    uint32_t r;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(d), "s"(0x00010001u));
+    return r;
+}
+
+// The 8 nonzero flags of the 16-bit halves of d[0..3] as bits 0..7 (half h
+// of word i -> bit 2i + h): the flags sit at bits 2i and 2i + 16 after the
+// shifts, and folding bit 16 + 2i onto 2i + 1 packs them.
+__device__ __forceinline__ uint32_t pack_nz16(uint32_t m0, uint32_t m1, uint32_t m2, uint32_t m3) {
+    const uint32_t x = m0 | (m1 << 2) | (m2 << 4) | (m3 << 6);
+    return (x | (x >> 15)) & 0xFFu;
+}
+
 // Changed-element bits of a 16-byte group of W-byte elements (d = old ^ new,
 // four 32-bit words); for W = 2 also the bits of elements whose high byte
-// changed.  Integer arithmetic only: x != 0 for an n-bit field x is
-// (x + 2^n - 1) >> n.
+// changed.  Integer arithmetic only (for bytes: x != 0 for an n-bit field x
+// is (x + 2^n - 1) >> n).
 template <int W>
 __device__ __forceinline__ uint32_t changed_bits(const uint32_t (&d)[4], uint32_t& hi_bits) {
+    if constexpr (W == 2) {
+        hi_bits = pack_nz16(nz16(d[0] & 0xFF00FF00u), nz16(d[1] & 0xFF00FF00u), nz16(d[2] & 0xFF00FF00u),
+                            nz16(d[3] & 0xFF00FF00u));
+        return pack_nz16(nz16(d[0]), nz16(d[1]), nz16(d[2]), nz16(d[3]));
+    }
     uint32_t b = 0, h = 0;
 #pragma unroll
     for (uint32_t i = 0; i < 4; i++) {
         const uint32_t x = d[i];
         if constexpr (W == 4) {
             b |= uint32_t(x != 0) << i;
-        } else if constexpr (W == 2) {
-            b |= (((x & 0xFFFFu) + 0xFFFFu) >> 16) << (2 * i);
-            b |= (((x >> 16) + 0xFFFFu) >> 16) << (2 * i + 1);
-            h |= ((((x >> 8) & 0xFFu) + 0xFFu) >> 8) << (2 * i);
-            h |= (((x >> 24) + 0xFFu) >> 8) << (2 * i + 1);
         } else {
             // high bit of each byte set iff the byte is nonzero
             const uint32_t t = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
@@ -482,7 +506,7 @@ __device__ __forceinline__ void digest_tile(EncodeShared& S, uint32_t owm, const
                                             const v4u (&ln)[kVecsPerThread], uint32_t (&meta)[kVecsPerThread],
                                             uint64_t (&cnt)[3]) {
     const uint32_t tid = threadIdx.x;
-    cnt[0] = cnt[1] = cnt[2] = 0;
+    uint32_t kx = 0, ko = 0, kh = 0;   // per-k counts, 8 bits each
 #pragma unroll
     for (uint32_t k = 0; k < kVecsPerThread; k++) {
         const uint32_t g = tid + k * kThreads;
@@ -496,11 +520,19 @@ __device__ __forceinline__ void digest_tile(EncodeShared& S, uint32_t owm, const
         }
         if (kd != DCR_KIND_XOR) h = 0;
         meta[k] = b | (h << 16) | (kd << 31);
-        const uint64_t cc = uint64_t(__popc(b)) << (16 * k);
-        cnt[0] |= kd == DCR_KIND_XOR ? cc : 0;
-        cnt[1] |= kd == DCR_KIND_XOR ? 0 : cc;
-        cnt[2] |= uint64_t(__popc(h)) << (16 * k);
+        const uint32_t pb = uint32_t(__popc(b)) << (8 * k);
+        kx |= kd == DCR_KIND_XOR ? pb : 0u;
+        ko |= kd == DCR_KIND_XOR ? 0u : pb;
+        kh |= uint32_t(__popc(h)) << (8 * k);
     }
+    // widened once to the scan's 16-bit fields
+    auto widen = [](uint32_t x) {
+        return uint64_t(x & 0xFFu) | (uint64_t((x >> 8) & 0xFFu) << 16) | (uint64_t((x >> 16) & 0xFFu) << 32) |
+               (uint64_t(x >> 24) << 48);
+    };
+    cnt[0] = widen(kx);
+    cnt[1] = widen(ko);
+    cnt[2] = widen(kh);
 }
 
 // Tile totals and, per k, the totals of all lower k (uniform).
@@ -648,7 +680,7 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
     }
     __syncthreads();
     const uint32_t n = ONE ? total : uint32_t(umin64(kWinBytes, total - w0));
-    for (uint32_t q = tid; q < n / 16; q += kThreads)
+    for (uint32_t q = opaque_tid(); q < n / 16; q += kThreads)
         reinterpret_cast<v4u*>(out + w0)[q] = reinterpret_cast<const v4u*>(win)[q];
 }
 
@@ -828,6 +860,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     if (blockIdx.x >= n_list) return;
     const uint32_t tid = threadIdx.x;
     const TileCtx c = tile_ctx(a, list[blockIdx.x]);
+    // the slot's address is uniform: read it before this workgroup stores
+    // anything, into scalar registers
+    uint8_t* const out = a.stage + uniform_load(a.slots + c.tile);
     const uint32_t owm = ow_mask<W>(a, c);
     v4u o[kVecsPerThread], n[kVecsPerThread];
     prefetch_direct(a, S, c, o, n);
@@ -841,7 +876,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         a.tile_agg[c.tile] = agg;
         a.tile_info[c.tile] = tile_counts(t);
     }
-    if (agg) write_tile<W>(S, a.stage + a.slots[c.tile], c.n_c, meta, cnt, t, L);
+    if (agg) write_tile<W>(S, out, c.n_c, meta, cnt, t, L);
 }
 
 // Encode fix-up: one workgroup of 256 threads per kFixTiles consecutive
