@@ -627,11 +627,8 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
         }
         const v4u q = *reinterpret_cast<const v4u*>(S.pw[g]);
         // byte planes of the group packed into 64-bit values
-        uint64_t pl0 = 0, pl1 = 0, ph = 0;
-        if constexpr (W == 1) {
-            pl0 = uint64_t(q.x) | (uint64_t(q.y) << 32);
-            pl1 = uint64_t(q.z) | (uint64_t(q.w) << 32);
-        } else if constexpr (W == 2) {
+        uint64_t pl0 = 0, ph = 0;
+        if constexpr (W == 2) {
             const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (uint32_t i = 0; i < 8; i++) {
@@ -654,7 +651,9 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
             const uint32_t i = uint32_t(__ffs(b) - 1);
             b &= b - 1;
             if constexpr (W == 1) {
-                put(lo + j, uint32_t((i < 8 ? pl0 : pl1) >> (8 * (i & 7))));
+                // byte i of the group: 32-bit selects and shifts only
+                const uint32_t wv = (i & 8u) ? ((i & 4u) ? q.w : q.z) : ((i & 4u) ? q.y : q.x);
+                put(lo + j, wv >> (8u * (i & 3u)));
             } else if constexpr (W == 2) {
                 put(lo + j, uint32_t(pl0 >> (8 * i)));
                 const uint32_t hb = uint32_t(ph >> (8 * i)) & 0xFFu;

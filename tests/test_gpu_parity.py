@@ -196,6 +196,22 @@ def test_determinism(gh):
             assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("seed,rate", [(31, None), (7, 0.2)])
+def test_dense_records_repeated(gh, orc, seed, rate):
+    """Dense chunks whose records span several LDS output windows (1-byte
+    overwrite records near 20 % change, 2-byte XOR records): twelve staged and
+    four in-order encodes of the same input all equal the oracle's stream."""
+    say("dense records repeated", seed)
+    lay = synth.random_layout(seed, rate=rate)
+    olds, news, _co, _cn = pins.canon_lists(lay)
+    g = gh.Gpu(lay, olds, news)
+    exp = oracle_stream(orc, lay, olds, news, 0)
+    full = stage_sizes(g)[2]
+    for i in range(16):
+        stage = full if i < 12 else 0
+        assert_same_stream(g.stream_host(g.encode(0, stage=stage)), exp, f"dense seed {seed} run {i} stage {stage}")
+
+
 def test_capacity_overflow(gh, orc):
     """Too-small buffers: status DCR_E_CAPACITY with the required sizes."""
     say("capacity overflow")
