@@ -215,6 +215,8 @@ def main():
              for i, op in enumerate(ops)}
     kern_ms = {op: float(np.mean([kev[s][i][0].elapsed_time(kev[s][i][1]) for s in range(args.steps)]))
                for i, op in enumerate(ops)}
+    kern_med = {op: float(np.median([kev[s][i][0].elapsed_time(kev[s][i][1]) for s in range(args.steps)]))
+                for i, op in enumerate(ops)}
     ms_per_step = wall * 1e3 / args.steps
     # the stream after timing is still new (each step ends with the retry)
     ok_after = True
@@ -241,12 +243,18 @@ def main():
                       "alg_GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
                       "scanned_GBps": round(cb / (op_ms[op] * 1e-3) / 1e9, 1),
                       "kernel": kname[op], "kernel_ms": round(kern_ms[op], 4),
+                      "kernel_ms_median": round(kern_med[op], 4),
                       "kernel_alg_GB": round(kalg[op] / 1e9, 4), "kernel_alg_GBps": round(kgbps, 1)}
     # the dominant kernel: its algorithmic bytes over its own launch duration
     dom = max(ops, key=lambda o: kern_ms[o])
     roof = {"bound": "hbm", "kernel": kname[dom], "op": dom, "achieved": per_op[dom]["kernel_alg_GBps"],
             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(per_op[dom]["kernel_alg_GBps"] / PEAK_HBM_GBPS, 4),
             "traffic": measured_traffic(dom)}
+
+    # measured ceilings on this GPU: a streaming read and a device copy
+    ceiling = measure_ceiling(old_buf, dev)
+    for op in ops:
+        per_op[op]["kernel_frac_of_read_ceiling"] = round(per_op[op]["kernel_alg_GBps"] / ceiling["read_GBps"], 4)
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
@@ -281,9 +289,47 @@ def main():
         "checks": {"apply_eq_new": bool(ok_apply), "retry_eq_new": bool(ok_retry),
                    "after_timing_eq_new": bool(ok_after), "oracle_sample": parity_sample},
         "roofline": roof,
+        "ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measure_ceiling(buf, dev, reps=3):
+    """Best of `reps`: one streaming read of `buf` (the probe kernel of the
+    synthetic-input library: 128-bit non-temporal loads, nothing written) and
+    a 4 GiB device-to-device copy (torch; read + write counted)."""
+    import torch
+    from bit_exact_xor_amd import synth
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    rd = []
+    for _ in range(reps):
+        a, b = ev(), ev()
+        a.record()
+        nread = synth.read_probe_gpu(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        rd.append(a.elapsed_time(b))
+    n = 1 << 32
+    src = buf[:n] if buf.numel() >= 2 * n else buf[: buf.numel() // 2]
+    dst = torch.empty_like(src)
+    cp = []
+    for _ in range(reps):
+        a, b = ev(), ev()
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        cp.append(a.elapsed_time(b))
+    del dst
+    torch.cuda.empty_cache()
+    read_gbps = nread / (min(rd) * 1e-3) / 1e9
+    copy_gbps = 2 * src.numel() / (min(cp) * 1e-3) / 1e9
+    return {"read_GBps": round(read_gbps, 1), "copy_GBps": round(copy_gbps, 1),
+            "read_frac_of_peak": round(read_gbps / PEAK_HBM_GBPS, 4),
+            "how": f"streaming read of {nread / 1e9:.2f} GB (128-bit non-temporal loads) and a "
+                   f"{src.numel() / 2**30:.0f} GiB torch device copy (read + write counted), best of {reps}"}
 
 
 def cpu_baseline(lay, delta, hdr_dev, reps):

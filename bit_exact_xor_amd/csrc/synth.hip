@@ -100,6 +100,26 @@ __global__ void gen_kernel(uint8_t* shard, Region r, const uint32_t* hot, uint32
     }
 }
 
+// Streaming-read probe, used only to measure this GPU's read ceiling: each
+// 256-thread workgroup reads one contiguous 64 KiB block with 16 non-temporal
+// 128-bit loads per thread, all in flight at once, and XORs them together.
+// Nothing is stored unless the fold hits one fixed value, which keeps the
+// loads alive.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void read_probe_kernel(const v4u* buf, uint64_t n16, uint32_t* sink) {
+    const uint64_t base = uint64_t(blockIdx.x) * 4096u + threadIdx.x;
+    v4u x = {0, 0, 0, 0};
+    if (base + 15u * 256u < n16) {
+#pragma unroll
+        for (uint32_t k = 0; k < 16; k++) x ^= __builtin_nontemporal_load(buf + base + k * 256u);
+    } else {
+        for (uint32_t k = 0; k < 16; k++)
+            if (base + k * 256u < n16) x ^= __builtin_nontemporal_load(buf + base + k * 256u);
+    }
+    const uint32_t f = x.x ^ x.y ^ x.z ^ x.w;
+    if (f == 0x9E3779B9u) sink[0] = f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +137,19 @@ int32_t dcr_synth_fill(void* shard, uint64_t elem_off, uint64_t n, uint32_t kind
     if (blocks > 0x7FFFFFFFull) return int32_t(hipErrorInvalidValue);
     hipLaunchKernelGGL(gen_kernel, dim3(uint32_t(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<uint8_t*>(shard), r, hot, version, scale_bits);
+    return int32_t(hipGetLastError());
+}
+
+// Read `bytes` of device memory at `buf` once (both 16-byte aligned/multiple)
+// with the streaming-read probe; `sink` is 4 bytes of device memory.  Returns
+// 0 or a HIP error code.
+int32_t dcr_synth_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+    if ((reinterpret_cast<uintptr_t>(buf) & 15u) || (bytes & 15u) || !sink) return int32_t(hipErrorInvalidValue);
+    if (bytes == 0) return 0;
+    const uint64_t blocks = (bytes / 16 + 4095) / 4096;
+    if (blocks > 0x7FFFFFFFull) return int32_t(hipErrorInvalidValue);
+    hipLaunchKernelGGL(read_probe_kernel, dim3(uint32_t(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const v4u*>(buf), bytes / 16, sink);
     return int32_t(hipGetLastError());
 }
 

@@ -675,6 +675,8 @@ def _load_synth():
         lib.dcr_synth_fill.restype = ctypes.c_int32
         lib.dcr_synth_fill.argtypes = [P, U64, U64, U32, U64, U64, U64, U64, P, U64, U32, U64, U64, U32,
                                        U32, U32, P]
+        lib.dcr_synth_read_probe.restype = ctypes.c_int32
+        lib.dcr_synth_read_probe.argtypes = [P, U64, P, P]
         _synth_lib = lib
     return _synth_lib
 
@@ -710,6 +712,19 @@ def fill_shards_gpu(lay: Layout, shards, version: int, stream=None):
             raise RuntimeError(f"dcr_synth_fill failed: {rc}")
         hot_off += n_hot
     return hot_dev  # keep alive until the fills have run
+
+
+def read_probe_gpu(buf, sink, stream=None):
+    """One streaming read of the device tensor `buf` (bandwidth probe)."""
+    import torch
+    lib = _load_synth()
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    n = buf.numel() * buf.element_size() // 16 * 16
+    rc = lib.dcr_synth_read_probe(buf.data_ptr(), n, sink.data_ptr(), stream or None)
+    if rc:
+        raise RuntimeError(f"dcr_synth_read_probe failed: {rc}")
+    return n
 
 
 # ------------------------------------------------- configs 3 / 4 (MoE)
