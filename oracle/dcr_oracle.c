@@ -256,15 +256,19 @@ static void put_header(uint8_t* p, uint32_t mode, uint64_t base_v, uint64_t new_
 
 /* ----------------------------------------------------------------- encode */
 
-int32_t orc_encode(const orc_tensor* T, uint32_t nT,
-                   const void* const* old_shards, const void* const* new_shards,
-                   const uint64_t* shard_bytes, uint32_t nS,
-                   const orc_segment* segs, uint64_t nseg,
-                   uint32_t mode, uint64_t base_version, uint64_t new_version,
-                   uint8_t* header_out,
-                   uint8_t* dir_out, uint64_t dir_cap, uint64_t* dir_bytes,
-                   uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes) {
-    uint64_t nrec = 0, poff = 0;
+/* The encode proper.  need: NULL (every chunk), or one byte per chunk in
+ * (tensor, chunk) order, nonzero for the chunks to encode; the others are
+ * treated as unchanged. */
+static int32_t encode_chunks(const orc_tensor* T, uint32_t nT,
+                             const void* const* old_shards, const void* const* new_shards,
+                             const uint64_t* shard_bytes, uint32_t nS,
+                             const orc_segment* segs, uint64_t nseg,
+                             uint32_t mode, uint64_t base_version, uint64_t new_version,
+                             uint8_t* header_out,
+                             uint8_t* dir_out, uint64_t dir_cap, uint64_t* dir_bytes,
+                             uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes,
+                             const uint8_t* need) {
+    uint64_t nrec = 0, poff = 0, ordinal = 0;
     uint32_t t;
     int32_t rc = check_tensors(T, nT);
     uint32_t* idx[2] = {NULL, NULL};
@@ -284,6 +288,11 @@ int32_t orc_encode(const orc_tensor* T, uint32_t nT,
         uint8_t *co = NULL, *cn = NULL, *so = NULL, *sn = NULL;
         const orc_tensor* sd = NULL;
         if (d->numel == 0) continue;
+        if (need) {   /* a tensor none of whose chunks is wanted is not read at all */
+            uint64_t any = 0;
+            for (c = 0; c < nc; c++) any |= need[ordinal + c];
+            if (!any) { ordinal += nc; continue; }
+        }
         co = (uint8_t*)malloc(d->numel * w);
         cn = (uint8_t*)malloc(d->numel * w);
         if (!co || !cn) { free(co); free(cn); rc = ORC_E_NOMEM; goto done; }
@@ -302,6 +311,7 @@ int32_t orc_encode(const orc_tensor* T, uint32_t nT,
             uint64_t n_c = (d->numel - c * E < E) ? d->numel - c * E : E;
             uint64_t K[2] = {0, 0}, i;
             uint32_t k;
+            if (need && !need[ordinal + c]) continue;
             for (i = 0; i < n_c; i++) {
                 uint64_t g = c * E + i;
                 uint32_t o = load_word(co, g, w), n = load_word(cn, g, w);
@@ -333,6 +343,7 @@ int32_t orc_encode(const orc_tensor* T, uint32_t nT,
             }
         }
         free(co); free(cn); free(so); free(sn);
+        ordinal += nc;
     }
     *dir_bytes = nrec * ORC_DIRENT_BYTES;
     *payload_bytes = poff;
@@ -341,6 +352,68 @@ int32_t orc_encode(const orc_tensor* T, uint32_t nT,
     rc = ORC_OK;
 done:
     free(idx[0]); free(idx[1]); free(word[0]); free(word[1]);
+    return rc;
+}
+
+int32_t orc_encode(const orc_tensor* T, uint32_t nT,
+                   const void* const* old_shards, const void* const* new_shards,
+                   const uint64_t* shard_bytes, uint32_t nS,
+                   const orc_segment* segs, uint64_t nseg,
+                   uint32_t mode, uint64_t base_version, uint64_t new_version,
+                   uint8_t* header_out,
+                   uint8_t* dir_out, uint64_t dir_cap, uint64_t* dir_bytes,
+                   uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes) {
+    return encode_chunks(T, nT, old_shards, new_shards, shard_bytes, nS, segs, nseg, mode, base_version,
+                         new_version, header_out, dir_out, dir_cap, dir_bytes, payload_out, payload_cap,
+                         payload_bytes, NULL);
+}
+
+/* Partial retry: a RETRY stream over the chunks that hold at least one record
+ * of the DELTA stream whose applied flag is 0 (the receiver's flags read back
+ * after a failure).  The DELTA header must be a DELTA stream of this tensor
+ * table (magic, format, chunk size, fingerprint); each directory entry must
+ * name an existing chunk (ORC_E_FORMAT otherwise). */
+int32_t orc_encode_retry_partial(const orc_tensor* T, uint32_t nT,
+                                 const void* const* old_shards, const void* const* new_shards,
+                                 const uint64_t* shard_bytes, uint32_t nS,
+                                 const orc_segment* segs, uint64_t nseg,
+                                 const uint8_t* delta_header, const uint8_t* delta_dir,
+                                 const uint8_t* delta_flags,
+                                 uint64_t base_version, uint64_t new_version,
+                                 uint8_t* header_out,
+                                 uint8_t* dir_out, uint64_t dir_cap, uint64_t* dir_bytes,
+                                 uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes) {
+    uint64_t total = 0, n, r;
+    uint64_t* first = NULL;
+    uint8_t* need = NULL;
+    uint32_t t;
+    int32_t rc = check_tensors(T, nT);
+    if (rc) return rc;
+    if (get_u32(delta_header + 0) != ORC_MAGIC || get_u16(delta_header + 4) != ORC_FORMAT_VER ||
+        get_u16(delta_header + 6) != ORC_MODE_DELTA || get_u32(delta_header + 8) != ORC_CHUNK_BYTES ||
+        get_u64(delta_header + 32) != orc_fingerprint(T, nT))
+        return ORC_E_FORMAT;
+    n = get_u64(delta_header + 40);
+    first = (uint64_t*)malloc((nT + 1) * sizeof(uint64_t));
+    if (!first) return ORC_E_NOMEM;
+    for (t = 0; t < nT; t++) {
+        first[t] = total;
+        total += n_chunks(&T[t]);
+    }
+    need = (uint8_t*)calloc(total + 1, 1);
+    if (!need) { free(first); return ORC_E_NOMEM; }
+    for (r = 0; r < n; r++) {
+        const uint8_t* e = delta_dir + r * ORC_DIRENT_BYTES;
+        uint32_t et = get_u32(e + 0), ec = get_u32(e + 4);
+        if (et >= nT || ec >= n_chunks(&T[et])) { rc = ORC_E_FORMAT; goto out; }
+        if (!delta_flags[r]) need[first[et] + ec] = 1;
+    }
+    rc = encode_chunks(T, nT, old_shards, new_shards, shard_bytes, nS, segs, nseg, ORC_MODE_RETRY,
+                       base_version, new_version, header_out, dir_out, dir_cap, dir_bytes, payload_out,
+                       payload_cap, payload_bytes, need);
+out:
+    free(first);
+    free(need);
     return rc;
 }
 

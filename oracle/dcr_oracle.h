@@ -104,6 +104,25 @@ int32_t orc_encode(const orc_tensor* T, uint32_t nT,
                    uint8_t* dir_out, uint64_t dir_cap, uint64_t* dir_bytes,
                    uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes);
 
+/* Partial retry (ai-feeds summary, "key modules" 4: after a failure only the
+ * partitions that did not finish are sent again): a RETRY stream, as
+ * orc_encode with ORC_MODE_RETRY would write it, restricted to the chunks that
+ * hold at least one record of the DELTA stream (delta_header, delta_dir)
+ * whose applied flag (delta_flags, one byte per record) is 0.  A chunk the
+ * receiver finished is left out; one it did not finish, or tore, is sent
+ * whole.  ORC_E_FORMAT if the header is not a DELTA stream of this tensor
+ * table or an entry names no chunk of it. */
+int32_t orc_encode_retry_partial(const orc_tensor* T, uint32_t nT,
+                                 const void* const* old_shards, const void* const* new_shards,
+                                 const uint64_t* shard_bytes, uint32_t nS,
+                                 const orc_segment* segs, uint64_t nseg,
+                                 const uint8_t* delta_header, const uint8_t* delta_dir,
+                                 const uint8_t* delta_flags,
+                                 uint64_t base_version, uint64_t new_version,
+                                 uint8_t* header_out,
+                                 uint8_t* dir_out, uint64_t dir_cap, uint64_t* dir_bytes,
+                                 uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes);
+
 /* Materialise canonical tensor t from shards (the direct projection alone). */
 int32_t orc_gather(const orc_tensor* T, uint32_t nT,
                    const void* const* shards, const uint64_t* shard_bytes, uint32_t nS,

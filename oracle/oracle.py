@@ -82,6 +82,9 @@ class Oracle:
         lib.orc_encode.restype = I32
         lib.orc_encode.argtypes = [P, U32, P, P, P, U32, P, U64, U32, U64, U64,
                                    P, P, U64, U64P, P, U64, U64P]
+        lib.orc_encode_retry_partial.restype = I32
+        lib.orc_encode_retry_partial.argtypes = [P, U32, P, P, P, U32, P, U64, P, P, P, U64, U64,
+                                                 P, P, U64, U64P, P, U64, U64P]
         lib.orc_gather.restype = I32
         lib.orc_gather.argtypes = [P, U32, P, P, U32, P, U64, U32, P]
         lib.orc_validate.restype = I32
@@ -139,6 +142,39 @@ class Oracle:
                                      base_version, new_version, hdr.ctypes.data,
                                      d.ctypes.data, dcap, ctypes.byref(dbytes),
                                      p.ctypes.data, pcap, ctypes.byref(pbytes))
+            if rc == E_CAPACITY and dir_cap is None and payload_cap is None:
+                dcap, pcap = int(dbytes.value), int(pbytes.value)
+                continue
+            break
+        if rc:
+            return rc, hdr, d[:0], p[:0]
+        return rc, hdr, d[: dbytes.value].copy(), p[: pbytes.value].copy()
+
+    def encode_retry_partial(self, tensors, segments, old_shards, new_shards, delta_hdr, delta_dir,
+                             delta_flags, base_version=0, new_version=1, dir_cap=None, payload_cap=None):
+        """RETRY stream over the chunks with an unflagged DELTA record.
+        Return (rc, header bytes, directory bytes, payload bytes)."""
+        T = _pack(tensors, ORC_TENSOR)
+        S = _pack(segments, ORC_SEGMENT)
+        olds = [np.ascontiguousarray(s).view(np.uint8).reshape(-1) for s in old_shards]
+        news = [np.ascontiguousarray(s).view(np.uint8).reshape(-1) for s in new_shards]
+        sb = np.array([s.nbytes for s in olds], dtype=np.uint64)
+        dh = np.ascontiguousarray(delta_hdr, dtype=np.uint8)
+        dd = _nz(np.ascontiguousarray(delta_dir, dtype=np.uint8))
+        df = _nz(np.ascontiguousarray(delta_flags, dtype=np.uint8))
+        hdr = np.zeros(HEADER_BYTES, dtype=np.uint8)
+        dbytes, pbytes = ctypes.c_uint64(0), ctypes.c_uint64(0)
+        dcap = 1 << 16 if dir_cap is None else dir_cap
+        pcap = 1 << 20 if payload_cap is None else payload_cap
+        while True:
+            d = np.zeros(max(dcap, 1), dtype=np.uint8)
+            p = np.zeros(max(pcap, 1), dtype=np.uint8)
+            rc = self.lib.orc_encode_retry_partial(T.ctypes.data, len(T), self._ptrs(olds), self._ptrs(news),
+                                                   sb.ctypes.data, len(olds), S.ctypes.data, len(S),
+                                                   dh.ctypes.data, dd.ctypes.data, df.ctypes.data,
+                                                   base_version, new_version, hdr.ctypes.data,
+                                                   d.ctypes.data, dcap, ctypes.byref(dbytes),
+                                                   p.ctypes.data, pcap, ctypes.byref(pbytes))
             if rc == E_CAPACITY and dir_cap is None and payload_cap is None:
                 dcap, pcap = int(dbytes.value), int(pbytes.value)
                 continue

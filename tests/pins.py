@@ -23,6 +23,7 @@ import os
 import numpy as np
 
 from bit_exact_xor_amd import synth
+from oracle.oracle import E_FORMAT as O_E_FORMAT
 from tests import fmt
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -168,6 +169,61 @@ def pin_retry_idempotent(orc, seeds=range(4)):
             for t in range(lay.n_tensors):
                 assert np.array_equal(W[t], cn[t])
                 assert np.array_equal(W[t], once[t])
+
+
+def pin_retry_partial(orc, seeds=range(3)):
+    """Partial retry (only chunks with an unflagged DELTA record are sent
+    again): all flags clear gives the full RETRY stream byte for byte, all
+    set gives an empty one; after a kill at record k (optionally with record k
+    torn) the stream holds exactly the chunks of records k.. (read from the
+    DELTA directory), each with the full RETRY stream's record, and applying
+    it heals the receiver to new."""
+    for seed in seeds:
+        lay = synth.random_layout(900 + seed)
+        olds, news, co, cn = canon_lists(lay)
+        hdr, d, p = encode_ok(orc, lay, olds, news)
+        rh, rd, rp = encode_ok(orc, lay, olds, news, mode=1)
+        n = len(d) // 32
+        ents = fmt.dirents(d)
+        full = {(e["t"], e["c"]): rp[e["off"]:e["off"] + e["size"]] for e in fmt.dirents(rd)}
+
+        def partial(flags):
+            rc, h2, d2, p2 = orc.encode_retry_partial(lay.tensors, lay.segments, olds, news, hdr, d, flags,
+                                                       base_version=7, new_version=8)
+            assert rc == 0
+            return h2, d2, p2
+
+        h0, d0, p0 = partial(np.zeros(max(n, 1), np.uint8))
+        assert np.array_equal(h0, rh) and np.array_equal(d0, rd) and np.array_equal(p0, rp)
+        h1, d1, p1 = partial(np.ones(max(n, 1), np.uint8))
+        assert len(d1) == 0 and len(p1) == 0 and int(h1[40:48].view("<u8")[0]) == 0
+        for k in sorted({0, n // 3, n // 2, max(n - 1, 0)}):
+            for torn in (False, True):
+                if torn and k >= n:
+                    continue
+                W = [x.copy() for x in co]
+                f = np.zeros(max(n, 1), np.uint8)
+                orc.apply(lay.tensors, W, hdr, d, p, f, 0, k, expected_base_version=7)
+                if torn:
+                    orc.apply_record_part(lay.tensors, W, d, p, k, 0, max(ents[k]["K"] // 2, 1))
+                hp, dp, pp = partial(f)
+                got = fmt.dirents(dp)
+                want = sorted({(e["t"], e["c"]) for r, e in enumerate(ents) if r >= k})
+                assert [(e["t"], e["c"]) for e in got] == want, (seed, k)
+                for e in got:
+                    assert np.array_equal(pp[e["off"]:e["off"] + e["size"]], full[(e["t"], e["c"])])
+                assert len(pp) <= len(rp)
+                assert orc.retry(lay.tensors, W, hp, dp, pp, expected_base_version=7) == 0
+                for t in range(lay.n_tensors):
+                    assert np.array_equal(W[t], cn[t]), (seed, k, torn, t)
+        # a RETRY header, or an entry naming no chunk, is refused
+        rc, *_ = orc.encode_retry_partial(lay.tensors, lay.segments, olds, news, rh, d, np.zeros(max(n, 1), np.uint8))
+        assert rc == O_E_FORMAT
+        if n:
+            bad = d.copy()
+            bad[0:4] = np.frombuffer(np.uint32(lay.n_tensors).tobytes(), np.uint8)
+            rc, *_ = orc.encode_retry_partial(lay.tensors, lay.segments, olds, news, hdr, bad, np.zeros(n, np.uint8))
+            assert rc == O_E_FORMAT
 
 
 def pin_signed_zero(orc):

@@ -2,7 +2,8 @@
 
 Each mutant is a plausible slip (wrong bit order, float-style comparison,
 wrong word, tie-break, byte plane, transposed strides, chunk size, missing
-dedup, inverted routing, missing padding); the copy is compiled in a temp
+dedup, inverted routing, missing padding, partial retry ignoring the flags or
+marking the wrong chunk); the copy is compiled in a temp
 directory and loaded beside the real oracle.  Nothing here touches a GPU.
 """
 import os
@@ -40,6 +41,10 @@ MUTANTS = {
                                  "(void)0;"),
     "shard_offset_dropped": ("int64_t c = (int64_t)g->canon_off, e = (int64_t)g->shard_off;",
                              "int64_t c = (int64_t)g->canon_off, e = 0;"),
+    "partial_retry_ignores_flags": ("if (!delta_flags[r]) need[first[et] + ec] = 1;",
+                                    "need[first[et] + ec] = 1;"),
+    "partial_retry_wrong_chunk": ("if (!delta_flags[r]) need[first[et] + ec] = 1;",
+                                  "if (!delta_flags[r]) need[first[et]] = 1;"),
 }
 
 
