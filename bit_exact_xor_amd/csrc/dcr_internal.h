@@ -36,6 +36,8 @@ constexpr uint32_t kCtrTile = 0, kCtrFix = 1, kCtrChanged = 2, kCtrTotal = 4;
 // apply counters (uint32 words at ws_counter): [8] records deferred to the
 // large-record kernel
 constexpr uint32_t kCtrBig = 8;
+// partial retry: [10] nonzero if a DELTA directory entry named no chunk
+constexpr uint32_t kCtrBad = 10;
 constexpr uint32_t kSmallThreads = 256;             // workgroup of the small-record apply
 constexpr uint32_t kSmallStage = 16384;             // its LDS stage (records up to this size)
 
@@ -95,7 +97,7 @@ struct Plan {
     uint64_t off_tensors = 0, off_chunks = 0, off_pieces = 0, off_scale_chunks = 0, off_slots = 0, off_slow = 0,
              off_direct[3] = {0, 0, 0}, table_bytes = 0;
     // workspace layout
-    uint64_t ws_status = 0, ws_fix = 0, ws_counter = 0, ws_old = 0, ws_new = 0, ws_scale = 0, ws_canon = 0,
+    uint64_t ws_status = 0, ws_fix = 0, ws_need = 0, ws_counter = 0, ws_old = 0, ws_new = 0, ws_scale = 0, ws_canon = 0,
              ws_agg = 0, ws_info = 0, ws_big = 0, big_cap = 0, ws_bytes = 0;
     std::vector<uint8_t> blob;            // host image of the device tables
     void* dev_tables = nullptr;           // bound by dcr_plan_upload

@@ -164,6 +164,7 @@ struct EncodeArgs {
     uint8_t* payload;
     uint64_t dir_cap;       // bytes
     uint64_t payload_cap;   // bytes
+    const uint64_t* need;   // partial retry: one bit per tile, set = encode it (NULL: every tile)
     uint32_t n_tiles;
     uint32_t mode;
 };
@@ -720,6 +721,22 @@ __device__ __forceinline__ uint64_t tile_counts(const TileSums& t) {
     return uint64_t(t.Kx) | (uint64_t(t.Ko) << 17) | (uint64_t(t.Hx) << 34);
 }
 
+// Partial retry: whether the tile is to be encoded (every tile without a
+// wanted-chunk mask).  Uniform.
+__device__ __forceinline__ bool tile_wanted(const EncodeArgs& a, uint32_t tile) {
+    return !a.need || ((uniform_load(a.need + (tile >> 6)) >> (tile & 63u)) & 1u) != 0;
+}
+
+// A tile left out of a partial retry: no records, no changes (and, in order,
+// an empty aggregate for the look-back).
+__device__ __forceinline__ void skip_tile(const EncodeArgs& a, uint32_t tile, bool publish) {
+    if (threadIdx.x == 0) {
+        if (publish) st_status(a.status + tile, tile == 0 ? kFlagIncl : kFlagAgg);
+        a.tile_agg[tile] = 0;
+        a.tile_info[tile] = 0;
+    }
+}
+
 // In-order encode of one tile of W-byte elements (no staging area): publish
 // the aggregate, look back for the exclusive prefix, write the records and
 // directory entries in place.
@@ -769,6 +786,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     __syncthreads();
     const uint32_t tile = sgpr(S.next);
     if (tile >= a.n_tiles) return;
+    if (!tile_wanted(a, tile)) {
+        skip_tile(a, tile, true);
+        return;
+    }
     const TileCtx c = tile_ctx(a, tile);
     if (c.w == 2) inorder_tile<2>(a, S, c);
     else if (c.w == 1) inorder_tile<1>(a, S, c);
@@ -804,7 +825,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     EncodeArgs a, const uint32_t* tiles, uint32_t n) {
     __shared__ EncodeShared S;
     if (blockIdx.x >= n) return;
-    const TileCtx c = tile_ctx(a, tiles[blockIdx.x]);
+    const uint32_t tile = tiles[blockIdx.x];
+    if (!tile_wanted(a, tile)) {
+        skip_tile(a, tile, false);
+        return;
+    }
+    const TileCtx c = tile_ctx(a, tile);
     if (c.w == 2) staged_tile<2>(a, S, c);
     else if (c.w == 1) staged_tile<1>(a, S, c);
     else staged_tile<4>(a, S, c);
@@ -858,6 +884,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     __shared__ EncodeShared S;
     if (blockIdx.x >= n_list) return;
     const uint32_t tid = threadIdx.x;
+    if (!tile_wanted(a, list[blockIdx.x])) {
+        skip_tile(a, list[blockIdx.x], false);
+        return;
+    }
     const TileCtx c = tile_ctx(a, list[blockIdx.x]);
     // the slot's address is uniform: read it before this workgroup stores
     // anything, into scalar registers
@@ -1017,11 +1047,31 @@ __global__ __launch_bounds__(256) void scale_flags_kernel(const DevTensor* tenso
 }
 
 // Stream header and encode result from the totals the fix-up stored.
+// Partial retry: from a DELTA stream's directory and the receiver's applied
+// flags, set the wanted bit of every chunk holding a record whose flag is 0.
+// An entry that names no chunk of the plan sets the bad-directory counter.
+__global__ __launch_bounds__(256) void retry_need_kernel(const uint8_t* dir, const uint8_t* flags, uint64_t n,
+                                                         const DevTensor* tensors, uint32_t n_tensors,
+                                                         uint64_t* need, uint32_t* counter) {
+    for (uint64_t r = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; r < n;
+         r += uint64_t(gridDim.x) * blockDim.x) {
+        const uint2 tc = *reinterpret_cast<const uint2*>(dir + r * DCR_DIRENT_BYTES);
+        if (tc.x >= n_tensors || tc.y >= tensors[tc.x].n_chunks) {
+            atomicOr(counter + kCtrBad, 1u);
+            continue;
+        }
+        if (flags[r]) continue;
+        const uint32_t chunk = tensors[tc.x].first_chunk + tc.y;
+        atomicOr(reinterpret_cast<unsigned long long*>(need + (chunk >> 6)), 1ull << (chunk & 63u));
+    }
+}
+
 __global__ void encode_finalize_kernel(const uint32_t* counter, uint32_t mode, uint64_t base_v, uint64_t new_v,
                                        uint64_t fp, uint64_t dir_cap, uint64_t payload_cap, uint8_t* header,
                                        dcr_encode_result* res) {
     if (threadIdx.x != 0) return;
-    const uint64_t v = *reinterpret_cast<const uint64_t*>(counter + kCtrTotal);
+    const bool bad = counter[kCtrBad] != 0;   // partial retry given a directory naming no chunk
+    const uint64_t v = bad ? 0 : *reinterpret_cast<const uint64_t*>(counter + kCtrTotal);
     const uint64_t nrec = v >> kRecShift, pbytes = (v & kP16Mask) << 4;
     const bool fits = nrec * DCR_DIRENT_BYTES <= dir_cap && pbytes <= payload_cap;
     uint4* h = reinterpret_cast<uint4*>(header);
@@ -1032,7 +1082,8 @@ __global__ void encode_finalize_kernel(const uint32_t* counter, uint32_t mode, u
     const uint64_t changed = *reinterpret_cast<const uint64_t*>(counter + kCtrChanged);
     uint4* r = reinterpret_cast<uint4*>(res);
     r[0] = make_uint4(uint32_t(nrec), uint32_t(nrec >> 32), uint32_t(pbytes), uint32_t(pbytes >> 32));
-    r[1] = make_uint4(uint32_t(changed), uint32_t(changed >> 32), uint32_t(fits ? DCR_OK : DCR_E_CAPACITY), 0u);
+    const int32_t st = bad ? DCR_E_FORMAT : (fits ? DCR_OK : DCR_E_CAPACITY);
+    r[1] = make_uint4(uint32_t(changed), uint32_t(changed >> 32), uint32_t(st), 0u);
 }
 
 __global__ void fill_u64_kernel(uint64_t* p, uint64_t n, uint64_t v) {
@@ -1688,12 +1739,18 @@ int32_t dcr_plan_upload(dcr_plan* plan, void* dev_tables, uint64_t bytes, void* 
     return DCR_OK;
 }
 
-int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards, uint32_t mode,
-                   uint64_t base_version, uint64_t new_version, void* header_dev, void* dir_dev, uint64_t dir_cap,
-                   void* payload_dev, uint64_t payload_cap, dcr_encode_result* result_dev, void* workspace_dev,
-                   uint64_t ws_bytes, void* stream) {
-    using namespace dcr;
-    set_error("");
+}  // extern "C"
+
+namespace dcr {
+
+// The encode.  delta_dir / delta_flags / n_delta: a partial retry (mode
+// RETRY restricted to the chunks with an unflagged record of that DELTA
+// directory); n_delta == UINT64_MAX for a whole encode.
+static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards,
+                           uint32_t mode, uint64_t base_version, uint64_t new_version, void* header_dev,
+                           void* dir_dev, uint64_t dir_cap, void* payload_dev, uint64_t payload_cap,
+                           dcr_encode_result* result_dev, void* workspace_dev, uint64_t ws_bytes, void* stream,
+                           const uint8_t* delta_dir, const uint8_t* delta_flags, uint64_t n_delta) {
     if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
     const Plan& p = *plan;
     if (!p.dev_tables) return fail(DCR_E_INVAL, "plan not uploaded");
@@ -1721,6 +1778,12 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
     const uint64_t n_zero = (p.ws_old) / 8;
     hipLaunchKernelGGL(fill_u64_kernel, dim3(uint32_t(std::min<uint64_t>((n_zero + 255) / 256, 4096))), dim3(256), 0,
                        s, reinterpret_cast<uint64_t*>(ws), n_zero, 0ull);
+    const bool partial = n_delta != UINT64_MAX;
+    uint64_t* need = reinterpret_cast<uint64_t*>(ws + p.ws_need);
+    if (partial && n_delta)
+        hipLaunchKernelGGL(retry_need_kernel, dim3(uint32_t(std::min<uint64_t>((n_delta + 255) / 256, 4096))),
+                           dim3(256), 0, s, delta_dir, delta_flags, n_delta, tab<DevTensor>(p, p.off_tensors),
+                           uint32_t(p.tensors.size()), need, reinterpret_cast<uint32_t*>(ws + p.ws_counter));
     const auto* tensors = tab<DevTensor>(p, p.off_tensors);
     const auto* chunks = tab<DevChunk>(p, p.off_chunks);
     const auto* pieces = tab<DevPiece>(p, p.off_pieces);
@@ -1753,6 +1816,7 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
         a.payload = static_cast<uint8_t*>(payload_dev);
         a.dir_cap = dir_cap;
         a.payload_cap = payload_cap;
+        a.need = partial ? need : nullptr;
         a.n_tiles = n_tiles;
         a.mode = mode;
         mark(true, s);
@@ -1795,6 +1859,43 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
     hipLaunchKernelGGL(encode_finalize_kernel, dim3(1), dim3(64), 0, s, counter, mode, base_version, new_version,
                        p.fingerprint, dir_cap, payload_cap, static_cast<uint8_t*>(header_dev), result_dev);
     return hip_check(hipGetLastError(), "encode launch");
+}
+
+}  // namespace dcr
+
+extern "C" {
+
+int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards, uint32_t mode,
+                   uint64_t base_version, uint64_t new_version, void* header_dev, void* dir_dev, uint64_t dir_cap,
+                   void* payload_dev, uint64_t payload_cap, dcr_encode_result* result_dev, void* workspace_dev,
+                   uint64_t ws_bytes, void* stream) {
+    using namespace dcr;
+    set_error("");
+    return encode_impl(plan, old_shards, new_shards, mode, base_version, new_version, header_dev, dir_dev, dir_cap,
+                       payload_dev, payload_cap, result_dev, workspace_dev, ws_bytes, stream, nullptr, nullptr,
+                       UINT64_MAX);
+}
+
+int32_t dcr_encode_retry_partial(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards,
+                                 const dcr_stream_header* delta_header, const void* delta_dir_dev,
+                                 uint64_t delta_dir_bytes, const uint8_t* delta_flags_dev, uint64_t base_version,
+                                 uint64_t new_version, void* header_dev, void* dir_dev, uint64_t dir_cap,
+                                 void* payload_dev, uint64_t payload_cap, dcr_encode_result* result_dev,
+                                 void* workspace_dev, uint64_t ws_bytes, void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
+    if (!delta_header) return fail(DCR_E_INVAL, "delta header is NULL");
+    int32_t rc = check_header(*plan, delta_header, delta_header->base_version);
+    if (rc) return rc;
+    if (delta_header->stream_kind != DCR_MODE_DELTA) return fail(DCR_E_FORMAT, "not a DELTA stream");
+    const uint64_t n = delta_header->n_records;
+    if (n > delta_dir_bytes / DCR_DIRENT_BYTES) return fail(DCR_E_INVAL, "delta directory smaller than n_records");
+    if (n && (!delta_dir_dev || !delta_flags_dev)) return fail(DCR_E_INVAL, "NULL delta directory or flags");
+    if (!al16(delta_dir_dev)) return fail(DCR_E_INVAL, "delta directory not 16-byte aligned");
+    return encode_impl(plan, old_shards, new_shards, DCR_MODE_RETRY, base_version, new_version, header_dev, dir_dev,
+                       dir_cap, payload_dev, payload_cap, result_dev, workspace_dev, ws_bytes, stream,
+                       static_cast<const uint8_t*>(delta_dir_dev), delta_flags_dev, n);
 }
 
 int32_t dcr_apply(const dcr_plan* plan, void* const* canon, const dcr_stream_header* header, const void* dir_dev,

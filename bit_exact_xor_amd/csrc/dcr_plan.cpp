@@ -291,16 +291,18 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
         if (!P.direct[i].empty())
             std::memcpy(P.blob.data() + P.off_direct[i], P.direct[i].data(), P.direct[i].size() * sizeof(uint32_t));
 
-    // workspace: tile look-back status | fix-up look-back status | counters |
-    // shard pointers | scale flags | canonical pointers | per-tile aggregates |
-    // per-tile change counts | apply's list of deferred large records.
-    // Everything before the shard pointers is zeroed at the start of an
-    // encode.  Bytes past ws_bytes are the optional
-    // staging area of encode (used when it holds every chunk's slot).
+    // workspace: tile look-back status | fix-up look-back status | partial
+    // retry's wanted-chunk bits | counters | shard pointers | scale flags |
+    // canonical pointers | per-tile aggregates | per-tile change counts |
+    // apply's list of deferred large records.  Everything before the shard
+    // pointers is zeroed at the start of an encode.  Bytes past ws_bytes are
+    // the optional staging area of encode (used when it holds every chunk's
+    // slot).
     const uint64_t n_tiles = P.chunks.size();
     P.ws_status = 0;
     P.ws_fix = pad256(n_tiles * 8);
-    P.ws_counter = pad256(P.ws_fix + (n_tiles + kFixTiles - 1) / kFixTiles * 8);
+    P.ws_need = pad256(P.ws_fix + (n_tiles + kFixTiles - 1) / kFixTiles * 8);
+    P.ws_counter = pad256(P.ws_need + (n_tiles + 63) / 64 * 8);
     P.ws_old = P.ws_counter + 256;
     P.ws_new = pad256(P.ws_old + uint64_t(nS) * 8);
     P.ws_scale = pad256(P.ws_new + uint64_t(nS) * 8);

@@ -5,8 +5,9 @@ this module packs descriptors into the C structs, turns torch tensors into
 device pointers and the current torch stream into a hipStream_t, and raises
 ``DcrError`` on a nonzero status.  PyTorch provides device memory and streams.
 
-The names follow the C-ABI: ``dcr_plan_build``, ``dcr_encode``, ``dcr_apply``,
-``dcr_apply_overwrite_retry`` (plus the small helpers around them).
+The names follow the C-ABI: ``dcr_plan_build``, ``dcr_encode``,
+``dcr_encode_retry_partial``, ``dcr_apply``, ``dcr_apply_overwrite_retry``
+(plus the small helpers around them).
 """
 from __future__ import annotations
 
@@ -76,6 +77,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dcr_plan_destroy.argtypes = [P]
     lib.dcr_encode.restype = I32
     lib.dcr_encode.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P, U64, P]
+    lib.dcr_encode_retry_partial.restype = I32
+    lib.dcr_encode_retry_partial.argtypes = [P, P, P, P, P, U64, P, U64, U64, P, P, U64, P, U64, P, P, U64, P]
     lib.dcr_apply.restype = I32
     lib.dcr_apply.argtypes = [P, P, P, P, P, P, U64, U64, U64, P, P, U64, P]
     lib.dcr_apply_overwrite_retry.restype = I32
@@ -168,6 +171,21 @@ def dcr_encode(plan: Plan, old_shards, new_shards, mode, base_version, new_versi
         mode, base_version, new_version, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload),
         _nbytes(payload), _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_encode")
+
+
+def dcr_encode_retry_partial(plan: Plan, old_shards, new_shards, delta_header: np.ndarray, delta_dir, delta_flags,
+                             base_version, new_version, header, dir_buf, payload, result, workspace,
+                             stream=None) -> None:
+    """Enqueue a partial retry encode: a RETRY stream over the chunks that hold
+    a record of the DELTA stream (host header bytes, device directory) whose
+    applied flag (device bytes) is 0."""
+    hdr = np.ascontiguousarray(np.asarray(delta_header, dtype=np.uint8))
+    rc = load_library().dcr_encode_retry_partial(
+        plan.handle, _ptr_array([_dptr(t) for t in old_shards]), _ptr_array([_dptr(t) for t in new_shards]),
+        hdr.ctypes.data, _dptr(delta_dir), _nbytes(delta_dir), _dptr(delta_flags), base_version, new_version,
+        _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload), _nbytes(payload), _dptr(result),
+        _dptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(rc, "dcr_encode_retry_partial")
 
 
 def dcr_apply(plan: Plan, canon, header: np.ndarray, dir_buf, payload, flags, first_record, n_records,

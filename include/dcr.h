@@ -145,7 +145,9 @@ typedef struct {
     uint64_t payload_bytes;     /* payload bytes of the stream (also when it did not fit) */
     uint64_t n_changed;         /* elements whose stored bits differ */
     int32_t status;             /* DCR_OK, or DCR_E_CAPACITY if dir_cap / payload_cap
-                                   was too small: grow the buffers and encode again */
+                                   was too small: grow the buffers and encode again;
+                                   DCR_E_FORMAT from dcr_encode_retry_partial if the
+                                   DELTA directory names a chunk the plan lacks */
     uint32_t reserved;
 } dcr_encode_result;
 
@@ -213,6 +215,36 @@ int32_t dcr_encode(const dcr_plan* plan,
                    void* payload_dev, uint64_t payload_cap,
                    dcr_encode_result* result_dev,
                    void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* Partial retry (sender side).  After a failure the receiver reads back the
+ * applied flags of a DELTA stream; this call writes a RETRY stream (as
+ * dcr_encode with DCR_MODE_RETRY would) restricted to the chunks that hold at
+ * least one record of that stream whose flag is 0, so only the partitions
+ * that did not finish are sent again (ai-feeds summary, "key modules" 4).
+ * A chunk whose records were all applied is left out; one that was not
+ * reached, or was torn by the failure, is sent whole.  The flags must be the
+ * ones the receiver's dcr_apply set (a flag is set only after all writes of
+ * its record); dcr_apply_overwrite_retry applies the result.
+ *   delta_header     the DELTA stream's header, in HOST memory (magic,
+ *                    format, chunk size and plan fingerprint are checked:
+ *                    DCR_E_FORMAT; stream_kind must be DCR_MODE_DELTA)
+ *   delta_dir_dev, delta_dir_bytes  its directory in device memory and the
+ *                    buffer's size (at least n_records * 32: DCR_E_INVAL)
+ *   delta_flags_dev  one byte per record of that stream, device memory
+ *   the remaining arguments as for dcr_encode (the workspace needs no more).
+ * Only the listed chunks are read from the shards.  A directory entry that
+ * names no chunk of the plan makes result->status DCR_E_FORMAT (no usable
+ * stream). */
+int32_t dcr_encode_retry_partial(const dcr_plan* plan,
+                                 const void* const* old_shards, const void* const* new_shards,
+                                 const dcr_stream_header* delta_header,
+                                 const void* delta_dir_dev, uint64_t delta_dir_bytes,
+                                 const uint8_t* delta_flags_dev,
+                                 uint64_t base_version, uint64_t new_version,
+                                 void* header_dev, void* dir_dev, uint64_t dir_cap,
+                                 void* payload_dev, uint64_t payload_cap,
+                                 dcr_encode_result* result_dev,
+                                 void* workspace_dev, uint64_t ws_bytes, void* stream);
 
 /* Apply records [first_record, first_record + n_records) of a stream in place
  * (receiver side).

@@ -43,6 +43,15 @@ class Gpu:
         torch.cuda.synchronize()
         return sb
 
+    def encode_retry_partial(self, delta_hdr, delta_sb, flags, base=7, new=8, stage=0):
+        """Partial retry encode from a DELTA stream and its applied flags."""
+        sb = dcr.StreamBuffers(self.plan, self.device)
+        ws = self.ws if not stage else dcr.workspace(self.plan, self.device, stage)
+        dcr.dcr_encode_retry_partial(self.plan, self.olds, self.news, delta_hdr, delta_sb.dir, flags, base, new,
+                                     sb.header, sb.dir, sb.payload, sb.result, ws)
+        torch.cuda.synchronize()
+        return sb
+
     def stream_host(self, sb):
         """(header, directory, payload) bytes as numpy, trimmed to the stream."""
         r = sb.result_host()

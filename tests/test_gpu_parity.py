@@ -212,6 +212,62 @@ def test_dense_records_repeated(gh, orc, seed, rate):
         assert_same_stream(g.stream_host(g.encode(0, stage=stage)), exp, f"dense seed {seed} run {i} stage {stage}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_retry_partial(gh, orc, seed):
+    """Partial retry after a kill at 0 %, 50 % and 100 % of the records: the
+    stream equals the oracle's byte for byte (staged, in order and with a
+    too-small staging area) and applying it heals the receiver to new."""
+    say("partial retry", seed)
+    lay = synth.random_layout(1000 + seed, max_tensors=6, max_chunks=8.0)
+    olds, news, co, cn = pins.canon_lists(lay)
+    g = gh.Gpu(lay, olds, news)
+    sb = g.encode(0)
+    hdr, d, _p = g.stream_host(sb)
+    n = len(d) // 32
+    for k in sorted({0, n // 2, n}):
+        buf, canon = g.canon_alloc(co)
+        flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+        if k:
+            g.apply(canon, hdr, sb, flags, 0, k)
+        fh = flags.cpu().numpy()
+        rc, eh, ed, ep = orc.encode_retry_partial(lay.tensors, lay.segments, olds, news, hdr, d, fh,
+                                                   base_version=7, new_version=8)
+        assert rc == 0
+        for stage in stage_sizes(g):
+            psb = g.encode_retry_partial(hdr, sb, flags, stage=stage)
+            assert_same_stream(g.stream_host(psb), (eh, ed, ep), f"partial seed {seed} kill {k} stage {stage}")
+        ph = g.stream_host(psb)[0]
+        r = g.retry(canon, ph, psb)
+        assert int(r["n_invalid"]) == 0
+        got = gh.host(canon)
+        for t in range(lay.n_tensors):
+            assert np.array_equal(got[t], cn[t]), (seed, k, t)
+
+
+def test_retry_partial_refused(gh):
+    """Partial retry refuses a RETRY header (host check), a short directory
+    buffer, and (on the device) an entry naming a tensor the plan lacks."""
+    say("partial retry refused")
+    lay = synth.random_layout(1001, max_tensors=6, max_chunks=8.0)
+    g = gh.Gpu(lay)
+    sb = g.encode(0)
+    hdr, d, _p = g.stream_host(sb)
+    n = len(d) // 32
+    flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+    rsb = g.encode(1)
+    with pytest.raises(dcr.DcrError):
+        g.encode_retry_partial(rsb.header.cpu().numpy(), sb, flags)
+    assert n > 1
+    short = type("S", (), {"dir": sb.dir[: 32 * (n - 1)]})()
+    with pytest.raises(dcr.DcrError):
+        g.encode_retry_partial(hdr, short, flags)
+    bad = sb.dir.clone()
+    bad[0:4] = torch.tensor(list(np.uint32(lay.n_tensors).tobytes()), dtype=torch.uint8, device="cuda")
+    bsb = type("S", (), {"dir": bad})()
+    psb = g.encode_retry_partial(hdr, bsb, flags)
+    assert int(psb.result_host()["status"]) == dcr.DCR_E_FORMAT
+
+
 def test_capacity_overflow(gh, orc):
     """Too-small buffers: status DCR_E_CAPACITY with the required sizes."""
     say("capacity overflow")
