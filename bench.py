@@ -224,6 +224,45 @@ def main():
     ok_after = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
     del canon_new
 
+    # partial retry after a kill at 50 % of the DELTA records (outside the
+    # step): the receiver is set back to old, applies the first half, and the
+    # sender re-encodes only the chunks of the unflagged records
+    canon_o = lay.assemble(as_i16(olds))
+    for t in range(len(T)):
+        canon[t].view(torch.int16).copy_(canon_o[t].reshape(-1))
+    del canon_o
+    flags.zero_()
+    dcr.dcr_apply(plan, canon, hdr, delta.dir, delta.payload, flags, 0, n_rec // 2, 41, ares, ws)
+    torch.cuda.synchronize()
+    pe, pa = [], []
+    for _ in range(3):
+        a_, b_ = pair()
+        a_.record()
+        dcr.dcr_encode_retry_partial(plan, olds, news, hdr, delta.dir, flags, 41, 42, retry.header, retry.dir,
+                                     retry.payload, retry.result, ws)
+        b_.record()
+        torch.cuda.synchronize()
+        pe.append(a_.elapsed_time(b_))
+    pr = retry.result_host()
+    ph = retry.header_host()
+    for _ in range(3):
+        a_, b_ = pair()
+        a_.record()
+        dcr.dcr_apply_overwrite_retry(plan, canon, ph, retry.dir, retry.payload, 41, ares, ws)
+        b_.record()
+        torch.cuda.synchronize()
+        pa.append(a_.elapsed_time(b_))
+    canon_new = lay.assemble(as_i16(news))
+    ok_partial = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
+    del canon_new
+    partial_retry = {"kill_at_records": n_rec // 2, "status": int(pr["status"]), "records": int(pr["n_records"]),
+                     "payload_GB": round(int(pr["payload_bytes"]) / 1e9, 4),
+                     "full_retry_payload_GB": round(rp_bytes / 1e9, 4),
+                     "encode_ms": round(float(np.median(pe)), 4), "full_retry_encode_ms": round(op_ms["encode_retry"], 4),
+                     "apply_ms": round(float(np.median(pa)), 4), "full_retry_apply_ms": round(op_ms["retry"], 4),
+                     "healed_eq_new": bool(ok_partial)}
+    log(f"partial retry at a 50 % kill: {partial_retry}")
+
     enc_bytes = 2 * cb + 32 * n_rec + p_bytes
     renc_bytes = 2 * cb + 32 * rn_rec + rp_bytes
     app_bytes = 32 * n_rec + p_bytes + LINE * touched + SECTOR * touched_sec
@@ -288,6 +327,7 @@ def main():
                     "touched_128B_lines": touched, "touched_32B_sectors": touched_sec},
         "checks": {"apply_eq_new": bool(ok_apply), "retry_eq_new": bool(ok_retry),
                    "after_timing_eq_new": bool(ok_after), "oracle_sample": parity_sample},
+        "partial_retry": partial_retry,
         "roofline": roof,
         "ceiling": ceiling,
         "cpu_baseline": cpu,

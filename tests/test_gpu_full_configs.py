@@ -41,7 +41,7 @@ def staged_workspace(plan, sb):
     return dcr.workspace(plan, "cuda", stage)
 
 
-def run_full(orc, lay, sample_names):
+def run_full(orc, lay, sample_names, partial=False):
     assert torch.cuda.is_available()
     say(lay.name, "plan")
     T = lay.tensors
@@ -126,7 +126,8 @@ def run_full(orc, lay, sample_names):
     del co
     flags.zero_()
     dcr.dcr_apply(plan, canon, hdr, sb.dir, sb.payload, flags, 0, n_rec // 2, 3, res, ws)
-    del sb
+    if not partial:
+        del sb
     rsb = dcr.StreamBuffers(plan, "cuda", dir_bytes=32 * int(plan.info.n_chunks),
                             payload_bytes=int(cb * 0.2) + (1 << 20))
     say(lay.name, "retry")
@@ -140,6 +141,38 @@ def run_full(orc, lay, sample_names):
     for t in range(len(T)):
         assert torch.equal(canon[t], cn[t].reshape(-1).view(torch.uint8)), lay.tensor_names[t]
     say(lay.name, "apply, kill at 50 % and retry: all tensors equal new")
+    if partial:
+        # again from old, killed at 50 %: the partial retry sends only the
+        # chunks of the unflagged records and heals everything
+        co = lay.assemble(typed(lay, olds))
+        for t in range(len(T)):
+            canon[t].copy_(co[t].reshape(-1).view(torch.uint8))
+        del co
+        flags.zero_()
+        dcr.dcr_apply(plan, canon, hdr, sb.dir, sb.payload, flags, 0, n_rec // 2, 3, res, ws)
+        say(lay.name, "partial retry")
+        wss = staged_workspace(plan, rsb)
+        dcr.dcr_encode_retry_partial(plan, olds, news, hdr, sb.dir, flags, 3, 4, rsb.header, rsb.dir, rsb.payload,
+                                     rsb.result, wss)
+        torch.cuda.synchronize()
+        del wss
+        pr = rsb.result_host()
+        assert int(pr["status"]) == 0, pr
+        ents = sb.dir[: n_rec * 32].cpu().numpy().reshape(-1, 32)
+        want = sorted(set(zip(ents[n_rec // 2:, 0:4].copy().view("<u4").ravel().tolist(),
+                              ents[n_rec // 2:, 4:8].copy().view("<u4").ravel().tolist())))
+        pn = int(pr["n_records"])
+        pents = rsb.dir[: pn * 32].cpu().numpy().reshape(-1, 32)
+        got = list(zip(pents[:, 0:4].copy().view("<u4").ravel().tolist(),
+                       pents[:, 4:8].copy().view("<u4").ravel().tolist()))
+        assert got == want, (len(got), len(want))
+        dcr.dcr_apply_overwrite_retry(plan, canon, rsb.header.cpu().numpy(), rsb.dir, rsb.payload, 3, res, ws)
+        torch.cuda.synchronize()
+        for t in range(len(T)):
+            assert torch.equal(canon[t], cn[t].reshape(-1).view(torch.uint8)), lay.tensor_names[t]
+        say(lay.name, f"kill at 50 % and partial retry ({pn} records, {int(pr['payload_bytes']) / 1e9:.2f} GB): "
+                      "all tensors equal new")
+        del sb
     del cbuf, canon, cn, ob, nb, olds, news, rsb
     torch.cuda.empty_cache()
 
@@ -148,7 +181,7 @@ def test_full_llama8b_tp4(orc):
     lay = synth.llama_layout()
     run_full(orc, lay, ["model.layers.0.input_layernorm.weight", "model.layers.0.self_attn.q_proj.weight",
                         "model.layers.0.self_attn.k_proj.weight", "model.layers.0.self_attn.o_proj.weight",
-                        "model.layers.31.mlp.down_proj.weight", "model.norm.weight"])
+                        "model.layers.31.mlp.down_proj.weight", "model.norm.weight"], partial=True)
 
 
 def test_full_qwen30b_ep8_beta(orc):
