@@ -163,10 +163,22 @@ static uint32_t xor_hi_mode(uint64_t K, uint64_t h) {
     return ORC_HI_DENSE;
 }
 
+/* Bytes of a record's first section: the change bitmap (one bit per chunk
+ * element), or in the index-list layout K 16-bit element indices; padded. */
+static uint64_t head_bytes(uint64_t n_c, uint64_t K, uint32_t layout) {
+    return layout == ORC_LAYOUT_LIST ? pad16(2 * K) : pad16((n_c + 7) / 8);
+}
+
+/* Layout of a record with K changes: the index list when allowed and
+ * strictly smaller than the bitmap. */
+static uint32_t choose_layout(uint64_t n_c, uint64_t K, int lists) {
+    return (lists && pad16(2 * K) < pad16((n_c + 7) / 8)) ? ORC_LAYOUT_LIST : ORC_LAYOUT_BITMAP;
+}
+
 /* Bytes of a record's payload. */
 static uint64_t record_bytes(uint64_t n_c, uint32_t w, uint32_t kind, uint64_t K,
-                             uint32_t hi_mode, uint64_t H) {
-    uint64_t sz = pad16((n_c + 7) / 8) + pad16(K);
+                             uint32_t hi_mode, uint64_t H, uint32_t layout) {
+    uint64_t sz = head_bytes(n_c, K, layout) + pad16(K);
     if (w == 2 && kind == ORC_KIND_XOR) {
         if (hi_mode == ORC_HI_SPARSE) sz += pad16((K + 7) / 8) + pad16(H);
         else if (hi_mode == ORC_HI_DENSE) sz += pad16(K);
@@ -183,7 +195,7 @@ static uint64_t record_bytes(uint64_t n_c, uint32_t w, uint32_t kind, uint64_t K
  * out (if non-NULL) and returns the byte size; fills hi_mode and H. */
 static uint64_t build_record(uint8_t* out, uint64_t n_c, uint32_t w, uint32_t kind,
                              uint64_t K, const uint32_t* idx, const uint32_t* word,
-                             uint32_t* hi_mode, uint32_t* H) {
+                             uint32_t layout, uint32_t* hi_mode, uint32_t* H) {
     uint64_t j, h = 0, pos, sz;
     uint32_t mode;
     if (w == 2 && kind == ORC_KIND_XOR) {
@@ -196,12 +208,17 @@ static uint64_t build_record(uint8_t* out, uint64_t n_c, uint32_t w, uint32_t ki
         mode = ORC_HI_DENSE; *H = (uint32_t)K;
     }
     *hi_mode = mode;
-    sz = record_bytes(n_c, w, kind, K, mode, *H);
+    sz = record_bytes(n_c, w, kind, K, mode, *H, layout);
     if (!out) return sz;
     memset(out, 0, sz);
-    /* section 1: change bitmap, bit i of the chunk = byte i/8, bit i%8 */
-    for (j = 0; j < K; j++) out[idx[j] / 8] |= (uint8_t)(1u << (idx[j] % 8));
-    pos = pad16((n_c + 7) / 8);
+    if (layout == ORC_LAYOUT_LIST) {
+        /* section 1: the chunk indices of the changes, 16-bit little-endian */
+        for (j = 0; j < K; j++) put_u16(out + 2 * j, (uint16_t)idx[j]);
+    } else {
+        /* section 1: change bitmap, bit i of the chunk = byte i/8, bit i%8 */
+        for (j = 0; j < K; j++) out[idx[j] / 8] |= (uint8_t)(1u << (idx[j] % 8));
+    }
+    pos = head_bytes(n_c, K, layout);
     /* section 2: low byte plane */
     for (j = 0; j < K; j++) out[pos + j] = (uint8_t)(word[j] & 0xFF);
     pos += pad16(K);
@@ -227,14 +244,14 @@ static uint64_t build_record(uint8_t* out, uint64_t n_c, uint32_t w, uint32_t ki
 }
 
 static void put_dirent(uint8_t* p, uint32_t t, uint32_t c, uint32_t K, uint32_t kind,
-                       uint32_t hi_mode, uint32_t w, uint64_t off, uint32_t sz, uint32_t H) {
+                       uint32_t hi_mode, uint32_t w, uint64_t off, uint32_t sz, uint32_t H, uint32_t layout) {
     put_u32(p + 0, t);
     put_u32(p + 4, c);
     put_u32(p + 8, K);
     p[12] = (uint8_t)kind;
     p[13] = (uint8_t)hi_mode;
     p[14] = (uint8_t)w;
-    p[15] = 0;
+    p[15] = (uint8_t)layout;
     put_u64(p + 16, off);
     put_u32(p + 24, sz);
     put_u32(p + 28, H);
@@ -273,7 +290,9 @@ static int32_t encode_chunks(const orc_tensor* T, uint32_t nT,
     int32_t rc = check_tensors(T, nT);
     uint32_t* idx[2] = {NULL, NULL};
     uint32_t* word[2] = {NULL, NULL};
+    const int lists = (mode & ORC_ENC_LISTS) != 0;
     if (rc) return rc;
+    mode &= ~(uint32_t)ORC_ENC_LISTS;
     if (mode != ORC_MODE_DELTA && mode != ORC_MODE_RETRY) return ORC_E_INVAL;
     idx[0] = (uint32_t*)malloc(65536 * sizeof(uint32_t));
     idx[1] = (uint32_t*)malloc(65536 * sizeof(uint32_t));
@@ -329,14 +348,15 @@ static int32_t encode_chunks(const orc_tensor* T, uint32_t nT,
                 K[kind]++;
             }
             for (k = 0; k < 2; k++) {
-                uint32_t hi_mode, H;
+                uint32_t hi_mode, H, layout;
                 uint64_t sz;
                 if (K[k] == 0) continue;
-                sz = build_record(NULL, n_c, w, k, K[k], idx[k], word[k], &hi_mode, &H);
+                layout = choose_layout(n_c, K[k], lists);
+                sz = build_record(NULL, n_c, w, k, K[k], idx[k], word[k], layout, &hi_mode, &H);
                 if ((nrec + 1) * ORC_DIRENT_BYTES <= dir_cap && poff + sz <= payload_cap) {
-                    build_record(payload_out + poff, n_c, w, k, K[k], idx[k], word[k], &hi_mode, &H);
+                    build_record(payload_out + poff, n_c, w, k, K[k], idx[k], word[k], layout, &hi_mode, &H);
                     put_dirent(dir_out + nrec * ORC_DIRENT_BYTES, t, (uint32_t)c, (uint32_t)K[k], k,
-                               hi_mode, w, poff, (uint32_t)sz, H);
+                               hi_mode, w, poff, (uint32_t)sz, H, layout);
                 }
                 nrec++;
                 poff += sz;
@@ -420,7 +440,7 @@ out:
 /* ------------------------------------------------------- stream parsing */
 
 typedef struct {
-    uint32_t t, c, K, kind, hi_mode, w, H;
+    uint32_t t, c, K, kind, hi_mode, w, H, layout;
     uint64_t off, sz;
 } orc_rec;
 
@@ -431,6 +451,7 @@ static void get_dirent(const uint8_t* p, orc_rec* r) {
     r->kind = p[12];
     r->hi_mode = p[13];
     r->w = p[14];
+    r->layout = p[15];
     r->off = get_u64(p + 16);
     r->sz = get_u32(p + 24);
     r->H = get_u32(p + 28);
@@ -446,7 +467,7 @@ static int32_t check_record(const orc_tensor* T, uint32_t nT, const uint8_t* dir
     const uint8_t* p;
     uint64_t E, n_c, i, cnt, pos, j;
     get_dirent(dirent, &r);
-    if (dirent[15] != 0) return ORC_E_FORMAT;
+    if (r.layout > ORC_LAYOUT_LIST) return ORC_E_FORMAT;
     if (r.t >= nT) return ORC_E_FORMAT;
     d = &T[r.t];
     if (r.w != d->elem_bytes) return ORC_E_FORMAT;
@@ -466,18 +487,28 @@ static int32_t check_record(const orc_tensor* T, uint32_t nT, const uint8_t* dir
         if (r.H == 0 || r.H > r.K || xor_hi_mode(r.K, r.H) != ORC_HI_SPARSE) return ORC_E_FORMAT;
     } else if (r.hi_mode == ORC_HI_DENSE) { if (r.H != r.K) return ORC_E_FORMAT; }
     else return ORC_E_FORMAT;
-    if (r.sz != record_bytes(n_c, r.w, r.kind, r.K, r.hi_mode, r.H)) return ORC_E_FORMAT;
+    if (r.sz != record_bytes(n_c, r.w, r.kind, r.K, r.hi_mode, r.H, r.layout)) return ORC_E_FORMAT;
 
     p = payload + r.off;
-    /* bitmap: popcount K, nothing set at or beyond n_c, zero padding */
-    cnt = 0;
-    for (i = 0; i < pad16((n_c + 7) / 8) * 8; i++) {
-        if (!bit(p, i)) continue;
-        if (i >= n_c) return ORC_E_FORMAT;
-        cnt++;
+    if (r.layout == ORC_LAYOUT_LIST) {
+        /* index list: K strictly ascending indices below n_c, zero padding */
+        for (j = 0; j < r.K; j++) {
+            uint64_t e = get_u16(p + 2 * j);
+            if (e >= n_c) return ORC_E_FORMAT;
+            if (j > 0 && e <= get_u16(p + 2 * (j - 1))) return ORC_E_FORMAT;
+        }
+        for (j = 2 * (uint64_t)r.K; j < pad16(2 * (uint64_t)r.K); j++) if (p[j]) return ORC_E_FORMAT;
+    } else {
+        /* bitmap: popcount K, nothing set at or beyond n_c, zero padding */
+        cnt = 0;
+        for (i = 0; i < pad16((n_c + 7) / 8) * 8; i++) {
+            if (!bit(p, i)) continue;
+            if (i >= n_c) return ORC_E_FORMAT;
+            cnt++;
+        }
+        if (cnt != r.K) return ORC_E_FORMAT;
     }
-    if (cnt != r.K) return ORC_E_FORMAT;
-    pos = pad16((n_c + 7) / 8);
+    pos = head_bytes(n_c, r.K, r.layout);
     for (j = r.K; j < pad16(r.K); j++) if (p[pos + j]) return ORC_E_FORMAT;
     pos += pad16(r.K);
     if (r.w == 2 && r.kind == ORC_KIND_XOR && r.hi_mode == ORC_HI_SPARSE) {
@@ -506,6 +537,20 @@ static int32_t check_record(const orc_tensor* T, uint32_t nT, const uint8_t* dir
     return ORC_OK;
 }
 
+/* The change bitmap of a (checked) record, whatever its layout, in out
+ * (pad16(n_c/8) bytes, zeroed by the caller). */
+static void record_marks(const uint8_t* p, const orc_rec* r, uint64_t n_c, uint8_t* out) {
+    uint64_t j;
+    if (r->layout != ORC_LAYOUT_LIST) {
+        memcpy(out, p, pad16((n_c + 7) / 8));
+        return;
+    }
+    for (j = 0; j < r->K; j++) {
+        uint64_t e = get_u16(p + 2 * j);
+        out[e / 8] |= (uint8_t)(1u << (e % 8));
+    }
+}
+
 /* Two records of one chunk may not mark elements of the same 16-byte group. */
 static int32_t check_pair(const orc_tensor* T, const uint8_t* payload, const orc_rec* a, const orc_rec* b) {
     uint32_t w = a->w;
@@ -513,14 +558,20 @@ static int32_t check_pair(const orc_tensor* T, const uint8_t* payload, const orc
     uint64_t numel = T[a->t].numel;
     uint64_t n_c = (numel - (uint64_t)a->c * E < E) ? numel - (uint64_t)a->c * E : E;
     uint64_t gs = 16u / w;
-    const uint8_t* ma = payload + a->off;
-    const uint8_t* mb = payload + b->off;
-    for (g = 0; g < n_c; g += gs) {
+    int32_t rc = ORC_OK;
+    uint8_t* ma = (uint8_t*)calloc(pad16((n_c + 7) / 8) + 1, 1);
+    uint8_t* mb = (uint8_t*)calloc(pad16((n_c + 7) / 8) + 1, 1);
+    if (!ma || !mb) { free(ma); free(mb); return ORC_E_NOMEM; }
+    record_marks(payload + a->off, a, n_c, ma);
+    record_marks(payload + b->off, b, n_c, mb);
+    for (g = 0; g < n_c && rc == ORC_OK; g += gs) {
         int ia = 0, ib = 0;
         for (i = g; i < g + gs && i < n_c; i++) { ia |= bit(ma, i); ib |= bit(mb, i); }
-        if (ia && ib) return ORC_E_FORMAT;
+        if (ia && ib) rc = ORC_E_FORMAT;
     }
-    return ORC_OK;
+    free(ma);
+    free(mb);
+    return rc;
 }
 
 int32_t orc_validate(const orc_tensor* T, uint32_t nT, const uint8_t* header,
@@ -575,18 +626,23 @@ static void apply_changes(const orc_tensor* T, void* const* canon, const uint8_t
     const uint8_t* p;
     uint64_t E, n_c, i, j = 0, rank_hi = 0;
     uint64_t lo_pos, hi_pos, pres_pos = 0;
+    uint8_t* marks;
     get_dirent(dirent, &r);
     d = &T[r.t];
     E = chunk_elems(r.w);
     n_c = (d->numel - (uint64_t)r.c * E < E) ? d->numel - (uint64_t)r.c * E : E;
     p = payload + r.off;
-    lo_pos = pad16((n_c + 7) / 8);
+    /* the changed elements in ascending order, from either layout */
+    marks = (uint8_t*)calloc(pad16((n_c + 7) / 8) + 1, 1);
+    if (!marks) return;
+    record_marks(p, &r, n_c, marks);
+    lo_pos = head_bytes(n_c, r.K, r.layout);
     hi_pos = lo_pos + pad16(r.K);
     if (r.hi_mode == ORC_HI_SPARSE) { pres_pos = hi_pos; hi_pos = pres_pos + pad16((r.K + 7) / 8); }
     for (i = 0; i < n_c; i++) {
         uint32_t v;
         uint64_t g;
-        if (!bit(p, i)) continue;
+        if (!bit(marks, i)) continue;
         /* change j sits at chunk element i */
         v = p[lo_pos + j];
         if (r.w == 2) {
@@ -607,6 +663,7 @@ static void apply_changes(const orc_tensor* T, void* const* canon, const uint8_t
         }
         j++;
     }
+    free(marks);
 }
 
 int32_t orc_apply(const orc_tensor* T, uint32_t nT, void* const* canon,

@@ -54,6 +54,16 @@ extern "C" {
 #define ORC_MODE_DELTA 0
 #define ORC_MODE_RETRY 1
 
+/* encode option (OR-ed into the mode): low-density records carry a list of
+ * 16-bit element indices instead of the change bitmap when that list is
+ * strictly smaller (next-step variant; the pages compress the mask stream,
+ * ai-feeds summary "key modules" 3) */
+#define ORC_ENC_LISTS 0x100u
+
+/* record layouts (directory entry byte 15) */
+#define ORC_LAYOUT_BITMAP 0
+#define ORC_LAYOUT_LIST   1
+
 /* record kinds, high-byte modes */
 #define ORC_KIND_XOR 0
 #define ORC_KIND_OW  1

@@ -30,6 +30,8 @@ SOURCES = [os.path.join(_HERE, "dcr_oracle.c")]
 OK, E_INVAL, E_COVERAGE, E_FORMAT, E_VERSION, E_CAPACITY, E_NOMEM = 0, -1, -2, -3, -4, -5, -7
 ROUTE_AFFINE_XOR, ROUTE_OVERWRITE, ROUTE_BLOCK_SCALED = 0, 1, 2
 MODE_DELTA, MODE_RETRY = 0, 1
+ENC_LISTS = 0x100                 # encode option: index-list layout for low-density records
+LAYOUT_BITMAP, LAYOUT_LIST = 0, 1
 KIND_XOR, KIND_OW = 0, 1
 HI_NONE, HI_SPARSE, HI_DENSE = 0, 1, 2
 HEADER_BYTES, DIRENT_BYTES, CHUNK_BYTES = 64, 32, 65536

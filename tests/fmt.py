@@ -1,8 +1,9 @@
 """Independent reader of the delta-stream format, for tests.
 
 Written from the format definition alone (header, 32-byte directory entries,
-16-byte-padded record sections: change bitmap, low byte plane, then for
-2-byte XOR records a presence bitmap + nonzero high bytes (SPARSE) or all
+16-byte-padded record sections: change bitmap (or, in the index-list layout
+marked by directory byte 15, K 16-bit element indices), low byte plane, then
+for 2-byte XOR records a presence bitmap + nonzero high bytes (SPARSE) or all
 high bytes (DENSE); for overwrite records the upper byte planes).  It shares
 nothing with the oracle or the GPU library.
 """
@@ -30,7 +31,7 @@ def dirents(d):
     for e in d:
         out.append(dict(t=int(e[0:4].view("<u4")[0]), c=int(e[4:8].view("<u4")[0]),
                         K=int(e[8:12].view("<u4")[0]), kind=int(e[12]), hi_mode=int(e[13]),
-                        w=int(e[14]), off=int(e[16:24].view("<u8")[0]),
+                        w=int(e[14]), layout=int(e[15]), off=int(e[16:24].view("<u8")[0]),
                         size=int(e[24:28].view("<u4")[0]), H=int(e[28:32].view("<u4")[0])))
     return out
 
@@ -40,10 +41,15 @@ def decode_record(e, payload, n_c):
     p = np.asarray(payload, dtype=np.uint8)[e["off"]:e["off"] + e["size"]]
     K, w = e["K"], e["w"]
     nb = (n_c + 7) // 8
-    bits = np.unpackbits(p[:nb], bitorder="little")[:n_c]
-    idx = np.nonzero(bits)[0]
-    assert len(idx) == K
-    pos = pad16(nb)
+    if e.get("layout", 0) == 1:
+        idx = p[:2 * K].view("<u2").astype(np.int64)
+        assert len(idx) == K and (np.diff(idx) > 0).all() and (idx < n_c).all()
+        pos = pad16(2 * K)
+    else:
+        bits = np.unpackbits(p[:nb], bitorder="little")[:n_c]
+        idx = np.nonzero(bits)[0]
+        assert len(idx) == K
+        pos = pad16(nb)
     words = p[pos:pos + K].astype(np.uint32)
     pos += pad16(K)
     if w == 2 and e["kind"] == 0:

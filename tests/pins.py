@@ -26,6 +26,8 @@ from bit_exact_xor_amd import synth
 from oracle.oracle import E_FORMAT as O_E_FORMAT
 from tests import fmt
 
+MODE_DELTA, MODE_RETRY = 0, 1
+
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -224,6 +226,79 @@ def pin_retry_partial(orc, seeds=range(3)):
             bad[0:4] = np.frombuffer(np.uint32(lay.n_tensors).tobytes(), np.uint8)
             rc, *_ = orc.encode_retry_partial(lay.tensors, lay.segments, olds, news, hdr, bad, np.zeros(n, np.uint8))
             assert rc == O_E_FORMAT
+
+
+def pin_index_lists(orc, seeds=range(6)):
+    """Index-list layout (encode option): the same records as the bitmap
+    stream in the same order, each in list layout exactly when 2K bytes
+    (padded) are fewer than the padded bitmap; a list record is the bitmap
+    record with the bitmap replaced by the ascending indices of its set bits
+    (everything after it byte-identical); offsets stay contiguous; apply,
+    XOR involution and retry work on it; malformed lists are refused."""
+    for seed in seeds:
+        lay = synth.random_layout(1200 + seed, rate=[0.002, 0.03, 0.2][seed % 3])
+        olds, news, co, cn = canon_lists(lay)
+        numels = [int(t["numel"]) for t in lay.tensors]
+        widths = [int(t["elem_bytes"]) for t in lay.tensors]
+        for mode in (MODE_DELTA, MODE_RETRY):
+            bh, bd, bp = encode_ok(orc, lay, olds, news, mode=mode)
+            rc, lh, ld, lp = orc.encode(lay.tensors, lay.segments, olds, news, mode=mode | 0x100,
+                                        base_version=7, new_version=8)
+            assert rc == 0
+            assert np.array_equal(lh[:40], bh[:40]) and int(lh[40:48].view("<u8")[0]) == len(bd) // 32
+            be, le = fmt.dirents(bd), fmt.dirents(ld)
+            assert len(be) == len(le)
+            off = 0
+            for b, l in zip(be, le):
+                for key in ("t", "c", "K", "kind", "hi_mode", "w", "H"):
+                    assert b[key] == l[key], (seed, key)
+                E = 65536 // b["w"]
+                n_c = min(E, numels[b["t"]] - b["c"] * E)
+                nb = (n_c + 7) // 8
+                want_list = (2 * b["K"] + 15) // 16 * 16 < (nb + 15) // 16 * 16
+                assert l["layout"] == (1 if want_list else 0), (seed, b["K"], n_c)
+                assert l["off"] == off
+                off += l["size"]
+                rb = bp[b["off"]:b["off"] + b["size"]]
+                rl = lp[l["off"]:l["off"] + l["size"]]
+                if not want_list:
+                    assert np.array_equal(rb, rl)
+                    continue
+                head_b, head_l = (nb + 15) // 16 * 16, (2 * b["K"] + 15) // 16 * 16
+                assert l["size"] == b["size"] - head_b + head_l
+                bits = np.unpackbits(rb[:nb], bitorder="little")[:n_c]
+                idx = np.nonzero(bits)[0].astype("<u2")
+                assert np.array_equal(rl[:2 * b["K"]], idx.view(np.uint8))
+                assert not rl[2 * b["K"]:head_l].any()
+                assert np.array_equal(rl[head_l:], rb[head_b:])
+            assert off == len(lp)
+            assert fmt.decode_stream(lh, ld, lp, numels, widths).__len__() == len(be)
+            if mode == MODE_DELTA:
+                W = [x.copy() for x in co]
+                f = np.zeros(max(len(le), 1), np.uint8)
+                assert orc.apply(lay.tensors, W, lh, ld, lp, f, expected_base_version=7) == 0
+                for t in range(lay.n_tensors):
+                    assert np.array_equal(W[t], cn[t])
+                if all(e["kind"] == 0 for e in le):
+                    f[:] = 0
+                    assert orc.apply(lay.tensors, W, lh, ld, lp, f, expected_base_version=7) == 0
+                    for t in range(lay.n_tensors):
+                        assert np.array_equal(W[t], co[t])
+            else:
+                W = [x.copy() for x in co]
+                assert orc.retry(lay.tensors, W, lh, ld, lp, expected_base_version=7) == 0
+                for t in range(lay.n_tensors):
+                    assert np.array_equal(W[t], cn[t])
+            lists = [i for i, e in enumerate(le) if e["layout"] == 1 and e["K"] >= 2]
+            if lists:
+                e = le[lists[0]]
+                bad = lp.copy()       # two indices swapped: not ascending
+                a0 = e["off"]
+                bad[a0:a0 + 2], bad[a0 + 2:a0 + 4] = lp[a0 + 2:a0 + 4].copy(), lp[a0:a0 + 2].copy()
+                assert orc.validate(lay.tensors, lh, ld, bad, 7) == O_E_FORMAT
+                bad = ld.copy()       # unknown layout
+                bad[lists[0] * 32 + 15] = 2
+                assert orc.validate(lay.tensors, lh, bad, lp, 7) == O_E_FORMAT
 
 
 def pin_signed_zero(orc):

@@ -3,7 +3,7 @@
 Each mutant is a plausible slip (wrong bit order, float-style comparison,
 wrong word, tie-break, byte plane, transposed strides, chunk size, missing
 dedup, inverted routing, missing padding, partial retry ignoring the flags or
-marking the wrong chunk); the copy is compiled in a temp
+marking the wrong chunk, index lists off by one or never chosen); the copy is compiled in a temp
 directory and loaded beside the real oracle.  Nothing here touches a GPU.
 """
 import os
@@ -45,6 +45,10 @@ MUTANTS = {
                                     "need[first[et] + ec] = 1;"),
     "partial_retry_wrong_chunk": ("if (!delta_flags[r]) need[first[et] + ec] = 1;",
                                   "if (!delta_flags[r]) need[first[et]] = 1;"),
+    "list_index_off_by_one": ("for (j = 0; j < K; j++) put_u16(out + 2 * j, (uint16_t)idx[j]);",
+                              "for (j = 0; j < K; j++) put_u16(out + 2 * j, (uint16_t)(idx[j] + 1));"),
+    "list_layout_never": ("return (lists && pad16(2 * K) < pad16((n_c + 7) / 8)) ? ORC_LAYOUT_LIST : ORC_LAYOUT_BITMAP;",
+                          "(void)lists; (void)K; (void)n_c; return ORC_LAYOUT_BITMAP;"),
 }
 
 
