@@ -167,6 +167,7 @@ struct EncodeArgs {
     const uint64_t* need;   // partial retry: one bit per tile, set = encode it (NULL: every tile)
     uint32_t n_tiles;
     uint32_t mode;
+    uint32_t lists;         // 1: index-list layout allowed for low-density records
 };
 
 struct EncodeShared {
@@ -185,18 +186,27 @@ struct EncodeShared {
 // Sizes and high-byte mode of a chunk's records (the record layout of the
 // format): bitmap, low plane, then for 2-byte XOR records a sparse (presence
 // bitmap + nonzero high bytes) or dense high plane, whichever is smaller
-// (dense on a tie); overwrite records carry all W byte planes.
+// (dense on a tie); overwrite records carry all W byte planes.  With index
+// lists allowed, a record whose K 16-bit indices (padded) take fewer bytes
+// than its padded bitmap carries them in the bitmap's place.
 struct RecLayout {
     uint32_t size_x, size_o;     // bytes of the XOR / overwrite record (0: none)
     uint32_t mode_x, h_x;        // XOR record: hi_mode and its H field
     uint32_t off_pres, off_hi_x; // XOR record: presence bitmap / high plane offsets
+    uint32_t head_x, head_o;     // bytes of each record's first section (bitmap or index list)
+    uint32_t list_x, list_o;     // 1: index-list layout
 };
 
-__device__ __forceinline__ RecLayout rec_layout(uint32_t w, uint32_t n_c, uint32_t Kx, uint32_t Ko, uint32_t Hx) {
-    RecLayout L{0, 0, DCR_HI_NONE, 0, 0, 0};
+__device__ __forceinline__ RecLayout rec_layout(uint32_t w, uint32_t n_c, uint32_t Kx, uint32_t Ko, uint32_t Hx,
+                                                uint32_t lists) {
+    RecLayout L{0, 0, DCR_HI_NONE, 0, 0, 0, 0, 0, 0, 0};
     const uint32_t bm = dpad16((n_c + 7) / 8);
+    L.list_x = (lists && Kx && dpad16(2 * Kx) < bm) ? 1u : 0u;
+    L.list_o = (lists && Ko && dpad16(2 * Ko) < bm) ? 1u : 0u;
+    L.head_x = L.list_x ? dpad16(2 * Kx) : bm;
+    L.head_o = L.list_o ? dpad16(2 * Ko) : bm;
     if (Kx) {
-        L.size_x = bm + dpad16(Kx);
+        L.size_x = L.head_x + dpad16(Kx);
         L.off_hi_x = L.size_x;
         if (w == 2 && Hx) {
             const uint32_t sparse = dpad16((Kx + 7) / 8) + dpad16(Hx);
@@ -213,7 +223,7 @@ __device__ __forceinline__ RecLayout rec_layout(uint32_t w, uint32_t n_c, uint32
             }
         }
     }
-    if (Ko) L.size_o = bm + w * dpad16(Ko);
+    if (Ko) L.size_o = L.head_o + w * dpad16(Ko);
     return L;
 }
 
@@ -228,7 +238,8 @@ __device__ __forceinline__ void put_dirent(uint8_t* dir, uint64_t index, uint32_
     e0.y = chunk;
     e0.z = x ? Kx : Ko;
     const uint32_t hm = x ? L.mode_x : (w == 1 ? uint32_t(DCR_HI_NONE) : uint32_t(DCR_HI_DENSE));
-    e0.w = (x ? 0u : 1u) | (hm << 8) | (w << 16);
+    const uint32_t layout = x ? L.list_x : L.list_o;
+    e0.w = (x ? 0u : 1u) | (hm << 8) | (w << 16) | (layout << 24);
     const uint64_t off = P + (x ? 0u : L.size_x);
     e1.x = uint32_t(off);
     e1.y = uint32_t(off >> 32);
@@ -575,6 +586,8 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
     const uint32_t Kx = t.Kx, Ko = t.Ko;
     const uint32_t base_o = L.size_x;
     const uint32_t pkx = dpad16(Kx), pko = dpad16(Ko);
+    // records in bitmap layout, non-empty (uniform)
+    const uint32_t bmx = sgpr(L.list_x ? 0u : Kx), bmo = sgpr(L.list_o ? 0u : Ko);
     const uint32_t hi_x_dense = sgpr(L.mode_x == DCR_HI_DENSE ? 1u : 0u);
     const uint32_t hi_x_sparse = sgpr(L.mode_x == DCR_HI_SPARSE ? 1u : 0u);
     const uint32_t w1 = w0 + kWinBytes;
@@ -584,6 +597,11 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
     auto inwin = [&](uint32_t pos) { return ONE || (pos >= w0 && pos < w1); };
     auto put = [&](uint32_t pos, uint32_t v) {
         if (inwin(pos)) win[pos - w0] = uint8_t(v);
+    };
+    // pos is even and windows start at multiples of kWinBytes: both bytes
+    // share the window
+    auto put16 = [&](uint32_t pos, uint32_t v) {
+        if (inwin(pos)) *reinterpret_cast<uint16_t*>(win + (pos - w0)) = uint16_t(v);
     };
 #pragma unroll
     for (uint32_t k = 0; k < kVecsPerThread; k++) {
@@ -599,26 +617,28 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
         }
         if (g * V < bm * 8) {
             if constexpr (W == 2) {
-                if (Kx) put(g, bx);
-                if (Ko) put(base_o + g, bo);
+                if (bmx) put(g, bx);
+                if (bmo) put(base_o + g, bo);
             } else if constexpr (W == 1) {
-                if (Kx) { put(2 * g, bx); put(2 * g + 1, bx >> 8); }
-                if (Ko) { put(base_o + 2 * g, bo); put(base_o + 2 * g + 1, bo >> 8); }
+                if (bmx) { put(2 * g, bx); put(2 * g + 1, bx >> 8); }
+                if (bmo) { put(base_o + 2 * g, bo); put(base_o + 2 * g + 1, bo >> 8); }
             } else {
                 if ((g & 1) == 0) {
-                    if (Kx) put(g / 2, bx | (px << 4));
-                    if (Ko) put(base_o + g / 2, bo | (po << 4));
+                    if (bmx) put(g / 2, bx | (px << 4));
+                    if (bmo) put(base_o + g / 2, bo | (po << 4));
                 }
             }
         }
         if (!b) continue;
         const uint32_t rb = x ? 0u : base_o;
         const uint32_t pk = x ? pkx : pko;
-        const uint32_t lo = rb + bm;
+        const uint32_t lst = ONE ? (x ? L.list_x : L.list_o) : 0u;   // several windows: lists written after
+
+        const uint32_t lo = rb + (x ? L.head_x : L.head_o);
         uint32_t j = x ? t.kb[0][k] + field16(cnt[0], k) : t.kb[1][k] + field16(cnt[1], k);
         uint32_t hr = t.kb[2][k] + field16(cnt[2], k);
         if (!ONE) {
-            // every byte of this group lies in [lo + j, end): skip the group
+            // every byte of this group lies in [start, end): skip the group
             // when that range misses the window
             const uint32_t nb = uint32_t(__popc(b));
             uint32_t end = lo + (W - 1) * pk + j + nb;
@@ -651,6 +671,7 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
         while (b) {
             const uint32_t i = uint32_t(__ffs(b) - 1);
             b &= b - 1;
+            if (lst) put16(rb + 2 * j, g * V + i);
             if constexpr (W == 1) {
                 // byte i of the group: 32-bit selects and shifts only
                 const uint32_t wv = (i & 8u) ? ((i & 4u) ? q.w : q.z) : ((i & 4u) ? q.y : q.x);
@@ -711,6 +732,26 @@ __device__ __forceinline__ void write_tile(EncodeShared& S, uint8_t* out, uint32
         write_window<W, false>(S, out, w0, total, bm, m, cc, t, L);
         __syncthreads();
     }
+    // index lists of records spanning several windows: the windows left their
+    // bytes zero; each thread stores its changes' indices over them (the
+    // barrier above orders these stores after the window copies)
+    if (L.list_x || L.list_o) {
+        constexpr uint32_t V = 16 / W;
+#pragma unroll
+        for (uint32_t k = 0; k < kVecsPerThread; k++) {
+            uint32_t b = meta[k] & 0xFFFFu;
+            const bool x = (meta[k] >> 31) == DCR_KIND_XOR;
+            if (!b || !(x ? L.list_x : L.list_o)) continue;
+            const uint32_t g = threadIdx.x + k * kThreads;
+            uint16_t* dst = reinterpret_cast<uint16_t*>(out + (x ? 0u : L.size_x));
+            uint32_t j = x ? t.kb[0][k] + field16(cnt[0], k) : t.kb[1][k] + field16(cnt[1], k);
+            while (b) {
+                const uint32_t i = uint32_t(__ffs(b) - 1);
+                b &= b - 1;
+                dst[j++] = uint16_t(g * V + i);
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ uint64_t tile_aggregate(const TileSums& t, const RecLayout& L) {
@@ -751,7 +792,7 @@ __device__ __forceinline__ void inorder_tile(const EncodeArgs& a, EncodeShared& 
     uint64_t cnt[3];
     digest_tile<W>(S, owm, lo, ln, meta, cnt);
     const TileSums t = scan_tile(S, cnt);
-    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx);
+    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx, a.lists);
     const uint64_t agg = tile_aggregate(t, L);
     const uint32_t nrec = uint32_t(agg >> kRecShift);
     const uint32_t tile = c.tile;
@@ -809,7 +850,7 @@ __device__ __forceinline__ void staged_tile(const EncodeArgs& a, EncodeShared& S
     uint64_t cnt[3];
     digest_tile<W>(S, owm, lo, ln, meta, cnt);
     const TileSums t = scan_tile(S, cnt);
-    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx);
+    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx, a.lists);
     const uint64_t agg = tile_aggregate(t, L);
     if (tid == 0) {
         a.tile_agg[c.tile] = agg;
@@ -878,7 +919,7 @@ __device__ __forceinline__ void prefetch_direct(const EncodeArgs& a, EncodeShare
 // Staged encode of the direct tiles of W-byte elements (the staging area
 // holds every chunk's slot): one workgroup per list entry; nothing waits on
 // another workgroup.
-template <int W>
+template <int W, bool LISTS>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_direct_kernel(
     EncodeArgs a, const uint32_t* list, uint32_t n_list) {
     __shared__ EncodeShared S;
@@ -899,7 +940,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     uint64_t cnt[3];
     digest_tile<W>(S, owm, o, n, meta, cnt);
     const TileSums t = scan_tile(S, cnt);
-    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx);
+    // LISTS is a.lists as a constant: without index lists every list path
+    // folds away
+    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx, LISTS ? 1u : 0u);
     const uint64_t agg = tile_aggregate(t, L);
     if (tid == 0) {
         a.tile_agg[c.tile] = agg;
@@ -930,6 +973,7 @@ struct FixArgs {
     uint32_t n_tiles;
     uint32_t n_blocks;
     uint32_t staged;
+    uint32_t lists;
 };
 
 __global__ __launch_bounds__(256) void encode_fixup_kernel(FixArgs a) {
@@ -1013,7 +1057,7 @@ __global__ __launch_bounds__(256) void encode_fixup_kernel(FixArgs a) {
             const uint32_t Hx = uint32_t((tinfo >> 34) & 0x1FFFFu);
             const uint64_t E = kChunkBytes / td.w;
             const uint32_t n_c = uint32_t(umin64(E, td.numel - uint64_t(ch.chunk_idx) * E));
-            const RecLayout L = rec_layout(td.w, n_c, Kx, Ko, Hx);
+            const RecLayout L = rec_layout(td.w, n_c, Kx, Ko, Hx, a.lists);
             put_dirent(a.dir, R + lane, lane, ch.tensor, ch.chunk_idx, td.w, L, Kx, Ko, P);
         }
     }
@@ -1119,8 +1163,8 @@ struct ApplyShared {
 };
 
 __device__ __forceinline__ uint32_t rec_bytes(uint32_t n_c, uint32_t w, uint32_t kind, uint32_t K, uint32_t hm,
-                                              uint32_t H) {
-    uint32_t sz = dpad16((n_c + 7) / 8) + dpad16(K);
+                                              uint32_t H, uint32_t layout) {
+    uint32_t sz = (layout == DCR_LAYOUT_LIST ? dpad16(2 * K) : dpad16((n_c + 7) / 8)) + dpad16(K);
     if (w == 2 && kind == DCR_KIND_XOR) {
         if (hm == DCR_HI_SPARSE) sz += dpad16((K + 7) / 8) + dpad16(H);
         else if (hm == DCR_HI_DENSE) sz += dpad16(K);
@@ -1135,7 +1179,7 @@ __device__ __forceinline__ bool entry_ok(const ApplyArgs& a, const uint32_t (&e)
     const uint32_t kind = e[3] & 0xFF, hm = (e[3] >> 8) & 0xFF, w = (e[3] >> 16) & 0xFF, z = e[3] >> 24;
     const uint64_t off = uint64_t(e[4]) | (uint64_t(e[5]) << 32);
     const uint32_t sz = e[6], H = e[7];
-    if (t >= a.n_tensors || z != 0) return false;
+    if (t >= a.n_tensors || z > DCR_LAYOUT_LIST) return false;
     const DevTensor td = a.tensors[t];
     if (w != td.w || c >= td.n_chunks) return false;
     const uint64_t E = kChunkBytes / w;
@@ -1156,7 +1200,7 @@ __device__ __forceinline__ bool entry_ok(const ApplyArgs& a, const uint32_t (&e)
     } else {
         return false;
     }
-    if (sz != rec_bytes(n_c, w, kind, K, hm, H)) return false;
+    if (sz != rec_bytes(n_c, w, kind, K, hm, H, z)) return false;
     if ((off & 15u) != 0 || off > a.payload_bytes || sz > a.payload_bytes - off) return false;
     n_c_out = n_c;
     return true;
@@ -1321,7 +1365,9 @@ __device__ __forceinline__ void apply_one(const ApplyArgs& a, ApplyShared& S, ui
         uint32_t e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
         for (int i = 0; i < 8; i++) S.ent[i] = e[i];
         uint32_t st;
-        if (!entry_ok(a, e, n_c)) st = 0;
+        // an index-list record always fits the small-record stage (its list
+        // is smaller than the bitmap): one here is malformed
+        if (!entry_ok(a, e, n_c) || (e[3] >> 24) != DCR_LAYOUT_BITMAP) st = 0;
         else if (!a.retry && a.flags[r]) st = 1;
         else st = 2;
         S.state = st;
@@ -1412,7 +1458,8 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     const uint64_t off = uint64_t(S.ent[4]) | (uint64_t(S.ent[5]) << 32);
     const uint32_t sz = S.ent[6], H = S.ent[7];
     const uint32_t bm = dpad16((n_c + 7) / 8);
-    const uint32_t lo = bm;
+    const uint32_t layout = S.ent[3] >> 24;   // bitmap or index list (checked by entry_ok)
+    const uint32_t lo = layout == DCR_LAYOUT_LIST ? dpad16(2 * K) : bm;
     const uint32_t pres = lo + dpad16(K);
     const uint32_t hi = hm == DCR_HI_SPARSE ? pres + dpad16((K + 7) / 8) : pres;
 
@@ -1431,7 +1478,29 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     // the thread's bitmap slice as whole 64- / 128-bit LDS reads (word reads
     // at this stride would collide on the banks)
     uint32_t raw[NW];
-    if constexpr (NW == 2) {
+    if (layout == DCR_LAYOUT_LIST) {
+        // the thread's elements [e_lo, e_lo + 8 BB): find the first listed
+        // index at or past e_lo, then set the bits of the indices below the
+        // end; the list must ascend strictly (checked pairwise across the
+        // workgroup); bits past n_c are refused below
+        const uint16_t* lst = reinterpret_cast<const uint16_t*>(S.stage);
+        const uint32_t e_lo = b0 * 8, e_hi = e_lo + BB * 8;
+        uint32_t l = 0, h = K;
+        while (l < h) {
+            const uint32_t m = (l + h) >> 1;
+            if (lst[m] < e_lo) l = m + 1;
+            else h = m;
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < NW; i++) raw[i] = 0;
+        for (uint32_t j = l; j < K && lst[j] < e_hi; j++) {
+            const uint32_t e = lst[j] - e_lo;
+#pragma unroll
+            for (uint32_t i = 0; i < NW; i++) raw[i] |= (e >> 5) == i ? (1u << (e & 31u)) : 0u;
+        }
+        for (uint32_t j = tid; j + 1 < K; j += kSmallThreads)
+            if (lst[j] >= lst[j + 1]) bad = true;
+    } else if constexpr (NW == 2) {
         const uint2 v = b0 < bm ? *reinterpret_cast<const uint2*>(S.stage + b0) : make_uint2(0, 0);
         raw[0] = v.x;
         raw[1] = v.y;
@@ -1754,6 +1823,8 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
     if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
     const Plan& p = *plan;
     if (!p.dev_tables) return fail(DCR_E_INVAL, "plan not uploaded");
+    const uint32_t lists = (mode & DCR_ENC_INDEX_LISTS) ? 1u : 0u;
+    mode &= ~uint32_t(DCR_ENC_INDEX_LISTS);
     if (mode > DCR_MODE_RETRY) return fail(DCR_E_INVAL, "bad mode");
     if (!header_dev || !result_dev || !workspace_dev) return fail(DCR_E_INVAL, "NULL device buffer");
     if ((dir_cap && !dir_dev) || (payload_cap && !payload_dev)) return fail(DCR_E_INVAL, "NULL device buffer");
@@ -1819,6 +1890,7 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
         a.need = partial ? need : nullptr;
         a.n_tiles = n_tiles;
         a.mode = mode;
+        a.lists = lists;
         mark(true, s);
         if (staged) {
             // direct tiles per element width, then the others (in any order:
@@ -1827,9 +1899,15 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
                 const uint32_t n = uint32_t(p.direct[i].size());
                 if (!n) continue;
                 const uint32_t* list = tab<uint32_t>(p, p.off_direct[i]);
-                if (i == 0) hipLaunchKernelGGL(encode_direct_kernel<1>, dim3(n), dim3(kThreads), 0, s, a, list, n);
-                else if (i == 1) hipLaunchKernelGGL(encode_direct_kernel<2>, dim3(n), dim3(kThreads), 0, s, a, list, n);
-                else hipLaunchKernelGGL(encode_direct_kernel<4>, dim3(n), dim3(kThreads), 0, s, a, list, n);
+                if (lists) {
+                    if (i == 0) hipLaunchKernelGGL((encode_direct_kernel<1, true>), dim3(n), dim3(kThreads), 0, s, a, list, n);
+                    else if (i == 1) hipLaunchKernelGGL((encode_direct_kernel<2, true>), dim3(n), dim3(kThreads), 0, s, a, list, n);
+                    else hipLaunchKernelGGL((encode_direct_kernel<4, true>), dim3(n), dim3(kThreads), 0, s, a, list, n);
+                } else {
+                    if (i == 0) hipLaunchKernelGGL((encode_direct_kernel<1, false>), dim3(n), dim3(kThreads), 0, s, a, list, n);
+                    else if (i == 1) hipLaunchKernelGGL((encode_direct_kernel<2, false>), dim3(n), dim3(kThreads), 0, s, a, list, n);
+                    else hipLaunchKernelGGL((encode_direct_kernel<4, false>), dim3(n), dim3(kThreads), 0, s, a, list, n);
+                }
             }
         } else {
             hipLaunchKernelGGL(encode_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
@@ -1854,6 +1932,7 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
         f.n_tiles = n_tiles;
         f.n_blocks = (n_tiles + kFixTiles - 1) / kFixTiles;
         f.staged = staged;
+        f.lists = lists;
         hipLaunchKernelGGL(encode_fixup_kernel, dim3(f.n_blocks), dim3(kFixTiles), 0, s, f);
     }
     hipLaunchKernelGGL(encode_finalize_kernel, dim3(1), dim3(64), 0, s, counter, mode, base_version, new_version,

@@ -364,10 +364,11 @@ void dcr_plan_destroy(dcr_plan* p) { delete p; }
 const char* dcr_last_error(void) { return dcr::g_err.c_str(); }
 
 uint32_t dcr_format_constants(uint32_t* out, uint32_t n) {
-    const uint32_t v[8] = {DCR_MAGIC, DCR_FORMAT_VERSION, DCR_CHUNK_BYTES, DCR_HEADER_BYTES, DCR_DIRENT_BYTES,
-                           uint32_t(sizeof(dcr_tensor_desc)), uint32_t(sizeof(dcr_segment)),
-                           uint32_t(sizeof(dcr_stream_header))};
-    uint32_t k = n < 8 ? n : 8;
+    const uint32_t v[10] = {DCR_MAGIC, DCR_FORMAT_VERSION, DCR_CHUNK_BYTES, DCR_HEADER_BYTES, DCR_DIRENT_BYTES,
+                            uint32_t(sizeof(dcr_tensor_desc)), uint32_t(sizeof(dcr_segment)),
+                            uint32_t(sizeof(dcr_stream_header)), uint32_t(DCR_ENC_INDEX_LISTS),
+                            uint32_t(DCR_LAYOUT_LIST)};
+    uint32_t k = n < 10 ? n : 10;
     for (uint32_t i = 0; i < k && out; i++) out[i] = v[i];
     return k;
 }

@@ -23,6 +23,8 @@ DCR_OK, DCR_E_INVAL, DCR_E_COVERAGE, DCR_E_FORMAT, DCR_E_VERSION, DCR_E_CAPACITY
     0, -1, -2, -3, -4, -5, -6, -7
 ROUTE_AFFINE_XOR, ROUTE_OVERWRITE, ROUTE_BLOCK_SCALED = 0, 1, 2
 MODE_DELTA, MODE_RETRY = 0, 1
+ENC_INDEX_LISTS = 0x100            # encode option: index-list layout for low-density records
+LAYOUT_BITMAP, LAYOUT_LIST = 0, 1  # directory entry byte 15
 
 # binary layouts of the C structs (include/dcr.h)
 TENSOR_DESC = np.dtype([("numel", "<u8"), ("elem_bytes", "<u4"), ("route", "<u4"),
@@ -219,8 +221,8 @@ def dcr_set_kernel_events(start=None, stop=None) -> None:
 
 
 def format_constants():
-    out = (ctypes.c_uint32 * 8)()
-    n = load_library().dcr_format_constants(out, 8)
+    out = (ctypes.c_uint32 * 10)()
+    n = load_library().dcr_format_constants(out, 10)
     return list(out)[:n]
 
 

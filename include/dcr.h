@@ -28,6 +28,11 @@
  * bytes with a presence bitmap when that is strictly smaller (SPARSE), keep
  * all high bytes otherwise (DENSE) or none when all are zero (NONE).  A
  * 64-byte stream header and 32-byte directory entries describe the stream.
+ * Encoded with DCR_ENC_INDEX_LISTS, a record whose K changes take fewer bytes
+ * as 16-bit element indices (padded) than as its padded bitmap carries the
+ * ascending indices in the bitmap's place, marked in byte 15 of its directory
+ * entry (DCR_LAYOUT_LIST); the mask stream is sparse and worth compressing
+ * (ai-feeds "key modules" 3).
  *
  * Conventions
  *   - All integers little-endian.  All status codes: 0 = DCR_OK, < 0 = error.
@@ -67,6 +72,11 @@ enum {
 };
 enum { DCR_ROUTE_AFFINE_XOR = 0, DCR_ROUTE_OVERWRITE = 1, DCR_ROUTE_BLOCK_SCALED = 2 };
 enum { DCR_MODE_DELTA = 0, DCR_MODE_RETRY = 1 };
+/* encode option, OR-ed into dcr_encode's mode: index-list layout for records
+ * where it is smaller than the bitmap (the stream kind stays mode & 0xFF) */
+enum { DCR_ENC_INDEX_LISTS = 0x100 };
+/* record layouts (byte 15 of a directory entry) */
+enum { DCR_LAYOUT_BITMAP = 0, DCR_LAYOUT_LIST = 1 };
 enum { DCR_KIND_XOR = 0, DCR_KIND_OW = 1 };
 enum { DCR_HI_NONE = 0, DCR_HI_SPARSE = 1, DCR_HI_DENSE = 2 };
 #define DCR_MAGIC 0x31524344u          /* "DCR1" */
@@ -190,7 +200,9 @@ void dcr_plan_destroy(dcr_plan* plan);
  *                  trainer shards of the committed base and of the new step
  *   mode           DCR_MODE_DELTA: XOR / overwrite records by route;
  *                  DCR_MODE_RETRY: one overwrite record per changed chunk
- *                  carrying the new stored bits of every changed element
+ *                  carrying the new stored bits of every changed element;
+ *                  either OR DCR_ENC_INDEX_LISTS: low-density records in the
+ *                  index-list layout (default: every record carries a bitmap)
  *   base_version, new_version  written to the header (version binding)
  *   header_dev     64 bytes of device memory for the stream header
  *   dir_dev, dir_cap           directory buffer and its size in bytes
@@ -293,8 +305,9 @@ void dcr_set_kernel_events(void* start, void* stop);
 const char* dcr_last_error(void);
 
 /* Format constants as this library defines them, for cross-checks:
- * out[0..7] = magic, format version, chunk bytes, header bytes, dirent bytes,
- * sizeof(dcr_tensor_desc), sizeof(dcr_segment), sizeof(dcr_stream_header).
+ * out[0..9] = magic, format version, chunk bytes, header bytes, dirent bytes,
+ * sizeof(dcr_tensor_desc), sizeof(dcr_segment), sizeof(dcr_stream_header),
+ * DCR_ENC_INDEX_LISTS, DCR_LAYOUT_LIST.
  * Returns the number written (at most n). */
 uint32_t dcr_format_constants(uint32_t* out, uint32_t n);
 

@@ -32,7 +32,7 @@ def test_format_constants_agree_with_oracle():
     from oracle import oracle as O
     c = dcr.format_constants()
     assert c == [0x31524344, 1, O.CHUNK_BYTES, O.HEADER_BYTES, O.DIRENT_BYTES,
-                 O.ORC_TENSOR.itemsize, O.ORC_SEGMENT.itemsize, 64]
+                 O.ORC_TENSOR.itemsize, O.ORC_SEGMENT.itemsize, 64, O.ENC_LISTS, O.LAYOUT_LIST]
     assert dcr.TENSOR_DESC == O.ORC_TENSOR or dcr.TENSOR_DESC.descr == O.ORC_TENSOR.descr
     assert dcr.SEGMENT.itemsize == O.ORC_SEGMENT.itemsize
 

@@ -268,6 +268,77 @@ def test_retry_partial_refused(gh):
     assert int(psb.result_host()["status"]) == dcr.DCR_E_FORMAT
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_index_lists_parity(gh, orc, seed):
+    """Index-list layout (encode option): DELTA and RETRY streams equal the
+    oracle's byte for byte with every staging mode, at change rates that put
+    list records in one LDS window and across several; applying them gives
+    new, from old and from a kill at 50 % through the RETRY stream."""
+    rate = [0.002, 0.03, 0.05, 0.2][seed % 4]
+    say("index lists", seed, rate)
+    lay = synth.random_layout(1300 + seed, rate=rate, max_tensors=5, max_chunks=6.0)
+    olds, news, co, cn = pins.canon_lists(lay)
+    g = gh.Gpu(lay, olds, news)
+    streams = {}
+    for mode in (0, 1):
+        rc, eh, ed, ep = orc.encode(lay.tensors, lay.segments, olds, news, mode=mode | 0x100,
+                                    base_version=7, new_version=8)
+        assert rc == 0
+        for stage in stage_sizes(g):
+            sb = g.encode(mode | dcr.ENC_INDEX_LISTS, stage=stage)
+            assert_same_stream(g.stream_host(sb), (eh, ed, ep), f"lists seed {seed} mode {mode} stage {stage}")
+        streams[mode] = sb
+    hdr, d, _p = g.stream_host(streams[0])
+    n = len(d) // 32
+    buf, canon = g.canon_alloc(co)
+    flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+    r = g.apply(canon, hdr, streams[0], flags)
+    assert int(r["n_applied"]) == n and int(r["n_invalid"]) == 0
+    got = gh.host(canon)
+    for t in range(lay.n_tensors):
+        assert np.array_equal(got[t], cn[t]), (seed, t)
+    buf, canon = g.canon_alloc(co)
+    flags.zero_()
+    g.apply(canon, hdr, streams[0], flags, 0, n // 2)
+    rh = g.stream_host(streams[1])[0]
+    r = g.retry(canon, rh, streams[1])
+    assert int(r["n_invalid"]) == 0
+    got = gh.host(canon)
+    for t in range(lay.n_tensors):
+        assert np.array_equal(got[t], cn[t]), (seed, t)
+
+
+def test_index_lists_corrupt_refused(gh):
+    """A list record whose indices do not ascend strictly (two swapped, or
+    one repeated) is refused before any write."""
+    say("index lists corrupt")
+    lay = synth.random_layout(1301, rate=0.03, max_tensors=5, max_chunks=6.0)
+    olds, news, co, cn = pins.canon_lists(lay)
+    g = gh.Gpu(lay, olds, news)
+    sb = g.encode(dcr.ENC_INDEX_LISTS)
+    hdr, d, p = g.stream_host(sb)
+    ents = fmt.dirents(d)
+    li = [i for i, e in enumerate(ents) if e["layout"] == 1 and e["K"] >= 2]
+    assert li
+    e = ents[li[0]]
+    for how in ("swap", "repeat"):
+        bad = sb.payload.clone()
+        o = e["off"]
+        if how == "swap":
+            bad[o:o + 2], bad[o + 2:o + 4] = sb.payload[o + 2:o + 4].clone(), sb.payload[o:o + 2].clone()
+        else:
+            last = o + 2 * (e["K"] - 1)
+            bad[last:last + 2] = sb.payload[last - 2:last].clone()
+        bsb = type("S", (), {"dir": sb.dir, "payload": bad})()
+        buf, canon = g.canon_alloc(co)
+        flags = torch.zeros(len(ents), dtype=torch.uint8, device="cuda")
+        r = g.apply(canon, hdr, bsb, flags, li[0], 1)
+        assert int(r["n_invalid"]) == 1 and int(r["first_invalid"]) == li[0], how
+        got = gh.host(canon)
+        for t in range(lay.n_tensors):
+            assert np.array_equal(got[t], co[t]), how
+
+
 def test_capacity_overflow(gh, orc):
     """Too-small buffers: status DCR_E_CAPACITY with the required sizes."""
     say("capacity overflow")
