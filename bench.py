@@ -263,6 +263,44 @@ def main():
                      "healed_eq_new": bool(ok_partial)}
     log(f"partial retry at a 50 % kill: {partial_retry}")
 
+    # index-list layout (encode option, outside the step): the same DELTA
+    # change set with low-density records carrying 16-bit indices instead of
+    # the bitmap; encoded into the retry buffers, applied to old, checked
+    canon_o = lay.assemble(as_i16(olds))
+    le, la = [], []
+    for _ in range(3):
+        a_, b_ = pair()
+        a_.record()
+        dcr.dcr_encode(plan, olds, news, dcr.MODE_DELTA | dcr.ENC_INDEX_LISTS, 41, 42, retry.header, retry.dir,
+                       retry.payload, retry.result, ws)
+        b_.record()
+        torch.cuda.synchronize()
+        le.append(a_.elapsed_time(b_))
+    lr = retry.result_host()
+    lh = retry.header_host()
+    ln = int(lr["n_records"])
+    lflags = torch.zeros(max(ln, 1), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        for t in range(len(T)):
+            canon[t].view(torch.int16).copy_(canon_o[t].reshape(-1))
+        lflags.zero_()
+        torch.cuda.synchronize()
+        a_, b_ = pair()
+        a_.record()
+        dcr.dcr_apply(plan, canon, lh, retry.dir, retry.payload, lflags, 0, ln, 41, ares, ws)
+        b_.record()
+        torch.cuda.synchronize()
+        la.append(a_.elapsed_time(b_))
+    del canon_o
+    canon_new = lay.assemble(as_i16(news))
+    ok_lists = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
+    del canon_new
+    index_lists = {"status": int(lr["status"]), "records": ln, "payload_GB": round(int(lr["payload_bytes"]) / 1e9, 4),
+                   "bitmap_payload_GB": round(p_bytes / 1e9, 4), "encode_ms": round(float(np.median(le)), 4),
+                   "bitmap_encode_ms": round(op_ms["encode"], 4), "apply_ms": round(float(np.median(la)), 4),
+                   "bitmap_apply_ms": round(op_ms["apply"], 4), "apply_eq_new": bool(ok_lists)}
+    log(f"index-list layout: {index_lists}")
+
     enc_bytes = 2 * cb + 32 * n_rec + p_bytes
     renc_bytes = 2 * cb + 32 * rn_rec + rp_bytes
     app_bytes = 32 * n_rec + p_bytes + LINE * touched + SECTOR * touched_sec
@@ -328,6 +366,7 @@ def main():
         "checks": {"apply_eq_new": bool(ok_apply), "retry_eq_new": bool(ok_retry),
                    "after_timing_eq_new": bool(ok_after), "oracle_sample": parity_sample},
         "partial_retry": partial_retry,
+        "index_lists": index_lists,
         "roofline": roof,
         "ceiling": ceiling,
         "cpu_baseline": cpu,
