@@ -91,6 +91,7 @@ struct Plan {
     std::vector<uint32_t> direct[3];      // direct chunks of 1-, 2-, 4-byte elements
     uint64_t fingerprint = 0;
     uint64_t canonical_bytes = 0;
+    bool shard_disjoint = true;           // no shard element holds two canonical elements
     uint64_t scale_bits = 0;              // total flag bits (multiple of 64)
     uint64_t max_dir_bytes = 0, max_payload_bytes = 0;
     // device table layout

@@ -1150,6 +1150,12 @@ struct ApplyArgs {
     uint64_t first;
     uint32_t n_tensors;
     uint32_t retry;          // 1: overwrite retry (ignore flags, OW records only)
+    // receiver layout: the records' chunks are written into shards through
+    // the plan's pieces instead of into canonical tensors
+    const DevChunk* rchunks;
+    const DevPiece* rpieces;
+    uint8_t* const* rshards;
+    uint32_t sharded;
 };
 
 struct ApplyShared {
@@ -1160,6 +1166,11 @@ struct ApplyShared {
     uint32_t state;                 // 0 invalid, 1 skip, 2 apply
     uint32_t n_c;                   // elements of the record's chunk
     uint32_t bad;                   // content check failed
+    // receiver layout: the chunk's pieces (direct chunks: start element and
+    // address of each piece, in LDS)
+    uint32_t mfirst, mnp, mdirect;
+    uint32_t mstart[kMaxCachedPieces];
+    uint64_t maddr[kMaxCachedPieces];
 };
 
 __device__ __forceinline__ uint32_t rec_bytes(uint32_t n_c, uint32_t w, uint32_t kind, uint32_t K, uint32_t hm,
@@ -1206,6 +1217,58 @@ __device__ __forceinline__ bool entry_ok(const ApplyArgs& a, const uint32_t (&e)
     return true;
 }
 
+// Receiver layout, thread 0: the record's chunk in the receiver plan.
+template <class Sh>
+__device__ __forceinline__ void map_chunk(const ApplyArgs& a, Sh& S, uint32_t t, uint32_t c) {
+    if (!a.sharded) return;
+    const DevChunk ch = a.rchunks[a.tensors[t].first_chunk + c];
+    S.mfirst = ch.first_piece;
+    S.mnp = ch.n_pieces & kPiecesMask;
+    S.mdirect = (ch.n_pieces & kChunkDirect) ? 1u : 0u;
+}
+
+// Receiver layout, all threads before a barrier: a direct chunk's piece
+// table in LDS.
+template <int W, class Sh>
+__device__ __forceinline__ void map_table(const ApplyArgs& a, Sh& S) {
+    if (!a.sharded || !S.mdirect || threadIdx.x >= S.mnp) return;
+    const DevPiece p = a.rpieces[S.mfirst + threadIdx.x];
+    S.mstart[threadIdx.x] = p.canon_start;
+    S.maddr[threadIdx.x] = reinterpret_cast<uint64_t>(a.rshards[p.shard]) + p.shard_elem_off * W;
+}
+
+// Address of the 16-byte group starting at chunk element e0: in the
+// canonical chunk at dst, or in a direct receiver chunk (every group inside
+// one piece, 16-byte aligned); NULL for other receiver chunks, whose
+// elements are mapped one by one.
+template <int W, class Sh>
+__device__ __forceinline__ uint8_t* group_ptr(const ApplyArgs& a, const Sh& S, uint8_t* dst, uint32_t e0) {
+    if (!a.sharded) return dst + uint64_t(e0) * W;
+    if (!S.mdirect) return nullptr;
+    uint32_t l = 0, h = S.mnp;
+    while (h - l > 1) {
+        const uint32_t m = (l + h) >> 1;
+        if (S.mstart[m] <= e0) l = m;
+        else h = m;
+    }
+    return reinterpret_cast<uint8_t*>(S.maddr[l] + uint64_t(e0 - S.mstart[l]) * W);
+}
+
+// Address of chunk element e of a receiver chunk (its pieces in global
+// memory, found by binary search on their first element).
+template <int W, class Sh>
+__device__ __forceinline__ uint8_t* elem_ptr(const ApplyArgs& a, const Sh& S, uint32_t e) {
+    const DevPiece* pc = a.rpieces + S.mfirst;
+    uint32_t l = 0, h = S.mnp;
+    while (h - l > 1) {
+        const uint32_t m = (l + h) >> 1;
+        if (pc[m].canon_start <= e) l = m;
+        else h = m;
+    }
+    const DevPiece p = pc[l];
+    return a.rshards[p.shard] + (p.shard_elem_off + (e - p.canon_start)) * W;
+}
+
 template <int W>
 __device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uint32_t n_c) {
     constexpr uint32_t V = 16 / W;
@@ -1224,6 +1287,7 @@ __device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uin
     const uint4* src = reinterpret_cast<const uint4*>(a.payload + off);
     for (uint32_t q = tid; q < sz / 16; q += kThreads) reinterpret_cast<uint4*>(S.stage)[q] = src[q];
     if (tid == 0) S.bad = 0;
+    map_table<W>(a, S);
     __syncthreads();
 
     // bitmap bits per 16-byte group; nothing may be set at or past n_c
@@ -1276,7 +1340,7 @@ __device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uin
 
     // read-modify-write of every touched 16-byte group; the group's new words
     // are assembled in two 64-bit values by a set-bit loop with dynamic shifts
-    uint8_t* dst = a.canon[t] + uint64_t(c) * E * W;
+    uint8_t* dst = a.sharded ? nullptr : a.canon[t] + uint64_t(c) * E * W;
     const uint32_t* pw32 = reinterpret_cast<const uint32_t*>(S.stage + pres);
     const uint32_t pk = dpad16(K);
     const bool is_xor = kind == DCR_KIND_XOR;
@@ -1315,8 +1379,8 @@ __device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uin
             else { val1 |= uint64_t(v) << sh; msk1 |= EM << sh; }
             j++;
         }
-        uint8_t* gp = dst + uint64_t(g) * 16;
-        if ((g + 1) * V <= n_c) {
+        uint8_t* gp = group_ptr<W>(a, S, dst, g * V);
+        if (gp && (g + 1) * V <= n_c) {
             v4u w4 = *reinterpret_cast<const v4u*>(gp);
             uint64_t q0 = uint64_t(w4.x) | (uint64_t(w4.y) << 32);
             uint64_t q1 = uint64_t(w4.z) | (uint64_t(w4.w) << 32);
@@ -1326,7 +1390,7 @@ __device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uin
             r4.x = uint32_t(q0); r4.y = uint32_t(q0 >> 32); r4.z = uint32_t(q1); r4.w = uint32_t(q1 >> 32);
             *reinterpret_cast<v4u*>(gp) = r4;
         } else {
-            // tail group of a tensor: element accesses only inside the tensor
+            // tail group of a tensor, or a receiver chunk whose groups are not whole in one piece: element accesses only, inside the tensor
             uint32_t bb = bcopy;
             while (bb) {
                 const uint32_t i = uint32_t(__ffs(bb) - 1);
@@ -1334,12 +1398,13 @@ __device__ void apply_record(const ApplyArgs& a, ApplyShared& S, uint64_t r, uin
                 if (g * V + i >= n_c) break;
                 const uint32_t bitpos = i * 8 * W;
                 const uint32_t v = uint32_t(((bitpos < 64) ? val0 : val1) >> (bitpos & 63));
-                if constexpr (W == 1) { gp[i] = is_xor ? uint8_t(gp[i] ^ v) : uint8_t(v); }
+                uint8_t* ep = gp ? gp + i * W : elem_ptr<W>(a, S, g * V + i);
+                if constexpr (W == 1) { *ep = is_xor ? uint8_t(*ep ^ v) : uint8_t(v); }
                 else if constexpr (W == 2) {
-                    uint16_t* p = reinterpret_cast<uint16_t*>(gp) + i;
+                    uint16_t* p = reinterpret_cast<uint16_t*>(ep);
                     *p = is_xor ? uint16_t(*p ^ v) : uint16_t(v);
                 } else {
-                    uint32_t* p = reinterpret_cast<uint32_t*>(gp) + i;
+                    uint32_t* p = reinterpret_cast<uint32_t*>(ep);
                     *p = is_xor ? (*p ^ v) : v;
                 }
             }
@@ -1370,6 +1435,7 @@ __device__ __forceinline__ void apply_one(const ApplyArgs& a, ApplyShared& S, ui
         if (!entry_ok(a, e, n_c) || (e[3] >> 24) != DCR_LAYOUT_BITMAP) st = 0;
         else if (!a.retry && a.flags[r]) st = 1;
         else st = 2;
+        if (st == 2) map_chunk(a, S, e[0], e[1]);
         S.state = st;
         S.n_c = n_c;
     }
@@ -1424,6 +1490,9 @@ struct SmallShared {
     uint32_t state;                     // 0 invalid, 1 skip, 2 apply, 3 deferred
     uint32_t n_c;
     uint32_t bad;
+    uint32_t mfirst, mnp, mdirect;      // receiver layout (as in ApplyShared)
+    uint32_t mstart[kMaxCachedPieces];
+    uint64_t maddr[kMaxCachedPieces];
 };
 
 // Exclusive scan of one value per thread over a kSmallThreads workgroup.
@@ -1467,6 +1536,7 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     const uint4* src = reinterpret_cast<const uint4*>(a.payload + off);
     for (uint32_t q = tid; q < sz / 16; q += kSmallThreads) reinterpret_cast<uint4*>(S.stage)[q] = src[q];
     if (tid == 0) S.bad = 0;
+    map_table<W>(a, S);
     __syncthreads();
 
     // this thread's bitmap words (bytes at or past bm are other sections: 0);
@@ -1549,7 +1619,7 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     if (S.bad) return;   // refused before any write
 
     // read-modify-write of every touched 16-byte group, in element order
-    uint8_t* dst = a.canon[t] + uint64_t(c) * E * W;
+    uint8_t* dst = a.sharded ? nullptr : a.canon[t] + uint64_t(c) * E * W;
     const uint32_t* pw32 = reinterpret_cast<const uint32_t*>(S.stage + pres);
     const uint32_t pk = dpad16(K);
     const bool is_xor = kind == DCR_KIND_XOR;
@@ -1590,8 +1660,8 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
                 else { val1 |= uint64_t(v) << sh; msk1 |= EM << sh; }
                 j++;
             }
-            uint8_t* gp = dst + uint64_t(g) * 16;
-            if ((g + 1) * V <= n_c) {
+            uint8_t* gp = group_ptr<W>(a, S, dst, g * V);
+            if (gp && (g + 1) * V <= n_c) {
                 v4u w4 = *reinterpret_cast<const v4u*>(gp);
                 uint64_t q0 = uint64_t(w4.x) | (uint64_t(w4.y) << 32);
                 uint64_t q1 = uint64_t(w4.z) | (uint64_t(w4.w) << 32);
@@ -1601,7 +1671,7 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
                 r4.x = uint32_t(q0); r4.y = uint32_t(q0 >> 32); r4.z = uint32_t(q1); r4.w = uint32_t(q1 >> 32);
                 *reinterpret_cast<v4u*>(gp) = r4;
             } else {
-                // tail group of a tensor: element accesses only inside the tensor
+                // tail group of a tensor, or a receiver chunk whose groups are not whole in one piece: element accesses only, inside the tensor
                 uint32_t bb = bcopy;
                 while (bb) {
                     const uint32_t i = uint32_t(__ffs(bb) - 1);
@@ -1609,12 +1679,13 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
                     if (g * V + i >= n_c) break;
                     const uint32_t bitpos = i * 8 * W;
                     const uint32_t v = uint32_t(((bitpos < 64) ? val0 : val1) >> (bitpos & 63));
-                    if constexpr (W == 1) { gp[i] = is_xor ? uint8_t(gp[i] ^ v) : uint8_t(v); }
+                    uint8_t* ep = gp ? gp + i * W : elem_ptr<W>(a, S, g * V + i);
+                    if constexpr (W == 1) { *ep = is_xor ? uint8_t(*ep ^ v) : uint8_t(v); }
                     else if constexpr (W == 2) {
-                        uint16_t* p = reinterpret_cast<uint16_t*>(gp) + i;
+                        uint16_t* p = reinterpret_cast<uint16_t*>(ep);
                         *p = is_xor ? uint16_t(*p ^ v) : uint16_t(v);
                     } else {
-                        uint32_t* p = reinterpret_cast<uint32_t*>(gp) + i;
+                        uint32_t* p = reinterpret_cast<uint32_t*>(ep);
                         *p = is_xor ? (*p ^ v) : v;
                     }
                 }
@@ -1644,6 +1715,7 @@ __global__ __launch_bounds__(kSmallThreads) void apply_small_kernel(ApplyArgs a)
             const bool fits = e[6] <= kSmallStage && (hm != DCR_HI_SPARSE || dpad16((K + 7) / 8) / 4 <= kSmallThreads);
             st = fits ? 2 : 3;
             if (!fits) a.big_list[atomicAdd(a.big_count, 1u)] = uint32_t(r - a.first);
+            else map_chunk(a, S, e[0], e[1]);
         }
         S.state = st;
         S.n_c = n_c;
@@ -1736,23 +1808,39 @@ static int32_t check_header(const Plan& p, const dcr_stream_header* h, uint64_t 
     return DCR_OK;
 }
 
+// canon: one pointer per canonical tensor, or with `sharded` one per shard
+// of the plan (a receiver layout: records go through the plan's pieces).
 static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_stream_header* hdr,
                             const void* dir, const void* payload, uint8_t* flags, uint64_t first, uint64_t n,
-                            dcr_apply_result* res, void* ws, uint64_t ws_bytes, hipStream_t s, bool retry) {
+                            dcr_apply_result* res, void* ws, uint64_t ws_bytes, hipStream_t s, bool retry,
+                            bool sharded = false) {
     const Plan& p = *plan;
     const uint32_t nT = uint32_t(p.tensors.size());
+    const uint32_t nS = uint32_t(p.shard_bytes.size());
     if ((n && !dir) || (n && !payload) || !res || !ws) return fail(DCR_E_INVAL, "NULL device buffer");
     if (!al16(dir) || !al16(payload) || !al16(res) || !al16(ws)) return fail(DCR_E_INVAL, "buffer not 16-byte aligned");
     if (!retry && n && !flags) return fail(DCR_E_INVAL, "applied_flags is NULL");
     if (ws_bytes < p.ws_bytes) return fail(DCR_E_CAPACITY, "workspace too small");
     if (n > 0x7FFFFFFFull) return fail(DCR_E_INVAL, "too many records in one call");
-    if (nT && !canon) return fail(DCR_E_INVAL, "canon is NULL");
-    for (uint32_t t = 0; t < nT; t++) {
-        if (p.tensors[t].numel && !canon[t]) return fail(DCR_E_INVAL, "canonical tensor " + std::to_string(t) + " is NULL");
-        if (!al16(canon[t])) return fail(DCR_E_INVAL, "canonical tensor " + std::to_string(t) + " not 16-byte aligned");
-    }
     uint8_t* wsb = static_cast<uint8_t*>(ws);
-    int32_t rc = copy_ptrs(wsb + p.ws_canon, reinterpret_cast<const void* const*>(canon), nT, s);
+    int32_t rc;
+    if (sharded) {
+        if (!p.shard_disjoint)
+            return fail(DCR_E_INVAL, "receiver layout maps two canonical elements to one shard element");
+        if (nS && !canon) return fail(DCR_E_INVAL, "shards is NULL");
+        for (uint32_t i = 0; i < nS; i++) {
+            if (p.shard_bytes[i] && !canon[i]) return fail(DCR_E_INVAL, "shard " + std::to_string(i) + " is NULL");
+            if (!al16(canon[i])) return fail(DCR_E_INVAL, "shard " + std::to_string(i) + " not 16-byte aligned");
+        }
+        rc = copy_ptrs(wsb + p.ws_old, reinterpret_cast<const void* const*>(canon), nS, s);
+    } else {
+        if (nT && !canon) return fail(DCR_E_INVAL, "canon is NULL");
+        for (uint32_t t = 0; t < nT; t++) {
+            if (p.tensors[t].numel && !canon[t]) return fail(DCR_E_INVAL, "canonical tensor " + std::to_string(t) + " is NULL");
+            if (!al16(canon[t])) return fail(DCR_E_INVAL, "canonical tensor " + std::to_string(t) + " not 16-byte aligned");
+        }
+        rc = copy_ptrs(wsb + p.ws_canon, reinterpret_cast<const void* const*>(canon), nT, s);
+    }
     if (rc) return rc;
     uint32_t* big_count = reinterpret_cast<uint32_t*>(wsb + p.ws_counter) + kCtrBig;
     hipLaunchKernelGGL(apply_init_kernel, dim3(1), dim3(64), 0, s, res, big_count);
@@ -1770,6 +1858,10 @@ static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_
         a.first = first;
         a.n_tensors = nT;
         a.retry = retry ? 1u : 0u;
+        a.sharded = sharded ? 1u : 0u;
+        a.rchunks = tab<DevChunk>(p, p.off_chunks);
+        a.rpieces = tab<DevPiece>(p, p.off_pieces);
+        a.rshards = reinterpret_cast<uint8_t* const*>(wsb + p.ws_old);
         mark(true, s);
         if (n <= p.big_cap) {
             // small records with many per compute unit; the rest deferred
@@ -2006,6 +2098,38 @@ int32_t dcr_apply_overwrite_retry(const dcr_plan* plan, void* const* canon, cons
     if (header->stream_kind != DCR_MODE_RETRY) return fail(DCR_E_FORMAT, "not a RETRY stream");
     return launch_apply(plan, canon, header, dir_dev, payload_dev, nullptr, 0, header->n_records, result_dev,
                         workspace_dev, ws_bytes, static_cast<hipStream_t>(stream), true);
+}
+
+int32_t dcr_apply_sharded(const dcr_plan* plan, void* const* shards, const dcr_stream_header* header,
+                          const void* dir_dev, const void* payload_dev, uint8_t* applied_flags_dev,
+                          uint64_t first_record, uint64_t n_records, uint64_t expected_base_version,
+                          dcr_apply_result* result_dev, void* workspace_dev, uint64_t ws_bytes, void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
+    if (!plan->dev_tables) return fail(DCR_E_INVAL, "plan not uploaded");
+    int32_t rc = check_header(*plan, header, expected_base_version);
+    if (rc) return rc;
+    if (first_record > header->n_records || n_records > header->n_records - first_record)
+        return fail(DCR_E_INVAL, "record range outside the stream");
+    return launch_apply(plan, shards, header, dir_dev, payload_dev, applied_flags_dev, first_record, n_records,
+                        result_dev, workspace_dev, ws_bytes, static_cast<hipStream_t>(stream), false, true);
+}
+
+int32_t dcr_apply_overwrite_retry_sharded(const dcr_plan* plan, void* const* shards,
+                                          const dcr_stream_header* header, const void* dir_dev,
+                                          const void* payload_dev, uint64_t expected_base_version,
+                                          dcr_apply_result* result_dev, void* workspace_dev, uint64_t ws_bytes,
+                                          void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
+    if (!plan->dev_tables) return fail(DCR_E_INVAL, "plan not uploaded");
+    int32_t rc = check_header(*plan, header, expected_base_version);
+    if (rc) return rc;
+    if (header->stream_kind != DCR_MODE_RETRY) return fail(DCR_E_FORMAT, "not a RETRY stream");
+    return launch_apply(plan, shards, header, dir_dev, payload_dev, nullptr, 0, header->n_records, result_dev,
+                        workspace_dev, ws_bytes, static_cast<hipStream_t>(stream), true, true);
 }
 
 }  // extern "C"

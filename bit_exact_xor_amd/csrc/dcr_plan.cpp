@@ -260,6 +260,28 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     for (uint32_t t = 0; t < nT; t++)
         if (T[t].route == DCR_ROUTE_BLOCK_SCALED) P.dt[t].scale_bit_off = bit_off[T[t].scale_tensor];
     P.fingerprint = fnv1a64(T, nT);
+    // does any shard element hold two canonical elements?  (harmless for a
+    // sender, which only reads; a receiver layout must not)
+    {
+        struct ByteRun { uint32_t shard; uint64_t off, len; };   // in bytes
+        std::vector<ByteRun> runs_s;
+        runs_s.reserve(P.pieces.size());
+        for (const DevChunk& ch : P.chunks) {
+            const uint64_t w = P.dt[ch.tensor].w;
+            const uint32_t np = ch.n_pieces & kPiecesMask;
+            for (uint32_t i = 0; i < np; i++) {
+                const DevPiece& pc = P.pieces[ch.first_piece + i];
+                runs_s.push_back({pc.shard, pc.shard_elem_off * w, (uint64_t(pc.len_m1) + 1) * w});
+            }
+        }
+        std::sort(runs_s.begin(), runs_s.end(), [](const ByteRun& x, const ByteRun& y) {
+            return x.shard != y.shard ? x.shard < y.shard : x.off < y.off;
+        });
+        P.shard_disjoint = true;
+        for (size_t i = 1; i < runs_s.size() && P.shard_disjoint; i++)
+            if (runs_s[i].shard == runs_s[i - 1].shard && runs_s[i - 1].off + runs_s[i - 1].len > runs_s[i].off)
+                P.shard_disjoint = false;
+    }
 
     // device tables: tensors | chunks | pieces | scale chunk list
     P.off_tensors = 0;

@@ -6,8 +6,9 @@ device pointers and the current torch stream into a hipStream_t, and raises
 ``DcrError`` on a nonzero status.  PyTorch provides device memory and streams.
 
 The names follow the C-ABI: ``dcr_plan_build``, ``dcr_encode``,
-``dcr_encode_retry_partial``, ``dcr_apply``, ``dcr_apply_overwrite_retry``
-(plus the small helpers around them).
+``dcr_encode_retry_partial``, ``dcr_apply``, ``dcr_apply_overwrite_retry``,
+``dcr_apply_sharded``, ``dcr_apply_overwrite_retry_sharded`` (plus the small
+helpers around them).
 """
 from __future__ import annotations
 
@@ -83,6 +84,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dcr_encode_retry_partial.argtypes = [P, P, P, P, P, U64, P, U64, U64, P, P, U64, P, U64, P, P, U64, P]
     lib.dcr_apply.restype = I32
     lib.dcr_apply.argtypes = [P, P, P, P, P, P, U64, U64, U64, P, P, U64, P]
+    lib.dcr_apply_sharded.restype = I32
+    lib.dcr_apply_sharded.argtypes = [P, P, P, P, P, P, U64, U64, U64, P, P, U64, P]
+    lib.dcr_apply_overwrite_retry_sharded.restype = I32
+    lib.dcr_apply_overwrite_retry_sharded.argtypes = [P, P, P, P, P, U64, P, P, U64, P]
     lib.dcr_apply_overwrite_retry.restype = I32
     lib.dcr_apply_overwrite_retry.argtypes = [P, P, P, P, P, U64, P, P, U64, P]
     lib.dcr_last_error.restype = ctypes.c_char_p
@@ -208,6 +213,28 @@ def dcr_apply_overwrite_retry(plan: Plan, canon, header: np.ndarray, dir_buf, pa
         plan.handle, _ptr_array([_dptr(t) for t in canon]), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
         expected_base_version, _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_apply_overwrite_retry")
+
+
+def dcr_apply_sharded(plan: Plan, shards, header: np.ndarray, dir_buf, payload, flags, first_record, n_records,
+                      expected_base_version, result, workspace, stream=None) -> None:
+    """Apply records [first, first+n) into a receiver layout: `plan` is the
+    receiver plan, `shards` its device shards."""
+    hdr = np.ascontiguousarray(np.asarray(header, dtype=np.uint8))
+    rc = load_library().dcr_apply_sharded(
+        plan.handle, _ptr_array([_dptr(t) for t in shards]), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
+        _dptr(flags), first_record, n_records, expected_base_version, _dptr(result), _dptr(workspace),
+        _nbytes(workspace), _stream(stream))
+    _check(rc, "dcr_apply_sharded")
+
+
+def dcr_apply_overwrite_retry_sharded(plan: Plan, shards, header: np.ndarray, dir_buf, payload,
+                                      expected_base_version, result, workspace, stream=None) -> None:
+    """Overwrite retry into a receiver layout (see dcr_apply_sharded)."""
+    hdr = np.ascontiguousarray(np.asarray(header, dtype=np.uint8))
+    rc = load_library().dcr_apply_overwrite_retry_sharded(
+        plan.handle, _ptr_array([_dptr(t) for t in shards]), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
+        expected_base_version, _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(rc, "dcr_apply_overwrite_retry_sharded")
 
 
 def dcr_set_kernel_events(start=None, stop=None) -> None:

@@ -455,6 +455,70 @@ def _assemble(recipe, shards, n_tensors):
 CFG1_LR = float(np.uint32(901110982).view(np.float32))  # bisected once, see config1_values
 
 
+def receiver_layout(lay: Layout, seed: int, n_shards_per_width=2) -> Layout:
+    """Another physical layout of the same canonical tensors (same tensor
+    table, hence the same plan fingerprint), as a receiver might store them.
+    Each tensor is, at random: stored whole; cut at random (unaligned) points
+    into contiguous pieces spread over the width's shards; cut into blocks of
+    a random size stored in reverse order; or stored transposed as 2-D
+    [rows, cols] for a random divisor cols of its size.  Every placement
+    starts after a random gap of 0-9 elements, which no segment covers.  The
+    layout carries no generated contents (regions)."""
+    rng = np.random.default_rng(seed)
+    b = _Builder(f"{lay.name}.recv{seed}", seed)
+    for name, tt in zip(lay.tensor_names, lay.tensors):
+        b.tensor(name, int(tt["numel"]), int(tt["elem_bytes"]), int(tt["route"]), int(tt["scale_tensor"]),
+                 int(tt["scale_block"]))
+    shards = {}      # width -> shard ids
+    fill = []        # elements used per shard
+
+    def shard_of(w):
+        if w not in shards:
+            shards[w] = []
+            for _ in range(n_shards_per_width):
+                shards[w].append(b.shard(0, w))
+                fill.append(0)
+        return shards[w][int(rng.integers(0, len(shards[w])))]
+
+    def place(s, n):
+        off = fill[s] + int(rng.integers(0, 10))
+        fill[s] = off + n
+        return off
+
+    for t, tt in enumerate(lay.tensors):
+        n, w = int(tt["numel"]), int(tt["elem_bytes"])
+        if n == 0:
+            continue
+        divs = [d for d in (3, 5, 7, 8, 24, 100, 129, 256, 1000, 4096) if n % d == 0 and 1 < d < n]
+        how = rng.choice(["whole", "pieces", "blocks", "transpose"] if divs else ["whole", "pieces", "blocks"])
+        if how == "whole":
+            s = shard_of(w)
+            b.seg(t, s, place(s, n), 0, [n], [1], [1])
+        elif how == "pieces":
+            k = int(rng.integers(2, 6))
+            cuts = sorted(set(int(x) for x in rng.integers(1, n, size=k - 1))) if n > 1 else []
+            bounds = [0] + cuts + [n]
+            for i in range(len(bounds) - 1):
+                e0, e1 = bounds[i], bounds[i + 1]
+                s = shard_of(w)
+                b.seg(t, s, place(s, e1 - e0), e0, [e1 - e0], [1], [1])
+        elif how == "blocks":
+            blk = int(rng.integers(1, 5000))
+            s = shard_of(w)
+            starts = list(range(0, n, blk))[::-1]
+            for e0 in starts:
+                e1 = min(n, e0 + blk)
+                b.seg(t, s, place(s, e1 - e0), e0, [e1 - e0], [1], [1])
+        else:
+            cols = int(rng.choice(divs))
+            rows = n // cols
+            s = shard_of(w)
+            b.seg(t, s, place(s, n), 0, [rows, cols], [1, rows], [cols, 1])
+    for s in range(len(fill)):
+        b.shard_elems[s] = fill[s] + int(rng.integers(0, 10))
+    return b.build(meta={"seed": seed, "receiver_of": lay.name})
+
+
 def random_layout(seed: int, max_tensors=4, max_chunks=3.0, allow_transpose=True,
                   allow_block_scaled=True, rate=None) -> Layout:
     """A small random layout with explicit random contents, for property tests.

@@ -293,6 +293,38 @@ int32_t dcr_apply_overwrite_retry(const dcr_plan* plan, void* const* canon,
                                   dcr_apply_result* result_dev,
                                   void* workspace_dev, uint64_t ws_bytes, void* stream);
 
+/* Apply into a receiver's own layout (receiver side).  The receiver stores the
+ * canonical tensors in shards of its own (its engine's sharding, interleaved
+ * or transposed storage), described by a plan built from its segments over
+ * the same tensor table, so the stream's plan fingerprint matches.  The
+ * records are written straight into those shards through the receiver plan's
+ * pieces; elements of a shard that no segment covers are never touched.
+ * The native loader then needs no reload (ai-feeds summary "key modules" 4:
+ * the receiver applies the delta to its local checkpoint storage).
+ *   plan          the RECEIVER plan (uploaded); DCR_E_INVAL if it maps two
+ *                 canonical elements to one shard element
+ *   shards        host array of its n_shards device pointers (16-byte
+ *                 aligned; NULL only for empty shards)
+ *   the remaining arguments as for dcr_apply.  Chunks whose 16-byte groups
+ *   sit inside one aligned piece get 128-bit read-modify-writes; the others
+ *   are updated element by element. */
+int32_t dcr_apply_sharded(const dcr_plan* plan, void* const* shards,
+                          const dcr_stream_header* header,
+                          const void* dir_dev, const void* payload_dev,
+                          uint8_t* applied_flags_dev,
+                          uint64_t first_record, uint64_t n_records,
+                          uint64_t expected_base_version,
+                          dcr_apply_result* result_dev,
+                          void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* dcr_apply_overwrite_retry into a receiver's own layout, as dcr_apply_sharded. */
+int32_t dcr_apply_overwrite_retry_sharded(const dcr_plan* plan, void* const* shards,
+                                          const dcr_stream_header* header,
+                                          const void* dir_dev, const void* payload_dev,
+                                          uint64_t expected_base_version,
+                                          dcr_apply_result* result_dev,
+                                          void* workspace_dev, uint64_t ws_bytes, void* stream);
+
 /* Benchmark hook.  While set (both non-NULL), every encode, apply or retry
  * call made on this host thread records `start` on its stream just before its
  * main kernel (the encode tile kernel, or the apply kernel) and `stop` just

@@ -339,6 +339,79 @@ def test_index_lists_corrupt_refused(gh):
             assert np.array_equal(got[t], co[t]), how
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_apply_sharded(gh, orc, seed):
+    """Apply into a receiver's own layout (random pieces at unaligned cuts,
+    reversed blocks, transposed storage, gaps between placements): the
+    receiver shards end byte-identical to the new tensors scattered into that
+    layout, gaps untouched, and the oracle's gather of them gives new; also
+    after a kill at 50 % and the overwrite retry into the same layout."""
+    say("apply sharded", seed)
+    lay = synth.random_layout(1400 + seed, max_tensors=5, max_chunks=6.0)
+    lay_r = synth.receiver_layout(lay, 77 + seed)
+    olds, news, co, cn = pins.canon_lists(lay)
+    g = gh.Gpu(lay, olds, news)
+    sb = g.encode(0)
+    hdr, d, _p = g.stream_host(sb)
+    n = len(d) // 32
+    rplan = dcr.dcr_plan_build(lay_r.tensors, [lay_r.shard_bytes(s) for s in range(lay_r.n_shards)],
+                               lay_r.segments)
+    dcr.dcr_plan_upload(rplan, "cuda")
+    ws = dcr.workspace(rplan, "cuda")
+    exp_buf, exp_sh = gh.scatter_shards(lay_r, cn)
+    eh = [x.cpu().numpy() for x in exp_sh]
+    for t in range(lay.n_tensors):   # the scatter is the receiver layout: the oracle's gather reads new back
+        assert np.array_equal(orc.gather(lay_r.tensors, lay_r.segments, eh, t), cn[t]), (seed, t)
+    res = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    rbuf, rsh = gh.scatter_shards(lay_r, co)
+    flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+    dcr.dcr_apply_sharded(rplan, rsh, hdr, sb.dir, sb.payload, flags, 0, n, 7, res, ws)
+    torch.cuda.synchronize()
+    r = dcr.apply_result(res)
+    assert int(r["n_applied"]) == n and int(r["n_invalid"]) == 0
+    assert torch.equal(rbuf, exp_buf), seed
+    # kill at 50 %, then the RETRY stream into the same layout
+    rbuf, rsh = gh.scatter_shards(lay_r, co)
+    flags.zero_()
+    dcr.dcr_apply_sharded(rplan, rsh, hdr, sb.dir, sb.payload, flags, 0, n // 2, 7, res, ws)
+    rsb = g.encode(1)
+    rh = g.stream_host(rsb)[0]
+    dcr.dcr_apply_overwrite_retry_sharded(rplan, rsh, rh, rsb.dir, rsb.payload, 7, res, ws)
+    torch.cuda.synchronize()
+    assert int(dcr.apply_result(res)["n_invalid"]) == 0
+    assert torch.equal(rbuf, exp_buf), seed
+
+
+def test_apply_sharded_refuses_overlapping_layout(gh):
+    """A receiver layout that maps two canonical elements to one shard
+    element cannot be applied into."""
+    say("apply sharded, overlapping layout")
+    lay = synth.random_layout(1401, max_tensors=5, max_chunks=6.0)
+    T = lay.tensors[:1].copy()
+    n = int(T[0]["numel"])
+    assert n >= 2
+    S = np.zeros(2, dtype=synth.SEGMENT_DT)
+    for i, (c0, c1) in enumerate(((0, n // 2), (n // 2, n))):
+        S[i]["tensor_id"], S[i]["shard_id"], S[i]["ndim"] = 0, 0, 1
+        S[i]["shard_off"], S[i]["canon_off"] = 0, c0          # both halves at shard offset 0
+        S[i]["extent"] = [c1 - c0, 1, 1, 1]
+        S[i]["shard_stride"] = [1, 0, 0, 0]
+        S[i]["canon_stride"] = [1, 0, 0, 0]
+    rplan = dcr.dcr_plan_build(T, [n * int(T[0]["elem_bytes"])], S)
+    dcr.dcr_plan_upload(rplan, "cuda")
+    shard = torch.zeros(n * int(T[0]["elem_bytes"]), dtype=torch.uint8, device="cuda")
+    hdr = np.zeros(64, dtype=np.uint8)
+    hdr[0:4] = np.frombuffer(np.uint32(0x31524344).tobytes(), np.uint8)
+    hdr[4:6] = np.frombuffer(np.uint16(1).tobytes(), np.uint8)
+    hdr[8:12] = np.frombuffer(np.uint32(65536).tobytes(), np.uint8)
+    hdr[32:40] = np.frombuffer(np.uint64(rplan.info.fingerprint).tobytes(), np.uint8)
+    res = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    flags = torch.zeros(1, dtype=torch.uint8, device="cuda")
+    dbuf = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dcr.DcrError):
+        dcr.dcr_apply_sharded(rplan, [shard], hdr, dbuf, dbuf, flags, 0, 0, 0, res, dcr.workspace(rplan, "cuda"))
+
+
 def test_capacity_overflow(gh, orc):
     """Too-small buffers: status DCR_E_CAPACITY with the required sizes."""
     say("capacity overflow")
