@@ -519,6 +519,29 @@ def receiver_layout(lay: Layout, seed: int, n_shards_per_width=2) -> Layout:
     return b.build(meta={"seed": seed, "receiver_of": lay.name})
 
 
+def scatter_canonical_gpu(lay: Layout, canon, device="cuda", fill=0xA5):
+    """Device shards of layout `lay` holding the canonical tensors `canon`
+    (numpy arrays or device tensors, any element view): every segment is
+    copied with strided views; bytes no segment covers hold `fill`.
+    Returns (buffer, per-shard byte views)."""
+    import torch
+    buf, shards = alloc_shards(lay, device)
+    buf.fill_(fill)
+    dts = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
+    cdev = [c if isinstance(c, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(c)).to(device)
+            for c in canon]
+    for g in lay.segments:
+        t, s, nd = int(g["tensor_id"]), int(g["shard_id"]), int(g["ndim"])
+        dt = dts[int(lay.tensors[t]["elem_bytes"])]
+        sv = shards[s].view(dt)
+        cv = cdev[t].reshape(-1).view(torch.uint8).view(dt)
+        size = [int(x) for x in g["extent"][:nd]]
+        dst = sv.as_strided(size, [int(x) for x in g["shard_stride"][:nd]], sv.storage_offset() + int(g["shard_off"]))
+        src = cv.as_strided(size, [int(x) for x in g["canon_stride"][:nd]], cv.storage_offset() + int(g["canon_off"]))
+        dst.copy_(src)
+    return buf, shards
+
+
 def random_layout(seed: int, max_tensors=4, max_chunks=3.0, allow_transpose=True,
                   allow_block_scaled=True, rate=None) -> Layout:
     """A small random layout with explicit random contents, for property tests.

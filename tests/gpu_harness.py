@@ -90,24 +90,8 @@ class Gpu:
 
 
 def scatter_shards(lay, canon, device="cuda", fill=0xA5):
-    """Receiver shards of layout `lay` holding the canonical tensors `canon`
-    (numpy uint8 arrays or device tensors): every segment copied with strided
-    views; bytes no segment covers hold `fill`."""
-    buf, shards = synth.alloc_shards(lay, device)
-    buf.fill_(fill)
-    dts = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
-    cdev = [c if isinstance(c, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(c)).to(device)
-            for c in canon]
-    for g in lay.segments:
-        t, s, nd = int(g["tensor_id"]), int(g["shard_id"]), int(g["ndim"])
-        dt = dts[int(lay.tensors[t]["elem_bytes"])]
-        sv = shards[s].view(dt)
-        cv = cdev[t].reshape(-1).view(torch.uint8).view(dt)
-        size = [int(x) for x in g["extent"][:nd]]
-        dst = sv.as_strided(size, [int(x) for x in g["shard_stride"][:nd]], sv.storage_offset() + int(g["shard_off"]))
-        src = cv.as_strided(size, [int(x) for x in g["canon_stride"][:nd]], cv.storage_offset() + int(g["canon_off"]))
-        dst.copy_(src)
-    return buf, shards
+    """Receiver shards of layout `lay` holding the canonical tensors `canon`."""
+    return synth.scatter_canonical_gpu(lay, canon, device, fill)
 
 
 def host(views):

@@ -177,6 +177,61 @@ def run_full(orc, lay, sample_names, partial=False):
     torch.cuda.empty_cache()
 
 
+def test_full_llama8b_receiver_tp2(orc):
+    """Config 2 encoded from TP=4 trainer shards, applied straight into a
+    receiver that stores the model as TP=2 engine shards (dcr_apply_sharded):
+    every tensor read back through the receiver layout equals new, also after
+    a kill at 50 % and the overwrite retry into the receiver layout."""
+    from tests import gpu_harness as gh
+    lay = synth.llama_layout()
+    lay_r = synth.llama_layout(tp=2)
+    say("cfg2 -> TP=2 receiver", "plans")
+    T = lay.tensors
+    plan = dcr.dcr_plan_build(T, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
+    dcr.dcr_plan_upload(plan, "cuda")
+    rplan = dcr.dcr_plan_build(lay_r.tensors, [lay_r.shard_bytes(s) for s in range(lay_r.n_shards)], lay_r.segments)
+    dcr.dcr_plan_upload(rplan, "cuda")
+    assert rplan.info.fingerprint == plan.info.fingerprint
+    ob, olds = synth.alloc_shards(lay, "cuda")
+    nb, news = synth.alloc_shards(lay, "cuda")
+    synth.fill_shards_gpu(lay, olds, 0)
+    synth.fill_shards_gpu(lay, news, 1)
+    cb = int(plan.info.canonical_bytes)
+    sb = dcr.StreamBuffers(plan, "cuda", dir_bytes=2 * 32 * int(plan.info.n_chunks),
+                           payload_bytes=int(cb * 0.2) + (1 << 20))
+    rsb = dcr.StreamBuffers(plan, "cuda", dir_bytes=32 * int(plan.info.n_chunks),
+                            payload_bytes=int(cb * 0.2) + (1 << 20))
+    wss = staged_workspace(plan, sb)
+    dcr.dcr_encode(plan, olds, news, 0, 3, 4, sb.header, sb.dir, sb.payload, sb.result, wss)
+    dcr.dcr_encode(plan, olds, news, 1, 3, 4, rsb.header, rsb.dir, rsb.payload, rsb.result, wss)
+    torch.cuda.synchronize()
+    del wss
+    assert int(sb.result_host()["status"]) == 0 and int(rsb.result_host()["status"]) == 0
+    n_rec = sb.n_records()
+    hdr, rhdr = sb.header.cpu().numpy(), rsb.header.cpu().numpy()
+    co = lay.assemble(typed(lay, olds))
+    ws = dcr.workspace(rplan, "cuda")
+    res = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    flags = torch.zeros(max(n_rec, 1), dtype=torch.uint8, device="cuda")
+    for kill in (None, n_rec // 2):
+        say("cfg2 -> TP=2 receiver", "apply" if kill is None else "kill at 50 % + retry")
+        rbuf, rsh = gh.scatter_shards(lay_r, co)
+        flags.zero_()
+        dcr.dcr_apply_sharded(rplan, rsh, hdr, sb.dir, sb.payload, flags, 0, n_rec if kill is None else kill, 3,
+                              res, ws)
+        if kill is not None:
+            dcr.dcr_apply_overwrite_retry_sharded(rplan, rsh, rhdr, rsb.dir, rsb.payload, 3, res, ws)
+        torch.cuda.synchronize()
+        assert int(dcr.apply_result(res)["n_invalid"]) == 0
+        got = lay_r.assemble(typed(lay_r, rsh))
+        cn = lay.assemble(typed(lay, news))
+        for t in range(len(T)):
+            assert torch.equal(got[t].reshape(-1), cn[t].reshape(-1)), lay.tensor_names[t]
+        del got, cn, rbuf, rsh
+        torch.cuda.empty_cache()
+    say("cfg2 -> TP=2 receiver: all tensors equal new")
+
+
 def test_full_llama8b_tp4(orc):
     lay = synth.llama_layout()
     run_full(orc, lay, ["model.layers.0.input_layernorm.weight", "model.layers.0.self_attn.q_proj.weight",
