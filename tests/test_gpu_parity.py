@@ -340,18 +340,20 @@ def test_index_lists_corrupt_refused(gh):
 
 
 @pytest.mark.parametrize("seed", range(10))
-def test_apply_sharded(gh, orc, seed):
+@pytest.mark.parametrize("lists", [False, True], ids=["bitmap", "lists"])
+def test_apply_sharded(gh, orc, seed, lists):
     """Apply into a receiver's own layout (random pieces at unaligned cuts,
     reversed blocks, transposed storage, gaps between placements): the
     receiver shards end byte-identical to the new tensors scattered into that
     layout, gaps untouched, and the oracle's gather of them gives new; also
     after a kill at 50 % and the overwrite retry into the same layout."""
-    say("apply sharded", seed)
+    say("apply sharded", seed, "lists" if lists else "bitmap")
     lay = synth.random_layout(1400 + seed, max_tensors=5, max_chunks=6.0)
     lay_r = synth.receiver_layout(lay, 77 + seed)
     olds, news, co, cn = pins.canon_lists(lay)
     g = gh.Gpu(lay, olds, news)
-    sb = g.encode(0)
+    opt = dcr.ENC_INDEX_LISTS if lists else 0
+    sb = g.encode(opt)
     hdr, d, _p = g.stream_host(sb)
     n = len(d) // 32
     rplan = dcr.dcr_plan_build(lay_r.tensors, [lay_r.shard_bytes(s) for s in range(lay_r.n_shards)],
@@ -374,7 +376,7 @@ def test_apply_sharded(gh, orc, seed):
     rbuf, rsh = gh.scatter_shards(lay_r, co)
     flags.zero_()
     dcr.dcr_apply_sharded(rplan, rsh, hdr, sb.dir, sb.payload, flags, 0, n // 2, 7, res, ws)
-    rsb = g.encode(1)
+    rsb = g.encode(1 | opt)
     rh = g.stream_host(rsb)[0]
     dcr.dcr_apply_overwrite_retry_sharded(rplan, rsh, rh, rsb.dir, rsb.payload, 7, res, ws)
     torch.cuda.synchronize()
