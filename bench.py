@@ -49,6 +49,9 @@ def parse():
                     help="only run a plain device copy of this many GiB, 3 times (counter calibration)")
     ap.add_argument("--pmc-report", metavar="DIR",
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs found under DIR and exit")
+    ap.add_argument("--lists-cfg5", action="store_true",
+                    help="only compare the bitmap and index-list streams on config 5's NVFP4 region (40 GB at "
+                         "0.085 %% bytes) and a 29 GB slice of its BF16 region (3 %%); print one JSON line")
     ap.add_argument("--pmc-dump", metavar="DIR",
                     help="per-kernel averages of every counter in the rocprofv3 runs under DIR/pmc_*; exit")
     return ap.parse_args()
@@ -89,6 +92,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": 4 * n, "reps": 3}), flush=True)
+        return
+    if args.lists_cfg5:
+        print(json.dumps(lists_cfg5(dev)), flush=True)
         return
 
     # ---------------------------------------------------------------- setup
@@ -403,6 +409,65 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def lists_cfg5(dev, reps=3):
+    """Bitmap against index-list streams on config 5's two regions (identity
+    layouts: shard i = tensor i, so the old shards are the canonical old
+    tensors): stream bytes, encode and apply times (median of reps), and the
+    weights after an odd number of XOR applies checked against new."""
+    import torch
+    from bit_exact_xor_amd import dcr, synth
+    out = {}
+    for name, kw in (("nvfp4 uint8, 0.085 % of bytes", dict(n_bf16=0, n_u8=5450)),
+                     ("bf16, 3 % (1000 of the 6812 tensors)", dict(n_bf16=1000, n_u8=0))):
+        lay = synth.config5_layout(**kw)
+        plan = dcr.dcr_plan_build(lay.tensors, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
+        dcr.dcr_plan_upload(plan, dev)
+        ob, olds = synth.alloc_shards(lay, dev)
+        nb, news = synth.alloc_shards(lay, dev)
+        synth.fill_shards_gpu(lay, olds, 0)
+        synth.fill_shards_gpu(lay, news, 1)
+        cb = int(plan.info.canonical_bytes)
+        cbuf = ob.clone()
+        canon = [cbuf[int(o.data_ptr() - ob.data_ptr()):int(o.data_ptr() - ob.data_ptr()) + o.numel()] for o in olds]
+        ws = dcr.workspace(plan, dev, int(plan.info.max_payload_bytes))
+        sb = dcr.StreamBuffers(plan, dev, dir_bytes=2 * 32 * int(plan.info.n_chunks),
+                               payload_bytes=int(cb * 0.2) + (1 << 20))
+        res = torch.zeros(32, dtype=torch.uint8, device=dev)
+        row = {}
+        for lname, opt in (("bitmap", 0), ("lists", dcr.ENC_INDEX_LISTS)):
+            te, ta = [], []
+            for _ in range(reps):
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record()
+                dcr.dcr_encode(plan, olds, news, dcr.MODE_DELTA | opt, 1, 2, sb.header, sb.dir, sb.payload,
+                               sb.result, ws)
+                b_.record()
+                torch.cuda.synchronize()
+                te.append(a_.elapsed_time(b_))
+            r = sb.result_host()
+            n = int(r["n_records"])
+            hdr = sb.header_host()
+            flags = torch.zeros(max(n, 1), dtype=torch.uint8, device=dev)
+            cbuf.copy_(ob)
+            for _ in range(reps):          # XOR records toggle old -> new -> old -> new
+                flags.zero_()
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record()
+                dcr.dcr_apply(plan, canon, hdr, sb.dir, sb.payload, flags, 0, n, 1, res, ws)
+                b_.record()
+                torch.cuda.synchronize()
+                ta.append(a_.elapsed_time(b_))
+            row[lname] = {"status": int(r["status"]), "records": n,
+                          "payload_GB": round(int(r["payload_bytes"]) / 1e9, 4),
+                          "encode_ms": round(float(np.median(te)), 3), "apply_ms": round(float(np.median(ta)), 3),
+                          "apply_eq_new": all(torch.equal(c, x) for c, x in zip(canon, news))}
+        out[name] = {"canonical_GB": round(cb / 1e9, 3), **row}
+        log(f"{name}: {out[name]}")
+        del ob, nb, olds, news, cbuf, canon, ws, sb, plan
+        torch.cuda.empty_cache()
+    return {"lists_cfg5": out}
 
 
 def measure_ceiling(buf, dev, reps=3):
