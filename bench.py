@@ -337,6 +337,10 @@ def main():
                      "eq_new": bool(ok_sharded)}
     log(f"apply into a TP=2 receiver layout: {sharded_apply}")
 
+    pipelined = pipelined_transfer(plan, lay, olds, news, canon, as_i16, ws, delta, n_rec, p_bytes, dev,
+                                   op_ms["encode"], op_ms["apply"])
+    log(f"pipelined transfer through pinned host memory: {pipelined}")
+
     enc_bytes = 2 * cb + 32 * n_rec + p_bytes
     renc_bytes = 2 * cb + 32 * rn_rec + rp_bytes
     app_bytes = 32 * n_rec + p_bytes + LINE * touched + SECTOR * touched_sec
@@ -404,11 +408,95 @@ def main():
         "partial_retry": partial_retry,
         "index_lists": index_lists,
         "sharded_apply": sharded_apply,
+        "pipelined": pipelined,
         "roofline": roof,
         "ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def pipelined_transfer(plan, lay, olds, news, canon, as_i16, ws, sb, n_rec, p_bytes, dev, encode_ms, apply_ms,
+                       n_slices=16, reps=5):
+    """Latency of moving a refit through pinned host memory (PCIe both ways;
+    the host buffer stands in for the network), without and with pipelining
+    (outside the step; the receiver is reset to old before each run):
+      sender    first encoded byte to the whole stream in host memory: the
+                encode then one copy out, against the pipelined encode whose
+                published slices are copied out while it runs;
+      receiver  stream in host memory to the last patched weight: one copy in
+                then one apply, against per-slice copies double-buffered
+                against per-slice applies;
+      loopback  both on this one GPU, which share its PCIe link and copy
+                engines (two machines would not)."""
+    import torch
+    from bit_exact_xor_amd import dcr
+    from bit_exact_xor_amd.pipeline import HostLoopback
+    T = lay.tensors
+    canon_o = lay.assemble(as_i16(olds))
+    canon_new = lay.assemble(as_i16(news))
+    lb = HostLoopback(plan, 32 * n_rec + (1 << 16), p_bytes + (1 << 20), dev)
+    rws = dcr.workspace(plan, dev)
+    flags = torch.zeros(max(n_rec, 1), dtype=torch.uint8, device=dev)
+
+    def reset():
+        for t in range(len(T)):
+            canon[t].view(torch.int16).copy_(canon_o[t].reshape(-1))
+        flags.zero_()
+        torch.cuda.synchronize()
+
+    def eq_new():
+        return all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
+
+    def timed(f):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        r = f()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, r
+
+    # PCIe rates of the payload alone, for reference
+    d2h, h2d = [], []
+    for _ in range(3):
+        d2h.append(timed(lambda: lb.host_payload[:p_bytes].copy_(sb.payload[:p_bytes], non_blocking=True))[0])
+        h2d.append(timed(lambda: lb.rpayload[:p_bytes].copy_(lb.host_payload[:p_bytes], non_blocking=True))[0])
+    res = {k: [] for k in ("send_serial", "send_pipelined", "recv_serial", "recv_pipelined", "loop_serial",
+                           "loop_pipelined")}
+    ok = {"sender_stream": True, "recv_serial": True, "recv_pipelined": True, "loop_serial": True,
+          "loop_pipelined": True}
+    ref_dir, ref_pay = sb.dir[: 32 * n_rec].cpu(), sb.payload[:p_bytes].cpu()
+    heads = None
+    for _ in range(reps):
+        dt, hdr = timed(lambda: lb.send_serial(olds, news, 0, 41, 42, sb, ws))
+        res["send_serial"].append(dt)
+        dt, (heads, _) = timed(lambda: lb.send(olds, news, 0, 41, 42, sb, ws, n_slices))
+        res["send_pipelined"].append(dt)
+        ok["sender_stream"] &= bool(torch.equal(lb.host_dir[: 32 * n_rec], ref_dir) and
+                                    torch.equal(lb.host_payload[:p_bytes], ref_pay))
+        reset()
+        res["recv_serial"].append(timed(lambda: lb.receive_serial(hdr, canon, flags, rws, 41))[0])
+        ok["recv_serial"] &= eq_new()
+        reset()
+        res["recv_pipelined"].append(timed(lambda: lb.receive(heads, canon, flags, rws, 41))[0])
+        ok["recv_pipelined"] &= eq_new()
+        reset()
+        res["loop_serial"].append(timed(lambda: lb.run_serial(olds, news, 0, 41, 42, sb, ws, canon, flags, rws))[0])
+        ok["loop_serial"] &= eq_new()
+        reset()
+        res["loop_pipelined"].append(timed(lambda: lb.run(olds, news, 0, 41, 42, sb, ws, n_slices, canon, flags,
+                                                          rws))[0])
+        ok["loop_pipelined"] &= eq_new()
+    del canon_o, canon_new, lb, rws
+    torch.cuda.empty_cache()
+    med = {k: round(float(np.median(v)) * 1e3, 3) for k, v in res.items()}
+    out = {"slices": len(heads), "payload_GB": round(p_bytes / 1e9, 4),
+           "d2h_GBps": round(p_bytes / float(np.median(d2h)) / 1e9, 1),
+           "h2d_GBps": round(p_bytes / float(np.median(h2d)) / 1e9, 1),
+           "encode_ms": round(encode_ms, 3), "apply_ms": round(apply_ms, 3), "median_ms": med,
+           "loop_pipelined_min_ms": round(min(res["loop_pipelined"]) * 1e3, 3),
+           "speedup": {k: round(med[k + "_serial"] / med[k + "_pipelined"], 3) for k in ("send", "recv", "loop")},
+           "checks": ok}
+    return out
 
 
 def lists_cfg5(dev, reps=3):

@@ -20,7 +20,11 @@
 //   overwrites (tokendh "no backup copy").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cstring>
+#include <thread>
 #include <string>
 
 #include "dcr_internal.h"
@@ -1110,6 +1114,14 @@ __global__ __launch_bounds__(256) void retry_need_kernel(const uint8_t* dir, con
     }
 }
 
+__device__ __forceinline__ void put_header(uint4* h, uint32_t mode, uint64_t base_v, uint64_t new_v, uint64_t fp,
+                                           uint64_t nrec, uint64_t pbytes) {
+    h[0] = make_uint4(DCR_MAGIC, DCR_FORMAT_VERSION | (mode << 16), DCR_CHUNK_BYTES, 0u);
+    h[1] = make_uint4(uint32_t(base_v), uint32_t(base_v >> 32), uint32_t(new_v), uint32_t(new_v >> 32));
+    h[2] = make_uint4(uint32_t(fp), uint32_t(fp >> 32), uint32_t(nrec), uint32_t(nrec >> 32));
+    h[3] = make_uint4(uint32_t(pbytes), uint32_t(pbytes >> 32), 0u, 0u);
+}
+
 __global__ void encode_finalize_kernel(const uint32_t* counter, uint32_t mode, uint64_t base_v, uint64_t new_v,
                                        uint64_t fp, uint64_t dir_cap, uint64_t payload_cap, uint8_t* header,
                                        dcr_encode_result* res) {
@@ -1118,16 +1130,39 @@ __global__ void encode_finalize_kernel(const uint32_t* counter, uint32_t mode, u
     const uint64_t v = bad ? 0 : *reinterpret_cast<const uint64_t*>(counter + kCtrTotal);
     const uint64_t nrec = v >> kRecShift, pbytes = (v & kP16Mask) << 4;
     const bool fits = nrec * DCR_DIRENT_BYTES <= dir_cap && pbytes <= payload_cap;
-    uint4* h = reinterpret_cast<uint4*>(header);
-    h[0] = make_uint4(DCR_MAGIC, DCR_FORMAT_VERSION | (mode << 16), DCR_CHUNK_BYTES, 0u);
-    h[1] = make_uint4(uint32_t(base_v), uint32_t(base_v >> 32), uint32_t(new_v), uint32_t(new_v >> 32));
-    h[2] = make_uint4(uint32_t(fp), uint32_t(fp >> 32), uint32_t(nrec), uint32_t(nrec >> 32));
-    h[3] = make_uint4(uint32_t(pbytes), uint32_t(pbytes >> 32), 0u, 0u);
+    put_header(reinterpret_cast<uint4*>(header), mode, base_v, new_v, fp, nrec, pbytes);
     const uint64_t changed = *reinterpret_cast<const uint64_t*>(counter + kCtrChanged);
     uint4* r = reinterpret_cast<uint4*>(res);
     r[0] = make_uint4(uint32_t(nrec), uint32_t(nrec >> 32), uint32_t(pbytes), uint32_t(pbytes >> 32));
     const int32_t st = bad ? DCR_E_FORMAT : (fits ? DCR_OK : DCR_E_CAPACITY);
     r[1] = make_uint4(uint32_t(changed), uint32_t(changed >> 32), uint32_t(st), 0u);
+}
+
+// Ready watermark of a sliced encode: after slice k's fix-up blocks (the last
+// being `last_blk`, or none when the plan has no tiles) the records before
+// the slice's end are final.  Writes the header of the stream cut there into
+// prefix slot k of the caller's host-visible region, then raises the count of
+// published slices with a system-scope release, so that a host thread which
+// reads the count also sees the header and, through the kernel boundary after
+// the fix-up, the records.  A stream that does not fit its buffers, or a bad
+// partial-retry directory, sets the region's status instead and publishes
+// nothing more (both conditions, once true, stay true for every later slice).
+__global__ void publish_kernel(const uint64_t* fix_status, uint32_t last_blk, const uint32_t* counter,
+                               uint32_t mode, uint64_t base_v, uint64_t new_v, uint64_t fp, uint64_t dir_cap,
+                               uint64_t payload_cap, uint8_t* ready, uint32_t k) {
+    if (threadIdx.x != 0) return;
+    const bool bad = counter[kCtrBad] != 0;
+    const uint64_t v = last_blk == UINT32_MAX ? 0 : ld_status(fix_status + last_blk) >> kValShift;
+    const uint64_t nrec = v >> kRecShift, pbytes = (v & kP16Mask) << 4;
+    const bool fits = nrec * DCR_DIRENT_BYTES <= dir_cap && pbytes <= payload_cap;
+    if (bad || !fits) {
+        __hip_atomic_store(reinterpret_cast<int32_t*>(ready + 8), int32_t(bad ? DCR_E_FORMAT : DCR_E_CAPACITY),
+                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        return;
+    }
+    put_header(reinterpret_cast<uint4*>(ready + 64 + 64 * uint64_t(k)), mode, base_v, new_v, fp, nrec, pbytes);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(ready), uint64_t(k) + 1u, __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 __global__ void fill_u64_kernel(uint64_t* p, uint64_t n, uint64_t v) {
@@ -1911,7 +1946,8 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
                            uint32_t mode, uint64_t base_version, uint64_t new_version, void* header_dev,
                            void* dir_dev, uint64_t dir_cap, void* payload_dev, uint64_t payload_cap,
                            dcr_encode_result* result_dev, void* workspace_dev, uint64_t ws_bytes, void* stream,
-                           const uint8_t* delta_dir, const uint8_t* delta_flags, uint64_t n_delta) {
+                           const uint8_t* delta_dir, const uint8_t* delta_flags, uint64_t n_delta,
+                           uint32_t n_slices = 0, uint8_t* ready_dev = nullptr) {
     if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
     const Plan& p = *plan;
     if (!p.dev_tables) return fail(DCR_E_INVAL, "plan not uploaded");
@@ -1961,36 +1997,58 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
     // chunk's slot (max_payload_bytes)
     uint8_t* stage = ws + p.ws_bytes;
     const uint32_t staged = ws_bytes - p.ws_bytes >= p.max_payload_bytes ? 1u : 0u;
-    if (n_tiles) {
-        EncodeArgs a;
-        a.tensors = tensors;
-        a.chunks = chunks;
-        a.pieces = pieces;
-        a.old_sh = old_sh;
-        a.new_sh = new_sh;
-        a.scale_flags = scale_flags;
-        a.status = reinterpret_cast<uint64_t*>(ws + p.ws_status);
-        a.counter = counter;
-        a.tile_agg = reinterpret_cast<uint64_t*>(ws + p.ws_agg);
-        a.tile_info = reinterpret_cast<uint64_t*>(ws + p.ws_info);
-        a.slots = tab<uint64_t>(p, p.off_slots);
-        a.stage = stage;
-        a.dir = static_cast<uint8_t*>(dir_dev);
-        a.payload = static_cast<uint8_t*>(payload_dev);
-        a.dir_cap = dir_cap;
-        a.payload_cap = payload_cap;
-        a.need = partial ? need : nullptr;
-        a.n_tiles = n_tiles;
-        a.mode = mode;
-        a.lists = lists;
-        mark(true, s);
+    EncodeArgs a;
+    a.tensors = tensors;
+    a.chunks = chunks;
+    a.pieces = pieces;
+    a.old_sh = old_sh;
+    a.new_sh = new_sh;
+    a.scale_flags = scale_flags;
+    a.status = reinterpret_cast<uint64_t*>(ws + p.ws_status);
+    a.counter = counter;
+    a.tile_agg = reinterpret_cast<uint64_t*>(ws + p.ws_agg);
+    a.tile_info = reinterpret_cast<uint64_t*>(ws + p.ws_info);
+    a.slots = tab<uint64_t>(p, p.off_slots);
+    a.stage = stage;
+    a.dir = static_cast<uint8_t*>(dir_dev);
+    a.payload = static_cast<uint8_t*>(payload_dev);
+    a.dir_cap = dir_cap;
+    a.payload_cap = payload_cap;
+    a.need = partial ? need : nullptr;
+    a.n_tiles = n_tiles;
+    a.mode = mode;
+    a.lists = lists;
+    FixArgs f;
+    f.tensors = tensors;
+    f.chunks = chunks;
+    f.tile_agg = a.tile_agg;
+    f.tile_info = a.tile_info;
+    f.slots = a.slots;
+    f.fix_status = reinterpret_cast<uint64_t*>(ws + p.ws_fix);
+    f.counter = counter;
+    f.stage = stage;
+    f.dir = a.dir;
+    f.payload = a.payload;
+    f.dir_cap = dir_cap;
+    f.payload_cap = payload_cap;
+    f.n_tiles = n_tiles;
+    f.n_blocks = (n_tiles + kFixTiles - 1) / kFixTiles;
+    f.staged = staged;
+    f.lists = lists;
+    // Tiles [t0, t1): in a staged launch the direct tiles of each element
+    // width, then the others (any order: every tile has its own slot); the
+    // lists hold tile ids in ascending order, so a range of tiles is a range
+    // of each list.  In order: one workgroup per tile, tile ids taken from a
+    // counter that carries over from the previous range.
+    auto run_tiles = [&](uint32_t t0, uint32_t t1, bool timed) {
+        if (timed) mark(true, s);
         if (staged) {
-            // direct tiles per element width, then the others (in any order:
-            // every tile has its own slot)
             for (int i = 0; i < 3; i++) {
-                const uint32_t n = uint32_t(p.direct[i].size());
+                const auto& L = p.direct[i];
+                const uint32_t lo = uint32_t(std::lower_bound(L.begin(), L.end(), t0) - L.begin());
+                const uint32_t n = uint32_t(std::lower_bound(L.begin(), L.end(), t1) - L.begin()) - lo;
                 if (!n) continue;
-                const uint32_t* list = tab<uint32_t>(p, p.off_direct[i]);
+                const uint32_t* list = tab<uint32_t>(p, p.off_direct[i]) + lo;
                 if (lists) {
                     if (i == 0) hipLaunchKernelGGL((encode_direct_kernel<1, true>), dim3(n), dim3(kThreads), 0, s, a, list, n);
                     else if (i == 1) hipLaunchKernelGGL((encode_direct_kernel<2, true>), dim3(n), dim3(kThreads), 0, s, a, list, n);
@@ -2001,34 +2059,49 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
                     else hipLaunchKernelGGL((encode_direct_kernel<4, false>), dim3(n), dim3(kThreads), 0, s, a, list, n);
                 }
             }
-        } else {
-            hipLaunchKernelGGL(encode_kernel, dim3(n_tiles), dim3(kThreads), 0, s, a);
+        } else if (t1 > t0) {
+            hipLaunchKernelGGL(encode_kernel, dim3(t1 - t0), dim3(kThreads), 0, s, a);
         }
-        mark(false, s);
-        if (staged && !p.slow.empty())
-            hipLaunchKernelGGL(encode_slow_kernel, dim3(uint32_t(p.slow.size())), dim3(kThreads), 0, s, a,
-                               tab<uint32_t>(p, p.off_slow), uint32_t(p.slow.size()));
-        FixArgs f;
-        f.tensors = tensors;
-        f.chunks = chunks;
-        f.tile_agg = a.tile_agg;
-        f.tile_info = a.tile_info;
-        f.slots = a.slots;
-        f.fix_status = reinterpret_cast<uint64_t*>(ws + p.ws_fix);
-        f.counter = counter;
-        f.stage = stage;
-        f.dir = a.dir;
-        f.payload = a.payload;
-        f.dir_cap = dir_cap;
-        f.payload_cap = payload_cap;
-        f.n_tiles = n_tiles;
-        f.n_blocks = (n_tiles + kFixTiles - 1) / kFixTiles;
-        f.staged = staged;
-        f.lists = lists;
-        hipLaunchKernelGGL(encode_fixup_kernel, dim3(f.n_blocks), dim3(kFixTiles), 0, s, f);
+        if (timed) mark(false, s);
+        if (staged) {
+            const auto& L = p.slow;
+            const uint32_t lo = uint32_t(std::lower_bound(L.begin(), L.end(), t0) - L.begin());
+            const uint32_t n = uint32_t(std::lower_bound(L.begin(), L.end(), t1) - L.begin()) - lo;
+            if (n)
+                hipLaunchKernelGGL(encode_slow_kernel, dim3(n), dim3(kThreads), 0, s, a,
+                                   tab<uint32_t>(p, p.off_slow) + lo, n);
+        }
+    };
+    // fix-up blocks [b0, b1); block ids come from a counter that carries over
+    auto run_fix = [&](uint32_t b0, uint32_t b1) {
+        if (b1 > b0) hipLaunchKernelGGL(encode_fixup_kernel, dim3(b1 - b0), dim3(kFixTiles), 0, s, f);
+    };
+    auto finalize = [&]() {
+        hipLaunchKernelGGL(encode_finalize_kernel, dim3(1), dim3(64), 0, s, counter, mode, base_version, new_version,
+                           p.fingerprint, dir_cap, payload_cap, static_cast<uint8_t*>(header_dev), result_dev);
+    };
+    if (!n_slices) {
+        if (n_tiles) {
+            run_tiles(0, n_tiles, true);
+            run_fix(0, f.n_blocks);
+        }
+        finalize();
+    } else {
+        // slice k: fix-up blocks [k * nb / n_slices, (k + 1) * nb / n_slices)
+        // and their tiles; the last slice also finalises the header before it
+        // is published
+        const uint32_t nb = f.n_blocks;
+        for (uint32_t k = 0; k < n_slices; k++) {
+            const uint32_t b0 = uint32_t(uint64_t(k) * nb / n_slices), b1 = uint32_t(uint64_t(k + 1) * nb / n_slices);
+            const uint32_t t0 = b0 * kFixTiles, t1 = std::min(b1 * kFixTiles, n_tiles);
+            run_tiles(t0, t1, false);
+            run_fix(b0, b1);
+            if (k + 1 == n_slices) finalize();
+            hipLaunchKernelGGL(publish_kernel, dim3(1), dim3(64), 0, s, f.fix_status, b1 > b0 ? b1 - 1 : UINT32_MAX,
+                               counter, mode, base_version, new_version, p.fingerprint, dir_cap, payload_cap, ready_dev,
+                               k);
+        }
     }
-    hipLaunchKernelGGL(encode_finalize_kernel, dim3(1), dim3(64), 0, s, counter, mode, base_version, new_version,
-                       p.fingerprint, dir_cap, payload_cap, static_cast<uint8_t*>(header_dev), result_dev);
     return hip_check(hipGetLastError(), "encode launch");
 }
 
@@ -2045,6 +2118,60 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
     return encode_impl(plan, old_shards, new_shards, mode, base_version, new_version, header_dev, dir_dev, dir_cap,
                        payload_dev, payload_cap, result_dev, workspace_dev, ws_bytes, stream, nullptr, nullptr,
                        UINT64_MAX);
+}
+
+int32_t dcr_encode_pipelined(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards,
+                             uint32_t mode, uint64_t base_version, uint64_t new_version, void* header_dev,
+                             void* dir_dev, uint64_t dir_cap, void* payload_dev, uint64_t payload_cap,
+                             dcr_encode_result* result_dev, void* workspace_dev, uint64_t ws_bytes,
+                             uint32_t n_slices, void* ready_host, uint64_t ready_bytes, void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
+    if (n_slices == 0) return fail(DCR_E_INVAL, "n_slices must be at least 1");
+    if (!ready_host || (reinterpret_cast<uintptr_t>(ready_host) & 63u))
+        return fail(DCR_E_INVAL, "ready region is NULL or not 64-byte aligned");
+    const uint32_t nb = uint32_t((plan->chunks.size() + kFixTiles - 1) / kFixTiles);
+    const uint32_t n_eff = std::min(n_slices, std::max(nb, 1u));
+    if (ready_bytes < 64 + 64 * uint64_t(n_eff)) return fail(DCR_E_CAPACITY, "ready region too small");
+    // the kernels write the region through its device address; anything but
+    // pinned host memory is refused before any launch
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, ready_host) != hipSuccess || at.type != hipMemoryTypeHost || !at.devicePointer) {
+        (void)hipGetLastError();
+        return fail(DCR_E_INVAL, "ready region is not pinned host memory (hipHostMalloc)");
+    }
+    auto* r = static_cast<uint8_t*>(ready_host);
+    __atomic_store_n(reinterpret_cast<int32_t*>(r + 8), 0, __ATOMIC_RELAXED);
+    __atomic_store_n(reinterpret_cast<uint32_t*>(r + 12), n_eff, __ATOMIC_RELAXED);
+    __atomic_store_n(reinterpret_cast<uint64_t*>(r), uint64_t(0), __ATOMIC_RELEASE);
+    return encode_impl(plan, old_shards, new_shards, mode, base_version, new_version, header_dev, dir_dev, dir_cap,
+                       payload_dev, payload_cap, result_dev, workspace_dev, ws_bytes, stream, nullptr, nullptr,
+                       UINT64_MAX, n_eff, static_cast<uint8_t*>(at.devicePointer));
+}
+
+int32_t dcr_ready_wait(const void* ready_host, uint32_t slice, uint64_t timeout_us, dcr_stream_header* out) {
+    using namespace dcr;
+    set_error("");
+    if (!ready_host || !out) return fail(DCR_E_INVAL, "NULL argument");
+    const auto* r = static_cast<const uint8_t*>(ready_host);
+    const uint32_t n = __atomic_load_n(reinterpret_cast<const uint32_t*>(r + 12), __ATOMIC_RELAXED);
+    if (slice >= n) return fail(DCR_E_INVAL, "slice " + std::to_string(slice) + " of " + std::to_string(n));
+    const auto t0 = std::chrono::steady_clock::now();
+    for (uint64_t spin = 0;; spin++) {
+        if (__atomic_load_n(reinterpret_cast<const uint64_t*>(r), __ATOMIC_ACQUIRE) > slice) {
+            std::memcpy(out, r + 64 + 64 * uint64_t(slice), sizeof(dcr_stream_header));
+            return DCR_OK;
+        }
+        const int32_t st = __atomic_load_n(reinterpret_cast<const int32_t*>(r + 8), __ATOMIC_ACQUIRE);
+        if (st) return fail(st, "the encode stopped publishing (status " + std::to_string(st) + ")");
+        if ((spin & 255u) == 255u) {
+            const uint64_t us = uint64_t(std::chrono::duration_cast<std::chrono::microseconds>(
+                                              std::chrono::steady_clock::now() - t0).count());
+            if (us >= timeout_us) return fail(DCR_E_TIMEOUT, "slice " + std::to_string(slice) + " not published");
+            std::this_thread::sleep_for(std::chrono::microseconds(5));
+        }
+    }
 }
 
 int32_t dcr_encode_retry_partial(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards,

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libdcr.so")
 
 DCR_OK, DCR_E_INVAL, DCR_E_COVERAGE, DCR_E_FORMAT, DCR_E_VERSION, DCR_E_CAPACITY, DCR_E_HIP, DCR_E_NOMEM = \
     0, -1, -2, -3, -4, -5, -6, -7
+DCR_E_TIMEOUT = -8
 ROUTE_AFFINE_XOR, ROUTE_OVERWRITE, ROUTE_BLOCK_SCALED = 0, 1, 2
 MODE_DELTA, MODE_RETRY = 0, 1
 ENC_INDEX_LISTS = 0x100            # encode option: index-list layout for low-density records
@@ -80,6 +81,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dcr_plan_destroy.argtypes = [P]
     lib.dcr_encode.restype = I32
     lib.dcr_encode.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P, U64, P]
+    lib.dcr_encode_pipelined.restype = I32
+    lib.dcr_encode_pipelined.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P, U64, U32, P, U64, P]
+    lib.dcr_ready_wait.restype = I32
+    lib.dcr_ready_wait.argtypes = [P, U32, U64, P]
     lib.dcr_encode_retry_partial.restype = I32
     lib.dcr_encode_retry_partial.argtypes = [P, P, P, P, P, U64, P, U64, U64, P, P, U64, P, U64, P, P, U64, P]
     lib.dcr_apply.restype = I32
@@ -124,7 +129,11 @@ def _ptr_array(ptrs):
 
 def _dptr(t) -> int:
     """Device pointer of a torch tensor (or an int address)."""
-    return int(t) if isinstance(t, int) else int(t.data_ptr())
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return int(t.ctypes.data)
+    return int(t.data_ptr())
 
 
 def _stream(stream) -> int | None:
@@ -178,6 +187,32 @@ def dcr_encode(plan: Plan, old_shards, new_shards, mode, base_version, new_versi
         mode, base_version, new_version, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload),
         _nbytes(payload), _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_encode")
+
+
+def ready_region_bytes(n_slices: int) -> int:
+    """Bytes of a dcr_encode_pipelined watermark region for n_slices."""
+    return 64 + 64 * int(n_slices)
+
+
+def dcr_encode_pipelined(plan: Plan, old_shards, new_shards, mode, base_version, new_version,
+                         header, dir_buf, payload, result, workspace, n_slices, ready, stream=None) -> None:
+    """Enqueue a sliced encode that publishes a ready watermark after each
+    slice into `ready`, a pinned host tensor of ready_region_bytes(n_slices)."""
+    rc = load_library().dcr_encode_pipelined(
+        plan.handle, _ptr_array([_dptr(t) for t in old_shards]), _ptr_array([_dptr(t) for t in new_shards]),
+        mode, base_version, new_version, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload),
+        _nbytes(payload), _dptr(result), _dptr(workspace), _nbytes(workspace), n_slices, _dptr(ready),
+        _nbytes(ready), _stream(stream))
+    _check(rc, "dcr_encode_pipelined")
+
+
+def dcr_ready_wait(ready, slice_index: int, timeout_us: int = 10_000_000) -> np.ndarray:
+    """Wait until slice `slice_index` of a watermark region is published;
+    returns its prefix header (64 bytes)."""
+    out = np.zeros(64, dtype=np.uint8)
+    rc = load_library().dcr_ready_wait(_dptr(ready), slice_index, timeout_us, out.ctypes.data)
+    _check(rc, "dcr_ready_wait")
+    return out
 
 
 def dcr_encode_retry_partial(plan: Plan, old_shards, new_shards, delta_header: np.ndarray, delta_dir, delta_flags,
@@ -254,6 +289,8 @@ def format_constants():
 
 
 def _nbytes(t) -> int:
+    if isinstance(t, np.ndarray):
+        return int(t.nbytes)
     return int(t.numel() * t.element_size()) if hasattr(t, "numel") else 0
 
 

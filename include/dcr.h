@@ -68,7 +68,8 @@ enum {
     DCR_E_VERSION = -4,   /* stream base_version != expected base version     */
     DCR_E_CAPACITY = -5,  /* a caller buffer is too small                     */
     DCR_E_HIP = -6,       /* a HIP runtime call failed                        */
-    DCR_E_NOMEM = -7      /* host allocation failed                           */
+    DCR_E_NOMEM = -7,     /* host allocation failed                           */
+    DCR_E_TIMEOUT = -8    /* dcr_ready_wait: slice not published in time      */
 };
 enum { DCR_ROUTE_AFFINE_XOR = 0, DCR_ROUTE_OVERWRITE = 1, DCR_ROUTE_BLOCK_SCALED = 2 };
 enum { DCR_MODE_DELTA = 0, DCR_MODE_RETRY = 1 };
@@ -227,6 +228,59 @@ int32_t dcr_encode(const dcr_plan* plan,
                    void* payload_dev, uint64_t payload_cap,
                    dcr_encode_result* result_dev,
                    void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* Pipelined encode (sender side): the trainer starts sending finished parts
+ * of the stream while the rest is still being built, so a refit costs about
+ * the larger of build and transfer time rather than their sum (ai-feeds
+ * summary "key modules" 5, pipelined transfer; tokendh blog, the paragraph
+ * on pipelining build and transfer).  Same arguments and the same stream as
+ * dcr_encode, plus a ready watermark:
+ *   n_slices       the encode runs as this many slices in plan (tensor,
+ *                  chunk) order; at most one per 256 chunks of the plan
+ *                  (fewer are used if asked for more; at least 1).  With
+ *                  nb = ceil(n_chunks / 256), slice k covers the plan's chunks
+ *                  [256 * floor(k * nb / n), min(256 * floor((k + 1) * nb / n),
+ *                  n_chunks)), n the slices used.
+ *   ready_host     the watermark region, 64 + 64 * n_slices bytes of pinned
+ *                  host memory (hipHostMalloc), 64-byte aligned; anything else
+ *                  is refused (DCR_E_INVAL) before any launch.  Layout:
+ *                    u64 @0   slices published so far (0 .. n), monotone
+ *                    i32 @8   0, or the stream's failure status once the
+ *                             stream stops fitting its buffers
+ *                             (DCR_E_CAPACITY) or a partial-retry directory
+ *                             is bad (DCR_E_FORMAT); nothing more is then
+ *                             published
+ *                    u32 @12  n, the slices used
+ *                    @64 + 64 k  prefix header k: the stream header of the
+ *                             stream cut after slice k (its n_records and
+ *                             payload_bytes count the records of chunks
+ *                             before the slice's end)
+ *                  This call resets @0 and @8 and sets @12 from the host; the
+ *                  region must not be in use by an encode still in flight.
+ *   ready_bytes    size of that region.
+ * Once slice k is published, directory entries [0, prefix[k].n_records) and
+ * payload bytes [0, prefix[k].payload_bytes) are final in device memory and
+ * may be copied out by any stream or engine while the encode goes on; the
+ * prefix is itself a valid stream, so a receiver may apply records
+ * [prefix[k-1].n_records, prefix[k].n_records) with prefix header k
+ * (dcr_apply) as they arrive.  When slice n - 1 is published, header_dev and
+ * result_dev are final too and prefix header n - 1 equals the header. */
+int32_t dcr_encode_pipelined(const dcr_plan* plan,
+                             const void* const* old_shards, const void* const* new_shards,
+                             uint32_t mode, uint64_t base_version, uint64_t new_version,
+                             void* header_dev, void* dir_dev, uint64_t dir_cap,
+                             void* payload_dev, uint64_t payload_cap,
+                             dcr_encode_result* result_dev,
+                             void* workspace_dev, uint64_t ws_bytes,
+                             uint32_t n_slices, void* ready_host, uint64_t ready_bytes,
+                             void* stream);
+
+/* Wait (host side, polling; no HIP call) until slice `slice` of a
+ * dcr_encode_pipelined watermark region is published and copy its prefix
+ * header to `out`.  Returns DCR_OK; the region's failure status if the encode
+ * stopped publishing; DCR_E_TIMEOUT after timeout_us microseconds;
+ * DCR_E_INVAL for a slice beyond the region's count. */
+int32_t dcr_ready_wait(const void* ready_host, uint32_t slice, uint64_t timeout_us, dcr_stream_header* out);
 
 /* Partial retry (sender side).  After a failure the receiver reads back the
  * applied flags of a DELTA stream; this call writes a RETRY stream (as

@@ -43,6 +43,16 @@ class Gpu:
         torch.cuda.synchronize()
         return sb
 
+    def encode_pipelined(self, mode=0, n_slices=4, base=7, new=8, stage=0):
+        """Sliced encode with a ready watermark; returns (buffers, region)."""
+        sb = dcr.StreamBuffers(self.plan, self.device)
+        ws = self.ws if not stage else dcr.workspace(self.plan, self.device, stage)
+        ready = torch.full((dcr.ready_region_bytes(n_slices),), 0xEE, dtype=torch.uint8, pin_memory=True)
+        dcr.dcr_encode_pipelined(self.plan, self.olds, self.news, mode, base, new, sb.header, sb.dir, sb.payload,
+                                 sb.result, ws, n_slices, ready)
+        torch.cuda.synchronize()
+        return sb, ready
+
     def encode_retry_partial(self, delta_hdr, delta_sb, flags, base=7, new=8, stage=0):
         """Partial retry encode from a DELTA stream and its applied flags."""
         sb = dcr.StreamBuffers(self.plan, self.device)
@@ -87,6 +97,34 @@ class Gpu:
         dcr.dcr_apply_overwrite_retry(self.plan, canon, hdr, sb.dir, sb.payload, base, res, self.ws)
         torch.cuda.synchronize()
         return dcr.apply_result(res)
+
+
+def chunk_starts(lay):
+    """Plan index of each tensor's first chunk (tensor order, 64 KiB chunks)."""
+    n = [(int(t["numel"]) * int(t["elem_bytes"]) + 65535) // 65536 for t in lay.tensors]
+    return np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+
+
+def expected_prefixes(lay, dir_bytes, payload_total, n_slices):
+    """(records, payload bytes) of the stream cut after each slice of a
+    pipelined encode, from a finished stream's directory and the slice rule
+    (slice k ends at chunk 256 * floor((k + 1) * nb / n), nb = fix-up blocks)."""
+    starts = chunk_starts(lay)
+    nch = int(starts[-1])
+    nb = (nch + 255) // 256
+    n = min(n_slices, max(nb, 1))
+    d = np.asarray(dir_bytes, dtype=np.uint8).reshape(-1, 32)
+    t = d[:, 0:4].copy().view("<u4").ravel().astype(np.int64)
+    c = d[:, 4:8].copy().view("<u4").ravel().astype(np.int64)
+    off = d[:, 16:24].copy().view("<u8").ravel().astype(np.int64)
+    g = starts[t] + c
+    assert (np.diff(g) >= 0).all()
+    out = []
+    for k in range(n):
+        end = min(256 * ((k + 1) * nb // n), nch)
+        r = int(np.searchsorted(g, end, side="left"))
+        out.append((r, int(off[r]) if r < len(g) else int(payload_total)))
+    return n, out
 
 
 def scatter_shards(lay, canon, device="cuda", fill=0xA5):

@@ -95,3 +95,32 @@ def test_plan_accepts_degenerate_tensors():
     S[1] = (2, 1, 1, 0, 0, 0, [7, 1, 1, 1], [1, 0, 0, 0], [1, 0, 0, 0])
     p = dcr.dcr_plan_build(T, [1, 14], S)
     assert p.info.n_chunks == 2
+
+
+def test_ready_wait_host_logic():
+    """dcr_ready_wait only reads host memory: published count, failure status
+    and the prefix headers of a watermark region (no GPU involved)."""
+    n = 3
+    r = np.zeros(dcr.ready_region_bytes(n) + 64, dtype=np.uint8)
+    reg = r[(-r.ctypes.data) % 64:][: dcr.ready_region_bytes(n)]   # 64-byte aligned view
+    assert reg.ctypes.data % 64 == 0
+    reg[12:16] = np.frombuffer(np.uint32(n).tobytes(), np.uint8)
+    for k in range(n):
+        reg[64 + 64 * k: 128 + 64 * k] = np.arange(64, dtype=np.uint8) + 16 * k
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_ready_wait(reg, 0, timeout_us=2000)
+    assert e.value.code == dcr.DCR_E_TIMEOUT
+    reg[0:8] = np.frombuffer(np.uint64(2).tobytes(), np.uint8)
+    assert np.array_equal(dcr.dcr_ready_wait(reg, 0, 1000), np.arange(64, dtype=np.uint8))
+    assert np.array_equal(dcr.dcr_ready_wait(reg, 1, 1000), np.arange(64, dtype=np.uint8) + 16)
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_ready_wait(reg, 2, timeout_us=2000)
+    assert e.value.code == dcr.DCR_E_TIMEOUT
+    reg[8:12] = np.frombuffer(np.int32(dcr.DCR_E_CAPACITY).tobytes(), np.uint8)
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_ready_wait(reg, 2, timeout_us=10_000_000)
+    assert e.value.code == dcr.DCR_E_CAPACITY
+    assert np.array_equal(dcr.dcr_ready_wait(reg, 1, 0), np.arange(64, dtype=np.uint8) + 16)
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_ready_wait(reg, 3, timeout_us=1000)
+    assert e.value.code == dcr.DCR_E_INVAL

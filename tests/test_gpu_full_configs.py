@@ -232,6 +232,74 @@ def test_full_llama8b_receiver_tp2(orc):
     say("cfg2 -> TP=2 receiver: all tensors equal new")
 
 
+def test_full_llama8b_pipelined():
+    """Config 2 through the pipelined transfer: the encode publishes 16
+    slices while it runs; each is copied to pinned host memory, back into
+    the receiver's buffers and applied with its prefix header on separate
+    streams.  The host copy equals the one-shot stream byte for byte, every
+    prefix header cuts the stream where the slice rule says, and the
+    receiver ends equal to new."""
+    from tests import gpu_harness as gh
+    from bit_exact_xor_amd.pipeline import HostLoopback
+    lay = synth.llama_layout()
+    say("cfg2 pipelined", "plan")
+    T = lay.tensors
+    plan = dcr.dcr_plan_build(T, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
+    dcr.dcr_plan_upload(plan, "cuda")
+    ob, olds = synth.alloc_shards(lay, "cuda")
+    nb, news = synth.alloc_shards(lay, "cuda")
+    synth.fill_shards_gpu(lay, olds, 0)
+    synth.fill_shards_gpu(lay, news, 1)
+    cb = int(plan.info.canonical_bytes)
+    ref = dcr.StreamBuffers(plan, "cuda", dir_bytes=2 * 32 * int(plan.info.n_chunks),
+                            payload_bytes=int(cb * 0.2) + (1 << 20))
+    sb = dcr.StreamBuffers(plan, "cuda", dir_bytes=2 * 32 * int(plan.info.n_chunks),
+                           payload_bytes=int(cb * 0.2) + (1 << 20))
+    wss = staged_workspace(plan, ref)
+    dcr.dcr_encode(plan, olds, news, 0, 3, 4, ref.header, ref.dir, ref.payload, ref.result, wss)
+    torch.cuda.synchronize()
+    r = ref.result_host()
+    assert int(r["status"]) == 0
+    n_rec, pbytes = int(r["n_records"]), int(r["payload_bytes"])
+    co = lay.assemble(typed(lay, olds))
+    sizes = [int(T[t]["numel"]) * int(T[t]["elem_bytes"]) for t in range(len(T))]
+    offs = np.concatenate([[0], np.cumsum([(s + 255) // 256 * 256 for s in sizes])]).astype(np.int64)
+    cbuf = torch.empty(int(offs[-1]), dtype=torch.uint8, device="cuda")
+    canon = [cbuf[int(offs[t]):int(offs[t]) + sizes[t]] for t in range(len(T))]
+    for t in range(len(T)):
+        canon[t].copy_(co[t].reshape(-1).view(torch.uint8))
+    del co
+    flags = torch.zeros(max(n_rec, 1), dtype=torch.uint8, device="cuda")
+    rws = dcr.workspace(plan, "cuda")
+    lb = HostLoopback(plan, 32 * n_rec + (1 << 16), pbytes + (1 << 20))
+    torch.cuda.synchronize()
+    say("cfg2 pipelined", f"encode + transfer + apply, {n_rec} records, {pbytes / 1e9:.2f} GB")
+    heads, results = lb.run(olds, news, 0, 3, 4, sb, wss, 16, canon, flags, rws)
+    torch.cuda.synchronize()
+    assert len(heads) == 16
+    assert int(sb.result_host()["status"]) == 0
+    ref_hdr = ref.header.cpu().numpy()
+    assert np.array_equal(sb.header.cpu().numpy(), ref_hdr) and np.array_equal(heads[-1], ref_hdr)
+    ref_dir = ref.dir[: n_rec * 32].cpu()
+    assert torch.equal(lb.host_dir[: n_rec * 32], ref_dir)
+    assert torch.equal(lb.host_payload[:pbytes], ref.payload[:pbytes].cpu())
+    n, pre = gh.expected_prefixes(lay, ref_dir.numpy(), pbytes, 16)
+    assert n == 16
+    for k, (rk, pk) in enumerate(pre):
+        assert int(heads[k][40:48].view("<u8")[0]) == rk and int(heads[k][48:56].view("<u8")[0]) == pk, k
+        want = ref_hdr.copy()
+        want[40:56] = heads[k][40:56]
+        assert np.array_equal(heads[k], want), k
+    ar = [dcr.apply_result(x) for x in results]
+    assert sum(int(a["n_applied"]) for a in ar) == n_rec and all(int(a["n_invalid"]) == 0 for a in ar)
+    cn = lay.assemble(typed(lay, news))
+    for t in range(len(T)):
+        assert torch.equal(canon[t], cn[t].reshape(-1).view(torch.uint8)), lay.tensor_names[t]
+    say("cfg2 pipelined: host copy equals the stream, prefixes cut at the slice ends, receiver equals new")
+    del wss, cbuf, canon, cn, ob, nb, olds, news, lb, ref, sb
+    torch.cuda.empty_cache()
+
+
 def test_full_llama8b_tp4(orc):
     lay = synth.llama_layout()
     run_full(orc, lay, ["model.layers.0.input_layernorm.weight", "model.layers.0.self_attn.q_proj.weight",

@@ -414,6 +414,113 @@ def test_apply_sharded_refuses_overlapping_layout(gh):
         dcr.dcr_apply_sharded(rplan, [shard], hdr, dbuf, dbuf, flags, 0, 0, 0, res, dcr.workspace(rplan, "cuda"))
 
 
+PIPE_CASES = [("random", 0), ("random", 4), ("random", 6), ("llama", 0), ("moe", 0)]
+
+
+def pipe_layout(kind, seed):
+    if kind == "random":
+        # 700-1200 chunks of all widths and routes: several fix-up blocks
+        return synth.random_layout(seed, max_tensors=24, max_chunks=120.0)
+    if kind == "llama":
+        return synth.llama_layout(hidden=1024, layers=4, ffn=2816, n_q=16, n_kv=4, head_dim=64, vocab=8000, tp=4,
+                                  rate=0.03)
+    # block-scaled experts with fp32 scale tensors
+    return synth.moe_layout(hidden=512, layers=2, n_exp=16, moe_ffn=256, n_q=8, n_kv=2, head_dim=64, vocab=4000,
+                            ep=4, rate=0.05, variant="hot")
+
+
+def pipe_canon(kind, lay):
+    """Host shards and canonical old / new (uint8) of a pipelined-encode case;
+    the model layouts assemble their tensors with torch ops."""
+    if kind == "random":
+        return pins.canon_lists(lay)
+    olds, news = lay.shards_host(0), lay.shards_host(1)
+    typed_t = {1: np.uint8, 2: np.int16, 4: np.int32}
+
+    def canon(xs):
+        ts = [torch.from_numpy(np.ascontiguousarray(x).view(typed_t[x.dtype.itemsize])) for x in xs]
+        return [t.reshape(-1).contiguous().view(torch.uint8).numpy().copy() for t in lay.assemble(ts)]
+    return olds, news, canon(olds), canon(news)
+
+
+@pytest.mark.parametrize("kind,seed", PIPE_CASES)
+def test_pipelined_encode(gh, orc, kind, seed):
+    """Sliced encode with a ready watermark (in-order and staged, DELTA and
+    RETRY, with and without index lists): the stream equals the oracle's; every
+    slice is published; prefix header k is the final header with the records
+    and payload bytes of the chunks before slice k's end; applying each
+    prefix's new records with its own header, slice by slice, gives new."""
+    say("pipelined encode", kind, seed)
+    lay = pipe_layout(kind, seed)
+    olds, news, co, cn = pipe_canon(kind, lay)
+    g = gh.Gpu(lay, olds, news)
+    starts = gh.chunk_starts(lay)
+    say("pipelined encode", kind, seed, f"{int(starts[-1])} chunks")
+    for mode in (0, 1, dcr.ENC_INDEX_LISTS):
+        exp = oracle_stream(orc, lay, olds, news, mode)
+        for stage in (0, int(g.plan.info.max_payload_bytes)):
+            for n_slices in (1, 3, 1000):
+                what = f"{kind} {seed} mode {mode} stage {stage} slices {n_slices}"
+                sb, ready = g.encode_pipelined(mode, n_slices, stage=stage)
+                got = g.stream_host(sb)
+                assert_same_stream(got, exp, what)
+                rg = ready.numpy()
+                n, pre = gh.expected_prefixes(lay, exp[1], len(exp[2]), n_slices)
+                assert int(rg[12:16].view("<u4")[0]) == n, what
+                assert int(rg[0:8].view("<u8")[0]) == n and int(rg[8:12].view("<i4")[0]) == 0, what
+                for k, (r, pb) in enumerate(pre):
+                    h = rg[64 + 64 * k: 128 + 64 * k].copy()
+                    assert int(h[40:48].view("<u8")[0]) == r and int(h[48:56].view("<u8")[0]) == pb, (what, k)
+                    want = exp[0].copy()
+                    want[40:56] = h[40:56]
+                    assert np.array_equal(h, want), (what, k)
+                    assert np.array_equal(dcr.dcr_ready_wait(ready, k, 0), h)
+                if mode == 1 or stage == 0 or n_slices != 3:
+                    continue
+                buf, canon = g.canon_alloc(co)
+                flags = torch.zeros(max(len(got[1]) // 32, 1), dtype=torch.uint8, device="cuda")
+                prev = 0
+                for k, (r, pb) in enumerate(pre):
+                    hk = rg[64 + 64 * k: 128 + 64 * k].copy()
+                    ar = g.apply(canon, hk, sb, flags, first=prev, n=r - prev)
+                    assert int(ar["n_applied"]) == r - prev and int(ar["n_invalid"]) == 0, (what, k)
+                    prev = r
+                for t in range(len(co)):
+                    assert np.array_equal(canon[t].cpu().numpy(), np.ascontiguousarray(cn[t]).view(np.uint8).ravel()), \
+                        (what, t)
+
+
+def test_pipelined_encode_refusals(gh):
+    """The watermark region must be pinned host memory of the right size and
+    alignment; refused before any launch.  A stream that outgrows its payload
+    buffer stops publishing with DCR_E_CAPACITY."""
+    say("pipelined encode refusals")
+    lay = pipe_layout("random", 3)
+    g = gh.Gpu(lay)
+    sb = dcr.StreamBuffers(g.plan, "cuda")
+    args = (g.plan, g.olds, g.news, 0, 7, 8, sb.header, sb.dir, sb.payload, sb.result, g.ws)
+    for bad in (torch.zeros(dcr.ready_region_bytes(4), dtype=torch.uint8, device="cuda"),   # device memory
+                torch.zeros(dcr.ready_region_bytes(4), dtype=torch.uint8),                  # pageable
+                torch.zeros(64, dtype=torch.uint8, pin_memory=True)):                       # too small
+        with pytest.raises(dcr.DcrError):
+            dcr.dcr_encode_pipelined(*args, 4, bad)
+    with pytest.raises(dcr.DcrError):
+        dcr.dcr_encode_pipelined(*args, 0, torch.zeros(128, dtype=torch.uint8, pin_memory=True))
+    torch.cuda.synchronize()
+    small = dcr.StreamBuffers(g.plan, "cuda", payload_bytes=4096)
+    ready = torch.zeros(dcr.ready_region_bytes(3), dtype=torch.uint8, pin_memory=True)
+    dcr.dcr_encode_pipelined(g.plan, g.olds, g.news, 0, 7, 8, small.header, small.dir, small.payload, small.result,
+                             g.ws, 3, ready)
+    torch.cuda.synchronize()
+    rg = ready.numpy()
+    assert int(rg[8:12].view("<i4")[0]) == dcr.DCR_E_CAPACITY
+    assert int(small.result_host()["status"]) == dcr.DCR_E_CAPACITY
+    n = int(rg[12:16].view("<u4")[0])
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_ready_wait(ready, n - 1, 1000)
+    assert e.value.code == dcr.DCR_E_CAPACITY
+
+
 def test_capacity_overflow(gh, orc):
     """Too-small buffers: status DCR_E_CAPACITY with the required sizes."""
     say("capacity overflow")
