@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
     ap.add_argument("--cpu-reps", type=int, default=4, help="oracle steps timed on the sample")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements outside the step (partial retry, index lists, receiver layout, "
+                         "pipelined transfer); for profiler runs")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of this many GiB, 3 times (counter calibration)")
     ap.add_argument("--pmc-report", metavar="DIR",
@@ -230,116 +233,122 @@ def main():
     ok_after = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
     del canon_new
 
-    # partial retry after a kill at 50 % of the DELTA records (outside the
-    # step): the receiver is set back to old, applies the first half, and the
-    # sender re-encodes only the chunks of the unflagged records
-    canon_o = lay.assemble(as_i16(olds))
-    for t in range(len(T)):
-        canon[t].view(torch.int16).copy_(canon_o[t].reshape(-1))
-    del canon_o
-    flags.zero_()
-    dcr.dcr_apply(plan, canon, hdr, delta.dir, delta.payload, flags, 0, n_rec // 2, 41, ares, ws)
-    torch.cuda.synchronize()
-    pe, pa = [], []
-    for _ in range(3):
-        a_, b_ = pair()
-        a_.record()
-        dcr.dcr_encode_retry_partial(plan, olds, news, hdr, delta.dir, flags, 41, 42, retry.header, retry.dir,
-                                     retry.payload, retry.result, ws)
-        b_.record()
-        torch.cuda.synchronize()
-        pe.append(a_.elapsed_time(b_))
-    pr = retry.result_host()
-    ph = retry.header_host()
-    for _ in range(3):
-        a_, b_ = pair()
-        a_.record()
-        dcr.dcr_apply_overwrite_retry(plan, canon, ph, retry.dir, retry.payload, 41, ares, ws)
-        b_.record()
-        torch.cuda.synchronize()
-        pa.append(a_.elapsed_time(b_))
-    canon_new = lay.assemble(as_i16(news))
-    ok_partial = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
-    del canon_new
-    partial_retry = {"kill_at_records": n_rec // 2, "status": int(pr["status"]), "records": int(pr["n_records"]),
-                     "payload_GB": round(int(pr["payload_bytes"]) / 1e9, 4),
-                     "full_retry_payload_GB": round(rp_bytes / 1e9, 4),
-                     "encode_ms": round(float(np.median(pe)), 4), "full_retry_encode_ms": round(op_ms["encode_retry"], 4),
-                     "apply_ms": round(float(np.median(pa)), 4), "full_retry_apply_ms": round(op_ms["retry"], 4),
-                     "healed_eq_new": bool(ok_partial)}
-    log(f"partial retry at a 50 % kill: {partial_retry}")
-
-    # index-list layout (encode option, outside the step): the same DELTA
-    # change set with low-density records carrying 16-bit indices instead of
-    # the bitmap; encoded into the retry buffers, applied to old, checked
-    canon_o = lay.assemble(as_i16(olds))
-    le, la = [], []
-    for _ in range(3):
-        a_, b_ = pair()
-        a_.record()
-        dcr.dcr_encode(plan, olds, news, dcr.MODE_DELTA | dcr.ENC_INDEX_LISTS, 41, 42, retry.header, retry.dir,
-                       retry.payload, retry.result, ws)
-        b_.record()
-        torch.cuda.synchronize()
-        le.append(a_.elapsed_time(b_))
-    lr = retry.result_host()
-    lh = retry.header_host()
-    ln = int(lr["n_records"])
-    lflags = torch.zeros(max(ln, 1), dtype=torch.uint8, device=dev)
-    for _ in range(3):
+    # extras outside the step (skipped for profiling runs, so that every
+    # launch of the step kernels in a trace belongs to the step)
+    partial_retry = index_lists = sharded_apply = pipelined = None
+    if not args.no_extras:
+        # partial retry after a kill at 50 % of the DELTA records (outside the
+        # step): the receiver is set back to old, applies the first half, and the
+        # sender re-encodes only the chunks of the unflagged records
+        canon_o = lay.assemble(as_i16(olds))
         for t in range(len(T)):
             canon[t].view(torch.int16).copy_(canon_o[t].reshape(-1))
-        lflags.zero_()
-        torch.cuda.synchronize()
-        a_, b_ = pair()
-        a_.record()
-        dcr.dcr_apply(plan, canon, lh, retry.dir, retry.payload, lflags, 0, ln, 41, ares, ws)
-        b_.record()
-        torch.cuda.synchronize()
-        la.append(a_.elapsed_time(b_))
-    del canon_o
-    canon_new = lay.assemble(as_i16(news))
-    ok_lists = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
-    del canon_new
-    index_lists = {"status": int(lr["status"]), "records": ln, "payload_GB": round(int(lr["payload_bytes"]) / 1e9, 4),
-                   "bitmap_payload_GB": round(p_bytes / 1e9, 4), "encode_ms": round(float(np.median(le)), 4),
-                   "bitmap_encode_ms": round(op_ms["encode"], 4), "apply_ms": round(float(np.median(la)), 4),
-                   "bitmap_apply_ms": round(op_ms["apply"], 4), "apply_eq_new": bool(ok_lists)}
-    log(f"index-list layout: {index_lists}")
-
-    # apply straight into a receiver that stores the model as TP=2 engine
-    # shards (outside the step): the DELTA stream through the receiver plan
-    lay_r = synth.llama_layout(tp=2)
-    rplan = dcr.dcr_plan_build(lay_r.tensors, [lay_r.shard_bytes(s) for s in range(lay_r.n_shards)],
-                               lay_r.segments)
-    dcr.dcr_plan_upload(rplan, dev)
-    rws = dcr.workspace(rplan, dev)
-    canon_o = lay.assemble(as_i16(olds))
-    rbuf, rsh = synth.scatter_canonical_gpu(lay_r, canon_o, dev)
-    del canon_o
-    torch.cuda.synchronize()
-    sa = []
-    for _ in range(3):       # XOR records toggle old -> new -> old -> new
+        del canon_o
         flags.zero_()
-        a_, b_ = pair()
-        a_.record()
-        dcr.dcr_apply_sharded(rplan, rsh, hdr, delta.dir, delta.payload, flags, 0, n_rec, 41, ares, rws)
-        b_.record()
+        dcr.dcr_apply(plan, canon, hdr, delta.dir, delta.payload, flags, 0, n_rec // 2, 41, ares, ws)
         torch.cuda.synchronize()
-        sa.append(a_.elapsed_time(b_))
-    got = lay_r.assemble([x.view(torch.int16) for x in rsh])
-    canon_new = lay.assemble(as_i16(news))
-    ok_sharded = all(torch.equal(got[t].reshape(-1), canon_new[t].reshape(-1)) for t in range(len(T)))
-    del got, canon_new, rbuf, rsh, rws
-    torch.cuda.empty_cache()
-    sharded_apply = {"receiver": "the same model as TP=2 engine shards (325 shards, 744 833 pieces)",
-                     "apply_ms": round(float(np.median(sa)), 4), "canonical_apply_ms": round(op_ms["apply"], 4),
-                     "eq_new": bool(ok_sharded)}
-    log(f"apply into a TP=2 receiver layout: {sharded_apply}")
+        pe, pa = [], []
+        for _ in range(3):
+            a_, b_ = pair()
+            a_.record()
+            dcr.dcr_encode_retry_partial(plan, olds, news, hdr, delta.dir, flags, 41, 42, retry.header, retry.dir,
+                                         retry.payload, retry.result, ws)
+            b_.record()
+            torch.cuda.synchronize()
+            pe.append(a_.elapsed_time(b_))
+        pr = retry.result_host()
+        ph = retry.header_host()
+        for _ in range(3):
+            a_, b_ = pair()
+            a_.record()
+            dcr.dcr_apply_overwrite_retry(plan, canon, ph, retry.dir, retry.payload, 41, ares, ws)
+            b_.record()
+            torch.cuda.synchronize()
+            pa.append(a_.elapsed_time(b_))
+        canon_new = lay.assemble(as_i16(news))
+        ok_partial = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
+        del canon_new
+        partial_retry = {"kill_at_records": n_rec // 2, "status": int(pr["status"]), "records": int(pr["n_records"]),
+                         "payload_GB": round(int(pr["payload_bytes"]) / 1e9, 4),
+                         "full_retry_payload_GB": round(rp_bytes / 1e9, 4),
+                         "encode_ms": round(float(np.median(pe)), 4),
+                         "full_retry_encode_ms": round(op_ms["encode_retry"], 4),
+                         "apply_ms": round(float(np.median(pa)), 4), "full_retry_apply_ms": round(op_ms["retry"], 4),
+                         "healed_eq_new": bool(ok_partial)}
+        log(f"partial retry at a 50 % kill: {partial_retry}")
 
-    pipelined = pipelined_transfer(plan, lay, olds, news, canon, as_i16, ws, delta, n_rec, p_bytes, dev,
-                                   op_ms["encode"], op_ms["apply"])
-    log(f"pipelined transfer through pinned host memory: {pipelined}")
+        # index-list layout (encode option, outside the step): the same DELTA
+        # change set with low-density records carrying 16-bit indices instead of
+        # the bitmap; encoded into the retry buffers, applied to old, checked
+        canon_o = lay.assemble(as_i16(olds))
+        le, la = [], []
+        for _ in range(3):
+            a_, b_ = pair()
+            a_.record()
+            dcr.dcr_encode(plan, olds, news, dcr.MODE_DELTA | dcr.ENC_INDEX_LISTS, 41, 42, retry.header, retry.dir,
+                           retry.payload, retry.result, ws)
+            b_.record()
+            torch.cuda.synchronize()
+            le.append(a_.elapsed_time(b_))
+        lr = retry.result_host()
+        lh = retry.header_host()
+        ln = int(lr["n_records"])
+        lflags = torch.zeros(max(ln, 1), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            for t in range(len(T)):
+                canon[t].view(torch.int16).copy_(canon_o[t].reshape(-1))
+            lflags.zero_()
+            torch.cuda.synchronize()
+            a_, b_ = pair()
+            a_.record()
+            dcr.dcr_apply(plan, canon, lh, retry.dir, retry.payload, lflags, 0, ln, 41, ares, ws)
+            b_.record()
+            torch.cuda.synchronize()
+            la.append(a_.elapsed_time(b_))
+        del canon_o
+        canon_new = lay.assemble(as_i16(news))
+        ok_lists = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
+        del canon_new
+        index_lists = {"status": int(lr["status"]), "records": ln,
+                       "payload_GB": round(int(lr["payload_bytes"]) / 1e9, 4),
+                       "bitmap_payload_GB": round(p_bytes / 1e9, 4), "encode_ms": round(float(np.median(le)), 4),
+                       "bitmap_encode_ms": round(op_ms["encode"], 4), "apply_ms": round(float(np.median(la)), 4),
+                       "bitmap_apply_ms": round(op_ms["apply"], 4), "apply_eq_new": bool(ok_lists)}
+        log(f"index-list layout: {index_lists}")
+
+        # apply straight into a receiver that stores the model as TP=2 engine
+        # shards (outside the step): the DELTA stream through the receiver plan
+        lay_r = synth.llama_layout(tp=2)
+        rplan = dcr.dcr_plan_build(lay_r.tensors, [lay_r.shard_bytes(s) for s in range(lay_r.n_shards)],
+                                   lay_r.segments)
+        dcr.dcr_plan_upload(rplan, dev)
+        rws = dcr.workspace(rplan, dev)
+        canon_o = lay.assemble(as_i16(olds))
+        rbuf, rsh = synth.scatter_canonical_gpu(lay_r, canon_o, dev)
+        del canon_o
+        torch.cuda.synchronize()
+        sa = []
+        for _ in range(3):       # XOR records toggle old -> new -> old -> new
+            flags.zero_()
+            a_, b_ = pair()
+            a_.record()
+            dcr.dcr_apply_sharded(rplan, rsh, hdr, delta.dir, delta.payload, flags, 0, n_rec, 41, ares, rws)
+            b_.record()
+            torch.cuda.synchronize()
+            sa.append(a_.elapsed_time(b_))
+        got = lay_r.assemble([x.view(torch.int16) for x in rsh])
+        canon_new = lay.assemble(as_i16(news))
+        ok_sharded = all(torch.equal(got[t].reshape(-1), canon_new[t].reshape(-1)) for t in range(len(T)))
+        del got, canon_new, rbuf, rsh, rws
+        torch.cuda.empty_cache()
+        sharded_apply = {"receiver": "the same model as TP=2 engine shards (325 shards, 744 833 pieces)",
+                         "apply_ms": round(float(np.median(sa)), 4), "canonical_apply_ms": round(op_ms["apply"], 4),
+                         "eq_new": bool(ok_sharded)}
+        log(f"apply into a TP=2 receiver layout: {sharded_apply}")
+
+        pipelined = pipelined_transfer(plan, lay, olds, news, canon, as_i16, ws, delta, n_rec, p_bytes, dev,
+                                       op_ms["encode"], op_ms["apply"])
+        log(f"pipelined transfer through pinned host memory: {pipelined}")
 
     enc_bytes = 2 * cb + 32 * n_rec + p_bytes
     renc_bytes = 2 * cb + 32 * rn_rec + rp_bytes

@@ -871,10 +871,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     __shared__ EncodeShared S;
     if (blockIdx.x >= n) return;
     const uint32_t tile = tiles[blockIdx.x];
-    if (!tile_wanted(a, tile)) {
-        skip_tile(a, tile, false);
-        return;
-    }
+    if (!tile_wanted(a, tile)) return;   // the fix-up counts it as empty
     const TileCtx c = tile_ctx(a, tile);
     if (c.w == 2) staged_tile<2>(a, S, c);
     else if (c.w == 1) staged_tile<1>(a, S, c);
@@ -929,10 +926,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     __shared__ EncodeShared S;
     if (blockIdx.x >= n_list) return;
     const uint32_t tid = threadIdx.x;
-    if (!tile_wanted(a, list[blockIdx.x])) {
-        skip_tile(a, list[blockIdx.x], false);
-        return;
-    }
+    if (!tile_wanted(a, list[blockIdx.x])) return;   // the fix-up counts it as empty
     const TileCtx c = tile_ctx(a, list[blockIdx.x]);
     // the slot's address is uniform: read it before this workgroup stores
     // anything, into scalar registers
@@ -967,6 +961,7 @@ struct FixArgs {
     const uint64_t* tile_agg;
     const uint64_t* tile_info;
     const uint64_t* slots;
+    const uint64_t* need;      // partial retry: wanted-chunk bits (others count as empty), else NULL
     uint64_t* fix_status;
     uint32_t* counter;
     const uint8_t* stage;
@@ -993,7 +988,7 @@ __global__ __launch_bounds__(256) void encode_fixup_kernel(FixArgs a) {
     __syncthreads();
     const uint32_t blk = sgpr(blk_s);
     const uint32_t t = blk * kFixTiles + tid;
-    const bool in = t < a.n_tiles;
+    const bool in = t < a.n_tiles && (!a.need || ((a.need[t >> 6] >> (t & 63u)) & 1u));
     const uint64_t v = in ? a.tile_agg[t] : 0;
     const uint64_t info = in ? a.tile_info[t] : 0;
     const uint64_t inc = wave_incl_scan(v, lane);
@@ -2024,6 +2019,7 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
     f.tile_agg = a.tile_agg;
     f.tile_info = a.tile_info;
     f.slots = a.slots;
+    f.need = a.need;
     f.fix_status = reinterpret_cast<uint64_t*>(ws + p.ws_fix);
     f.counter = counter;
     f.stage = stage;
