@@ -51,7 +51,9 @@ class HostLoopback:
         the prefix headers and, per slice, an event that completes when the
         slice is in host memory."""
         import torch
-        ready = torch.zeros(dcr.ready_region_bytes(n_slices), dtype=torch.uint8, pin_memory=True)
+        # kept on the object: after a failed wait the encode may still
+        # publish into it, so it must not go back to torch's pinned pool
+        self._ready = ready = torch.zeros(dcr.ready_region_bytes(n_slices), dtype=torch.uint8, pin_memory=True)
         dcr.dcr_encode_pipelined(self.plan, old_shards, new_shards, mode, base_version, new_version, sb.header,
                                  sb.dir, sb.payload, sb.result, workspace, n_slices, ready)
         n = int(ready.numpy()[12:16].view("<u4")[0])
