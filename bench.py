@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--lists-cfg5", action="store_true",
                     help="only compare the bitmap and index-list streams on config 5's NVFP4 region (40 GB at "
                          "0.085 %% bytes) and a 29 GB slice of its BF16 region (3 %%); print one JSON line")
+    ap.add_argument("--configs", action="store_true",
+                    help="only time encode / apply / retry on the other workloads at full size (4096x4096 "
+                         "tensor at 1 %%; Qwen3-30B-A3B-shaped EP=8 at 3 %% Beta(2,60) rates; the same at 5 %% "
+                         "hot rows, block-scaled; the 240 GB receiver share, apply and retry only); print one "
+                         "JSON line")
     ap.add_argument("--pmc-dump", metavar="DIR",
                     help="per-kernel averages of every counter in the rocprofv3 runs under DIR/pmc_*; exit")
     return ap.parse_args()
@@ -98,6 +103,9 @@ def main():
         return
     if args.lists_cfg5:
         print(json.dumps(lists_cfg5(dev)), flush=True)
+        return
+    if args.configs:
+        print(json.dumps(bench_configs(dev)), flush=True)
         return
 
     # ---------------------------------------------------------------- setup
@@ -177,9 +185,18 @@ def main():
     # touched 128-byte lines and 32-byte sectors (apply traffic model), from old vs new
     touched = touched_sec = 0
     canon_o = lay.assemble(as_i16(olds))
+    # one flag per 16-byte group of canon_buf holding a change (the groups an
+    # apply patches), for the read-modify-write ceiling below
+    n_groups = (int(offs[-1]) // 16 + 127) // 128 * 128
+    gflags = torch.zeros(n_groups, dtype=torch.bool, device=dev)
     for t in range(len(T)):
         d = (canon_o[t].reshape(-1) != canon_new[t].reshape(-1))
         n = d.numel()
+        ng = (n + 7) // 8
+        gd = torch.zeros(ng * 8, dtype=torch.bool, device=dev)
+        gd[:n] = d
+        gflags[int(offs[t]) // 16:int(offs[t]) // 16 + ng] = gd.view(-1, 8).any(1)
+        del gd
         for gran in (LINE, SECTOR):
             per = gran // 2
             full = n // per * per
@@ -189,6 +206,12 @@ def main():
             else:
                 touched_sec += cnt
     del canon_new, canon_o
+    gbits = torch.zeros(n_groups // 8, dtype=torch.uint8, device=dev)
+    gv = gflags.view(-1, 8)
+    for k in range(8):
+        gbits |= gv[:, k].to(torch.uint8) << k
+    n_touched_groups = int(gflags.sum())
+    del gflags, gv
     torch.cuda.empty_cache()
     log(f"first step: apply==new {ok_apply}, retry==new {ok_retry}; {n_rec} records "
         f"{p_bytes / 1e9:.3f} GB payload; retry {rn_rec} records {rp_bytes / 1e9:.3f} GB; "
@@ -378,9 +401,12 @@ def main():
             "traffic": measured_traffic(dom)}
 
     # measured ceilings on this GPU: a streaming read and a device copy
-    ceiling = measure_ceiling(old_buf, dev)
+    ceiling = measure_ceiling(old_buf, dev, rmw=(canon_buf, gbits, n_touched_groups, touched))
     for op in ops:
         per_op[op]["kernel_frac_of_read_ceiling"] = round(per_op[op]["kernel_alg_GBps"] / ceiling["read_GBps"], 4)
+    # apply / retry against the bare patch of the same groups (no records read)
+    for op in ("apply", "retry"):
+        per_op[op]["kernel_frac_of_rmw_ceiling"] = round(ceiling["rmw"]["ms"] / kern_ms[op], 4)
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
@@ -580,10 +606,359 @@ def lists_cfg5(dev, reps=3):
     return {"lists_cfg5": out}
 
 
-def measure_ceiling(buf, dev, reps=3):
+def _views(lay, buf, shards):
+    """Per canonical tensor, a view of the flat shard buffer holding it (every
+    tensor of these layouts is one contiguous run of one shard)."""
+    import torch
+    base = buf.data_ptr()
+    out = [None] * lay.n_tensors
+    for g in lay.segments:
+        t, sh = int(g["tensor_id"]), int(g["shard_id"])
+        n, w = int(lay.tensors[t]["numel"]), int(lay.tensors[t]["elem_bytes"])
+        assert int(g["ndim"]) == 1 and int(g["shard_stride"][0]) == 1 and int(g["canon_off"]) == 0
+        assert int(g["extent"][0]) == n and out[t] is None
+        o = shards[sh].data_ptr() - base + int(g["shard_off"]) * w
+        out[t] = buf[o:o + n * w]
+    return out
+
+
+def _touched(old_views, new_views, gbits_buf, byte_offs):
+    """Touched 16-byte groups, 32-byte sectors and 128-byte lines of the
+    tensors (old vs new bytes); sets each touched group's bit in gbits_buf,
+    one bit per 16-byte group of the flat receiver buffer in which tensor i
+    starts at byte byte_offs[i] (a multiple of 128)."""
+    import torch
+    g = s_ = l_ = 0
+    for o, n, boff in zip(old_views, new_views, byte_offs):
+        nb = o.numel()
+        assert nb % 16 == 0 and boff % 128 == 0
+        d = (o.view(torch.int64) != n.view(torch.int64)).view(-1, 2).any(1)
+        ng = d.numel()
+        g += int(d.sum())
+        pad = torch.zeros((ng + 7) // 8 * 8, dtype=torch.bool, device=d.device)
+        pad[:ng] = d
+        sec = pad.view(-1, 2).any(1)
+        s_ += int(sec.sum())
+        l_ += int(pad.view(-1, 8).any(1).sum())
+        g0 = boff // 16
+        byte = torch.zeros(pad.numel() // 8, dtype=torch.uint8, device=d.device)
+        pv = pad.view(-1, 8)
+        for k in range(8):
+            byte |= pv[:, k].to(torch.uint8) << k
+        gbits_buf[g0 // 8:g0 // 8 + byte.numel()] |= byte
+    return g, s_, l_
+
+
+def _op_stats(ms, kms, alg, scanned):
+    return {"ms": round(float(np.median(ms)), 4), "kernel_ms": round(float(np.median(kms)), 4),
+            "alg_GB": round(alg / 1e9, 4), "kernel_alg_GBps": round(alg / (np.median(kms) * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg / (np.median(kms) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "scanned_GBps": round(scanned / (np.median(ms) * 1e-3) / 1e9, 1)}
+
+
+def _timed(fn, reps):
+    """Median-able lists of call and main-kernel times (HIP events)."""
+    import torch
+    from bit_exact_xor_amd import dcr
+    ms, kms = [], []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[2].record()
+        e[3].record()         # creates the events the library records into
+        dcr.dcr_set_kernel_events(e[2], e[3])
+        e[0].record()
+        fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        dcr.dcr_set_kernel_events(None, None)
+        ms.append(e[0].elapsed_time(e[1]))
+        kms.append(e[2].elapsed_time(e[3]))
+    return ms, kms
+
+
+def _bench_layout(lay, dev, reps, host_values=None):
+    """Encode DELTA / RETRY (staged when the staging area fits), apply and
+    retry of one full-size layout whose canonical tensors are contiguous
+    shard runs: the receiver is a copy of the old shard buffer, patched in
+    place through per-tensor views."""
+    import torch
+    from bit_exact_xor_amd import dcr, synth
+    T = lay.tensors
+    plan = dcr.dcr_plan_build(T, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
+    dcr.dcr_plan_upload(plan, dev)
+    info = plan.info
+    cb = int(info.canonical_bytes)
+    old_buf, olds = synth.alloc_shards(lay, dev)
+    new_buf, news = synth.alloc_shards(lay, dev)
+    if host_values is not None:
+        for dst, src in zip(olds, host_values[0]):
+            dst.copy_(torch.from_numpy(src.view(np.uint8)))
+        for dst, src in zip(news, host_values[1]):
+            dst.copy_(torch.from_numpy(src.view(np.uint8)))
+    else:
+        synth.fill_shards_gpu(lay, olds, 0)
+        synth.fill_shards_gpu(lay, news, 1)
+    torch.cuda.synchronize()
+    cap = int(cb * 0.16) + (1 << 24)
+    delta = dcr.StreamBuffers(plan, dev, dir_bytes=2 * 32 * int(info.n_chunks), payload_bytes=cap)
+    retry = dcr.StreamBuffers(plan, dev, dir_bytes=2 * 32 * int(info.n_chunks), payload_bytes=cap)
+    free, _ = torch.cuda.mem_get_info()
+    stage = int(info.max_payload_bytes)
+    # the receiver copy and the group bits come after the encodes
+    staged = stage + cb + (8 << 30) < int(free)
+    ws = dcr.workspace(plan, dev, stage if staged else 0)
+
+    def enc(sb, mode):
+        dcr.dcr_encode(plan, olds, news, mode, 41, 42, sb.header, sb.dir, sb.payload, sb.result, ws)
+
+    enc(delta, 0)
+    enc(retry, 1)
+    torch.cuda.synchronize()
+    for nm, sb in (("delta", delta), ("retry", retry)):
+        r = sb.result_host()
+        if int(r["status"]) != 0:
+            raise SystemExit(f"{lay.name} {nm} stream does not fit: {r}")
+    n_rec, p_bytes = delta.n_records(), delta.payload_bytes()
+    rn_rec, rp_bytes = retry.n_records(), retry.payload_bytes()
+    n_changed = int(delta.result_host()["n_changed"])
+    e_ms, e_kms = _timed(lambda: enc(delta, 0), reps)
+    r_ms, r_kms = _timed(lambda: enc(retry, 1), reps)
+    del ws
+    torch.cuda.empty_cache()
+    ws = dcr.workspace(plan, dev)
+    hdr, rhdr = delta.header_host(), retry.header_host()
+    recv = old_buf.clone()
+    canon = _views(lay, recv, [recv[s.data_ptr() - old_buf.data_ptr():][:s.numel()] for s in olds])
+    ov = _views(lay, old_buf, olds)
+    nv = _views(lay, new_buf, news)
+    gbits = torch.zeros((old_buf.numel() // 16 + 127) // 128 * 16, dtype=torch.uint8, device=dev)
+    n_groups, n_sec, n_lines = _touched(ov, nv, gbits, [v.data_ptr() - old_buf.data_ptr() for v in ov])
+    flags = torch.zeros(max(n_rec, 1), dtype=torch.uint8, device=dev)
+    res = torch.zeros(32, dtype=torch.uint8, device=dev)
+
+    def apply():
+        flags.zero_()
+        dcr.dcr_apply(plan, canon, hdr, delta.dir, delta.payload, flags, 0, n_rec, 41, res, ws)
+
+    def do_retry():
+        dcr.dcr_apply_overwrite_retry(plan, canon, rhdr, retry.dir, retry.payload, 41, res, ws)
+
+    apply()
+    torch.cuda.synchronize()
+    ok_apply = all(torch.equal(a, b) for a, b in zip(canon, nv))
+    a_ms, a_kms = [], []
+    t_ms, t_kms = [], []
+    for _ in range(reps):
+        x = _timed(apply, 1)
+        y = _timed(do_retry, 1)     # back to new: every apply starts from the same state
+        a_ms += x[0]
+        a_kms += x[1]
+        t_ms += y[0]
+        t_kms += y[1]
+    ok_retry = all(torch.equal(a, b) for a, b in zip(canon, nv))
+    # read-modify-write ceiling over the touched groups (even count: restored)
+    rm = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        synth.rmw_probe_gpu(recv, gbits)
+        e1.record()
+        torch.cuda.synchronize()
+        rm.append(e0.elapsed_time(e1))
+    rmw_ms = min(rm)
+    app_alg = 32 * n_rec + p_bytes + LINE * n_lines + SECTOR * n_sec
+    ret_alg = 32 * rn_rec + rp_bytes + LINE * n_lines + SECTOR * n_sec
+    out = {"canonical_GB": round(cb / 1e9, 3), "tensors": int(info.n_tensors), "chunks": int(info.n_chunks),
+           "changed_frac_of_elements": round(n_changed / sum(int(t["numel"]) for t in T), 6),
+           "staged_encode": bool(staged),
+           "delta": {"records": n_rec, "payload_GB": round(p_bytes / 1e9, 4)},
+           "retry_stream": {"records": rn_rec, "payload_GB": round(rp_bytes / 1e9, 4)},
+           "touched": {"groups16": n_groups, "sectors32": n_sec, "lines128": n_lines},
+           "encode": _op_stats(e_ms, e_kms, 2 * cb + p_bytes, cb),
+           "encode_retry": _op_stats(r_ms, r_kms, 2 * cb + rp_bytes, cb),
+           "apply": _op_stats(a_ms, a_kms, app_alg, cb),
+           "retry": _op_stats(t_ms, t_kms, ret_alg, cb),
+           "rmw_ceiling_ms": round(rmw_ms, 4),
+           "checks": {"apply_eq_new": bool(ok_apply), "retry_eq_new": bool(ok_retry)}}
+    for op in ("apply", "retry"):
+        out[op]["kernel_frac_of_rmw_ceiling"] = round(rmw_ms / out[op]["kernel_ms"], 4)
+    del recv, canon, old_buf, new_buf, olds, news, delta, retry, ws, gbits, flags
+    torch.cuda.empty_cache()
+    return out
+
+
+def _bench_cfg5(dev, reps, window=256):
+    """The 240 GB receiver share: streams built window by window (the new
+    values never fit beside the receiver), then the DELTA apply of every
+    record and the overwrite retry of every record, timed in place."""
+    import torch
+    from bit_exact_xor_amd import dcr, synth
+    lay = synth.config5_layout()
+    T = lay.tensors
+    plan_full = dcr.dcr_plan_build(T, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
+    dcr.dcr_plan_upload(plan_full, dev)
+    n_chunks = int(plan_full.info.n_chunks)
+    sizes = [lay.shard_bytes(s) for s in range(lay.n_shards)]
+    offs = np.concatenate([[0], np.cumsum([(s + 255) // 256 * 256 for s in sizes])]).astype(np.int64)
+    cbuf = torch.empty(int(offs[-1]), dtype=torch.uint8, device=dev)
+    canon = [cbuf[int(offs[t]):int(offs[t]) + sizes[t]] for t in range(len(sizes))]
+    synth.fill_shards_gpu(lay, canon, 0)
+    wbytes = max(sum((sizes[t] + 255) // 256 * 256 for t in range(a, min(len(sizes), a + window)))
+                 for a in range(0, len(sizes), window))
+    t_old = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    t_new = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    gbits = torch.zeros((cbuf.numel() // 16 + 127) // 128 * 16, dtype=torch.uint8, device=dev)
+    ws = dcr.workspace(plan_full, dev)
+    res = torch.zeros(32, dtype=torch.uint8, device=dev)
+    touched = [0, 0, 0]
+
+    def build(mode, dir_buf, payload, count):
+        r_off = p_off = changed = 0
+        for a in range(0, lay.n_tensors, window):
+            b_ = min(lay.n_tensors, a + window)
+            wl = synth.window_layout(lay, a, b_)
+            plan = dcr.dcr_plan_build(wl.tensors, [wl.shard_bytes(s) for s in range(wl.n_shards)], wl.segments)
+            dcr.dcr_plan_upload(plan, dev)
+            olds, news, off = [], [], 0
+            for s in range(wl.n_shards):
+                nb = wl.shard_bytes(s)
+                olds.append(t_old[off:off + nb])
+                news.append(t_new[off:off + nb])
+                off += (nb + 255) // 256 * 256
+            synth.fill_shards_gpu(wl, olds, 0)
+            synth.fill_shards_gpu(wl, news, 1)
+            if count:
+                # this window's old / new bytes, flagged at the receiver's offsets
+                gi, si, li = _touched(olds, news, gbits,
+                                      [canon[a + i].data_ptr() - cbuf.data_ptr() for i in range(b_ - a)])
+                touched[0] += gi
+                touched[1] += si
+                touched[2] += li
+            wsw = dcr.workspace(plan, dev)
+            hdr_w = torch.zeros(64, dtype=torch.uint8, device=dev)
+            rs = torch.zeros(32, dtype=torch.uint8, device=dev)
+            dcr.dcr_encode(plan, olds, news, mode, 5, 6, hdr_w, dir_buf[r_off * 32:], payload[p_off:], rs, wsw)
+            torch.cuda.synchronize()
+            r = np.frombuffer(rs.cpu().numpy().tobytes(), dtype=dcr.ENCODE_RESULT)[0]
+            assert int(r["status"]) == 0, (a, r)
+            n, pb = int(r["n_records"]), int(r["payload_bytes"])
+            if n:
+                e32 = dir_buf[r_off * 32:(r_off + n) * 32].view(torch.int32).view(-1, 8)
+                e64 = dir_buf[r_off * 32:(r_off + n) * 32].view(torch.int64).view(-1, 4)
+                e32[:, 0] += a
+                e64[:, 2] += p_off
+            r_off += n
+            p_off += pb
+            changed += int(r["n_changed"])
+        hdr = np.zeros(64, dtype=np.uint8)
+        h = hdr.view(np.uint32)
+        h[0], h[2] = 0x31524344, 65536
+        hdr[4:6].view(np.uint16)[0] = 1
+        hdr[6:8].view(np.uint16)[0] = mode
+        hdr[16:24].view(np.uint64)[0] = 5
+        hdr[24:32].view(np.uint64)[0] = 6
+        hdr[32:40].view(np.uint64)[0] = plan_full.info.fingerprint
+        hdr[40:48].view(np.uint64)[0] = r_off
+        hdr[48:56].view(np.uint64)[0] = p_off
+        return hdr, r_off, p_off, changed
+
+    def eq_new():
+        ok = True
+        for a in range(0, lay.n_tensors, window):
+            b_ = min(lay.n_tensors, a + window)
+            wl = synth.window_layout(lay, a, b_)
+            news, off = [], 0
+            for s in range(wl.n_shards):
+                nb = wl.shard_bytes(s)
+                news.append(t_new[off:off + nb])
+                off += (nb + 255) // 256 * 256
+            synth.fill_shards_gpu(wl, news, 1)
+            ok = ok and all(torch.equal(canon[a + i], news[i]) for i in range(b_ - a))
+        return ok
+
+    cb = int(plan_full.info.canonical_bytes)
+    dir_buf = torch.empty(32 * n_chunks, dtype=torch.uint8, device=dev)
+    payload = torch.empty(26 * 10**9, dtype=torch.uint8, device=dev)
+    hdr, n_rec, p_bytes, changed = build(0, dir_buf, payload, True)
+    flags = torch.zeros(n_rec, dtype=torch.uint8, device=dev)
+
+    def apply():
+        flags.zero_()
+        dcr.dcr_apply(plan_full, canon, hdr, dir_buf, payload, flags, 0, n_rec, 5, res, ws)
+
+    # every rep applies the same XOR stream: old -> new -> old ...
+    a_ms, a_kms = _timed(apply, 2 * ((reps + 1) // 2) + 1)
+    ok_apply = eq_new()
+    rm = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        synth.rmw_probe_gpu(cbuf, gbits)
+        e1.record()
+        torch.cuda.synchronize()
+        rm.append(e0.elapsed_time(e1))
+    del dir_buf, payload, flags
+    torch.cuda.empty_cache()
+    rdir = torch.empty(32 * n_chunks, dtype=torch.uint8, device=dev)
+    rpay = torch.empty(28 * 10**9, dtype=torch.uint8, device=dev)
+    rhdr, rn, rpb, _ = build(1, rdir, rpay, False)
+    t_ms, t_kms = _timed(lambda: dcr.dcr_apply_overwrite_retry(plan_full, canon, rhdr, rdir, rpay, 5, res, ws), reps)
+    ok_retry = eq_new()
+    rmw_ms = min(rm)
+    g, s_, l_ = touched
+    out = {"canonical_GB": round(cb / 1e9, 3), "tensors": int(plan_full.info.n_tensors), "chunks": n_chunks,
+           "delta": {"records": n_rec, "payload_GB": round(p_bytes / 1e9, 4), "changed": changed},
+           "retry_stream": {"records": rn, "payload_GB": round(rpb / 1e9, 4)},
+           "touched": {"groups16": g, "sectors32": s_, "lines128": l_},
+           "apply": _op_stats(a_ms, a_kms, 32 * n_rec + p_bytes + LINE * l_ + SECTOR * s_, cb),
+           "retry": _op_stats(t_ms, t_kms, 32 * rn + rpb + LINE * l_ + SECTOR * s_, cb),
+           "rmw_ceiling_ms": round(rmw_ms, 4),
+           "checks": {"apply_eq_new": bool(ok_apply), "retry_eq_new": bool(ok_retry)},
+           "note": "apply-only workload: the streams are built window by window outside the timing"}
+    for op in ("apply", "retry"):
+        out[op]["kernel_frac_of_rmw_ceiling"] = round(rmw_ms / out[op]["kernel_ms"], 4)
+    del cbuf, canon, rdir, rpay, t_old, t_new, gbits, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_configs(dev, reps=5):
+    """Encode / apply / retry timings on the other full-size workloads."""
+    import gc
+    import torch
+    from bit_exact_xor_amd import synth
+    out = {"what": "encode/apply/retry kernel and call times (medians, HIP events) on full-size workloads; "
+                   "hbm_frac = algorithmic bytes / kernel time / 8 TB/s"}
+    lay1 = synth.config1_layout()
+    o1, n1, _lr, _pos = synth.config1_values(lay1, lr=synth.CFG1_LR)
+    for name, lay, hv in (("tensor_4096x4096_1pct", lay1, ([o1], [n1])),
+                          ("qwen3_30b_a3b_ep8_3pct_beta", None, None),
+                          ("qwen3_30b_a3b_5pct_hot_block_scaled", None, None)):
+        if lay is None:
+            lay = synth.config3_layout() if "beta" in name else synth.config4_layout()
+        log(f"configs: {name}")
+        out[name] = _bench_layout(lay, dev, reps, hv)
+        gc.collect()
+        torch.cuda.empty_cache()
+    log("configs: receiver_share_240GB")
+    free, _ = torch.cuda.mem_get_info()
+    need = 240 * 10**9 + 16 * 10**9 + 2 * 10**9 + 26 * 10**9
+    if free < need:
+        out["receiver_share_240GB"] = {"skipped": f"needs {need / 1e9:.0f} GB of free HBM, "
+                                                  f"{free / 1e9:.0f} GB available"}
+    else:
+        out["receiver_share_240GB"] = _bench_cfg5(dev, reps=3)
+    return out
+
+
+def measure_ceiling(buf, dev, reps=3, rmw=None):
     """Best of `reps`: one streaming read of `buf` (the probe kernel of the
-    synthetic-input library: 128-bit non-temporal loads, nothing written) and
-    a 4 GiB device-to-device copy (torch; read + write counted)."""
+    synthetic-input library: 128-bit non-temporal loads, nothing written), a
+    4 GiB device-to-device copy (torch; read + write counted) and a 4 GiB
+    fill (torch; write only).  With `rmw` = (canonical buffer, group bits,
+    touched groups, touched lines): best of four runs of the synthetic
+    library's read-modify-write probe over the groups an apply patches (an
+    even count, so the buffer ends as it started)."""
     import torch
     from bit_exact_xor_amd import synth
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -607,14 +982,41 @@ def measure_ceiling(buf, dev, reps=3):
         b.record()
         torch.cuda.synchronize()
         cp.append(a.elapsed_time(b))
+    wr = []
+    for _ in range(reps):
+        a, b = ev(), ev()
+        a.record()
+        dst.zero_()
+        b.record()
+        torch.cuda.synchronize()
+        wr.append(a.elapsed_time(b))
     del dst
     torch.cuda.empty_cache()
     read_gbps = nread / (min(rd) * 1e-3) / 1e9
     copy_gbps = 2 * src.numel() / (min(cp) * 1e-3) / 1e9
-    return {"read_GBps": round(read_gbps, 1), "copy_GBps": round(copy_gbps, 1),
-            "read_frac_of_peak": round(read_gbps / PEAK_HBM_GBPS, 4),
-            "how": f"streaming read of {nread / 1e9:.2f} GB (128-bit non-temporal loads) and a "
-                   f"{src.numel() / 2**30:.0f} GiB torch device copy (read + write counted), best of {reps}"}
+    write_gbps = src.numel() / (min(wr) * 1e-3) / 1e9
+    out = {"read_GBps": round(read_gbps, 1), "write_GBps": round(write_gbps, 1), "copy_GBps": round(copy_gbps, 1),
+           "read_frac_of_peak": round(read_gbps / PEAK_HBM_GBPS, 4),
+           "how": f"streaming read of {nread / 1e9:.2f} GB (128-bit non-temporal loads), a "
+                  f"{src.numel() / 2**30:.0f} GiB torch device copy (read + write counted) and fill, best of {reps}"}
+    if rmw is not None:
+        cbuf, bits, n_groups, n_lines = rmw
+        rm = []
+        for _ in range(4):
+            a, b = ev(), ev()
+            a.record()
+            synth.rmw_probe_gpu(cbuf, bits)
+            b.record()
+            torch.cuda.synchronize()
+            rm.append(a.elapsed_time(b))
+        ms = min(rm)
+        out["rmw"] = {"ms": round(ms, 4), "groups": n_groups, "lines": n_lines,
+                      "line_GBps": round(2 * LINE * n_lines / (ms * 1e-3) / 1e9, 1),
+                      "how": "read-modify-write (XOR) of the 16-byte groups an apply of this stream patches, "
+                             "in place in the canonical buffer, no records read; one thread per 16 consecutive "
+                             "groups; best of 4 (even: the buffer ends unchanged); line_GBps counts a 128-byte "
+                             "line read and written per touched line"}
+    return out
 
 
 def cpu_baseline(lay, delta, hdr_dev, reps):

@@ -120,6 +120,26 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const v4u* buf, uint64_
     if (f == 0x9E3779B9u) sink[0] = f;
 }
 
+// Read-modify-write probe, used only to measure this GPU's ceiling for the
+// access pattern of an in-place patch: every 16-byte group whose bit is set
+// in `bits` (LSB first, one bit per group) is read, XORed with a fixed
+// nonzero mask and written back, nothing else is touched.  Thread t owns the
+// 16 consecutive groups 16t .. 16t + 15 (bits[t]).  Two runs restore the
+// buffer.
+__global__ __launch_bounds__(256) void rmw_probe_kernel(v4u* buf, const uint16_t* bits, uint64_t n16) {
+    const uint64_t t = uint64_t(blockIdx.x) * 256u + threadIdx.x;
+    const uint64_t g0 = t * 16u;
+    if (g0 >= n16) return;
+    uint32_t b = bits[t];
+    if (n16 - g0 < 16u) b &= (1u << uint32_t(n16 - g0)) - 1u;
+    const v4u m = {0x00010001u, 0x00800080u, 0x01000100u, 0x80008000u};
+    while (b) {
+        const uint32_t i = uint32_t(__ffs(b) - 1);
+        b &= b - 1u;
+        buf[g0 + i] ^= m;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,6 +170,21 @@ int32_t dcr_synth_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, vo
     if (blocks > 0x7FFFFFFFull) return int32_t(hipErrorInvalidValue);
     hipLaunchKernelGGL(read_probe_kernel, dim3(uint32_t(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const v4u*>(buf), bytes / 16, sink);
+    return int32_t(hipGetLastError());
+}
+
+// XOR a fixed mask into every 16-byte group of `buf` (`bytes`, 16-byte
+// aligned and a multiple of 16) whose bit is set in the device bit array
+// `bits` (ceil(groups / 16) 16-bit words, LSB first), with the
+// read-modify-write probe.  Returns 0 or a HIP error code.
+int32_t dcr_synth_rmw_probe(void* buf, uint64_t bytes, const void* bits, void* stream) {
+    if ((reinterpret_cast<uintptr_t>(buf) & 15u) || (bytes & 15u) || (reinterpret_cast<uintptr_t>(bits) & 1u) || !bits)
+        return int32_t(hipErrorInvalidValue);
+    if (bytes == 0) return 0;
+    const uint64_t n16 = bytes / 16, threads = (n16 + 15) / 16, blocks = (threads + 255) / 256;
+    if (blocks > 0x7FFFFFFFull) return int32_t(hipErrorInvalidValue);
+    hipLaunchKernelGGL(rmw_probe_kernel, dim3(uint32_t(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<v4u*>(buf), static_cast<const uint16_t*>(bits), n16);
     return int32_t(hipGetLastError());
 }
 

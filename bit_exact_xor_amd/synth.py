@@ -764,6 +764,8 @@ def _load_synth():
                                        U32, U32, P]
         lib.dcr_synth_read_probe.restype = ctypes.c_int32
         lib.dcr_synth_read_probe.argtypes = [P, U64, P, P]
+        lib.dcr_synth_rmw_probe.restype = ctypes.c_int32
+        lib.dcr_synth_rmw_probe.argtypes = [P, U64, P, P]
         _synth_lib = lib
     return _synth_lib
 
@@ -812,6 +814,23 @@ def read_probe_gpu(buf, sink, stream=None):
     if rc:
         raise RuntimeError(f"dcr_synth_read_probe failed: {rc}")
     return n
+
+
+def rmw_probe_gpu(buf, bits, stream=None):
+    """XOR a fixed mask into the 16-byte groups of the device tensor `buf`
+    whose bits are set in the device bit array `bits` (LSB first, one bit per
+    group; bandwidth probe for the in-place patch pattern)."""
+    import torch
+    lib = _load_synth()
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    n = buf.numel() * buf.element_size()
+    groups = n // 16
+    if n % 16 or bits.numel() * bits.element_size() < (groups + 15) // 16 * 2:
+        raise ValueError("rmw_probe_gpu: buffer not a multiple of 16 bytes, or too few bits")
+    rc = lib.dcr_synth_rmw_probe(buf.data_ptr(), n, bits.data_ptr(), stream or None)
+    if rc:
+        raise RuntimeError(f"dcr_synth_rmw_probe failed: {rc}")
 
 
 # ------------------------------------------------- configs 3 / 4 (MoE)

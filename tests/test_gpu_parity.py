@@ -589,3 +589,26 @@ def test_corrupt_records_refused(gh):
         exp = old[sl] if i in (1, 2) else new[sl]
         assert np.array_equal(w[sl], exp), i
     assert flags[1].item() == 0 and flags[2].item() == 0 and flags[0].item() == 1
+
+
+def test_rmw_probe(gh):
+    """The read-modify-write probe that bench.py times as the apply's ceiling
+    XORs its fixed mask into exactly the flagged 16-byte groups (a ragged
+    last word of bits included), and a second run restores the buffer."""
+    say("rmw probe: 1000 groups, ragged bit word")
+    rng = np.random.default_rng(5)
+    groups = 1000
+    host = rng.integers(0, 256, size=16 * groups, dtype=np.uint8)
+    flags = rng.random(groups) < 0.3
+    bits = np.packbits(np.concatenate([flags, np.ones(1008 - groups, bool)]), bitorder="little")
+    buf = torch.from_numpy(host.copy()).cuda()
+    bdev = torch.from_numpy(bits).cuda()
+    synth.rmw_probe_gpu(buf, bdev)
+    torch.cuda.synchronize()
+    mask = np.array([0x00010001, 0x00800080, 0x01000100, 0x80008000], dtype="<u4").view(np.uint8)
+    exp = host.reshape(groups, 16).copy()
+    exp[flags] ^= mask
+    assert np.array_equal(buf.cpu().numpy().reshape(groups, 16), exp)
+    synth.rmw_probe_gpu(buf, bdev)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), host)
