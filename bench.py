@@ -149,8 +149,12 @@ def main():
     log(f"inputs ready ({time.time() - t0:.1f}s)")
 
     # ---------------------------------------------------- first step + checks
+    # address tables built once (pinned host memory), as a caller that keeps
+    # its buffers would
+    olds_t, news_t, canon_t = dcr.PtrTable(olds), dcr.PtrTable(news), dcr.PtrTable(canon)
+
     def encode(sb, mode):
-        dcr.dcr_encode(plan, olds, news, mode, 41, 42, sb.header, sb.dir, sb.payload, sb.result, ws)
+        dcr.dcr_encode(plan, olds_t, news_t, mode, 41, 42, sb.header, sb.dir, sb.payload, sb.result, ws)
 
     encode(delta, 0)
     encode(retry, 1)
@@ -169,10 +173,10 @@ def main():
 
     def apply():
         flags.zero_()
-        dcr.dcr_apply(plan, canon, hdr, delta.dir, delta.payload, flags, 0, n_rec, 41, ares, ws)
+        dcr.dcr_apply(plan, canon_t, hdr, delta.dir, delta.payload, flags, 0, n_rec, 41, ares, ws)
 
     def do_retry():
-        dcr.dcr_apply_overwrite_retry(plan, canon, rhdr, retry.dir, retry.payload, 41, ares, ws)
+        dcr.dcr_apply_overwrite_retry(plan, canon_t, rhdr, retry.dir, retry.payload, 41, ares, ws)
 
     # apply on old must give new; the retry keeps new; checked on the whole model
     canon_new = lay.assemble(as_i16(news))
@@ -708,8 +712,10 @@ def _bench_layout(lay, dev, reps, host_values=None):
     staged = stage + cb + (8 << 30) < int(free)
     ws = dcr.workspace(plan, dev, stage if staged else 0)
 
+    olds_t, news_t = dcr.PtrTable(olds), dcr.PtrTable(news)
+
     def enc(sb, mode):
-        dcr.dcr_encode(plan, olds, news, mode, 41, 42, sb.header, sb.dir, sb.payload, sb.result, ws)
+        dcr.dcr_encode(plan, olds_t, news_t, mode, 41, 42, sb.header, sb.dir, sb.payload, sb.result, ws)
 
     enc(delta, 0)
     enc(retry, 1)
@@ -736,12 +742,14 @@ def _bench_layout(lay, dev, reps, host_values=None):
     flags = torch.zeros(max(n_rec, 1), dtype=torch.uint8, device=dev)
     res = torch.zeros(32, dtype=torch.uint8, device=dev)
 
+    canon_t = dcr.PtrTable(canon)
+
     def apply():
         flags.zero_()
-        dcr.dcr_apply(plan, canon, hdr, delta.dir, delta.payload, flags, 0, n_rec, 41, res, ws)
+        dcr.dcr_apply(plan, canon_t, hdr, delta.dir, delta.payload, flags, 0, n_rec, 41, res, ws)
 
     def do_retry():
-        dcr.dcr_apply_overwrite_retry(plan, canon, rhdr, retry.dir, retry.payload, 41, res, ws)
+        dcr.dcr_apply_overwrite_retry(plan, canon_t, rhdr, retry.dir, retry.payload, 41, res, ws)
 
     apply()
     torch.cuda.synchronize()
@@ -782,7 +790,7 @@ def _bench_layout(lay, dev, reps, host_values=None):
            "checks": {"apply_eq_new": bool(ok_apply), "retry_eq_new": bool(ok_retry)}}
     for op in ("apply", "retry"):
         out[op]["kernel_frac_of_rmw_ceiling"] = round(rmw_ms / out[op]["kernel_ms"], 4)
-    del recv, canon, old_buf, new_buf, olds, news, delta, retry, ws, gbits, flags
+    del recv, canon, canon_t, olds_t, news_t, old_buf, new_buf, olds, news, delta, retry, ws, gbits, flags
     torch.cuda.empty_cache()
     return out
 
@@ -882,9 +890,11 @@ def _bench_cfg5(dev, reps, window=256):
     hdr, n_rec, p_bytes, changed = build(0, dir_buf, payload, True)
     flags = torch.zeros(n_rec, dtype=torch.uint8, device=dev)
 
+    canon_t = dcr.PtrTable(canon)
+
     def apply():
         flags.zero_()
-        dcr.dcr_apply(plan_full, canon, hdr, dir_buf, payload, flags, 0, n_rec, 5, res, ws)
+        dcr.dcr_apply(plan_full, canon_t, hdr, dir_buf, payload, flags, 0, n_rec, 5, res, ws)
 
     # every rep applies the same XOR stream: old -> new -> old ...
     a_ms, a_kms = _timed(apply, 2 * ((reps + 1) // 2) + 1)
@@ -902,7 +912,8 @@ def _bench_cfg5(dev, reps, window=256):
     rdir = torch.empty(32 * n_chunks, dtype=torch.uint8, device=dev)
     rpay = torch.empty(28 * 10**9, dtype=torch.uint8, device=dev)
     rhdr, rn, rpb, _ = build(1, rdir, rpay, False)
-    t_ms, t_kms = _timed(lambda: dcr.dcr_apply_overwrite_retry(plan_full, canon, rhdr, rdir, rpay, 5, res, ws), reps)
+    t_ms, t_kms = _timed(lambda: dcr.dcr_apply_overwrite_retry(plan_full, canon_t, rhdr, rdir, rpay, 5, res, ws),
+                         reps)
     ok_retry = eq_new()
     rmw_ms = min(rm)
     g, s_, l_ = touched
@@ -917,7 +928,7 @@ def _bench_cfg5(dev, reps, window=256):
            "note": "apply-only workload: the streams are built window by window outside the timing"}
     for op in ("apply", "retry"):
         out[op]["kernel_frac_of_rmw_ceiling"] = round(rmw_ms / out[op]["kernel_ms"], 4)
-    del cbuf, canon, rdir, rpay, t_old, t_new, gbits, ws
+    del cbuf, canon, canon_t, rdir, rpay, t_old, t_new, gbits, ws
     torch.cuda.empty_cache()
     return out
 

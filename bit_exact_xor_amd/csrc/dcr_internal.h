@@ -40,6 +40,9 @@ constexpr uint32_t kCtrBig = 8;
 constexpr uint32_t kCtrBad = 10;
 constexpr uint32_t kSmallThreads = 256;             // workgroup of the small-record apply
 constexpr uint32_t kSmallStage = 16384;             // its LDS stage (records up to this size)
+// the small-record apply reads and writes whole 128-byte lines for records
+// whose changes are at least 1/kLineDensity of their chunk's elements
+constexpr uint32_t kLineDensity = 80;
 
 // Device-side tensor descriptor.  48 bytes.
 struct DevTensor {

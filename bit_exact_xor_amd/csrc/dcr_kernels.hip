@@ -1515,6 +1515,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 struct SmallShared {
     alignas(16) uint8_t stage[kSmallStage];
     uint32_t pres_pre[kSmallThreads];   // SPARSE: set presence bits before each 32-bit word
+    uint32_t jpre[kSmallThreads];       // line mode: changes before each thread's bitmap slice
     uint64_t scan[kSmallThreads / 64];
     uint32_t ent[8];
     uint32_t state;                     // 0 invalid, 1 skip, 2 apply, 3 deferred
@@ -1540,6 +1541,165 @@ __device__ __forceinline__ uint64_t small_excl_scan(uint64_t v, uint64_t& total,
     __syncthreads();
     total = tot;
     return pre + inc - v;
+}
+
+// The new bits (overwrite) or XOR mask of the changed elements of one
+// 16-byte group, b = the group's change bits, j = the record index of its
+// first change (advanced past the group): packed into a 128-bit value with
+// the mask of the elements it covers.
+template <int W>
+__device__ __forceinline__ void group_value(const SmallShared& S, uint32_t b, uint32_t& j, uint32_t lo, uint32_t hi,
+                                            uint32_t pres, uint32_t pk, uint32_t hm, bool is_xor, uint64_t& val0,
+                                            uint64_t& val1, uint64_t& msk0, uint64_t& msk1) {
+    const uint32_t* pw32 = reinterpret_cast<const uint32_t*>(S.stage + pres);
+    val0 = val1 = msk0 = msk1 = 0;
+    while (b) {
+        const uint32_t i = uint32_t(__ffs(b) - 1);
+        b &= b - 1;
+        uint32_t v = S.stage[lo + j];
+        if constexpr (W == 2) {
+            if (!is_xor || hm == DCR_HI_DENSE) {
+                v |= uint32_t(S.stage[hi + j]) << 8;
+            } else if (hm == DCR_HI_SPARSE) {
+                const uint32_t pwj = pw32[j >> 5];
+                if ((pwj >> (j & 31)) & 1u) {
+                    const uint32_t rank = S.pres_pre[j >> 5] + __popc(pwj & ((1u << (j & 31)) - 1u));
+                    v |= uint32_t(S.stage[hi + rank]) << 8;
+                }
+            }
+        } else if constexpr (W == 4) {
+            v |= uint32_t(S.stage[lo + pk + j]) << 8;
+            v |= uint32_t(S.stage[lo + 2 * pk + j]) << 16;
+            v |= uint32_t(S.stage[lo + 3 * pk + j]) << 24;
+        }
+        constexpr uint32_t EB = 8 * W;
+        constexpr uint64_t EM = (W == 4) ? 0xFFFFFFFFull : ((1ull << EB) - 1);
+        const uint32_t bitpos = i * EB;
+        const uint32_t sh = bitpos & 63;
+        if (bitpos < 64) { val0 |= uint64_t(v) << sh; msk0 |= EM << sh; }
+        else { val1 |= uint64_t(v) << sh; msk1 |= EM << sh; }
+        j++;
+    }
+}
+
+// One patched 16-byte group (XOR or merge under the mask).
+__device__ __forceinline__ v4u patch16(v4u w4, bool is_xor, uint64_t val0, uint64_t val1, uint64_t msk0,
+                                       uint64_t msk1) {
+    uint64_t q0 = uint64_t(w4.x) | (uint64_t(w4.y) << 32);
+    uint64_t q1 = uint64_t(w4.z) | (uint64_t(w4.w) << 32);
+    q0 = is_xor ? (q0 ^ val0) : ((q0 & ~msk0) | val0);
+    q1 = is_xor ? (q1 ^ val1) : ((q1 & ~msk1) | val1);
+    v4u r4;
+    r4.x = uint32_t(q0); r4.y = uint32_t(q0 >> 32); r4.z = uint32_t(q1); r4.w = uint32_t(q1 >> 32);
+    return r4;
+}
+
+// Element-wise patch of the changed elements (bits b) of group g of a
+// canonical chunk at dst, those below n_c only.
+template <int W>
+__device__ __forceinline__ void patch_elems(uint8_t* dst, uint32_t g, uint32_t b, uint32_t n_c, bool is_xor,
+                                            uint64_t val0, uint64_t val1) {
+    constexpr uint32_t V = 16 / W;
+    while (b) {
+        const uint32_t i = uint32_t(__ffs(b) - 1);
+        b &= b - 1;
+        if (g * V + i >= n_c) break;
+        const uint32_t bitpos = i * 8 * W;
+        const uint32_t v = uint32_t(((bitpos < 64) ? val0 : val1) >> (bitpos & 63));
+        uint8_t* ep = dst + (uint64_t(g) * V + i) * W;
+        if constexpr (W == 1) { *ep = is_xor ? uint8_t(*ep ^ v) : uint8_t(v); }
+        else if constexpr (W == 2) {
+            uint16_t* p = reinterpret_cast<uint16_t*>(ep);
+            *p = is_xor ? uint16_t(*p ^ v) : uint16_t(v);
+        } else {
+            uint32_t* p = reinterpret_cast<uint32_t*>(ep);
+            *p = is_xor ? (*p ^ v) : v;
+        }
+    }
+}
+
+// Line mode of the small-record apply (canonical chunk at dst, 128-byte
+// aligned): in iteration k lane l takes group k * kSmallThreads + l, so each
+// wave covers 64 consecutive groups; every 128-byte line that holds a change
+// of the record and lies wholly inside the chunk's elements is read and
+// written whole by its 8 lanes (unchanged groups written back as read), which
+// the memory takes as full-line writes.  Groups of a line that crosses the
+// chunk's end are patched on their own (whole groups with 128-bit accesses,
+// the ragged one element by element).  Needs S.jpre: the changes before each
+// thread's 16-group bitmap slice.
+template <int W>
+__device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, uint32_t n_c, uint32_t lo,
+                                            uint32_t hi, uint32_t pres, uint32_t pk, uint32_t hm, bool is_xor) {
+    constexpr uint32_t V = 16 / W;                        // change bits per group
+    constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;  // groups per bitmap slice (16)
+    constexpr uint32_t BB = GT * V / 8;                   // bitmap bytes per slice
+    constexpr uint32_t LG = 8;                            // groups per 128-byte line
+    constexpr uint32_t KB = 4;                            // groups per lane loaded before patching
+    constexpr uint32_t GM = (V == 16) ? 0xFFFFu : ((1u << V) - 1u);
+    const uint32_t tid = threadIdx.x;
+    const uint32_t n_groups = (n_c + V - 1) / V;
+    const uint32_t whole_lines = n_c / (LG * V);
+    for (uint32_t k0 = 0; k0 < GT; k0 += KB) {
+        v4u v[KB];
+        uint32_t gb[KB], st[KB];   // change bits; 0 skip, 1 whole line, 2 group alone
+#pragma unroll
+        for (uint32_t kk = 0; kk < KB; kk++) {
+            const uint32_t g = (k0 + kk) * kSmallThreads + tid;
+            const uint32_t L = g / LG, q = g % LG;
+            uint32_t s_ = 0, b = 0;
+            if (g < n_groups) {
+                // the line's change bits (inside the bitmap section: bits past
+                // n_c were refused, so they are zero)
+                bool touched;
+                if constexpr (W == 2) {
+                    const uint64_t lb = *reinterpret_cast<const uint64_t*>(S.stage + 8 * L);
+                    touched = lb != 0;
+                    b = uint32_t(lb >> (8 * q)) & GM;
+                } else if constexpr (W == 1) {
+                    const uint4 lb = *reinterpret_cast<const uint4*>(S.stage + 16 * L);
+                    touched = (lb.x | lb.y | lb.z | lb.w) != 0;
+                    const uint32_t wv = (q & 4u) ? ((q & 2u) ? lb.w : lb.z) : ((q & 2u) ? lb.y : lb.x);
+                    b = (wv >> (16 * (q & 1u))) & GM;
+                } else {
+                    const uint32_t lb = *reinterpret_cast<const uint32_t*>(S.stage + 4 * L);
+                    touched = lb != 0;
+                    b = (lb >> (4 * q)) & GM;
+                }
+                if (touched) s_ = L < whole_lines ? 1u : (b ? 2u : 0u);
+            }
+            st[kk] = s_;
+            gb[kk] = b;
+            if (s_ == 1) v[kk] = *reinterpret_cast<const v4u*>(dst + uint64_t(g) * 16);
+        }
+#pragma unroll
+        for (uint32_t kk = 0; kk < KB; kk++) {
+            if (!st[kk]) continue;
+            const uint32_t g = (k0 + kk) * kSmallThreads + tid;
+            uint64_t val0 = 0, val1 = 0, msk0 = 0, msk1 = 0;
+            if (gb[kk]) {
+                // record index of the group's first change: the changes before
+                // its slice plus those of the slice's earlier groups
+                const uint32_t sl = g / GT, nb = (g % GT) * V;
+                uint32_t j = S.jpre[sl];
+#pragma unroll
+                for (uint32_t i = 0; i < BB / 4; i++) {
+                    const uint32_t wd = *reinterpret_cast<const uint32_t*>(S.stage + sl * BB + 4 * i);
+                    const uint32_t m = nb >= 32 * (i + 1) ? 0xFFFFFFFFu
+                                                           : (nb <= 32 * i ? 0u : ((1u << (nb - 32 * i)) - 1u));
+                    j += __popc(wd & m);
+                }
+                group_value<W>(S, gb[kk], j, lo, hi, pres, pk, hm, is_xor, val0, val1, msk0, msk1);
+            }
+            uint8_t* gp = dst + uint64_t(g) * 16;
+            if (st[kk] == 1) {
+                *reinterpret_cast<v4u*>(gp) = gb[kk] ? patch16(v[kk], is_xor, val0, val1, msk0, msk1) : v[kk];
+            } else if ((g + 1) * V <= n_c) {
+                *reinterpret_cast<v4u*>(gp) = patch16(*reinterpret_cast<const v4u*>(gp), is_xor, val0, val1, msk0, msk1);
+            } else {
+                patch_elems<W>(dst, g, gb[kk], n_c, is_xor, val0, val1);
+            }
+        }
+    }
 }
 
 template <int W>
@@ -1648,11 +1808,29 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     __syncthreads();
     if (S.bad) return;   // refused before any write
 
-    // read-modify-write of every touched 16-byte group, in element order
     uint8_t* dst = a.sharded ? nullptr : a.canon[t] + uint64_t(c) * E * W;
-    const uint32_t* pw32 = reinterpret_cast<const uint32_t*>(S.stage + pres);
     const uint32_t pk = dpad16(K);
     const bool is_xor = kind == DCR_KIND_XOR;
+    // Line mode for records dense enough that most lines hold a change, when
+    // no other record or tensor can write the same 128-byte lines: a
+    // canonical chunk at a 128-byte aligned address (lines past the chunk's
+    // elements are never written whole), and for a block-scaled tensor,
+    // whose XOR and overwrite records share chunks, scale blocks made of
+    // whole lines (a line's changes then all belong to one record).
+    const DevTensor td = uniform_load(a.tensors + t);
+    const bool line_mode = !a.sharded && layout != DCR_LAYOUT_LIST && uint64_t(K) * kLineDensity >= n_c &&
+                           (reinterpret_cast<uintptr_t>(dst) & 127u) == 0 &&
+                           (td.route != DCR_ROUTE_BLOCK_SCALED || (uint64_t(td.scale_block) * W) % 128u == 0);
+    if (line_mode) {
+        S.jpre[tid] = j;
+        __syncthreads();
+        apply_lines<W>(S, dst, n_c, lo, hi, pres, pk, hm, is_xor);
+        __syncthreads();
+        if (tid == 0 && !a.retry) a.flags[r] = 1;   // visible with the writes at kernel completion
+        return;
+    }
+
+    // read-modify-write of every touched 16-byte group, in element order
 #pragma unroll
     for (uint32_t wi = 0; wi < NW; wi++) {
         uint32_t wv = bw[wi];
@@ -1661,45 +1839,13 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
             uint32_t b = (wv >> (gi * V)) & GM;
             wv &= ~(GM << (gi * V));
             const uint32_t g = tid * GT + wi * GPW + gi;
-            uint64_t val0 = 0, val1 = 0, msk0 = 0, msk1 = 0;
+            uint64_t val0, val1, msk0, msk1;
             const uint32_t bcopy = b;
-            while (b) {
-                const uint32_t i = uint32_t(__ffs(b) - 1);
-                b &= b - 1;
-                uint32_t v = S.stage[lo + j];
-                if constexpr (W == 2) {
-                    if (!is_xor || hm == DCR_HI_DENSE) {
-                        v |= uint32_t(S.stage[hi + j]) << 8;
-                    } else if (hm == DCR_HI_SPARSE) {
-                        const uint32_t pwj = pw32[j >> 5];
-                        if ((pwj >> (j & 31)) & 1u) {
-                            const uint32_t rank = S.pres_pre[j >> 5] + __popc(pwj & ((1u << (j & 31)) - 1u));
-                            v |= uint32_t(S.stage[hi + rank]) << 8;
-                        }
-                    }
-                } else if constexpr (W == 4) {
-                    v |= uint32_t(S.stage[lo + pk + j]) << 8;
-                    v |= uint32_t(S.stage[lo + 2 * pk + j]) << 16;
-                    v |= uint32_t(S.stage[lo + 3 * pk + j]) << 24;
-                }
-                constexpr uint32_t EB = 8 * W;
-                constexpr uint64_t EM = (W == 4) ? 0xFFFFFFFFull : ((1ull << EB) - 1);
-                const uint32_t bitpos = i * EB;
-                const uint32_t sh = bitpos & 63;
-                if (bitpos < 64) { val0 |= uint64_t(v) << sh; msk0 |= EM << sh; }
-                else { val1 |= uint64_t(v) << sh; msk1 |= EM << sh; }
-                j++;
-            }
+            group_value<W>(S, b, j, lo, hi, pres, pk, hm, is_xor, val0, val1, msk0, msk1);
             uint8_t* gp = group_ptr<W>(a, S, dst, g * V);
             if (gp && (g + 1) * V <= n_c) {
-                v4u w4 = *reinterpret_cast<const v4u*>(gp);
-                uint64_t q0 = uint64_t(w4.x) | (uint64_t(w4.y) << 32);
-                uint64_t q1 = uint64_t(w4.z) | (uint64_t(w4.w) << 32);
-                q0 = is_xor ? (q0 ^ val0) : ((q0 & ~msk0) | val0);
-                q1 = is_xor ? (q1 ^ val1) : ((q1 & ~msk1) | val1);
-                v4u r4;
-                r4.x = uint32_t(q0); r4.y = uint32_t(q0 >> 32); r4.z = uint32_t(q1); r4.w = uint32_t(q1 >> 32);
-                *reinterpret_cast<v4u*>(gp) = r4;
+                *reinterpret_cast<v4u*>(gp) = patch16(*reinterpret_cast<const v4u*>(gp), is_xor, val0, val1, msk0,
+                                                      msk1);
             } else {
                 // tail group of a tensor, or a receiver chunk whose groups are not whole in one piece: element accesses only, inside the tensor
                 uint32_t bb = bcopy;

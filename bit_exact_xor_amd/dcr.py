@@ -127,6 +127,35 @@ def _ptr_array(ptrs):
     return arr
 
 
+class PtrTable:
+    """The device addresses of a fixed list of buffers (shards or canonical
+    tensors), packed once into pinned host memory.  Pass it wherever a list
+    of buffers is taken: calls on plans with many tensors then skip
+    rebuilding the address array, and the library's copy of it to the
+    workspace is an asynchronous DMA instead of a staged pageable copy.  The
+    buffers are kept alive by the table; it must not outlive their storage
+    moving (torch never moves a tensor's storage)."""
+
+    def __init__(self, bufs):
+        import torch
+        self.bufs = list(bufs)
+        n = len(self.bufs)
+        self.host = torch.empty(max(1, n), dtype=torch.int64, pin_memory=True)
+        if n:
+            self.host.numpy()[:n] = np.array([_dptr(t) for t in self.bufs], dtype=np.uint64).view(np.int64)
+        self.address = int(self.host.data_ptr())
+
+    def __len__(self):
+        return len(self.bufs)
+
+
+def _ptrs(bufs):
+    """A C array of device addresses for a list of buffers or a PtrTable."""
+    if isinstance(bufs, PtrTable):
+        return ctypes.c_void_p(bufs.address)
+    return _ptr_array([_dptr(t) for t in bufs])
+
+
 def _dptr(t) -> int:
     """Device pointer of a torch tensor (or an int address)."""
     if isinstance(t, int):
@@ -183,7 +212,7 @@ def dcr_encode(plan: Plan, old_shards, new_shards, mode, base_version, new_versi
                header, dir_buf, payload, result, workspace, stream=None) -> None:
     """Enqueue an encode; buffers are torch device tensors (or int addresses)."""
     rc = load_library().dcr_encode(
-        plan.handle, _ptr_array([_dptr(t) for t in old_shards]), _ptr_array([_dptr(t) for t in new_shards]),
+        plan.handle, _ptrs(old_shards), _ptrs(new_shards),
         mode, base_version, new_version, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload),
         _nbytes(payload), _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_encode")
@@ -199,7 +228,7 @@ def dcr_encode_pipelined(plan: Plan, old_shards, new_shards, mode, base_version,
     """Enqueue a sliced encode that publishes a ready watermark after each
     slice into `ready`, a pinned host tensor of ready_region_bytes(n_slices)."""
     rc = load_library().dcr_encode_pipelined(
-        plan.handle, _ptr_array([_dptr(t) for t in old_shards]), _ptr_array([_dptr(t) for t in new_shards]),
+        plan.handle, _ptrs(old_shards), _ptrs(new_shards),
         mode, base_version, new_version, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload),
         _nbytes(payload), _dptr(result), _dptr(workspace), _nbytes(workspace), n_slices, _dptr(ready),
         _nbytes(ready), _stream(stream))
@@ -223,7 +252,7 @@ def dcr_encode_retry_partial(plan: Plan, old_shards, new_shards, delta_header: n
     applied flag (device bytes) is 0."""
     hdr = np.ascontiguousarray(np.asarray(delta_header, dtype=np.uint8))
     rc = load_library().dcr_encode_retry_partial(
-        plan.handle, _ptr_array([_dptr(t) for t in old_shards]), _ptr_array([_dptr(t) for t in new_shards]),
+        plan.handle, _ptrs(old_shards), _ptrs(new_shards),
         hdr.ctypes.data, _dptr(delta_dir), _nbytes(delta_dir), _dptr(delta_flags), base_version, new_version,
         _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload), _nbytes(payload), _dptr(result),
         _dptr(workspace), _nbytes(workspace), _stream(stream))
@@ -235,7 +264,7 @@ def dcr_apply(plan: Plan, canon, header: np.ndarray, dir_buf, payload, flags, fi
     """Enqueue an apply of records [first, first+n); header is host bytes (64)."""
     hdr = np.ascontiguousarray(np.asarray(header, dtype=np.uint8))
     rc = load_library().dcr_apply(
-        plan.handle, _ptr_array([_dptr(t) for t in canon]), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
+        plan.handle, _ptrs(canon), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
         _dptr(flags), first_record, n_records, expected_base_version, _dptr(result), _dptr(workspace),
         _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_apply")
@@ -245,7 +274,7 @@ def dcr_apply_overwrite_retry(plan: Plan, canon, header: np.ndarray, dir_buf, pa
                               expected_base_version, result, workspace, stream=None) -> None:
     hdr = np.ascontiguousarray(np.asarray(header, dtype=np.uint8))
     rc = load_library().dcr_apply_overwrite_retry(
-        plan.handle, _ptr_array([_dptr(t) for t in canon]), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
+        plan.handle, _ptrs(canon), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
         expected_base_version, _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_apply_overwrite_retry")
 
@@ -256,7 +285,7 @@ def dcr_apply_sharded(plan: Plan, shards, header: np.ndarray, dir_buf, payload, 
     receiver plan, `shards` its device shards."""
     hdr = np.ascontiguousarray(np.asarray(header, dtype=np.uint8))
     rc = load_library().dcr_apply_sharded(
-        plan.handle, _ptr_array([_dptr(t) for t in shards]), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
+        plan.handle, _ptrs(shards), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
         _dptr(flags), first_record, n_records, expected_base_version, _dptr(result), _dptr(workspace),
         _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_apply_sharded")
@@ -267,7 +296,7 @@ def dcr_apply_overwrite_retry_sharded(plan: Plan, shards, header: np.ndarray, di
     """Overwrite retry into a receiver layout (see dcr_apply_sharded)."""
     hdr = np.ascontiguousarray(np.asarray(header, dtype=np.uint8))
     rc = load_library().dcr_apply_overwrite_retry_sharded(
-        plan.handle, _ptr_array([_dptr(t) for t in shards]), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
+        plan.handle, _ptrs(shards), hdr.ctypes.data, _dptr(dir_buf), _dptr(payload),
         expected_base_version, _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_apply_overwrite_retry_sharded")
 

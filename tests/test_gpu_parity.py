@@ -612,3 +612,82 @@ def test_rmw_probe(gh):
     synth.rmw_probe_gpu(buf, bdev)
     torch.cuda.synchronize()
     assert np.array_equal(buf.cpu().numpy(), host)
+
+
+def _line_mode_layout(seed):
+    """Identity tensors around the apply's line-mode cases: densities on both
+    sides of its threshold, ragged last chunks and groups, 1-byte and 2-byte
+    elements, overwrite routes, and block-scaled tensors whose scale blocks
+    are (64 BF16 = one 128-byte line) and are not (8 BF16) whole lines."""
+    rng = np.random.default_rng(seed)
+    b = synth._Builder("lines", seed)
+    olds, news = [], []
+
+    def add(numel, w, rate, route=synth.ROUTE_AFFINE_XOR, scale_block=0):
+        dt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[w]
+        st = -1
+        if route == synth.ROUTE_BLOCK_SCALED:
+            ns = (numel + scale_block - 1) // scale_block
+            st = b.tensor(f"s{len(olds)}", ns, 4, synth.ROUTE_OVERWRITE)
+            s = b.shard(ns, 4)
+            b.seg(st, s, 0, 0, [ns], [1], [1])
+            so = rng.integers(0, 1 << 32, size=ns, dtype=np.uint64).astype(np.uint32)
+            sn = so.copy()
+            hit = rng.random(ns) < 0.3
+            sn[hit] ^= 1
+            olds.append(so)
+            news.append(sn)
+        t = b.tensor(f"t{len(olds)}", numel, w, route, st, scale_block)
+        s = b.shard(numel, w)
+        b.seg(t, s, 0, 0, [numel], [1], [1])
+        o = rng.integers(0, 1 << (8 * w), size=numel, dtype=np.uint64).astype(dt)
+        n = o.copy()
+        ch = rng.random(numel) < rate
+        n[ch] ^= rng.integers(1, 1 << (8 * w), size=int(ch.sum()), dtype=np.uint64).astype(dt)
+        olds.append(o)
+        news.append(n)
+
+    add(2 * 32768 + 1003, 2, 0.03)                       # ragged last chunk and group
+    add(40000, 2, 0.013, synth.ROUTE_OVERWRITE)          # just above the threshold
+    add(3 * 32768, 2, 0.011)                             # just below it
+    add(65536 + 777, 1, 0.05)
+    add(50000, 2, 0.05, synth.ROUTE_BLOCK_SCALED, 8)     # blocks of 16 bytes: group path
+    add(50000, 2, 0.05, synth.ROUTE_BLOCK_SCALED, 64)    # blocks of one line: line path
+    add(1000, 2, 0.2)
+    lay = b.build()
+    lay.values = (olds, news)
+    return lay, olds, news
+
+
+@pytest.mark.parametrize("align", [16, 256])
+def test_apply_line_mode_edges(gh, orc, align):
+    """Apply and retry give the new tensors bit for bit when the canonical
+    tensors are packed at 16-byte offsets (no 128-byte aligned chunk: group
+    path, neighbours sharing lines) and at 256-byte offsets (line path for
+    the dense records); the streams equal the oracle's."""
+    lay, olds, news = _line_mode_layout(11)
+    say("line-mode edges, canonical alignment", align)
+    g = gh.Gpu(lay, olds, news)
+    for mode in (0, 1):
+        sb = g.encode(mode)
+        got = g.stream_host(sb)
+        assert_same_stream(got, oracle_stream(orc, lay, olds, news, mode), f"mode {mode}")
+    sb = g.encode(0)
+    hdr, d, p = g.stream_host(sb)
+    n = len(d) // 32
+    buf, canon = g.canon_alloc(olds, align=align)
+    flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+    r = g.apply(canon, hdr, sb, flags)
+    assert int(r["n_applied"]) == n and int(r["n_invalid"]) == 0
+    for v, e in zip(gh.host(canon), news):
+        assert np.array_equal(v, e.view(np.uint8)), "apply"
+    # kill at half the records from old, then the overwrite retry
+    buf, canon = g.canon_alloc(olds, align=align)
+    flags.zero_()
+    g.apply(canon, hdr, sb, flags, 0, n // 2)
+    rsb = g.encode(1)
+    rh, _rd, _rp = g.stream_host(rsb)
+    r = g.retry(canon, rh, rsb)
+    assert int(r["n_invalid"]) == 0
+    for v, e in zip(gh.host(canon), news):
+        assert np.array_equal(v, e.view(np.uint8)), "retry"
