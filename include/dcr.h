@@ -44,7 +44,16 @@
  *     allocates host memory only (the plan) and never calls hipMalloc.
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  All device
  *     work is enqueued on it; the library never synchronises it.  Host arrays
- *     of device pointers passed to a call are copied during the call.
+ *     of device pointers passed to a call are copied to the workspace by an
+ *     asynchronous copy on `stream`: from pageable memory the copy has read
+ *     the array when the call returns; from pinned memory (hipHostMalloc) it
+ *     reads it when the stream reaches it, so the array must stay unchanged
+ *     until then.
+ *   - Graph capture: the calls enqueue only kernels and those pointer-array
+ *     copies (no memset, allocation or synchronisation), so they may be
+ *     captured into a HIP graph.  A captured copy reads its host array at
+ *     every replay: pass pinned arrays that outlive the graph.  Sizes, plan
+ *     and stream header are fixed at capture.
  *   - Alignment: every shard, canonical tensor, directory, payload, result and
  *     workspace pointer must be 16-byte aligned (DCR_E_INVAL otherwise).
  *   - Concurrency: a plan is immutable after upload and may be shared; calls

@@ -691,3 +691,66 @@ def test_apply_line_mode_edges(gh, orc, align):
     assert int(r["n_invalid"]) == 0
     for v, e in zip(gh.host(canon), news):
         assert np.array_equal(v, e.view(np.uint8)), "retry"
+
+
+def test_graph_replay(gh, orc):
+    """Encode (staged) and apply captured once in a HIP graph (torch's graph
+    capture over the library's own launches) and replayed: every replay,
+    with eager work between replays, gives the oracle's stream byte for byte
+    and patches a fresh copy of the old tensors into the new ones.  The
+    address tables are pinned PtrTables that outlive the graph (the copy of a
+    table is a node of the graph and reads it at each replay)."""
+    lay = synth.llama_layout(hidden=256, layers=2, ffn=640, n_q=8, n_kv=4, head_dim=32, vocab=1000, tp=4,
+                             rate=0.03)
+    say("graph replay: scaled TP=4 llama, 3 %")
+    olds, news = lay.shards_host(0), lay.shards_host(1)
+    g = gh.Gpu(lay, olds, news)
+    exp = oracle_stream(orc, lay, olds, news, 0)
+    n = len(exp[1]) // 32
+    canon_new = lay.assemble([torch.from_numpy(x.view(np.int16)) for x in news])
+    canon_old = lay.assemble([torch.from_numpy(x.view(np.int16)) for x in olds])
+    buf, canon = g.canon_alloc()
+    old_img = torch.cat([c.reshape(-1).view(torch.uint8) for c in canon_old]).cuda() if canon_old else None
+
+    def reset_receiver():
+        off = 0
+        for v in canon:
+            v.copy_(old_img[off:off + v.numel()])
+            off += v.numel()
+
+    ws = dcr.workspace(g.plan, "cuda", int(g.plan.info.max_payload_bytes))
+    sb = dcr.StreamBuffers(g.plan, "cuda")
+    ot, nt, ct = dcr.PtrTable(g.olds), dcr.PtrTable(g.news), dcr.PtrTable(canon)
+    flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+    res = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    hdr = exp[0]
+    # eager warm-up on the side stream torch captures on
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dcr.dcr_encode(g.plan, ot, nt, 0, 7, 8, sb.header, sb.dir, sb.payload, sb.result, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dcr.dcr_encode(g.plan, ot, nt, 0, 7, 8, sb.header, sb.dir, sb.payload, sb.result, ws)
+        flags.zero_()
+        dcr.dcr_apply(g.plan, ct, hdr, sb.dir, sb.payload, flags, 0, n, 7, res, g.ws)
+    for rep in range(4):
+        say("graph replay", rep)
+        sb.dir.fill_(0xEE)
+        sb.payload[: len(exp[2]) + 64].fill_(0xEE)
+        reset_receiver()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = g.stream_host(sb)
+        assert_same_stream(got, exp, f"replay {rep}")
+        ar = dcr.apply_result(res)
+        assert int(ar["n_applied"]) == n and int(ar["n_invalid"]) == 0, (rep, ar)
+        for v, e in zip(canon, canon_new):
+            assert torch.equal(v.view(torch.int16).cpu(), e.reshape(-1)), f"replay {rep}: apply"
+        # eager work between replays: a RETRY encode into other buffers
+        other = g.encode(1)
+        assert int(other.result_host()["status"]) == 0
+    del graph
