@@ -1521,6 +1521,7 @@ struct SmallShared {
     uint32_t state;                     // 0 invalid, 1 skip, 2 apply, 3 deferred
     uint32_t n_c;
     uint32_t bad;
+    uint32_t solo;                      // no other record of this call names the same chunk
     uint32_t mfirst, mnp, mdirect;      // receiver layout (as in ApplyShared)
     uint32_t mstart[kMaxCachedPieces];
     uint64_t maddr[kMaxCachedPieces];
@@ -1812,15 +1813,14 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     const uint32_t pk = dpad16(K);
     const bool is_xor = kind == DCR_KIND_XOR;
     // Line mode for records dense enough that most lines hold a change, when
-    // no other record or tensor can write the same 128-byte lines: a
-    // canonical chunk at a 128-byte aligned address (lines past the chunk's
-    // elements are never written whole), and for a block-scaled tensor,
-    // whose XOR and overwrite records share chunks, scale blocks made of
-    // whole lines (a line's changes then all belong to one record).
-    const DevTensor td = uniform_load(a.tensors + t);
-    const bool line_mode = !a.sharded && layout != DCR_LAYOUT_LIST && uint64_t(K) * kLineDensity >= n_c &&
-                           (reinterpret_cast<uintptr_t>(dst) & 127u) == 0 &&
-                           (td.route != DCR_ROUTE_BLOCK_SCALED || (uint64_t(td.scale_block) * W) % 128u == 0);
+    // no other writer can touch the same 128-byte lines: the record is the
+    // only one of this call for its chunk (the other record a chunk may have
+    // sits next to it in the directory; one applied by another call or by
+    // the large-record kernel does not run concurrently), and the chunk is
+    // canonical at a 128-byte aligned address (lines past the chunk's
+    // elements are never written whole).
+    const bool line_mode = !a.sharded && S.solo && layout != DCR_LAYOUT_LIST &&
+                           uint64_t(K) * kLineDensity >= n_c && (reinterpret_cast<uintptr_t>(dst) & 127u) == 0;
     if (line_mode) {
         S.jpre[tid] = j;
         __syncthreads();
@@ -1892,6 +1892,17 @@ __global__ __launch_bounds__(kSmallThreads) void apply_small_kernel(ApplyArgs a)
             st = fits ? 2 : 3;
             if (!fits) a.big_list[atomicAdd(a.big_count, 1u)] = uint32_t(r - a.first);
             else map_chunk(a, S, e[0], e[1]);
+            // a chunk's records are adjacent in the directory
+            uint32_t solo = 1;
+            if (r > a.first) {
+                const uint4 p = reinterpret_cast<const uint4*>(a.dir + (r - 1) * DCR_DIRENT_BYTES)[0];
+                solo &= (p.x != e[0] || p.y != e[1]) ? 1u : 0u;
+            }
+            if (r + 1 < a.first + gridDim.x) {
+                const uint4 q = reinterpret_cast<const uint4*>(a.dir + (r + 1) * DCR_DIRENT_BYTES)[0];
+                solo &= (q.x != e[0] || q.y != e[1]) ? 1u : 0u;
+            }
+            S.solo = solo;
         }
         S.state = st;
         S.n_c = n_c;
