@@ -60,6 +60,8 @@ def parse():
                          "tensor at 1 %%; Qwen3-30B-A3B-shaped EP=8 at 3 %% Beta(2,60) rates; the same at 5 %% "
                          "hot rows, block-scaled; the 240 GB receiver share, apply and retry only); print one "
                          "JSON line")
+    ap.add_argument("--configs-only", default=None, metavar="NAME",
+                    help="with --configs: only the workload whose name contains NAME (for profiler runs)")
     ap.add_argument("--pmc-dump", metavar="DIR",
                     help="per-kernel averages of every counter in the rocprofv3 runs under DIR/pmc_*; exit")
     return ap.parse_args()
@@ -105,7 +107,7 @@ def main():
         print(json.dumps(lists_cfg5(dev)), flush=True)
         return
     if args.configs:
-        print(json.dumps(bench_configs(dev)), flush=True)
+        print(json.dumps(bench_configs(dev, only=args.configs_only)), flush=True)
         return
 
     # ---------------------------------------------------------------- setup
@@ -975,8 +977,9 @@ def _bench_cfg5(dev, reps, window=256):
     return out
 
 
-def bench_configs(dev, reps=5):
-    """Encode / apply / retry timings on the other full-size workloads."""
+def bench_configs(dev, reps=5, only=None):
+    """Encode / apply / retry timings on the other full-size workloads (those
+    whose name contains `only`, if given)."""
     import gc
     import torch
     from bit_exact_xor_amd import synth
@@ -987,12 +990,16 @@ def bench_configs(dev, reps=5):
     for name, lay, hv in (("tensor_4096x4096_1pct", lay1, ([o1], [n1])),
                           ("qwen3_30b_a3b_ep8_3pct_beta", None, None),
                           ("qwen3_30b_a3b_5pct_hot_block_scaled", None, None)):
+        if only and only not in name:
+            continue
         if lay is None:
             lay = synth.config3_layout() if "beta" in name else synth.config4_layout()
         log(f"configs: {name}")
         out[name] = _bench_layout(lay, dev, reps, hv)
         gc.collect()
         torch.cuda.empty_cache()
+    if only and only not in "receiver_share_240GB":
+        return out
     log("configs: receiver_share_240GB")
     free, _ = torch.cuda.mem_get_info()
     need = 240 * 10**9 + 16 * 10**9 + 2 * 10**9 + 26 * 10**9
@@ -1140,15 +1147,21 @@ def cpu_baseline(lay, delta, hdr_dev, reps):
 # kernel source they were measured on; the bench reports them only while the
 # source is unchanged, else null.
 
-KERNEL_SRC = os.path.join(ROOT, "bit_exact_xor_amd", "csrc", "dcr_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "bit_exact_xor_amd", "csrc", "dcr_kernels.hip"),
+               os.path.join(ROOT, "bit_exact_xor_amd", "csrc", "dcr_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_apply_llama8b_tp4_hbm_traffic.md")
 TRAFFIC_TAG = "traffic-json:"
 
 
 def _src_sha256():
+    """SHA-256 over the kernel sources the counters depend on (the kernels and
+    the constants they are built with)."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(op):

@@ -16,7 +16,7 @@ constexpr uint32_t kVecsPerChunk = kChunkBytes / kVecBytes;  // 4096
 constexpr uint32_t kThreads = 1024;                 // workgroup of encode / apply
 constexpr uint32_t kVecsPerThread = kVecsPerChunk / kThreads;  // 4
 constexpr uint32_t kMaxCachedPieces = 64;           // pieces of a chunk kept in LDS
-constexpr uint32_t kWinBytes = 8192;                // LDS output window of the encode record writer
+constexpr uint32_t kWinBytes = 12288;               // LDS output window of the encode record writer
 // largest payload of one chunk's records (mixed XOR + OW on BF16: two 4 KiB
 // bitmaps + 2 bytes per change + padding), rounded up to 16
 constexpr uint32_t kStageBytes = 73792;

@@ -618,7 +618,8 @@ def _line_mode_layout(seed):
     """Identity tensors around the apply's line-mode cases: densities on both
     sides of its threshold, ragged last chunks and groups, 1-byte and 2-byte
     elements, overwrite routes, and block-scaled tensors whose scale blocks
-    are (64 BF16 = one 128-byte line) and are not (8 BF16) whole lines."""
+    are (64 BF16 = one 128-byte line) and are not (8 BF16) whole lines, and
+    one whose block (96 BF16) is not a power of two."""
     rng = np.random.default_rng(seed)
     b = synth._Builder("lines", seed)
     olds, news = [], []
@@ -653,6 +654,7 @@ def _line_mode_layout(seed):
     add(65536 + 777, 1, 0.05)
     add(50000, 2, 0.05, synth.ROUTE_BLOCK_SCALED, 8)     # blocks of 16 bytes: group path
     add(50000, 2, 0.05, synth.ROUTE_BLOCK_SCALED, 64)    # blocks of one line: line path
+    add(70000, 2, 0.05, synth.ROUTE_BLOCK_SCALED, 96)    # blocks of 12 groups (not a power of two)
     add(1000, 2, 0.2)
     lay = b.build()
     lay.values = (olds, news)
