@@ -432,7 +432,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 (bit patterns, integer ops)",
+        "dtype": "u16",
         "data": "synthetic, seeded (GPU-generated shards)",
         "config": {"workload": "llama-8B-shaped BF16 checkpoint, TP=4 trainer shards, fused QKV -> overwrite, "
                                "1% uniform +-1ulp changes",
