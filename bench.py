@@ -158,6 +158,9 @@ def main():
     def encode(sb, mode):
         dcr.dcr_encode(plan, olds_t, news_t, mode, 41, 42, sb.header, sb.dir, sb.payload, sb.result, ws)
 
+    def encode_ws(sb, mode, w):
+        dcr.dcr_encode(plan, olds_t, news_t, mode, 41, 42, sb.header, sb.dir, sb.payload, sb.result, w)
+
     encode(delta, 0)
     encode(retry, 1)
     torch.cuda.synchronize()
@@ -264,7 +267,7 @@ def main():
 
     # extras outside the step (skipped for profiling runs, so that every
     # launch of the step kernels in a trace belongs to the step)
-    partial_retry = index_lists = sharded_apply = pipelined = None
+    partial_retry = index_lists = sharded_apply = pipelined = staging_modes = None
     if not args.no_extras:
         # partial retry after a kill at 50 % of the DELTA records (outside the
         # step): the receiver is set back to old, applies the first half, and the
@@ -379,6 +382,35 @@ def main():
                                        op_ms["encode"], op_ms["apply"])
         log(f"pipelined transfer through pinned host memory: {pipelined}")
 
+        # staging area sizes: the whole worst case (the step's launch
+        # configuration), windows of fix-up blocks in 4 GiB and 1 GiB, and
+        # none (in-order look-back); each stream compared with the step's
+        staging_modes = {"window_stage_bytes": int(info.window_stage_bytes),
+                         "full_stage_bytes": int(info.max_payload_bytes)}
+        ref = (delta.header.clone(), delta.dir[:32 * n_rec].clone(), delta.payload[:p_bytes].clone())
+        del ws
+        torch.cuda.empty_cache()
+        for name, sbytes in (("full", int(info.max_payload_bytes)), ("window_4GiB", 4 << 30),
+                             ("window_1GiB", 1 << 30), ("in_order", 0)):
+            wsm = dcr.workspace(plan, dev, stage_bytes=sbytes)
+            tm = []
+            for _ in range(4):
+                a_, b_ = pair()
+                a_.record()
+                encode_ws(delta, 0, wsm)
+                b_.record()
+                torch.cuda.synchronize()
+                tm.append(a_.elapsed_time(b_))
+            same = (torch.equal(delta.header, ref[0]) and torch.equal(delta.dir[:32 * n_rec], ref[1])
+                    and torch.equal(delta.payload[:p_bytes], ref[2]))
+            staging_modes[name] = {"stage_GB": round(sbytes / 1e9, 3), "encode_ms": round(float(np.median(tm[1:])), 3),
+                                   "stream_eq": bool(same)}
+            del wsm
+            torch.cuda.empty_cache()
+        ws = dcr.workspace(plan, dev, stage_bytes=int(info.max_payload_bytes))
+        del ref
+        log(f"staging area sizes: {staging_modes}")
+
     enc_bytes = 2 * cb + 32 * n_rec + p_bytes
     renc_bytes = 2 * cb + 32 * rn_rec + rp_bytes
     app_bytes = 32 * n_rec + p_bytes + LINE * touched + SECTOR * touched_sec
@@ -450,6 +482,7 @@ def main():
         "index_lists": index_lists,
         "sharded_apply": sharded_apply,
         "pipelined": pipelined,
+        "staging_modes": staging_modes,
         "roofline": roof,
         "ceiling": ceiling,
         "cpu_baseline": cpu,

@@ -97,6 +97,7 @@ struct Plan {
     bool shard_disjoint = true;           // no shard element holds two canonical elements
     uint64_t scale_bits = 0;              // total flag bits (multiple of 64)
     uint64_t max_dir_bytes = 0, max_payload_bytes = 0;
+    uint64_t window_stage_bytes = 0;      // slots of the largest fix-up block
     // device table layout
     uint64_t off_tensors = 0, off_chunks = 0, off_pieces = 0, off_scale_chunks = 0, off_slots = 0, off_slow = 0,
              off_direct[3] = {0, 0, 0}, table_bytes = 0;

@@ -2145,10 +2145,21 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
         hipLaunchKernelGGL(scale_flags_kernel, dim3(uint32_t(p.scale_chunks.size())), dim3(256), 0, s, tensors,
                            chunks, pieces, tab<uint32_t>(p, p.off_scale_chunks), old_sh, new_sh, scale_flags);
     uint32_t* counter = reinterpret_cast<uint32_t*>(ws + p.ws_counter);
-    // bytes past the plan's workspace: staging area, used when it holds every
-    // chunk's slot (max_payload_bytes)
+    // bytes past the plan's workspace: staging area.  It is used whole when
+    // it holds every chunk's slot (max_payload_bytes).  A smaller one that
+    // holds the slots of any single fix-up block is used in windows: runs of
+    // whole fix-up blocks whose slots fit, each window's tiles and fix-up
+    // launched before the next window reuses the area (stream order), with
+    // the staging base moved back by the window's first slot offset (the
+    // fix-up block counter and look-back carry over between launches).
+    // Anything smaller: the in-order encode, no staging.
     uint8_t* stage = ws + p.ws_bytes;
-    const uint32_t staged = ws_bytes - p.ws_bytes >= p.max_payload_bytes ? 1u : 0u;
+    const uint64_t stage_bytes = ws_bytes - p.ws_bytes;
+    const uint32_t n_blocks = (n_tiles + kFixTiles - 1) / kFixTiles;
+    auto slot_end = [&](uint32_t t1) { return t1 < n_tiles ? p.slots[t1] : p.max_payload_bytes; };
+    const bool full = stage_bytes >= p.max_payload_bytes;
+    const bool windowed = !full && !n_slices && n_tiles && stage_bytes >= p.window_stage_bytes;
+    const uint32_t staged = (full || windowed) ? 1u : 0u;
     EncodeArgs a;
     a.tensors = tensors;
     a.chunks = chunks;
@@ -2234,9 +2245,21 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
                            p.fingerprint, dir_cap, payload_cap, static_cast<uint8_t*>(header_dev), result_dev);
     };
     if (!n_slices) {
-        if (n_tiles) {
+        if (n_tiles && !windowed) {
             run_tiles(0, n_tiles, true);
             run_fix(0, f.n_blocks);
+        } else if (n_tiles) {
+            for (uint32_t b0 = 0; b0 < n_blocks;) {
+                const uint32_t t0 = b0 * kFixTiles;
+                uint32_t b1 = b0 + 1;
+                while (b1 < n_blocks && slot_end(std::min((b1 + 1) * kFixTiles, n_tiles)) - p.slots[t0] <= stage_bytes)
+                    b1++;
+                a.stage = stage - p.slots[t0];
+                f.stage = a.stage;
+                run_tiles(t0, std::min(b1 * kFixTiles, n_tiles), false);
+                run_fix(b0, b1);
+                b0 = b1;
+            }
         }
         finalize();
     } else {

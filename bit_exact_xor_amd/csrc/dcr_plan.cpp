@@ -248,6 +248,13 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
         P.canonical_bytes += d.numel * w;
         if (d.route == DCR_ROUTE_BLOCK_SCALED) is_scale_used[d.scale_tensor] = 1;
     }
+    // the staging bytes of the largest fix-up block (kFixTiles consecutive
+    // chunks): the least staging area the encode can run in windows with
+    for (uint64_t t0 = 0; t0 < P.slots.size(); t0 += kFixTiles) {
+        const uint64_t t1 = std::min<uint64_t>(t0 + kFixTiles, P.slots.size());
+        const uint64_t end = t1 < P.slots.size() ? P.slots[t1] : P.max_payload_bytes;
+        P.window_stage_bytes = std::max(P.window_stage_bytes, end - P.slots[t0]);
+    }
     // per-block "scale changed" flag bits, one bit per element of each gating scale tensor
     std::vector<uint64_t> bit_off(nT, 0);
     for (uint32_t s = 0; s < nT; s++) {
@@ -378,6 +385,7 @@ int32_t dcr_plan_query(const dcr_plan* p, dcr_plan_info* out) {
     out->max_payload_bytes = p->max_payload_bytes;
     out->fingerprint = p->fingerprint;
     out->canonical_bytes = p->canonical_bytes;
+    out->window_stage_bytes = p->window_stage_bytes;
     return DCR_OK;
 }
 

@@ -49,7 +49,7 @@ assert ENCODE_RESULT.itemsize == 32 and APPLY_RESULT.itemsize == 32
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "n_tensors", "n_shards", "n_chunks", "n_pieces", "table_bytes", "workspace_bytes",
-        "max_dir_bytes", "max_payload_bytes", "fingerprint", "canonical_bytes")]
+        "max_dir_bytes", "max_payload_bytes", "fingerprint", "canonical_bytes", "window_stage_bytes")]
 
 
 class DcrError(RuntimeError):

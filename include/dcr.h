@@ -142,6 +142,9 @@ typedef struct {
                                    the size of encode's staging area          */
     uint64_t fingerprint;       /* FNV-1a-64 of the serialised tensor table       */
     uint64_t canonical_bytes;   /* sum of numel * elem_bytes                      */
+    uint64_t window_stage_bytes; /* the least staging area dcr_encode runs in
+                                   windows with (the worst-case slots of the
+                                   largest run of 256 consecutive chunks)     */
 } dcr_plan_info;
 
 /* Stream header, 64 bytes (the first bytes of every stream). */
@@ -219,13 +222,17 @@ void dcr_plan_destroy(dcr_plan* plan);
  *   payload_dev, payload_cap   payload buffer and its size in bytes
  *   result_dev     a dcr_encode_result in device memory
  *   workspace_dev, ws_bytes    at least workspace_bytes of device memory.
- *                  With at least workspace_bytes + max_payload_bytes, the
- *                  excess is a staging area: each chunk writes its records to
- *                  a slot of its own at once and a second pass moves them into
- *                  place, so no chunk waits for another.  With less, each
- *                  chunk waits until every earlier chunk has published its
- *                  sizes (decoupled look-back) and writes in place.  Both give
- *                  the same stream.
+ *                  The excess past workspace_bytes is a staging area.  With
+ *                  at least max_payload_bytes of it, each chunk writes its
+ *                  records to a slot of its own at once and a second pass
+ *                  moves them into place, so no chunk waits for another.
+ *                  With less, but at least window_stage_bytes (the slots of
+ *                  any 256 consecutive chunks; dcr_encode_pipelined excepted),
+ *                  the same runs in windows of whole blocks whose slots fit,
+ *                  one after the other on the stream.  With less than that,
+ *                  each chunk waits until every earlier chunk has published
+ *                  its sizes (decoupled look-back) and writes in place.  All
+ *                  give the same stream.
  * Records are written in (tensor, chunk, kind) order with contiguous 16-byte
  * aligned payload offsets.  If a buffer is too small, result->status becomes
  * DCR_E_CAPACITY with the required totals; the buffers then hold no usable

@@ -756,3 +756,22 @@ def test_graph_replay(gh, orc):
         other = g.encode(1)
         assert int(other.result_host()["status"]) == 0
     del graph
+
+
+def test_windowed_staging(gh, orc):
+    """A staging area smaller than every chunk's slot but at least
+    window_stage_bytes runs the staged encode in windows of whole fix-up
+    blocks: on config 1's tensor (512 chunks, two blocks) with the smallest
+    such area, one a little larger, and one just short of the full worst
+    case, the DELTA and RETRY streams equal the oracle's, byte for byte."""
+    lay = synth.config1_layout()
+    old, new, _lr, _pos = synth.config1_values(lay, lr=synth.CFG1_LR)
+    g = gh.Gpu(lay, [old], [new])
+    info = g.plan.info
+    win, full = int(info.window_stage_bytes), int(info.max_payload_bytes)
+    say("windowed staging", win, full)
+    assert 0 < win < full
+    for mode in (0, 1):
+        exp = oracle_stream(orc, lay, [old], [new], mode)
+        for stage in (win, win + 16, full - 16):
+            assert_same_stream(g.stream_host(g.encode(mode, stage=stage)), exp, f"mode {mode} stage {stage}")
