@@ -775,3 +775,19 @@ def test_windowed_staging(gh, orc):
         exp = oracle_stream(orc, lay, [old], [new], mode)
         for stage in (win, win + 16, full - 16):
             assert_same_stream(g.stream_host(g.encode(mode, stage=stage)), exp, f"mode {mode} stage {stage}")
+    # the index-list layout and the partial retry take the same windows
+    rc, lh, ld, lp = orc.encode(lay.tensors, lay.segments, [old], [new], mode=dcr.ENC_INDEX_LISTS,
+                                base_version=7, new_version=8)
+    assert rc == 0
+    assert_same_stream(g.stream_host(g.encode(dcr.ENC_INDEX_LISTS, stage=win)), (lh, ld, lp), "lists, window")
+    sb = g.encode(0)
+    hdr, d, _p = g.stream_host(sb)
+    n = len(d) // 32
+    buf, canon = g.canon_alloc([old])
+    flags = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    g.apply(canon, hdr, sb, flags, 0, n // 3)
+    rc, eh, ed, ep = orc.encode_retry_partial(lay.tensors, lay.segments, [old], [new], hdr, d, flags.cpu().numpy(),
+                                               base_version=7, new_version=8)
+    assert rc == 0
+    assert_same_stream(g.stream_host(g.encode_retry_partial(hdr, sb, flags, stage=win)), (eh, ed, ep),
+                       "partial retry, window")
