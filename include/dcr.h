@@ -400,7 +400,10 @@ int32_t dcr_apply_overwrite_retry_sharded(const dcr_plan* plan, void* const* sha
  * main kernel (the encode tile kernel, or the apply kernel) and `stop` just
  * after it, so that hipEventElapsedTime gives that kernel's duration alone.
  * The events are hipEvent_t handles the caller created; NULL, NULL turns the
- * hook off.  Never fails. */
+ * hook off.  An encode that runs in windows (a staging area below
+ * max_payload_bytes but at least window_stage_bytes) or in slices
+ * (dcr_encode_pipelined) has no single main kernel and records neither
+ * event.  Never fails. */
 void dcr_set_kernel_events(void* start, void* stop);
 
 /* Message of the last error on this thread ("" if none). */
