@@ -1627,10 +1627,13 @@ __device__ __forceinline__ void patch_elems(uint8_t* dst, uint32_t g, uint32_t b
 // the memory takes as full-line writes.  Groups of a line that crosses the
 // chunk's end are patched on their own (whole groups with 128-bit accesses,
 // the ragged one element by element).  Needs S.jpre: the changes before each
-// thread's 16-group bitmap slice.
+// thread's 16-group bitmap slice, and the record's change bitmap in the
+// stage at byte bmo (0 for a bitmap record; a list record's bitmap is
+// rebuilt past the record).
 template <int W>
 __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, uint32_t n_c, uint32_t lo,
-                                            uint32_t hi, uint32_t pres, uint32_t pk, uint32_t hm, bool is_xor) {
+                                            uint32_t hi, uint32_t pres, uint32_t pk, uint32_t hm, bool is_xor,
+                                            uint32_t bmo) {
     constexpr uint32_t V = 16 / W;                        // change bits per group
     constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;  // groups per bitmap slice (16)
     constexpr uint32_t BB = GT * V / 8;                   // bitmap bytes per slice
@@ -1653,16 +1656,16 @@ __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, 
                 // n_c were refused, so they are zero)
                 bool touched;
                 if constexpr (W == 2) {
-                    const uint64_t lb = *reinterpret_cast<const uint64_t*>(S.stage + 8 * L);
+                    const uint64_t lb = *reinterpret_cast<const uint64_t*>(S.stage + bmo + 8 * L);
                     touched = lb != 0;
                     b = uint32_t(lb >> (8 * q)) & GM;
                 } else if constexpr (W == 1) {
-                    const uint4 lb = *reinterpret_cast<const uint4*>(S.stage + 16 * L);
+                    const uint4 lb = *reinterpret_cast<const uint4*>(S.stage + bmo + 16 * L);
                     touched = (lb.x | lb.y | lb.z | lb.w) != 0;
                     const uint32_t wv = (q & 4u) ? ((q & 2u) ? lb.w : lb.z) : ((q & 2u) ? lb.y : lb.x);
                     b = (wv >> (16 * (q & 1u))) & GM;
                 } else {
-                    const uint32_t lb = *reinterpret_cast<const uint32_t*>(S.stage + 4 * L);
+                    const uint32_t lb = *reinterpret_cast<const uint32_t*>(S.stage + bmo + 4 * L);
                     touched = lb != 0;
                     b = (lb >> (4 * q)) & GM;
                 }
@@ -1684,7 +1687,7 @@ __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, 
                 uint32_t j = S.jpre[sl];
 #pragma unroll
                 for (uint32_t i = 0; i < BB / 4; i++) {
-                    const uint32_t wd = *reinterpret_cast<const uint32_t*>(S.stage + sl * BB + 4 * i);
+                    const uint32_t wd = *reinterpret_cast<const uint32_t*>(S.stage + bmo + sl * BB + 4 * i);
                     const uint32_t m = nb >= 32 * (i + 1) ? 0xFFFFFFFFu
                                                            : (nb <= 32 * i ? 0u : ((1u << (nb - 32 * i)) - 1u));
                     j += __popc(wd & m);
@@ -1819,12 +1822,20 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     // the large-record kernel does not run concurrently), and the chunk is
     // canonical at a 128-byte aligned address (lines past the chunk's
     // elements are never written whole).
-    const bool line_mode = !a.sharded && S.solo && layout != DCR_LAYOUT_LIST &&
+    // A list record's bitmap is rebuilt past the record in the stage (each
+    // thread stores its checked slice whole, so a slice that straddles the
+    // bitmap's end needs room for all of it), when it fits.
+    const uint32_t bmo = layout == DCR_LAYOUT_LIST ? dpad16(sz) : 0u;
+    const bool line_mode = !a.sharded && S.solo && bmo + bm + BB <= kSmallStage &&
                            uint64_t(K) * kLineDensity >= n_c && (reinterpret_cast<uintptr_t>(dst) & 127u) == 0;
     if (line_mode) {
         S.jpre[tid] = j;
+        if (layout == DCR_LAYOUT_LIST && b0 < bm) {
+#pragma unroll
+            for (uint32_t i = 0; i < NW; i++) reinterpret_cast<uint32_t*>(S.stage + bmo + b0)[i] = bw[i];
+        }
         __syncthreads();
-        apply_lines<W>(S, dst, n_c, lo, hi, pres, pk, hm, is_xor);
+        apply_lines<W>(S, dst, n_c, lo, hi, pres, pk, hm, is_xor, bmo);
         __syncthreads();
         if (tid == 0 && !a.retry) a.flags[r] = 1;   // visible with the writes at kernel completion
         return;
@@ -1879,6 +1890,11 @@ __global__ __launch_bounds__(kSmallThreads) void apply_small_kernel(ApplyArgs a)
     if (threadIdx.x == 0) {
         const uint4* de = reinterpret_cast<const uint4*>(a.dir + r * DCR_DIRENT_BYTES);
         const uint4 e0 = de[0], e1 = de[1];
+        // the neighbouring entries' (tensor, chunk), loaded with the entry
+        // (a chunk's records are adjacent in the directory)
+        const bool has_prev = r > a.first, has_next = r + 1 < a.first + gridDim.x;
+        const uint4 pv = has_prev ? de[-2] : make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0, 0);
+        const uint4 nx = has_next ? de[2] : make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0, 0);
         uint32_t e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
         for (int i = 0; i < 8; i++) S.ent[i] = e[i];
         uint32_t st;
@@ -1892,17 +1908,8 @@ __global__ __launch_bounds__(kSmallThreads) void apply_small_kernel(ApplyArgs a)
             st = fits ? 2 : 3;
             if (!fits) a.big_list[atomicAdd(a.big_count, 1u)] = uint32_t(r - a.first);
             else map_chunk(a, S, e[0], e[1]);
-            // a chunk's records are adjacent in the directory
-            uint32_t solo = 1;
-            if (r > a.first) {
-                const uint4 p = reinterpret_cast<const uint4*>(a.dir + (r - 1) * DCR_DIRENT_BYTES)[0];
-                solo &= (p.x != e[0] || p.y != e[1]) ? 1u : 0u;
-            }
-            if (r + 1 < a.first + gridDim.x) {
-                const uint4 q = reinterpret_cast<const uint4*>(a.dir + (r + 1) * DCR_DIRENT_BYTES)[0];
-                solo &= (q.x != e[0] || q.y != e[1]) ? 1u : 0u;
-            }
-            S.solo = solo;
+            S.solo = (!has_prev || pv.x != e[0] || pv.y != e[1]) && (!has_next || nx.x != e[0] || nx.y != e[1]) ? 1u
+                                                                                                                : 0u;
         }
         S.state = st;
         S.n_c = n_c;
