@@ -134,7 +134,9 @@ class PtrTable:
     rebuilding the address array, and the library's copy of it to the
     workspace is an asynchronous DMA instead of a staged pageable copy.  The
     buffers are kept alive by the table; it must not outlive their storage
-    moving (torch never moves a tensor's storage)."""
+    moving (torch never moves a tensor's storage).  Needs a GPU runtime
+    (pinned host memory); a table passed to calls captured into a HIP graph
+    must outlive the graph, whose copy nodes read it at every replay."""
 
     def __init__(self, bufs):
         import torch
