@@ -80,7 +80,7 @@ def main():
         print(pmc_dump(args.pmc_dump))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: --gpus {args.gpus}: this build runs the hot path on one GPU only "
+        print(f"bench.py: --gpus {args.gpus}: the library runs the hot path on one GPU only "
               "(no cross-GPU sharding or collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
