@@ -267,7 +267,7 @@ def main():
 
     # extras outside the step (skipped for profiling runs, so that every
     # launch of the step kernels in a trace belongs to the step)
-    partial_retry = index_lists = sharded_apply = pipelined = staging_modes = None
+    partial_retry = retry_from_delta = index_lists = sharded_apply = pipelined = staging_modes = None
     if not args.no_extras:
         # partial retry after a kill at 50 % of the DELTA records (outside the
         # step): the receiver is set back to old, applies the first half, and the
@@ -308,6 +308,35 @@ def main():
                          "apply_ms": round(float(np.median(pa)), 4), "full_retry_apply_ms": round(op_ms["retry"], 4),
                          "healed_eq_new": bool(ok_partial)}
         log(f"partial retry at a 50 % kill: {partial_retry}")
+
+        # the RETRY stream written from the step's DELTA stream and old only
+        # (outside the step): timed, then applied to old, which must give new
+        te = []
+        for _ in range(3):
+            a_, b_ = pair()
+            a_.record()
+            dcr.dcr_encode_retry_from_delta(plan, olds, hdr, delta.dir, delta.payload, 0, retry.header, retry.dir,
+                                            retry.payload, retry.result, ws)
+            b_.record()
+            torch.cuda.synchronize()
+            te.append(a_.elapsed_time(b_))
+        tr = retry.result_host()
+        canon_o = lay.assemble(as_i16(olds))
+        for t in range(len(T)):
+            canon[t].view(torch.int16).copy_(canon_o[t].reshape(-1))
+        del canon_o
+        dcr.dcr_apply_overwrite_retry(plan, canon, retry.header_host(), retry.dir, retry.payload, 41, ares, ws)
+        torch.cuda.synchronize()
+        canon_new = lay.assemble(as_i16(news))
+        ok_tx = all(torch.equal(canon[t].view(torch.int16), canon_new[t].reshape(-1)) for t in range(len(T)))
+        del canon_new
+        retry_from_delta = {"status": int(tr["status"]), "records": int(tr["n_records"]),
+                            "payload_GB": round(int(tr["payload_bytes"]) / 1e9, 4),
+                            "same_size_as_retry": int(tr["payload_bytes"]) == rp_bytes,
+                            "encode_ms": round(float(np.median(te)), 4),
+                            "full_retry_encode_ms": round(op_ms["encode_retry"], 4),
+                            "applied_eq_new": bool(ok_tx)}
+        log(f"RETRY stream from the DELTA stream: {retry_from_delta}")
 
         # index-list layout (encode option, outside the step): the same DELTA
         # change set with low-density records carrying 16-bit indices instead of
@@ -479,6 +508,7 @@ def main():
         "checks": {"apply_eq_new": bool(ok_apply), "retry_eq_new": bool(ok_retry),
                    "after_timing_eq_new": bool(ok_after), "oracle_sample": parity_sample},
         "partial_retry": partial_retry,
+        "retry_from_delta": retry_from_delta,
         "index_lists": index_lists,
         "sharded_apply": sharded_apply,
         "pipelined": pipelined,

@@ -6,8 +6,8 @@ device pointers and the current torch stream into a hipStream_t, and raises
 ``DcrError`` on a nonzero status.  PyTorch provides device memory and streams.
 
 The names follow the C-ABI: ``dcr_plan_build``, ``dcr_encode``,
-``dcr_encode_retry_partial``, ``dcr_apply``, ``dcr_apply_overwrite_retry``,
-``dcr_apply_sharded``, ``dcr_apply_overwrite_retry_sharded`` (plus the small
+``dcr_encode_retry_partial``, ``dcr_encode_retry_from_delta``, ``dcr_apply``,
+``dcr_apply_overwrite_retry``, ``dcr_apply_sharded``, ``dcr_apply_overwrite_retry_sharded`` (plus the small
 helpers around them).
 """
 from __future__ import annotations
@@ -87,6 +87,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dcr_ready_wait.argtypes = [P, U32, U64, P]
     lib.dcr_encode_retry_partial.restype = I32
     lib.dcr_encode_retry_partial.argtypes = [P, P, P, P, P, U64, P, U64, U64, P, P, U64, P, U64, P, P, U64, P]
+    lib.dcr_encode_retry_from_delta.restype = I32
+    lib.dcr_encode_retry_from_delta.argtypes = [P, P, P, P, U64, P, U64, U32, P, P, U64, P, U64, P, P, U64, P]
     lib.dcr_apply.restype = I32
     lib.dcr_apply.argtypes = [P, P, P, P, P, P, U64, U64, U64, P, P, U64, P]
     lib.dcr_apply_sharded.restype = I32
@@ -259,6 +261,19 @@ def dcr_encode_retry_partial(plan: Plan, old_shards, new_shards, delta_header: n
         _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload), _nbytes(payload), _dptr(result),
         _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_encode_retry_partial")
+
+
+def dcr_encode_retry_from_delta(plan: Plan, old_shards, delta_header: np.ndarray, delta_dir, delta_payload,
+                                options, header, dir_buf, payload, result, workspace, stream=None) -> None:
+    """Enqueue a RETRY stream written from a DELTA stream (host header bytes,
+    device directory and payload) and the old shards; options 0 or
+    DCR_ENC_INDEX_LISTS."""
+    hdr = np.ascontiguousarray(np.asarray(delta_header, dtype=np.uint8))
+    rc = load_library().dcr_encode_retry_from_delta(
+        plan.handle, _ptrs(old_shards), hdr.ctypes.data, _dptr(delta_dir), _nbytes(delta_dir),
+        _dptr(delta_payload), _nbytes(delta_payload), options, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf),
+        _dptr(payload), _nbytes(payload), _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(rc, "dcr_encode_retry_from_delta")
 
 
 def dcr_apply(plan: Plan, canon, header: np.ndarray, dir_buf, payload, flags, first_record, n_records,

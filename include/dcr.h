@@ -328,6 +328,42 @@ int32_t dcr_encode_retry_partial(const dcr_plan* plan,
                                  dcr_encode_result* result_dev,
                                  void* workspace_dev, uint64_t ws_bytes, void* stream);
 
+/* RETRY stream from a DELTA stream (sender side).  The overwrite retry
+ * re-sends every changed element with its new bits (tokendh blog, "no backup
+ * copy"; the Italian summary on retries).  The DELTA stream of the same
+ * refit step names every changed element with its XOR mask or its new bits,
+ * so this call writes the stream dcr_encode with DCR_MODE_RETRY would write
+ * (the same bytes, the same header versions as the DELTA stream's) while
+ * reading only the DELTA stream and old at the changed elements; the new
+ * shards are not read.
+ *   old_shards       the plan's old shards (device; as for dcr_encode)
+ *   delta_header     the DELTA stream's header, in HOST memory (magic,
+ *                    format, chunk size, plan fingerprint and stream_kind
+ *                    DCR_MODE_DELTA are checked: DCR_E_FORMAT)
+ *   delta_dir_dev, delta_dir_bytes          its directory (device) and the
+ *                    buffer's size (at least n_records * 32: DCR_E_INVAL)
+ *   delta_payload_dev, delta_payload_bytes  its payload (device) and the
+ *                    buffer's size (at least payload_bytes: DCR_E_INVAL)
+ *   options          0, or DCR_ENC_INDEX_LISTS for the index-list layout
+ *   the remaining arguments as for dcr_encode (the workspace needs
+ *   workspace_bytes; no staging area is used).
+ * Every directory entry is checked (tensor, chunk, sizes, order, at most an
+ * XOR then an overwrite record per chunk) and every record's change set
+ * (bounds, popcounts, disjoint records); a malformed DELTA stream makes
+ * result->status DCR_E_FORMAT and no record is written.  A stream that does
+ * not fit dir_cap / payload_cap gives DCR_E_CAPACITY with its sizes in the
+ * result, as dcr_encode does.  Like every call, one workspace serves one call
+ * at a time. */
+int32_t dcr_encode_retry_from_delta(const dcr_plan* plan, const void* const* old_shards,
+                                    const dcr_stream_header* delta_header,
+                                    const void* delta_dir_dev, uint64_t delta_dir_bytes,
+                                    const void* delta_payload_dev, uint64_t delta_payload_bytes,
+                                    uint32_t options,
+                                    void* header_dev, void* dir_dev, uint64_t dir_cap,
+                                    void* payload_dev, uint64_t payload_cap,
+                                    dcr_encode_result* result_dev,
+                                    void* workspace_dev, uint64_t ws_bytes, void* stream);
+
 /* Apply records [first_record, first_record + n_records) of a stream in place
  * (receiver side).
  *   canon          host array of n_tensors device pointers, one per canonical

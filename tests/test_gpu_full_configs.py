@@ -41,7 +41,7 @@ def staged_workspace(plan, sb):
     return dcr.workspace(plan, "cuda", stage)
 
 
-def run_full(orc, lay, sample_names, partial=False):
+def run_full(orc, lay, sample_names, partial=False, transcode=False):
     assert torch.cuda.is_available()
     say(lay.name, "plan")
     T = lay.tensors
@@ -126,7 +126,7 @@ def run_full(orc, lay, sample_names, partial=False):
     del co
     flags.zero_()
     dcr.dcr_apply(plan, canon, hdr, sb.dir, sb.payload, flags, 0, n_rec // 2, 3, res, ws)
-    if not partial:
+    if not (partial or transcode):
         del sb
     rsb = dcr.StreamBuffers(plan, "cuda", dir_bytes=32 * int(plan.info.n_chunks),
                             payload_bytes=int(cb * 0.2) + (1 << 20))
@@ -136,6 +136,26 @@ def run_full(orc, lay, sample_names, partial=False):
     torch.cuda.synchronize()
     del wss
     assert int(rsb.result_host()["status"]) == 0
+    if transcode:
+        # the same RETRY stream, written from the DELTA stream and old only
+        say(lay.name, "retry stream from the DELTA stream")
+        tsb = dcr.StreamBuffers(plan, "cuda", dir_bytes=32 * int(plan.info.n_chunks),
+                                payload_bytes=int(cb * 0.2) + (1 << 20))
+        dcr.dcr_encode_retry_from_delta(plan, olds, hdr, sb.dir, sb.payload, 0, tsb.header, tsb.dir, tsb.payload,
+                                        tsb.result, ws)
+        torch.cuda.synchronize()
+        tr, rr = tsb.result_host(), rsb.result_host()
+        assert int(tr["status"]) == 0, tr
+        for k in ("n_records", "payload_bytes", "n_changed"):
+            assert int(tr[k]) == int(rr[k]), (k, tr, rr)
+        nr, pb = int(rr["n_records"]), int(rr["payload_bytes"])
+        assert torch.equal(tsb.header, rsb.header)
+        assert torch.equal(tsb.dir[: nr * 32], rsb.dir[: nr * 32])
+        assert torch.equal(tsb.payload[:pb], rsb.payload[:pb])
+        say(lay.name, f"retry stream from the DELTA stream: identical ({nr} records, {pb / 1e9:.2f} GB)")
+        del tsb
+        if not partial:
+            del sb
     dcr.dcr_apply_overwrite_retry(plan, canon, rsb.header.cpu().numpy(), rsb.dir, rsb.payload, 3, res, ws)
     torch.cuda.synchronize()
     for t in range(len(T)):
@@ -304,7 +324,8 @@ def test_full_llama8b_tp4(orc):
     lay = synth.llama_layout()
     run_full(orc, lay, ["model.layers.0.input_layernorm.weight", "model.layers.0.self_attn.q_proj.weight",
                         "model.layers.0.self_attn.k_proj.weight", "model.layers.0.self_attn.o_proj.weight",
-                        "model.layers.31.mlp.down_proj.weight", "model.norm.weight"], partial=True)
+                        "model.layers.31.mlp.down_proj.weight", "model.norm.weight"], partial=True,
+             transcode=True)
 
 
 def test_full_qwen30b_ep8_beta(orc):
@@ -320,4 +341,4 @@ def test_full_qwen30b_hot_block_scaled(orc):
     run_full(orc, lay, ["model.layers.0.self_attn.q_proj.weight", "model.layers.0.mlp.gate.weight",
                         "model.layers.0.mlp.experts.0.gate_proj.weight",
                         "model.layers.0.mlp.experts.5.down_proj.weight",
-                        "model.layers.47.mlp.experts.127.up_proj.weight", "model.norm.weight"])
+                        "model.layers.47.mlp.experts.127.up_proj.weight", "model.norm.weight"], transcode=True)
