@@ -18,6 +18,7 @@
 // workgroup per chunk); write the header and the result.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <string>
 
 #include "dcr_internal.h"
@@ -26,8 +27,6 @@ namespace dcr {
 namespace {
 
 constexpr uint32_t kTT = 256;                          // threads of the record kernel
-constexpr uint32_t kMaxWords = kChunkBytes / 32;       // change-bitmap words of a 1-byte chunk
-constexpr uint32_t kMaxPresWords = kChunkBytes / 2 / 32;   // presence words of a 2-byte XOR record
 constexpr uint32_t kCached = 64;                       // pieces of a chunk resolved in LDS
 constexpr uint32_t kScanT = 1024, kScanPer = 4, kScanBlock = kScanT * kScanPer;
 constexpr uint32_t kValBits = 36;                      // scan value: records << 36 | bytes / 16
@@ -252,24 +251,27 @@ struct TxArgs {
     const DevChunk* chunks;
     const DevPiece* pieces;
     const uint8_t* const* old_sh;
-    const uint64_t* first;       // per tile, from tx_index_kernel
     const uint64_t* excl;        // per tile: exclusive prefix of the RETRY records
     unsigned long long* ctr;
     uint8_t* out_dir;
     uint8_t* out_payload;
     uint64_t dir_cap, payload_cap;
     uint32_t lists;
+    uint32_t maxw;               // bitmap words of the plan's largest chunk
 };
 
+// LDS of the record kernel, sized at launch for the plan's largest chunk
+// bitmap (maxw words) and, with 2-byte tensors, the largest presence bitmap
+// (presw words): this fixed part, then M (changed elements of the chunk, both
+// records), B (those of the overwrite record when the chunk has two) and pre
+// (per word: exclusive count of M | of B << 16), maxw words each, then pp
+// (per presence word of the XOR record: exclusive count).
 struct TxShared {
-    uint32_t M[kMaxWords];            // changed elements of the chunk (both records)
-    uint32_t B[kMaxWords];            // those of the overwrite record, when the chunk has two
-    uint32_t pre[kMaxWords];          // per word: exclusive count of M | of B << 16
-    uint32_t pp[kMaxPresWords];       // per presence word of the XOR record: exclusive count
-    uint64_t red[kTT / 64];
     uint64_t paddr[kCached];          // resolved pieces: shard address of canonical element canon_start
+    uint64_t red[kTT / 64];
     uint32_t pstart[kCached];
 };
+constexpr uint32_t kTxFixed = (sizeof(uint64_t) * (kCached + kTT / 64) + sizeof(uint32_t) * kCached + 15) & ~15u;
 
 // Address of chunk element e in the old shards.
 __device__ __forceinline__ const uint8_t* old_elem(const TxArgs& a, const TxShared& S, uint32_t fp, uint32_t np,
@@ -296,31 +298,36 @@ __device__ __forceinline__ const uint8_t* old_elem(const TxArgs& a, const TxShar
 // One workgroup per DELTA record; the first record of each chunk writes the
 // chunk's RETRY record and directory entry.
 __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
-    __shared__ TxShared S;
+    extern __shared__ __align__(16) uint8_t tx_lds[];
+    TxShared& S = *reinterpret_cast<TxShared*>(tx_lds);
+    uint32_t* const M = reinterpret_cast<uint32_t*>(tx_lds + kTxFixed);
+    uint32_t* const B = M + a.maxw;
+    uint32_t* const pre = B + a.maxw;
+    uint32_t* const pp = pre + a.maxw;
     const uint32_t tid = threadIdx.x;
     const uint64_t i = blockIdx.x;
-    if (a.ctr[kErr]) return;   // a malformed directory: nothing is written
+    // the counters and the entry (with its neighbours) in one round of loads
+    const uint64_t err = a.ctr[kErr], tot = a.ctr[kTotal];
     const uint32_t* d = reinterpret_cast<const uint32_t*>(a.dir + i * DCR_DIRENT_BYTES);
     const uint32_t t = d[0], c = d[1];
+    const bool first_rec = i == 0 || d[-8] != t || d[-7] != c;
+    if (err || !first_rec) return;   // a malformed directory writes nothing
+    if ((tot >> kValBits) * DCR_DIRENT_BYTES > a.dir_cap || ((tot & kValMask) << 4) > a.payload_cap) return;
     const DevTensor td = a.tensors[t];
     const uint32_t tile = td.first_chunk + c;
-    const uint64_t fr = a.first[tile];
-    if (uint32_t(fr) != uint32_t(i + 1)) return;   // not the chunk's first record
-    const uint64_t tot = a.ctr[kTotal];
-    if ((tot >> kValBits) * DCR_DIRENT_BYTES > a.dir_cap || ((tot & kValMask) << 4) > a.payload_cap) return;
 
     const uint32_t w = td.w;
     const uint32_t n_c = chunk_elems(td, c);
     const uint32_t nw = (n_c + 31) / 32;            // bitmap words holding elements
     const uint32_t bmb = p16((n_c + 7) / 8);        // bitmap section bytes
     const uint32_t nwp = bmb / 4;
-    const uint32_t Ktot = uint32_t(fr >> 32);
     const bool two = i + 1 < a.n && d[8] == t && d[9] == c;
     // record A (the first), record B (the overwrite record after an XOR one)
     const uint32_t KA = d[2], kindA = d[3] & 0xFF, hmA = (d[3] >> 8) & 0xFF, layA = d[3] >> 24;
     const uint64_t offA = uint64_t(d[4]) | (uint64_t(d[5]) << 32);
     const uint32_t HA = d[7];
     const uint32_t KB = two ? d[10] : 0u, layB = two ? (d[11] >> 24) : 0u;
+    const uint32_t Ktot = KA + KB;
     const uint64_t offB = two ? (uint64_t(d[12]) | (uint64_t(d[13]) << 32)) : 0u;
     const uint32_t s0A = layA == DCR_LAYOUT_LIST ? p16(2 * KA) : bmb, pkA = p16(KA);
     const uint32_t s0B = layB == DCR_LAYOUT_LIST ? p16(2 * KB) : bmb, pkB = p16(KB);
@@ -332,11 +339,6 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
 
     const DevChunk ch = a.chunks[tile];
     const uint32_t fp = ch.first_piece, np = ch.n_pieces & kPiecesMask;
-    if (np <= kCached && tid < np) {
-        const DevPiece p = a.pieces[fp + tid];
-        S.pstart[tid] = p.canon_start;
-        S.paddr[tid] = reinterpret_cast<uint64_t>(a.old_sh[p.shard]) + p.shard_elem_off * w;
-    }
 
     // the change sets: bitmap records word by word, then index lists
     bool bad = false;
@@ -348,8 +350,14 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
             if (two && layB == DCR_LAYOUT_BITMAP) xb = reinterpret_cast<const uint32_t*>(PB)[wi];
             if (((xa | xb) & ~valid) || (xa & xb)) bad = true;
         }
-        S.M[wi] = xa | xb;
-        S.B[wi] = xb;
+        M[wi] = xa | xb;
+        B[wi] = xb;
+    }
+    // the chunk's pieces (read only for XOR changes, after the bitmaps)
+    if (np <= kCached && tid < np) {
+        const DevPiece p = a.pieces[fp + tid];
+        S.pstart[tid] = p.canon_start;
+        S.paddr[tid] = reinterpret_cast<uint64_t>(a.old_sh[p.shard]) + p.shard_elem_off * w;
     }
     __syncthreads();
     if (layA == DCR_LAYOUT_LIST || (two && layB == DCR_LAYOUT_LIST)) {
@@ -364,8 +372,8 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
                     bad = true;
                     continue;
                 }
-                atomicOr(&S.M[e >> 5], 1u << (e & 31));
-                if (isB) atomicOr(&S.B[e >> 5], 1u << (e & 31));
+                atomicOr(&M[e >> 5], 1u << (e & 31));
+                if (isB) atomicOr(&B[e >> 5], 1u << (e & 31));
             }
         }
         __syncthreads();
@@ -376,8 +384,8 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
     const uint32_t ppt = (npw + kTT - 1) / kTT, q0 = tid * ppt, q1 = min(npw, q0 + ppt);
     uint32_t cM = 0, cB = 0, cP = 0;
     for (uint32_t wi = w0; wi < w1; wi++) {
-        cM += __popc(S.M[wi]);
-        cB += __popc(S.B[wi]);
+        cM += __popc(M[wi]);
+        cB += __popc(B[wi]);
     }
     for (uint32_t pw = q0; pw < q1; pw++) {
         uint32_t x = reinterpret_cast<const uint32_t*>(PA + presA)[pw];
@@ -390,12 +398,12 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
     {
         uint32_t rM = uint32_t(ex & 0x1FFFFF), rB = uint32_t((ex >> 21) & 0x1FFFFF), rP = uint32_t(ex >> 42);
         for (uint32_t wi = w0; wi < w1; wi++) {
-            S.pre[wi] = rM | (rB << 16);
-            rM += __popc(S.M[wi]);
-            rB += __popc(S.B[wi]);
+            pre[wi] = rM | (rB << 16);
+            rM += __popc(M[wi]);
+            rB += __popc(B[wi]);
         }
         for (uint32_t pw = q0; pw < q1; pw++) {
-            S.pp[pw] = rP;
+            pp[pw] = rP;
             const uint32_t vm = KA - 32 * pw >= 32 ? 0xFFFFFFFFu : ((1u << (KA - 32 * pw)) - 1u);
             rP += __popc(reinterpret_cast<const uint32_t*>(PA + presA)[pw] & vm);
         }
@@ -415,9 +423,9 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
     const uint32_t s0o = retry_sec0(n_c, Ktot, a.lists), pko = p16(Ktot);
     const bool listo = s0o != bmb;
     for (uint32_t wi = w0; wi < w1; wi++) {
-        uint32_t m = S.M[wi];
-        const uint32_t bb = S.B[wi];
-        uint32_t r = S.pre[wi] & 0xFFFFu, rb = S.pre[wi] >> 16;
+        uint32_t m = M[wi];
+        const uint32_t bb = B[wi];
+        uint32_t r = pre[wi] & 0xFFFFu, rb = pre[wi] >> 16;
         while (m) {
             const uint32_t bit = uint32_t(__ffs(m) - 1);
             m &= m - 1;
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
                 } else if (hmA == DCR_HI_SPARSE) {
                     const uint32_t pwd = reinterpret_cast<const uint32_t*>(P + presA)[j >> 5];
                     if ((pwd >> (j & 31)) & 1u) {
-                        const uint32_t rank = S.pp[j >> 5] + __popc(pwd & ((1u << (j & 31)) - 1u));
+                        const uint32_t rank = pp[j >> 5] + __popc(pwd & ((1u << (j & 31)) - 1u));
                         v |= uint32_t(P[presA + p16((KA + 7) / 8) + rank]) << 8;
                     }
                 }
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
     }
     // first section and zero padding
     if (!listo) {
-        for (uint32_t wi = tid; wi < nwp; wi += kTT) reinterpret_cast<uint32_t*>(out)[wi] = S.M[wi];
+        for (uint32_t wi = tid; wi < nwp; wi += kTT) reinterpret_cast<uint32_t*>(out)[wi] = M[wi];
     } else {
         for (uint32_t k = Ktot + tid; k < s0o / 2; k += kTT) reinterpret_cast<uint16_t*>(out)[k] = 0;
     }
@@ -580,7 +588,6 @@ extern "C" int32_t dcr_encode_retry_from_delta(
         a.chunks = reinterpret_cast<const DevChunk*>(tables + p.off_chunks);
         a.pieces = reinterpret_cast<const DevPiece*>(tables + p.off_pieces);
         a.old_sh = reinterpret_cast<const uint8_t* const*>(ws + p.ws_old);
-        a.first = first;
         a.excl = val;
         a.ctr = ctr;
         a.out_dir = static_cast<uint8_t*>(dir_dev);
@@ -588,7 +595,17 @@ extern "C" int32_t dcr_encode_retry_from_delta(
         a.dir_cap = dir_cap;
         a.payload_cap = payload_cap;
         a.lists = lists;
-        hipLaunchKernelGGL(tx_record_kernel, dim3(uint32_t(n)), dim3(kTT), 0, st, a);
+        // LDS for the largest chunk bitmap and (2-byte tensors) presence bitmap
+        uint32_t maxw = 1, presw = 1;
+        for (const DevTensor& td : p.dt) {
+            const uint64_t E = kChunkBytes / td.w;
+            const uint64_t ne = td.numel < E ? td.numel : E;
+            maxw = std::max<uint32_t>(maxw, uint32_t((ne + 31) / 32));
+            if (td.w == 2) presw = std::max<uint32_t>(presw, uint32_t((ne + 31) / 32));
+        }
+        a.maxw = (maxw + 3) & ~3u;
+        const size_t lds = kTxFixed + sizeof(uint32_t) * (3 * size_t(a.maxw) + presw);
+        hipLaunchKernelGGL(tx_record_kernel, dim3(uint32_t(n)), dim3(kTT), lds, st, a);
     }
     hipLaunchKernelGGL(tx_finish_kernel, dim3(1), dim3(64), 0, st, ctr, h->base_version, h->new_version,
                        p.fingerprint, dir_cap, payload_cap, static_cast<dcr_stream_header*>(header_dev), result_dev);
