@@ -202,8 +202,16 @@ __global__ __launch_bounds__(kScanT) void tx_scan_sums_kernel(uint64_t* bsum, ui
 }
 
 // Rescan each block with its prefix: val[tile] becomes the tile's exclusive
-// prefix (records << 36 | bytes / 16).
-__global__ __launch_bounds__(kScanT) void tx_downsweep_kernel(uint64_t* val, uint64_t n, const uint64_t* bsum) {
+// prefix (records << 36 | bytes / 16).  When the stream fits and the
+// directory is well formed, each chunk with a record also gets a descriptor
+// for the record kernel, written into the output directory slot its entry
+// will take (32 bytes: DELTA record index, tile, prefix (2 words), first
+// piece, piece count, elements | width << 24, 0).
+__global__ __launch_bounds__(kScanT) void tx_downsweep_kernel(uint64_t* val, uint64_t n, const uint64_t* bsum,
+                                                              const uint64_t* first, const DevChunk* chunks,
+                                                              const DevTensor* tensors,
+                                                              const unsigned long long* ctr, uint8_t* out_dir,
+                                                              uint64_t dir_cap, uint64_t payload_cap) {
     __shared__ uint64_t s[kScanT];
     const uint64_t t0 = uint64_t(blockIdx.x) * kScanBlock + uint64_t(threadIdx.x) * kScanPer;
     uint64_t v[kScanPer], sum = 0;
@@ -213,8 +221,22 @@ __global__ __launch_bounds__(kScanT) void tx_downsweep_kernel(uint64_t* val, uin
     }
     uint64_t tot = 0;
     uint64_t run = bsum[2 * blockIdx.x] + scan_block_excl(sum, s, tot);
+    const uint64_t all = ctr[kTotal];
+    const bool desc = !ctr[kErr] && (all >> kValBits) * DCR_DIRENT_BYTES <= dir_cap &&
+                      ((all & kValMask) << 4) <= payload_cap;
     for (uint32_t j = 0; j < kScanPer; j++) {
-        if (t0 + j < n) val[t0 + j] = run;
+        const uint64_t tile = t0 + j;
+        if (tile < n) {
+            val[tile] = run;
+            if (desc && v[j]) {
+                const DevChunk ch = chunks[tile];
+                const DevTensor td = tensors[ch.tensor];
+                const uint32_t n_c = chunk_elems(td, ch.chunk_idx);
+                uint4* de = reinterpret_cast<uint4*>(out_dir + (run >> kValBits) * DCR_DIRENT_BYTES);
+                de[0] = uint4{uint32_t(first[tile]) - 1u, uint32_t(tile), uint32_t(run), uint32_t(run >> 32)};
+                de[1] = uint4{ch.first_piece, ch.n_pieces & kPiecesMask, n_c | (td.w << 24), 0u};
+            }
+        }
         run += v[j];
     }
 }
@@ -247,11 +269,8 @@ struct TxArgs {
     const uint8_t* dir;          // DELTA directory
     const uint8_t* payload;      // DELTA payload
     uint64_t n;                  // DELTA records
-    const DevTensor* tensors;
-    const DevChunk* chunks;
     const DevPiece* pieces;
     const uint8_t* const* old_sh;
-    const uint64_t* excl;        // per tile: exclusive prefix of the RETRY records
     unsigned long long* ctr;
     uint8_t* out_dir;
     uint8_t* out_payload;
@@ -297,7 +316,7 @@ __device__ __forceinline__ const uint8_t* old_elem(const TxArgs& a, const TxShar
 
 // One workgroup per DELTA record; the first record of each chunk writes the
 // chunk's RETRY record and directory entry.
-__global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
+__global__ __launch_bounds__(kTT) __attribute__((amdgpu_waves_per_eu(8, 8))) void tx_record_kernel(TxArgs a) {
     extern __shared__ __align__(16) uint8_t tx_lds[];
     TxShared& S = *reinterpret_cast<TxShared*>(tx_lds);
     uint32_t* const M = reinterpret_cast<uint32_t*>(tx_lds + kTxFixed);
@@ -305,19 +324,21 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
     uint32_t* const pre = B + a.maxw;
     uint32_t* const pp = pre + a.maxw;
     const uint32_t tid = threadIdx.x;
-    const uint64_t i = blockIdx.x;
-    // the counters and the entry (with its neighbours) in one round of loads
+    // the counters and this record's descriptor in one round of loads (the
+    // descriptor is valid when r is below the record count and the stream fits)
+    const uint64_t r = blockIdx.x;
+    if ((r + 1) * DCR_DIRENT_BYTES > a.dir_cap) return;
     const uint64_t err = a.ctr[kErr], tot = a.ctr[kTotal];
+    const uint32_t* ds = reinterpret_cast<const uint32_t*>(a.out_dir + r * DCR_DIRENT_BYTES);
+    const uint32_t ds0 = ds[0], ds2 = ds[2], ds3 = ds[3], fp = ds[4], np = ds[5], ds6 = ds[6];
+    if (err || r >= (tot >> kValBits) || (tot >> kValBits) * DCR_DIRENT_BYTES > a.dir_cap ||
+        ((tot & kValMask) << 4) > a.payload_cap)
+        return;
+    const uint64_t i = ds0;
+    const uint64_t eo = uint64_t(ds2) | (uint64_t(ds3) << 32);
+    const uint32_t n_c = ds6 & 0xFFFFFFu, w = ds6 >> 24;
     const uint32_t* d = reinterpret_cast<const uint32_t*>(a.dir + i * DCR_DIRENT_BYTES);
     const uint32_t t = d[0], c = d[1];
-    const bool first_rec = i == 0 || d[-8] != t || d[-7] != c;
-    if (err || !first_rec) return;   // a malformed directory writes nothing
-    if ((tot >> kValBits) * DCR_DIRENT_BYTES > a.dir_cap || ((tot & kValMask) << 4) > a.payload_cap) return;
-    const DevTensor td = a.tensors[t];
-    const uint32_t tile = td.first_chunk + c;
-
-    const uint32_t w = td.w;
-    const uint32_t n_c = chunk_elems(td, c);
     const uint32_t nw = (n_c + 31) / 32;            // bitmap words holding elements
     const uint32_t bmb = p16((n_c + 7) / 8);        // bitmap section bytes
     const uint32_t nwp = bmb / 4;
@@ -336,9 +357,6 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
     const uint32_t npw = sparse ? (KA + 31) / 32 : 0u;
     const uint8_t* PA = a.payload + offA;
     const uint8_t* PB = a.payload + offB;
-
-    const DevChunk ch = a.chunks[tile];
-    const uint32_t fp = ch.first_piece, np = ch.n_pieces & kPiecesMask;
 
     // the change sets: bitmap records word by word, then index lists
     bool bad = false;
@@ -417,7 +435,6 @@ __global__ __launch_bounds__(kTT) void tx_record_kernel(TxArgs a) {
     }
 
     // the RETRY record
-    const uint64_t eo = a.excl[tile];
     const uint64_t rec = eo >> kValBits;
     uint8_t* out = a.out_payload + ((eo & kValMask) << 4);
     const uint32_t s0o = retry_sec0(n_c, Ktot, a.lists), pko = p16(Ktot);
@@ -578,17 +595,17 @@ extern "C" int32_t dcr_encode_retry_from_delta(
                            uint32_t(p.tensors.size()), lists, first, val, ctr);
     if (nb) hipLaunchKernelGGL(tx_reduce_kernel, dim3(uint32_t(nb)), dim3(kScanT), 0, st, val, first, n_tiles, bsum);
     hipLaunchKernelGGL(tx_scan_sums_kernel, dim3(1), dim3(kScanT), 0, st, bsum, nb, ctr);
-    if (nb) hipLaunchKernelGGL(tx_downsweep_kernel, dim3(uint32_t(nb)), dim3(kScanT), 0, st, val, n_tiles, bsum);
+    const auto* chunks = reinterpret_cast<const DevChunk*>(tables + p.off_chunks);
+    if (nb)
+        hipLaunchKernelGGL(tx_downsweep_kernel, dim3(uint32_t(nb)), dim3(kScanT), 0, st, val, n_tiles, bsum, first,
+                           chunks, tensors, ctr, static_cast<uint8_t*>(dir_dev), dir_cap, payload_cap);
     if (n) {
         TxArgs a;
         a.dir = static_cast<const uint8_t*>(delta_dir_dev);
         a.payload = static_cast<const uint8_t*>(delta_payload_dev);
         a.n = n;
-        a.tensors = tensors;
-        a.chunks = reinterpret_cast<const DevChunk*>(tables + p.off_chunks);
         a.pieces = reinterpret_cast<const DevPiece*>(tables + p.off_pieces);
         a.old_sh = reinterpret_cast<const uint8_t* const*>(ws + p.ws_old);
-        a.excl = val;
         a.ctr = ctr;
         a.out_dir = static_cast<uint8_t*>(dir_dev);
         a.out_payload = static_cast<uint8_t*>(payload_dev);
