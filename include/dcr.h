@@ -350,10 +350,14 @@ int32_t dcr_encode_retry_partial(const dcr_plan* plan,
  * Every directory entry is checked (tensor, chunk, sizes, order, at most an
  * XOR then an overwrite record per chunk) and every record's change set
  * (bounds, popcounts, disjoint records); a malformed DELTA stream makes
- * result->status DCR_E_FORMAT and no record is written.  A stream that does
- * not fit dir_cap / payload_cap gives DCR_E_CAPACITY with its sizes in the
- * result, as dcr_encode does.  Like every call, one workspace serves one call
- * at a time. */
+ * result->status DCR_E_FORMAT, and the output buffers then hold no usable
+ * stream (a bad entry stops the call before any record is written; a bad
+ * change set is found per record, while others are written).  The
+ * directory buffer also carries per-record scratch during the call, each
+ * slot replaced by its entry.  A stream that does not fit dir_cap /
+ * payload_cap gives DCR_E_CAPACITY with its sizes in the result, as
+ * dcr_encode does.  Like every call, one workspace serves one call at a
+ * time. */
 int32_t dcr_encode_retry_from_delta(const dcr_plan* plan, const void* const* old_shards,
                                     const dcr_stream_header* delta_header,
                                     const void* delta_dir_dev, uint64_t delta_dir_bytes,
