@@ -2,7 +2,7 @@
 // shards, without reading the new shards.
 //
 // After a failed refit the whole change set is sent again as overwrites
-// (tokendh blog, "no backup copy"; the Italian summary on retries): per
+// (tokendh blog, "no backup copy"; ai.info abstract): per
 // changed chunk, one overwrite record with the new bits of every changed
 // element.  The DELTA stream of the same step already names every changed
 // element of a chunk, with either its XOR mask (new = old ^ mask) or its new

@@ -330,7 +330,7 @@ int32_t dcr_encode_retry_partial(const dcr_plan* plan,
 
 /* RETRY stream from a DELTA stream (sender side).  The overwrite retry
  * re-sends every changed element with its new bits (tokendh blog, "no backup
- * copy"; the Italian summary on retries).  The DELTA stream of the same
+ * copy"; ai.info abstract).  The DELTA stream of the same
  * refit step names every changed element with its XOR mask or its new bits,
  * so this call writes the stream dcr_encode with DCR_MODE_RETRY would write
  * (the same bytes, the same header versions as the DELTA stream's) while
