@@ -879,6 +879,19 @@ def _bench_layout(lay, dev, reps, host_values=None):
         graph = {"encode_apply_replay_ms": round(float(np.median(gt)), 4),
                  "encode_apply_eager_ms": round(float(np.median(et)), 4), "stream_eq_eager": bool(same)}
         del g, gsb, wsg
+    # the RETRY stream written from the DELTA stream, into the retry buffers
+    # (after the retry timings): the same stream again, checked by its sizes,
+    # header and the sums of its 64-bit words
+    def words(t, n):
+        return int(t[:n].view(torch.int64).sum()) if n else 0
+    want = (words(retry.dir, 32 * rn_rec), words(retry.payload, rp_bytes))
+    x_ms, _ = _timed(lambda: dcr.dcr_encode_retry_from_delta(plan, olds_t, hdr, delta.dir, delta.payload, 0,
+                                                             retry.header, retry.dir, retry.payload, retry.result,
+                                                             ws), reps)
+    xr = retry.result_host()
+    x_same = (int(xr["status"]) == 0 and retry.n_records() == rn_rec and retry.payload_bytes() == rp_bytes
+              and np.array_equal(retry.header_host(), rhdr)
+              and (words(retry.dir, 32 * rn_rec), words(retry.payload, rp_bytes)) == want)
     app_alg = 32 * n_rec + p_bytes + LINE * n_lines + SECTOR * n_sec
     ret_alg = 32 * rn_rec + rp_bytes + LINE * n_lines + SECTOR * n_sec
     out = {"canonical_GB": round(cb / 1e9, 3), "tensors": int(info.n_tensors), "chunks": int(info.n_chunks),
@@ -892,6 +905,7 @@ def _bench_layout(lay, dev, reps, host_values=None):
            "apply": _op_stats(a_ms, a_kms, app_alg, cb),
            "retry": _op_stats(t_ms, t_kms, ret_alg, cb),
            "rmw_ceiling_ms": round(rmw_ms, 4),
+           "retry_from_delta": {"ms": round(float(np.median(x_ms)), 4), "same_stream": bool(x_same)},
            "checks": {"apply_eq_new": bool(ok_apply), "retry_eq_new": bool(ok_retry)}}
     if graph is not None:
         out["graph"] = graph

@@ -335,7 +335,9 @@ int32_t dcr_encode_retry_partial(const dcr_plan* plan,
  * so this call writes the stream dcr_encode with DCR_MODE_RETRY would write
  * (the same bytes, the same header versions as the DELTA stream's) while
  * reading only the DELTA stream and old at the changed elements; the new
- * shards are not read.
+ * shards are not read.  It pays off at low change rates (about half the
+ * time of the RETRY encode at 1 % of BF16 elements changed); on dense
+ * chunks, where each thread walks many changes, the encode is faster.
  *   old_shards       the plan's old shards (device; as for dcr_encode)
  *   delta_header     the DELTA stream's header, in HOST memory (magic,
  *                    format, chunk size, plan fingerprint and stream_kind
