@@ -85,3 +85,89 @@ def fnv1a64(data: bytes) -> int:
         h ^= b
         h = (h * 0x100000001B3) & ((1 << 64) - 1)
     return h
+
+
+def hi_mode_of(K, h):
+    """High-byte mode of a 2-byte XOR record with K changes, h of them with a
+    nonzero high byte: NONE, SPARSE when strictly smaller than DENSE, else DENSE."""
+    if h == 0:
+        return 0
+    return 1 if pad16((K + 7) // 8) + pad16(h) < pad16(K) else 2
+
+
+def build_record(n_c, w, kind, idx, words):
+    """-> (payload bytes, hi_mode, H) of one bitmap-layout record written from
+    the format definition: changes idx (ascending chunk indices) carrying
+    words (XOR masks or new bits)."""
+    idx = [int(i) for i in idx]
+    words = [int(x) for x in words]
+    K = len(idx)
+    out = bytearray(pad16((n_c + 7) // 8))
+    for i in idx:
+        out[i // 8] |= 1 << (i % 8)
+    lo = bytearray(pad16(K))
+    for j, x in enumerate(words):
+        lo[j] = x & 0xFF
+    out += lo
+    if w == 1:
+        return bytes(out), 0, 0
+    if kind == 0:                       # XOR on 2-byte elements
+        his = [(x >> 8) & 0xFF for x in words]
+        h = sum(1 for b in his if b)
+        mode = hi_mode_of(K, h)
+        if mode == 1:
+            pres = bytearray(pad16((K + 7) // 8))
+            for j, b in enumerate(his):
+                if b:
+                    pres[j // 8] |= 1 << (j % 8)
+            hp = bytearray(pad16(h))
+            for q, b in enumerate(b for b in his if b):
+                hp[q] = b
+            out += pres + hp
+            return bytes(out), 1, h
+        if mode == 2:
+            hp = bytearray(pad16(K))
+            for j, b in enumerate(his):
+                hp[j] = b
+            out += hp
+            return bytes(out), 2, K
+        return bytes(out), 0, 0
+    for b in range(1, w):               # overwrite: the upper planes
+        plane = bytearray(pad16(K))
+        for j, x in enumerate(words):
+            plane[j] = (x >> (8 * b)) & 0xFF
+        out += plane
+    return bytes(out), 2, K
+
+
+def build_stream(records, kind, base, new, fingerprint, numels, widths):
+    """-> (header, directory, payload) as uint8 arrays for records given as
+    (tensor, chunk, record kind, chunk indices, words), in the order given."""
+    dirb, pay = bytearray(), bytearray()
+    for (t, c, k, idx, words) in records:
+        w = widths[t]
+        E = 65536 // w
+        n_c = min(E, numels[t] - c * E)
+        body, mode, H = build_record(n_c, w, k, idx, words)
+        e = bytearray(32)
+        e[0:4] = int(t).to_bytes(4, "little")
+        e[4:8] = int(c).to_bytes(4, "little")
+        e[8:12] = len(idx).to_bytes(4, "little")
+        e[12], e[13], e[14], e[15] = k, mode, w, 0
+        e[16:24] = len(pay).to_bytes(8, "little")
+        e[24:28] = len(body).to_bytes(4, "little")
+        e[28:32] = int(H).to_bytes(4, "little")
+        dirb += e
+        pay += body
+    h = bytearray(64)
+    h[0:4] = MAGIC.to_bytes(4, "little")
+    h[4:6] = (1).to_bytes(2, "little")
+    h[6:8] = int(kind).to_bytes(2, "little")
+    h[8:12] = (65536).to_bytes(4, "little")
+    h[16:24] = int(base).to_bytes(8, "little")
+    h[24:32] = int(new).to_bytes(8, "little")
+    h[32:40] = int(fingerprint).to_bytes(8, "little")
+    h[40:48] = (len(records)).to_bytes(8, "little")
+    h[48:56] = len(pay).to_bytes(8, "little")
+    as_u8 = lambda b: np.frombuffer(bytes(b), dtype=np.uint8).copy()
+    return as_u8(h), as_u8(dirb), as_u8(pay)

@@ -622,4 +622,131 @@ def pin_golden_records(orc):
         assert bytes(p).hex() == spec["payload"].replace(" ", "").lower(), fn
 
 
+def _golden_spec(fn):
+    spec = {}
+    with open(os.path.join(GOLDEN, fn)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                k, v = line.split("=", 1)
+                spec[k.strip()] = v.strip()
+    return spec
+
+
+def pin_golden_header(orc):
+    """A 64-byte stream header worked out by hand (tests/golden/worked_header.txt):
+    magic, format version, stream kind, chunk size, base and new versions,
+    the plan fingerprint (FNV-1a-64 of the serialised tensor table, checked
+    against the FNV reference vectors in pin_fingerprint), record and payload
+    totals and the zero reserved words, byte for byte."""
+    spec = _golden_spec("worked_header.txt")
+    src = _golden_spec(spec["source"])
+    old = np.array([int(x, 16) for x in src["old"].split()], np.uint16)
+    new = np.array([int(x, 16) for x in src["new"].split()], np.uint16)
+    T, S = _one_tensor(len(old), 2)
+    table = bytes.fromhex(spec["table"])
+    assert np.zeros(1, dtype=synth.TENSOR_DT).itemsize == len(table)
+    Tb = np.zeros(1, dtype=synth.TENSOR_DT)
+    Tb[:] = T
+    assert Tb.tobytes() == table
+    assert fmt.fnv1a64(table) == int(spec["fingerprint"], 16)
+    assert orc.fingerprint(T) == int(spec["fingerprint"], 16)
+    rc, hdr, d, p = orc.encode(T, S, [old], [new], base_version=int(spec["base_version"], 16),
+                               new_version=int(spec["new_version"], 16))
+    assert rc == 0
+    assert bytes(hdr).hex() == spec["header"].replace(" ", "").lower()
+    assert len(d) == 32 and len(p) == int.from_bytes(bytes(hdr[48:56]), "little")
+
+
+def pin_group_disjoint_records(orc):
+    """The XOR and overwrite records of one chunk may not mark elements of the
+    same 16-byte group (the rule that lets apply patch each group with one
+    128-bit read-modify-write and keeps records independent, so dedup by
+    record id holds: tokendh blog, "XOR or overwrite").  Streams written by
+    hand from the format definition: records on different groups of one chunk
+    validate and apply element by element; records sharing a group are
+    refused by validate, apply and retry, and apply writes nothing."""
+    n = 64
+    T, S = _one_tensor(n, 2)
+    fp = orc.fingerprint(T)
+    old = (np.arange(n, dtype=np.uint16) * 0x0101 + 0x3C00).astype(np.uint16)
+    # element 0 by XOR mask 0x0001; element 8 (the next group) overwritten
+    good = [(0, 0, 0, [0], [0x0001]), (0, 0, 1, [8], [0xBEEF])]
+    hdr, d, p = fmt.build_stream(good, 0, 5, 6, fp, [n], [2])
+    assert orc.validate(T, hdr, d, p, 5) == 0
+    W = [old.view(np.uint8).copy()]
+    assert orc.apply(T, W, hdr, d, p, np.zeros(2, np.uint8), expected_base_version=5) == 0
+    exp = old.copy()
+    exp[0] ^= 0x0001
+    exp[8] = 0xBEEF
+    assert np.array_equal(W[0].view(np.uint16), exp)
+    # the overwrite marks element 7, in the XOR record's group 0..7; and the
+    # same clash in a RETRY-kind stream of two overwrite records
+    for second in ([7], [3]):
+        bad = [(0, 0, 0, [0], [0x0001]), (0, 0, 1, second, [0xBEEF])]
+        hdr, d, p = fmt.build_stream(bad, 0, 5, 6, fp, [n], [2])
+        assert orc.validate(T, hdr, d, p, 5) == O_E_FORMAT, second
+        W = [old.view(np.uint8).copy()]
+        assert orc.apply(T, W, hdr, d, p, np.zeros(2, np.uint8), expected_base_version=5) == O_E_FORMAT
+        assert np.array_equal(W[0].view(np.uint16), old)
+    # group 15..15 of a ragged chunk: elements 56..63 form the last group
+    bad = [(0, 0, 0, [63], [0x0100]), (0, 0, 1, [56], [0x1234])]
+    hdr, d, p = fmt.build_stream(bad, 0, 5, 6, fp, [n], [2])
+    assert orc.validate(T, hdr, d, p, 5) == O_E_FORMAT
+
+
+def pin_tensor_table_refusals(orc):
+    """The oracle refuses tensor tables the format cannot carry (its own
+    checks, not the GPU plan builder's): a width other than 1/2/4 bytes, an
+    unknown route, XOR routes on 4-byte elements (fp32 tensors go out as
+    overwrites), block-scaled tensors without a valid fp32 overwrite scale
+    tensor of ceil(numel / block) elements, blocks that split a 16-byte
+    group, and scale fields on other routes.  A valid table passes."""
+    from oracle import oracle as O
+
+    def table(rows):
+        T = np.zeros(len(rows), dtype=synth.TENSOR_DT)
+        for i, r in enumerate(rows):
+            T[i] = r
+        S = np.zeros(len(rows), dtype=synth.SEGMENT_DT)
+        for i, r in enumerate(rows):
+            S[i]["tensor_id"] = i
+            S[i]["shard_id"] = i
+            S[i]["ndim"] = 1
+            S[i]["extent"] = [int(r[0]), 1, 1, 1]
+            S[i]["shard_stride"] = [1, 0, 0, 0]
+            S[i]["canon_stride"] = [1, 0, 0, 0]
+        return T, S
+
+    def run(rows):
+        T, S = table(rows)
+        sh = [np.zeros(int(r[0]) * max(int(r[1]), 1), np.uint8) for r in rows]
+        rc, *_ = orc.encode(T, S, sh, [x.copy() for x in sh])
+        return rc
+
+    ok = [(256, 2, 2, 1, 128), (2, 4, 1, -1, 0)]          # block-scaled BF16 + its fp32 scales
+    assert run(ok) == 0
+    cases = {
+        "width 3": [(16, 3, 1, -1, 0)],
+        "route 3": [(16, 2, 3, -1, 0)],
+        "XOR on 4-byte": [(16, 4, 0, -1, 0)],
+        "block-scaled on 4-byte": [(256, 4, 2, 1, 128), (2, 4, 1, -1, 0)],
+        "scale tensor missing": [(256, 2, 2, -1, 128)],
+        "scale tensor out of range": [(256, 2, 2, 5, 128), (2, 4, 1, -1, 0)],
+        "scale tensor is itself": [(256, 2, 2, 0, 128)],
+        "scale tensor not fp32": [(256, 2, 2, 1, 128), (2, 2, 1, -1, 0)],
+        "scale tensor not overwrite": [(256, 2, 2, 1, 128), (2, 4, 2, 0, 128)],
+        "block of 0": [(256, 2, 2, 1, 0), (2, 4, 1, -1, 0)],
+        "block splits a group": [(256, 2, 2, 1, 4), (64, 4, 1, -1, 0)],
+        "scale length long": [(256, 2, 2, 1, 128), (3, 4, 1, -1, 0)],
+        "scale length short": [(256, 2, 2, 1, 128), (1, 4, 1, -1, 0)],
+        "scale fields on affine": [(16, 2, 0, -1, 8)],
+        "scale tensor on overwrite": [(16, 2, 1, 0, 0)],
+    }
+    for name, rows in cases.items():
+        assert run(rows) == O.E_INVAL, name
+        T, S = table(rows)
+        assert orc.validate(T, np.zeros(64, np.uint8), np.zeros(0, np.uint8), np.zeros(0, np.uint8)) == O.E_INVAL, name
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

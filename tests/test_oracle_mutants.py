@@ -3,8 +3,10 @@
 Each mutant is a plausible slip (wrong bit order, float-style comparison,
 wrong word, tie-break, byte plane, transposed strides, chunk size, missing
 dedup, inverted routing, missing padding, partial retry ignoring the flags or
-marking the wrong chunk, index lists off by one or never chosen); the copy is compiled in a temp
-directory and loaded beside the real oracle.  Nothing here touches a GPU.
+marking the wrong chunk, index lists off by one or never chosen, the same-group
+check between a chunk's two records skipped, a header field left unwritten,
+tensor-table refusals dropped); the copy is compiled in a temp directory and
+loaded beside the real oracle.  Nothing here touches a GPU.
 """
 import os
 import shutil
@@ -47,6 +49,12 @@ MUTANTS = {
                                   "if (!delta_flags[r]) need[first[et]] = 1;"),
     "list_index_off_by_one": ("for (j = 0; j < K; j++) put_u16(out + 2 * j, (uint16_t)idx[j]);",
                               "for (j = 0; j < K; j++) put_u16(out + 2 * j, (uint16_t)(idx[j] + 1));"),
+    "check_pair_skipped": ("rc = check_pair(T, payload, &prev, &cur);",
+                           "rc = ORC_OK;"),
+    "header_new_version_dropped": ("put_u64(p + 24, new_v);", "(void)new_v;"),
+    "xor_on_w4_allowed": ("if (d->route != ORC_ROUTE_OVERWRITE && w == 4) return ORC_E_INVAL;", "(void)0;"),
+    "scale_length_unchecked": ("if (s->numel != (d->numel + d->scale_block - 1) / d->scale_block) return ORC_E_INVAL;",
+                               "(void)s;"),
     "list_layout_never": ("return (lists && pad16(2 * K) < pad16((n_c + 7) / 8)) ? ORC_LAYOUT_LIST : ORC_LAYOUT_BITMAP;",
                           "(void)lists; (void)K; (void)n_c; return ORC_LAYOUT_BITMAP;"),
 }
