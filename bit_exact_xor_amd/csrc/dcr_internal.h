@@ -27,7 +27,10 @@ constexpr uint64_t kFlagAgg = 1, kFlagIncl = 2;
 constexpr int kValShift = 2;
 constexpr int kRecShift = 36;
 constexpr uint64_t kP16Mask = (uint64_t(1) << kRecShift) - 1;
-constexpr uint64_t kMaxTiles = uint64_t(1) << 25;   // 2 records per tile < 2^26
+// tiles (chunks) of a plan: the encode launches one kThreads workgroup per
+// tile in one grid, whose work-items must fit 32 bits (4 194 303 chunks,
+// 256 GiB of canonical BF16); this also keeps 2 records per tile below 2^26
+constexpr uint64_t kMaxTiles = uint64_t(0xFFFFFFFFu) / kThreads;
 constexpr uint32_t kFixTiles = 256;                 // tiles per workgroup of the encode fix-up
 // encode counters (uint32 words at ws_counter): [0] tile claim, [1] fix-up
 // block claim, [2..3] changed elements, [4..5] stream total

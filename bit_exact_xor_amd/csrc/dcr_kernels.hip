@@ -6,10 +6,14 @@
 //   "key modules" 1), 16 bytes per lane per load.  It compares stored bits as
 //   integers (tokendh blog "shard owner": +0/-0 differ) and routes each
 //   16-byte group to XOR or overwrite (ai-feeds "key modules" 2-3).  Change
-//   counts are scanned per workgroup; the tile's record count and payload size
-//   go through a device-wide decoupled look-back that yields the directory
-//   index and the payload offset.  The records are staged in LDS and written
-//   with 128-bit stores.
+//   counts are scanned per workgroup and the records are assembled in LDS and
+//   written with 128-bit stores.  With a staging area (the default), each
+//   tile writes its records to a slot of its own and publishes its record
+//   count and payload size; a fix-up pass scans those sizes (a decoupled
+//   look-back across fix-up blocks of 256 tiles) into directory indices and
+//   payload offsets and moves the records into place.  Without one, each
+//   tile finds its offsets by a decoupled look-back over all earlier tiles
+//   and writes in place.
 // apply (receiver): one workgroup per directory entry.  It checks the entry
 //   and the record bytes before touching anything, stages the record in LDS,
 //   ranks the changes by a workgroup scan of the bitmap, and updates every
@@ -2015,7 +2019,11 @@ static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_
     if (!al16(dir) || !al16(payload) || !al16(res) || !al16(ws)) return fail(DCR_E_INVAL, "buffer not 16-byte aligned");
     if (!retry && n && !flags) return fail(DCR_E_INVAL, "applied_flags is NULL");
     if (ws_bytes < p.ws_bytes) return fail(DCR_E_CAPACITY, "workspace too small");
-    if (n > 0x7FFFFFFFull) return fail(DCR_E_INVAL, "too many records in one call");
+    // one workgroup per record in one grid (work-items must fit 32 bits): at
+    // most kSmallThreads-wide workgroups for a call within the plan's record
+    // capacity, kThreads-wide ones beyond it
+    if (n > (n <= p.big_cap ? UINT32_MAX / kSmallThreads : UINT32_MAX / kThreads))
+        return fail(DCR_E_INVAL, "too many records in one call");
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     int32_t rc;
     if (sharded) {

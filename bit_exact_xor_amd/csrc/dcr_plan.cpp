@@ -190,7 +190,9 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
             return fail(DCR_E_COVERAGE, "tensor " + std::to_string(t) + ": canonical element " +
                                             std::to_string(cursor) + " not covered");
         const uint64_t nch = (d.numel + E - 1) / E;
-        if (P.chunks.size() + nch > kMaxTiles) return fail(DCR_E_INVAL, "plan has too many chunks");
+        if (P.chunks.size() + nch > kMaxTiles)
+            return fail(DCR_E_INVAL, "plan has more than " + std::to_string(kMaxTiles) +
+                                         " chunks (one encode workgroup per chunk in one grid)");
         DevTensor& dt = P.dt[t];
         dt = DevTensor{};
         dt.numel = d.numel;

@@ -358,18 +358,19 @@ __global__ __launch_bounds__(kTT) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const uint8_t* PA = a.payload + offA;
     const uint8_t* PB = a.payload + offB;
 
-    // the change sets: bitmap records word by word, then index lists
+    // the change sets: bitmap records word by word (the padding words past
+    // the chunk's elements too: a bit there is refused, as apply refuses it),
+    // then index lists
     bool bad = false;
     for (uint32_t wi = tid; wi < nwp; wi += kTT) {
         uint32_t xa = 0, xb = 0;
-        if (wi < nw) {
-            const uint32_t valid = n_c - 32 * wi >= 32 ? 0xFFFFFFFFu : ((1u << (n_c - 32 * wi)) - 1u);
-            if (layA == DCR_LAYOUT_BITMAP) xa = reinterpret_cast<const uint32_t*>(PA)[wi];
-            if (two && layB == DCR_LAYOUT_BITMAP) xb = reinterpret_cast<const uint32_t*>(PB)[wi];
-            if (((xa | xb) & ~valid) || (xa & xb)) bad = true;
-        }
-        M[wi] = xa | xb;
-        B[wi] = xb;
+        const uint32_t valid =
+            wi >= nw ? 0u : (n_c - 32 * wi >= 32 ? 0xFFFFFFFFu : ((1u << (n_c - 32 * wi)) - 1u));
+        if (layA == DCR_LAYOUT_BITMAP) xa = reinterpret_cast<const uint32_t*>(PA)[wi];
+        if (two && layB == DCR_LAYOUT_BITMAP) xb = reinterpret_cast<const uint32_t*>(PB)[wi];
+        if (((xa | xb) & ~valid) || (xa & xb)) bad = true;
+        M[wi] = (xa | xb) & valid;
+        B[wi] = xb & valid;
     }
     // the chunk's pieces (read only for XOR changes, after the bitmaps)
     if (np <= kCached && tid < np) {
@@ -551,7 +552,10 @@ extern "C" int32_t dcr_encode_retry_from_delta(
         return fail(DCR_E_FORMAT, "DELTA header: bad magic / version / chunk size / stream kind");
     if (h->plan_fingerprint != p.fingerprint) return fail(DCR_E_FORMAT, "DELTA header: plan fingerprint mismatch");
     const uint64_t n = h->n_records;
-    if (n > 0xFFFFFFFFull) return fail(DCR_E_INVAL, "too many DELTA records");
+    // a valid DELTA stream holds at most an XOR and an overwrite record per
+    // chunk (this also keeps the record kernel's grid within its limits)
+    if (n > 2 * uint64_t(p.chunks.size()))
+        return fail(DCR_E_FORMAT, "DELTA header: more records than two per chunk of the plan");
     if (n && (!delta_dir_dev || delta_dir_bytes / DCR_DIRENT_BYTES < n))
         return fail(DCR_E_INVAL, "DELTA directory buffer smaller than n_records entries");
     if (h->payload_bytes && (!delta_payload_dev || delta_payload_bytes < h->payload_bytes))

@@ -185,7 +185,14 @@ typedef struct {
 /* --------------------------------------------------------------- calls */
 
 /* Build a plan from the canonical tensor table, the shard sizes (bytes) and
- * the affine segments (see dcr_segment).  Checks every descriptor, that every
+ * the affine segments (see dcr_segment).
+ * Passages: a fixed affine map that depends only on the static shard layout
+ * projects a shard-local index to canonical checkpoint coordinates (ai-feeds
+ * summary "key modules" 1, direct projection); each training shard has one
+ * owner, so replicas are checked once (tokendh blog "shard owner"); ownership
+ * is remapped so that the ranks cover the checkpoint exactly once and the
+ * tiling / address metadata is prepared on the CPU (humansand "weight
+ * teleportation" page, "A strong baseline with Blackwell-native DE").  Checks every descriptor, that every
  * segment stays inside its tensor and shard (DCR_E_INVAL) and that every
  * canonical element is covered exactly once (DCR_E_COVERAGE; the ownership
  * invariant: one owner per element, replicas are not listed).  Expands the
@@ -209,6 +216,15 @@ int32_t dcr_plan_upload(dcr_plan* plan, void* dev_tables, uint64_t bytes, void* 
 void dcr_plan_destroy(dcr_plan* plan);
 
 /* Encode one refit step (sender side).
+ * Passages: the owner of each training shard detects the weights whose stored
+ * value changed since the last version (ai-feeds summary "Method / input and
+ * change detection"), comparing stored bit patterns rather than float values,
+ * so +0/-0 and other sign flips count (tokendh blog "shard owner"); affine
+ * changes are projected to canonical coordinates and carried as XOR masks,
+ * the residual ones (fused QKV, shared scales) as overwrites, both in one
+ * delta stream (ai-feeds "key modules" 1-3; tokendh "XOR or overwrite");
+ * mask = old ^ new on a flat bit buffer (humansand "weight teleportation"
+ * page, "Delta update algebra").
  *   old_shards / new_shards  host arrays of n_shards device pointers: the
  *                  trainer shards of the committed base and of the new step
  *   mode           DCR_MODE_DELTA: XOR / overwrite records by route;
@@ -372,6 +388,12 @@ int32_t dcr_encode_retry_from_delta(const dcr_plan* plan, const void* const* old
 
 /* Apply records [first_record, first_record + n_records) of a stream in place
  * (receiver side).
+ * Passages: the receiver XORs each mask into its existing parameter buffer and
+ * writes overwrite records in place, and the stream is bound to the base
+ * version it was computed from (ai-feeds summary "key modules" 4); a XOR
+ * applied twice undoes itself, so each record carries a unique id and is
+ * applied once (tokendh blog "XOR or overwrite"); new = old ^ mask
+ * (humansand "weight teleportation" page, "Delta update algebra").
  *   canon          host array of n_tensors device pointers, one per canonical
  *                  tensor (numel * elem_bytes bytes, 16-byte aligned)
  *   header         the stream header, in HOST memory; its magic, format, chunk
@@ -396,7 +418,11 @@ int32_t dcr_apply(const dcr_plan* plan, void* const* canon,
 
 /* Re-apply every record of a RETRY stream (header stream_kind must be
  * DCR_MODE_RETRY, every record an overwrite) as an overwrite, ignoring and
- * not touching dedup flags.  Overwrites are idempotent, so any partial, torn
+ * not touching dedup flags.
+ * Passages: after a failure the whole change set is re-sent as overwrites,
+ * which are idempotent, so no backup copy is kept (tokendh blog "no backup
+ * copy"); receivers end with the same bits a dense refit gives and recover
+ * fully from failures during the refit (ai.info abstract).  Overwrites are idempotent, so any partial, torn
  * or duplicated earlier apply ends at the new bits. */
 int32_t dcr_apply_overwrite_retry(const dcr_plan* plan, void* const* canon,
                                   const dcr_stream_header* header,

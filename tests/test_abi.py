@@ -142,3 +142,25 @@ def test_window_stage_bytes():
     p2 = dcr.dcr_plan_build(small.tensors, [small.shard_bytes(s) for s in range(small.n_shards)], small.segments)
     assert p2.info.n_chunks < 256
     assert p2.info.window_stage_bytes == p2.info.max_payload_bytes
+
+
+def test_plan_chunk_limit():
+    """A plan holds at most (2^32 - 1) / 1024 chunks, since the encode runs one
+    1024-thread workgroup per chunk in one grid: one uint8 tensor of exactly
+    that many 64 KiB chunks builds, one more chunk is refused (no memory is
+    touched: sizes only, the plan tables are a few dozen bytes per chunk)."""
+    limit = (2 ** 32 - 1) // 1024
+    for n_chunks, ok in ((limit, True), (limit + 1, False)):
+        numel = n_chunks * 65536
+        T = np.zeros(1, dtype=synth.TENSOR_DT)
+        T[0] = (numel, 1, 1, -1, 0)
+        S = np.zeros(1, dtype=synth.SEGMENT_DT)
+        S[0] = (0, 0, 1, 0, 0, 0, [numel, 1, 1, 1], [1, 0, 0, 0], [1, 0, 0, 0])
+        if ok:
+            p = dcr.dcr_plan_build(T, [numel], S)
+            assert p.info.n_chunks == limit
+            del p
+        else:
+            with pytest.raises(dcr.DcrError) as e:
+                dcr.dcr_plan_build(T, [numel], S)
+            assert e.value.code == dcr.DCR_E_INVAL

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from bit_exact_xor_amd import dcr, synth
-from tests import pins
+from tests import fmt, pins
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -118,10 +118,13 @@ def test_retry_from_delta_empty_and_capacity(gh, orc):
 
 
 def test_retry_from_delta_refused(gh, orc):
-    """Host checks: a RETRY header, a short directory or payload buffer raise.
-    Device checks (status DCR_E_FORMAT, nothing written): an entry naming a
-    tensor the plan lacks, a record size that disagrees with its fields,
-    records out of order, a bitmap whose popcount is not K."""
+    """Host checks: a RETRY header, a short directory or payload buffer, a
+    header claiming more records than two per chunk raise.  Device checks
+    (status DCR_E_FORMAT, no usable stream): an entry naming a tensor the
+    plan lacks, a record size that disagrees with its fields, records out of
+    order (these stop the call before any record is written), a bitmap whose
+    popcount is not K, a bit set in a bitmap's padding words past the
+    chunk's elements (found per record, while other records are written)."""
     say("retry from delta: refused")
     lay = synth.random_layout(1751, max_tensors=6, max_chunks=8.0)
     olds, news, co, cn = pins.canon_lists(lay)
@@ -158,3 +161,23 @@ def test_retry_from_delta_refused(gh, orc):
     nz = int(np.nonzero(p[off:off + size])[0][0])   # inside the bitmap, which comes first
     p[off + nz] &= np.uint8(p[off + nz] - 1)
     refused(dd, p, "popcount")
+    # a bit in a padding word of a bitmap (past the chunk's elements, inside
+    # the 16-byte padded section): K stays right, the bit is still refused
+    T = lay.tensors
+    hit = False
+    for r, ent in enumerate(fmt.dirents(dd)):
+        w = ent["w"]
+        E = 65536 // w
+        n_c = min(E, int(T[ent["t"]]["numel"]) - ent["c"] * E)
+        nw = (n_c + 31) // 32
+        if ent["layout"] == 0 and fmt.pad16((n_c + 7) // 8) * 8 > nw * 32:
+            p = dp.copy()
+            p[ent["off"] + 4 * nw] |= np.uint8(1)
+            refused(dd, p, f"padding bit of record {r}")
+            hit = True
+            break
+    assert hit
+    bad_h = dh.copy()
+    bad_h[40:48] = np.frombuffer(np.uint64(2 * g.plan.info.n_chunks + 1).tobytes(), np.uint8)
+    with pytest.raises(dcr.DcrError):
+        transcode(g, bad_h, dev(np.zeros(32 * (2 * g.plan.info.n_chunks + 1), np.uint8)), dev(dp))
