@@ -1,10 +1,11 @@
 """Full-size GPU runs of the Llama-8B TP=4, Qwen3-30B-A3B EP=8 (3 %, Beta(2,60)
 rates) and block-scaled 5 % hot-row MoE workloads.
 
-At these sizes the oracle cannot run the whole model in seconds, so:
-  * sampled parity: the GPU's records of a sample of tensors equal, byte for
-    byte, the oracle's records for those tensors (oracle inputs regenerated on
-    the CPU from the seeded generator);
+  * whole-stream parity: every record of the DELTA and the RETRY stream
+    equals, byte for byte, the oracle's record for the same inputs (the
+    oracle runs unchanged once per tensor group, on a pool of host threads,
+    fed with the device shards copied to host memory); the header and the
+    directory's order and contiguous offsets are checked on the whole stream;
   * properties on the whole model: records count exactly the elements whose
     stored bits differ; apply turns the old canonical tensors into the new
     ones; after a kill at 50 % of the records the overwrite retry heals all.
@@ -15,7 +16,7 @@ import numpy as np
 import pytest
 
 from bit_exact_xor_amd import dcr, synth
-from tests import fmt
+from tests import fmt, stream_check
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -55,7 +56,7 @@ def run_full(orc, lay, sample_names, partial=False, transcode=False):
     ws = dcr.workspace(plan, "cuda")
     cb = int(plan.info.canonical_bytes)
     sb = dcr.StreamBuffers(plan, "cuda", dir_bytes=2 * 32 * int(plan.info.n_chunks),
-                           payload_bytes=int(cb * 0.2) + (1 << 20))
+                           payload_bytes=int(cb * 0.16) + (1 << 24))
     torch.cuda.synchronize()
     say(lay.name, "encode")
     wss = staged_workspace(plan, sb)
@@ -75,29 +76,34 @@ def run_full(orc, lay, sample_names, partial=False, transcode=False):
     assert int(r["n_changed"]) == diff
     say(lay.name, f"{n_rec} records, {pbytes / 1e9:.2f} GB payload, {diff} changed")
 
-    # sampled parity against the oracle
-    name_to_t = {n: i for i, n in enumerate(lay.tensor_names)}
-    sample = [name_to_t[n] for n in sample_names]
-    for t in list(sample):
-        st = int(T[t]["scale_tensor"])
-        if st >= 0 and st not in sample:
-            sample.append(st)
-    sample.sort()
-    Ts, Ss, so, sn = synth.sub_layout(lay, sample)
-    rc, h, d, p = orc.encode(Ts, Ss, so, sn, base_version=3, new_version=4)
-    assert rc == 0
-    gd = sb.dir[: n_rec * 32].cpu().numpy()
-    ents = fmt.dirents(gd)
-    remap = {t: i for i, t in enumerate(sample)}
-    mine = [e for e in ents if e["t"] in remap]
-    theirs = fmt.dirents(d)
-    assert len(mine) == len(theirs) and len(theirs) > 0
-    for e, o in zip(mine, theirs):
-        assert (remap[e["t"]], e["c"], e["K"], e["kind"], e["hi_mode"], e["w"], e["size"], e["H"]) == \
-               (o["t"], o["c"], o["K"], o["kind"], o["hi_mode"], o["w"], o["size"], o["H"])
-        got = sb.payload[e["off"]:e["off"] + e["size"]].cpu().numpy()
-        assert np.array_equal(got, p[o["off"]:o["off"] + o["size"]]), (lay.tensor_names[e["t"]], e["c"])
-    say(lay.name, f"sampled parity: {len(theirs)} records of {len(sample)} tensors identical")
+    # the RETRY stream now, so that both streams are checked against the oracle
+    rsb = dcr.StreamBuffers(plan, "cuda", dir_bytes=32 * int(plan.info.n_chunks),
+                            payload_bytes=int(cb * 0.16) + (1 << 24))
+    say(lay.name, "encode RETRY")
+    wss = staged_workspace(plan, rsb)
+    dcr.dcr_encode(plan, olds, news, 1, 3, 4, rsb.header, rsb.dir, rsb.payload, rsb.result, wss)
+    torch.cuda.synchronize()
+    del wss
+    rr = rsb.result_host()
+    assert int(rr["status"]) == 0, rr
+    assert int(rr["n_changed"]) == diff
+
+    # whole-stream parity against the oracle
+    streams = {0: stream_check.HostStream(sb.header.cpu().numpy(), sb.dir[: n_rec * 32].cpu().numpy(),
+                                          sb.payload[:pbytes].cpu().numpy()),
+               1: stream_check.HostStream(rsb.header.cpu().numpy(),
+                                          rsb.dir[: int(rr["n_records"]) * 32].cpu().numpy(),
+                                          rsb.payload[: int(rr["payload_bytes"])].cpu().numpy())}
+    for mode, hs in streams.items():
+        err = stream_check.check_layout(hs, lay.n_tensors, mode, 3, 4, plan.info.fingerprint)
+        assert err is None, (mode, err)
+    say(lay.name, f"oracle parity of every record ({stream_check.host_cores()} threads)")
+    pr = stream_check.full_parity(orc, lay, olds, news, streams, 3, 4, log=lambda m: say(lay.name, m))
+    assert pr["identical"], pr["first_mismatch"]
+    assert pr["records"] == n_rec + int(rr["n_records"]) and pr["groups"] > 0
+    say(lay.name, f"oracle parity: {pr['records']} records of {pr['groups']} tensor groups identical "
+                  f"({pr['seconds']} s)")
+    del streams
 
     # apply / kill at 50 % / retry, on canonical tensors
     co = lay.assemble(typed(lay, olds))
@@ -128,14 +134,7 @@ def run_full(orc, lay, sample_names, partial=False, transcode=False):
     dcr.dcr_apply(plan, canon, hdr, sb.dir, sb.payload, flags, 0, n_rec // 2, 3, res, ws)
     if not (partial or transcode):
         del sb
-    rsb = dcr.StreamBuffers(plan, "cuda", dir_bytes=32 * int(plan.info.n_chunks),
-                            payload_bytes=int(cb * 0.2) + (1 << 20))
     say(lay.name, "retry")
-    wss = staged_workspace(plan, rsb)
-    dcr.dcr_encode(plan, olds, news, 1, 3, 4, rsb.header, rsb.dir, rsb.payload, rsb.result, wss)
-    torch.cuda.synchronize()
-    del wss
-    assert int(rsb.result_host()["status"]) == 0
     if transcode:
         # the same RETRY stream, written from the DELTA stream and old only
         say(lay.name, "retry stream from the DELTA stream")

@@ -4,17 +4,19 @@ plus 40 GB of uint8 NVFP4-packed tensors resident in HBM.
 The DELTA stream (3 % BF16 changes, 0.085 % byte changes) is encoded window by
 window (the trainer side's new values never fit beside 240 GB of receiver
 state) and stitched into one stream.  The receiver is killed after 50 % of the
-records; the overwrite retry stream then heals everything.  Checked: sampled
-records byte-identical to the oracle, and every tensor equal to the new
-weights after the retry (compared window by window against regenerated new
-values)."""
+records; the overwrite retry stream then heals everything.  Checked: every
+record of both streams byte-identical to the oracle's (window by window,
+while the window's old and new values are on the device: the oracle runs per
+tensor on a pool of host threads), the stitched streams' headers, order and
+contiguous offsets, and every tensor equal to the new weights after the
+retry (compared window by window against regenerated new values)."""
 import time
 
 import numpy as np
 import pytest
 
 from bit_exact_xor_amd import dcr, synth
-from tests import fmt
+from tests import stream_check
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -26,10 +28,13 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def build_stream(lay, plan_full, mode, dir_buf, payload, t_old, t_new):
-    """Encode tensors window by window into one stream; returns the header."""
+def build_stream(lay, plan_full, mode, dir_buf, payload, t_old, t_new, orc=None):
+    """Encode tensors window by window into one stream; returns the header.
+    With the oracle given, every record of each window is compared with the
+    oracle's before the window's inputs are replaced."""
     n_t = lay.n_tensors
     r_off, p_off, changed = 0, 0, 0
+    checked = {"records": 0, "seconds": 0.0}
     for a in range(0, n_t, WINDOW_TENSORS):
         b = min(n_t, a + WINDOW_TENSORS)
         wl = synth.window_layout(lay, a, b)
@@ -52,6 +57,19 @@ def build_stream(lay, plan_full, mode, dir_buf, payload, t_old, t_new):
         r = np.frombuffer(res.cpu().numpy().tobytes(), dtype=dcr.ENCODE_RESULT)[0]
         assert int(r["status"]) == 0, (a, r)
         n, pb = int(r["n_records"]), int(r["payload_bytes"])
+        if orc is not None:
+            hs = stream_check.HostStream(hdr_w.cpu().numpy(), dir_buf[r_off * 32:(r_off + n) * 32].cpu().numpy(),
+                                         payload[p_off:p_off + pb].cpu().numpy())
+            err = stream_check.check_layout(hs, wl.n_tensors, mode, 5, 6, plan.info.fingerprint)
+            assert err is None, (a, err)
+            pr = stream_check.full_parity(orc, wl, olds, news, {mode: hs}, 5, 6)
+            assert pr["identical"], (a, pr["first_mismatch"])
+            assert pr["records"] == n
+            checked["records"] += n
+            checked["seconds"] += pr["seconds"]
+            if (a // WINDOW_TENSORS) % 8 == 0:
+                say("cfg5", f"mode {mode}: tensors [{a}, {b}) identical to the oracle "
+                            f"({checked['records']} records so far, {checked['seconds']:.0f} s of oracle)")
         if n:
             e32 = dir_buf[r_off * 32:(r_off + n) * 32].view(torch.int32).view(-1, 8)
             e64 = dir_buf[r_off * 32:(r_off + n) * 32].view(torch.int64).view(-1, 4)
@@ -70,6 +88,9 @@ def build_stream(lay, plan_full, mode, dir_buf, payload, t_old, t_new):
     hdr[32:40].view(np.uint64)[0] = plan_full.info.fingerprint
     hdr[40:48].view(np.uint64)[0] = r_off
     hdr[48:56].view(np.uint64)[0] = p_off
+    if orc is not None:
+        assert checked["records"] == r_off
+        say("cfg5", f"mode {mode}: all {r_off} records identical to the oracle ({checked['seconds']:.0f} s)")
     return hdr, r_off, p_off, changed
 
 
@@ -103,23 +124,12 @@ def test_receiver_share_1t(orc):
     dir_buf = torch.empty(32 * n_chunks, dtype=torch.uint8, device="cuda")
     payload = torch.empty(26 * 10**9, dtype=torch.uint8, device="cuda")
     t0 = time.time()
-    hdr, n_rec, p_bytes, changed = build_stream(lay, plan_full, 0, dir_buf, payload, t_old, t_new)
+    hdr, n_rec, p_bytes, changed = build_stream(lay, plan_full, 0, dir_buf, payload, t_old, t_new, orc)
     say("cfg5", f"DELTA stream: {n_rec} records, {p_bytes / 1e9:.2f} GB, {changed} changed ({time.time() - t0:.1f}s)")
-    # sampled parity: one BF16 and one uint8 tensor against the oracle
-    ents = fmt.dirents(dir_buf[: n_rec * 32].cpu().numpy())
-    for t in (1, lay.n_tensors - 1):
-        Ts, Ss, so, sn = synth.sub_layout(lay, [t])
-        rc, h, d, p = orc.encode(Ts, Ss, so, sn, base_version=5, new_version=6)
-        assert rc == 0
-        mine = [e for e in ents if e["t"] == t]
-        theirs = fmt.dirents(d)
-        assert len(mine) == len(theirs) > 0
-        for e, o in zip(mine, theirs):
-            assert (e["c"], e["K"], e["kind"], e["hi_mode"], e["size"], e["H"]) == \
-                   (o["c"], o["K"], o["kind"], o["hi_mode"], o["size"], o["H"])
-            assert np.array_equal(payload[e["off"]:e["off"] + e["size"]].cpu().numpy(),
-                                  p[o["off"]:o["off"] + o["size"]])
-    say("cfg5", "sampled parity (one BF16, one uint8 tensor): identical")
+    # the stitched stream: header, order and contiguous offsets
+    hs = stream_check.HostStream(hdr, dir_buf[: n_rec * 32].cpu().numpy(), None, p_len=p_bytes)
+    assert stream_check.check_layout(hs, lay.n_tensors, 0, 5, 6, plan_full.info.fingerprint) is None
+    del hs
     flags = torch.zeros(n_rec, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -136,8 +146,11 @@ def test_receiver_share_1t(orc):
     # ---- RETRY stream over everything
     rdir = torch.empty(32 * n_chunks, dtype=torch.uint8, device="cuda")
     rpay = torch.empty(28 * 10**9, dtype=torch.uint8, device="cuda")
-    rhdr, rn, rpb, rchanged = build_stream(lay, plan_full, 1, rdir, rpay, t_old, t_new)
+    rhdr, rn, rpb, rchanged = build_stream(lay, plan_full, 1, rdir, rpay, t_old, t_new, orc)
     assert rchanged == changed and rn > 0
+    hs = stream_check.HostStream(rhdr, rdir[: rn * 32].cpu().numpy(), None, p_len=rpb)
+    assert stream_check.check_layout(hs, lay.n_tensors, 1, 5, 6, plan_full.info.fingerprint) is None
+    del hs
     say("cfg5", f"RETRY stream: {rn} records, {rpb / 1e9:.2f} GB")
     ev[2].record()
     dcr.dcr_apply_overwrite_retry(plan_full, canon, rhdr, rdir, rpay, 5, res, ws)
