@@ -701,3 +701,192 @@ int32_t orc_apply_record_part(const orc_tensor* T, uint32_t nT, void* const* can
     apply_changes(T, canon, dir + rec * ORC_DIRENT_BYTES, payload, change_lo, change_hi);
     return ORC_OK;
 }
+
+/* ------------------------------------------------ transport packing */
+
+/* Bytes of the unsigned LEB128 form of v. */
+static uint64_t leb_len(uint32_t v) {
+    uint64_t n = 1;
+    while (v >= 0x80u) { v >>= 7; n++; }
+    return n;
+}
+
+/* Write v as unsigned LEB128 at p; returns the bytes written. */
+static uint64_t leb_put(uint8_t* p, uint32_t v) {
+    uint64_t n = 0;
+    while (v >= 0x80u) {
+        p[n++] = (uint8_t)((v & 0x7Fu) | 0x80u);
+        v >>= 7;
+    }
+    p[n++] = (uint8_t)v;
+    return n;
+}
+
+/* Bytes of the sections after the first one (low plane and upper planes),
+ * which packing leaves as they are. */
+static uint64_t tail_bytes(const orc_rec* r, uint64_t n_c) {
+    return record_bytes(n_c, r->w, r->kind, r->K, r->hi_mode, r->H, ORC_LAYOUT_LIST) - pad16(2 * (uint64_t)r->K);
+}
+
+static uint64_t rec_n_c(const orc_tensor* T, const orc_rec* r) {
+    uint64_t E = chunk_elems(r->w);
+    uint64_t numel = T[r->t].numel;
+    return (numel - (uint64_t)r->c * E < E) ? numel - (uint64_t)r->c * E : E;
+}
+
+int32_t orc_stream_pack(const orc_tensor* T, uint32_t nT, const uint8_t* header,
+                        const uint8_t* dir, const uint8_t* payload,
+                        uint8_t* header_out, uint8_t* dir_out,
+                        uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes) {
+    uint64_t nrec, r, pos = 0, j;
+    int32_t rc = orc_validate(T, nT, header, dir, payload, get_u64(header + 16), -1);
+    if (rc) return rc;
+    nrec = get_u64(header + 40);
+    /* first the sizes, so that nothing is written when the buffer is short */
+    for (r = 0; r < nrec; r++) {
+        orc_rec e;
+        get_dirent(dir + r * ORC_DIRENT_BYTES, &e);
+        if (e.layout == ORC_LAYOUT_LIST) {
+            const uint8_t* p = payload + e.off;
+            uint64_t vb = 0;
+            for (j = 0; j < e.K; j++) {
+                uint32_t prev = j ? get_u16(p + 2 * (j - 1)) : 0;
+                uint32_t gap = j ? get_u16(p + 2 * j) - prev - 1 : get_u16(p);
+                vb += leb_len(gap);
+            }
+            if (pad16(vb) < pad16(2 * (uint64_t)e.K)) {
+                pos += pad16(vb) + tail_bytes(&e, rec_n_c(T, &e));
+                continue;
+            }
+        }
+        pos += e.sz;
+    }
+    *payload_bytes = pos;
+    if (pos > payload_cap) return ORC_E_CAPACITY;
+    pos = 0;
+    for (r = 0; r < nrec; r++) {
+        orc_rec e;
+        const uint8_t* p;
+        uint8_t* d = dir_out + r * ORC_DIRENT_BYTES;
+        uint64_t sz = 0;
+        int packed = 0;
+        get_dirent(dir + r * ORC_DIRENT_BYTES, &e);
+        p = payload + e.off;
+        memcpy(d, dir + r * ORC_DIRENT_BYTES, ORC_DIRENT_BYTES);
+        if (e.layout == ORC_LAYOUT_LIST) {
+            uint64_t vb = 0, tail = tail_bytes(&e, rec_n_c(T, &e));
+            for (j = 0; j < e.K; j++) {
+                uint32_t gap = j ? get_u16(p + 2 * j) - get_u16(p + 2 * (j - 1)) - 1 : get_u16(p);
+                vb += leb_len(gap);
+            }
+            if (pad16(vb) < pad16(2 * (uint64_t)e.K)) {
+                uint64_t q = 0;
+                memset(payload_out + pos, 0, pad16(vb));
+                for (j = 0; j < e.K; j++) {
+                    uint32_t gap = j ? get_u16(p + 2 * j) - get_u16(p + 2 * (j - 1)) - 1 : get_u16(p);
+                    q += leb_put(payload_out + pos + q, gap);
+                }
+                memcpy(payload_out + pos + pad16(vb), p + pad16(2 * (uint64_t)e.K), tail);
+                sz = pad16(vb) + tail;
+                d[15] = ORC_LAYOUT_GAPS;
+                packed = 1;
+            }
+        }
+        if (!packed) {
+            memcpy(payload_out + pos, p, e.sz);
+            sz = e.sz;
+        }
+        put_u64(d + 16, pos);
+        put_u32(d + 24, (uint32_t)sz);
+        pos += sz;
+    }
+    memcpy(header_out, header, ORC_HEADER_BYTES);
+    put_u32(header_out, ORC_MAGIC_PACKED);
+    put_u64(header_out + 48, pos);
+    return ORC_OK;
+}
+
+int32_t orc_stream_unpack(const orc_tensor* T, uint32_t nT, const uint8_t* header,
+                          const uint8_t* dir, const uint8_t* payload,
+                          uint8_t* header_out, uint8_t* dir_out,
+                          uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes) {
+    uint64_t nrec, pbytes, r, pos = 0, off = 0;
+    int32_t rc = check_tensors(T, nT);
+    if (rc) return rc;
+    if (get_u32(header) != ORC_MAGIC_PACKED || get_u16(header + 4) != ORC_FORMAT_VER ||
+        get_u32(header + 8) != ORC_CHUNK_BYTES || get_u32(header + 12) != 0 || get_u64(header + 56) != 0 ||
+        get_u16(header + 6) > ORC_MODE_RETRY || get_u64(header + 32) != orc_fingerprint(T, nT))
+        return ORC_E_FORMAT;
+    nrec = get_u64(header + 40);
+    pbytes = get_u64(header + 48);
+    /* sizes first: every entry's own fields give its unpacked size */
+    for (r = 0; r < nrec; r++) {
+        orc_rec e;
+        get_dirent(dir + r * ORC_DIRENT_BYTES, &e);
+        if (e.t >= nT || e.w != T[e.t].elem_bytes || (uint64_t)e.c >= n_chunks(&T[e.t])) return ORC_E_FORMAT;
+        if (e.off != off || e.off + e.sz > pbytes) return ORC_E_FORMAT;
+        off += e.sz;
+        if (e.layout == ORC_LAYOUT_GAPS)
+            pos += record_bytes(rec_n_c(T, &e), e.w, e.kind, e.K, e.hi_mode, e.H, ORC_LAYOUT_LIST);
+        else
+            pos += e.sz;
+    }
+    if (off != pbytes) return ORC_E_FORMAT;
+    *payload_bytes = pos;
+    if (pos > payload_cap) return ORC_E_CAPACITY;
+    pos = 0;
+    for (r = 0; r < nrec; r++) {
+        orc_rec e;
+        const uint8_t* p;
+        uint8_t* d = dir_out + r * ORC_DIRENT_BYTES;
+        uint64_t sz;
+        get_dirent(dir + r * ORC_DIRENT_BYTES, &e);
+        p = payload + e.off;
+        memcpy(d, dir + r * ORC_DIRENT_BYTES, ORC_DIRENT_BYTES);
+        if (e.layout == ORC_LAYOUT_GAPS) {
+            uint64_t n_c = rec_n_c(T, &e), tail, sec, q = 0, j;
+            uint32_t prev = 0;
+            if (e.K == 0 || e.K > n_c) return ORC_E_FORMAT;
+            tail = tail_bytes(&e, n_c);
+            if (e.sz < tail) return ORC_E_FORMAT;
+            sec = e.sz - tail;             /* the padded gap section */
+            if (sec % 16 || sec >= pad16(2 * (uint64_t)e.K)) return ORC_E_FORMAT;
+            sz = pad16(2 * (uint64_t)e.K) + tail;
+            memset(payload_out + pos, 0, pad16(2 * (uint64_t)e.K));
+            for (j = 0; j < e.K; j++) {
+                uint32_t v = 0, shift = 0, idx;
+                uint64_t start = q;
+                for (;;) {
+                    uint8_t b;
+                    if (q >= sec || shift > 14) return ORC_E_FORMAT;   /* cut off, or past 3 bytes */
+                    b = p[q++];
+                    v |= (uint32_t)(b & 0x7Fu) << shift;
+                    shift += 7;
+                    if (!(b & 0x80u)) {
+                        if (q - start > 1 && b == 0) return ORC_E_FORMAT;   /* not minimal */
+                        break;
+                    }
+                }
+                if (v > 0xFFFFu) return ORC_E_FORMAT;
+                idx = j ? prev + 1 + v : v;
+                if (idx >= n_c) return ORC_E_FORMAT;
+                put_u16(payload_out + pos + 2 * j, (uint16_t)idx);
+                prev = idx;
+            }
+            for (; q < sec; q++)
+                if (p[q]) return ORC_E_FORMAT;
+            memcpy(payload_out + pos + pad16(2 * (uint64_t)e.K), p + sec, tail);
+            d[15] = ORC_LAYOUT_LIST;
+        } else {
+            memcpy(payload_out + pos, p, e.sz);
+            sz = e.sz;
+        }
+        put_u64(d + 16, pos);
+        put_u32(d + 24, (uint32_t)sz);
+        pos += sz;
+    }
+    memcpy(header_out, header, ORC_HEADER_BYTES);
+    put_u32(header_out, ORC_MAGIC);
+    put_u64(header_out + 48, pos);
+    return orc_validate(T, nT, header_out, dir_out, payload_out, get_u64(header_out + 16), -1);
+}

@@ -159,6 +159,39 @@ int32_t orc_apply_overwrite_retry(const orc_tensor* T, uint32_t nT, void* const*
                                   const uint8_t* header, const uint8_t* dir,
                                   const uint8_t* payload, uint64_t expected_base_version);
 
+/* Transport packing of a stream (the pages compress the sparse mask stream
+ * before it travels: ai-feeds summary, "key modules" 3; humansand "weight
+ * teleportation" page, "A strong baseline with Blackwell-native DE", on
+ * codecs for masks that are mostly runs of zeros).  Every index-list record
+ * whose list takes fewer padded bytes as gap varints gets its first section
+ * replaced: change j's index i_j becomes the gap g_0 = i_0, g_j = i_j - i_{j-1} - 1,
+ * each written as an unsigned LEB128 varint (seven bits per byte, low
+ * group first, high bit set on every byte but the last), the K varints
+ * back to back and zero-padded to 16 bytes; its directory entry gets
+ * layout ORC_LAYOUT_GAPS.  Other records are copied unchanged.  Offsets
+ * are recomputed; the header's magic becomes ORC_MAGIC_PACKED and its
+ * payload_bytes the packed total.  The input must validate (ORC_E_FORMAT /
+ * ORC_E_VERSION otherwise); *payload_bytes gets the packed size, and
+ * ORC_E_CAPACITY if payload_cap is smaller (nothing usable written). */
+#define ORC_LAYOUT_GAPS  2
+#define ORC_MAGIC_PACKED 0x50524344u /* "DCRP" little-endian */
+int32_t orc_stream_pack(const orc_tensor* T, uint32_t nT, const uint8_t* header,
+                        const uint8_t* dir, const uint8_t* payload,
+                        uint8_t* header_out, uint8_t* dir_out,
+                        uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes);
+
+/* The inverse: a packed stream back to the stream it was packed from.
+ * Refused (ORC_E_FORMAT): a header that is not a packed stream of this
+ * tensor table; a gap section that does not hold exactly K minimal varints
+ * (a longer encoding of a value, a value that does not fit 16 bits, a
+ * varint cut off by the section's end) followed by zero bytes; an index at
+ * or past the chunk's elements; any record of the output that does not
+ * validate. */
+int32_t orc_stream_unpack(const orc_tensor* T, uint32_t nT, const uint8_t* header,
+                          const uint8_t* dir, const uint8_t* payload,
+                          uint8_t* header_out, uint8_t* dir_out,
+                          uint8_t* payload_out, uint64_t payload_cap, uint64_t* payload_bytes);
+
 /* Apply only elements [elem_lo, elem_hi) of one record (a torn write); no flag. */
 int32_t orc_apply_record_part(const orc_tensor* T, uint32_t nT, void* const* canon,
                               const uint8_t* dir, const uint8_t* payload,

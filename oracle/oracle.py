@@ -97,6 +97,9 @@ class Oracle:
         lib.orc_apply_overwrite_retry.argtypes = [P, U32, P, P, P, P, U64]
         lib.orc_apply_record_part.restype = I32
         lib.orc_apply_record_part.argtypes = [P, U32, P, P, P, U64, U32, U32]
+        for fn in (lib.orc_stream_pack, lib.orc_stream_unpack):
+            fn.restype = I32
+            fn.argtypes = [P, U32, P, P, P, P, P, P, U64, U64P]
         self.lib = lib
 
     # -------------------------------------------------------------- helpers
@@ -212,6 +215,45 @@ class Oracle:
         return int(self.lib.orc_apply_record_part(T.ctypes.data, len(T), self._ptrs(canon),
                                                   _nz(d).ctypes.data, _nz(p).ctypes.data,
                                                   rec, lo, hi))
+
+
+def _transport(lib_fn, tensors, hdr, d, p):
+    """Run orc_stream_pack / orc_stream_unpack; (rc, header, directory, payload)."""
+    T = _pack(tensors, ORC_TENSOR)
+    hdr = np.ascontiguousarray(hdr, dtype=np.uint8)
+    d = np.ascontiguousarray(d, dtype=np.uint8)
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    ho = np.zeros(HEADER_BYTES, dtype=np.uint8)
+    do = np.zeros(max(len(d), 1), dtype=np.uint8)
+    need = ctypes.c_uint64(0)
+    cap = 0
+    while True:
+        po = np.zeros(max(cap, 1), dtype=np.uint8)
+        rc = lib_fn(T.ctypes.data, len(T), hdr.ctypes.data, _nz(d).ctypes.data, _nz(p).ctypes.data,
+                    ho.ctypes.data, do.ctypes.data, po.ctypes.data, cap, ctypes.byref(need))
+        if rc == E_CAPACITY and cap < int(need.value):
+            cap = int(need.value)
+            continue
+        break
+    if rc:
+        return rc, ho, d[:0], p[:0]
+    return rc, ho, do[: len(d)].copy(), po[: int(need.value)].copy()
+
+
+def _pack_stream(self, tensors, hdr, d, p):
+    """Transport packing (index-list records as gap varints)."""
+    return _transport(self.lib.orc_stream_pack, tensors, hdr, d, p)
+
+
+def _unpack_stream(self, tensors, hdr, d, p):
+    """The inverse of pack_stream."""
+    return _transport(self.lib.orc_stream_unpack, tensors, hdr, d, p)
+
+
+Oracle.pack_stream = _pack_stream
+Oracle.unpack_stream = _unpack_stream
+LAYOUT_GAPS = 2
+MAGIC_PACKED = 0x50524344
 
 
 def _nz(a):

@@ -171,3 +171,35 @@ def build_stream(records, kind, base, new, fingerprint, numels, widths):
     h[48:56] = len(pay).to_bytes(8, "little")
     as_u8 = lambda b: np.frombuffer(bytes(b), dtype=np.uint8).copy()
     return as_u8(h), as_u8(dirb), as_u8(pay)
+
+
+def leb128(v):
+    """Unsigned LEB128 bytes of v: seven bits per byte, low group first, the
+    high bit set on every byte but the last."""
+    out = bytearray()
+    while True:
+        b = v & 0x7F
+        v >>= 7
+        if v:
+            out.append(b | 0x80)
+        else:
+            out.append(b)
+            return bytes(out)
+
+
+def read_gaps(sec, K):
+    """-> (K indices, bytes used) from a gap section: K unsigned LEB128
+    varints, gap 0 = index 0, gap j = index j - index j-1 - 1."""
+    idx, pos, prev = [], 0, -1
+    for _ in range(K):
+        v = shift = 0
+        while True:
+            b = int(sec[pos])
+            pos += 1
+            v |= (b & 0x7F) << shift
+            shift += 7
+            if not b & 0x80:
+                break
+        prev = prev + 1 + v
+        idx.append(prev)
+    return np.array(idx, dtype=np.int64), pos

@@ -749,4 +749,136 @@ def pin_tensor_table_refusals(orc):
         assert orc.validate(T, np.zeros(64, np.uint8), np.zeros(0, np.uint8), np.zeros(0, np.uint8)) == O.E_INVAL, name
 
 
+def _gaps_stream(orc, idx, n, w=2, mask=0x0001):
+    """A one-tensor stream (index-list layout) whose only record changes the
+    given elements by `mask`."""
+    from oracle import oracle as O
+    T, S = _one_tensor(n, w)
+    dt = {1: np.uint8, 2: np.uint16}[w]
+    old = (0x3C00 + (np.arange(n) % 256)).astype(dt) if w == 2 else (np.arange(n) % 251).astype(dt)
+    new = old.copy()
+    new[np.asarray(idx, dtype=np.int64)] ^= dt(mask)
+    rc, hdr, d, p = orc.encode(T, S, [old], [new], mode=O.MODE_DELTA | O.ENC_LISTS)
+    assert rc == 0
+    return T, old, new, hdr, d, p
+
+
+def pin_golden_gaps_record(orc):
+    """A packed record worked out by hand (tests/golden/worked_packed_record.txt):
+    the index list of 12 changes, and its gap section as unsigned LEB128
+    varints, byte for byte; unpacking gives the list record back."""
+    from oracle import oracle as O
+    spec = _golden_spec("worked_packed_record.txt")
+    idx = [int(x) for x in spec["indices"].split()]
+    T, old, new, hdr, d, p = _gaps_stream(orc, idx, int(spec["numel"]))
+    hx = lambda k: spec[k].replace(" ", "").lower()
+    assert bytes(d).hex() == hx("list_dirent") and bytes(p).hex() == hx("list_payload")
+    rc, ph, pd, pp = orc.pack_stream(T, hdr, d, p)
+    assert rc == 0
+    assert bytes(pd).hex() == hx("packed_dirent") and bytes(pp).hex() == hx("packed_payload")
+    assert bytes(ph[0:4]).hex() == hx("packed_magic")
+    assert int(ph[48:56].view("<u8")[0]) == len(pp) and np.array_equal(ph[4:48], hdr[4:48])
+    rc, uh, ud, up = orc.unpack_stream(T, ph, pd, pp)
+    assert rc == 0 and np.array_equal(uh, hdr) and np.array_equal(ud, d) and np.array_equal(up, p)
+    assert orc.validate(T, ph, pd, pp) == O.E_FORMAT        # a packed stream is not applied as such
+
+
+def pin_leb128_vectors(orc):
+    """Gap varints against hand-derived unsigned LEB128 bytes: one change at
+    each of elements 0..7 (eight gaps of 0, one byte each) and then one at
+    8 + v, so the ninth varint is v's, for v at the one-, two- and
+    three-byte boundaries (uint8 tensor of one 65536-element chunk)."""
+    vectors = {0: "00", 1: "01", 127: "7f", 128: "8001", 300: "ac02", 16383: "ff7f", 16384: "808001",
+               65527: "f7ff03"}
+    for v, hx in vectors.items():
+        idx = list(range(8)) + [8 + v]
+        T, old, new, hdr, d, p = _gaps_stream(orc, idx, 65536, w=1, mask=0x10)
+        rc, ph, pd, pp = orc.pack_stream(T, hdr, d, p)
+        assert rc == 0
+        assert pd[15] == 2, v                                   # packed: 8 + len(v) bytes < 32
+        assert bytes(pp[:8 + len(hx) // 2]).hex() == "00" * 8 + hx, v
+        assert not pp[8 + len(hx) // 2:16].any(), v             # zero padding
+        assert fmt.leb128(v).hex() == hx
+
+
+def pin_pack_roundtrip(orc, seeds=range(10)):
+    """On random layouts at low change rates with index lists: a list record
+    is packed exactly when its padded gap section is strictly smaller than
+    its padded list (sizes computed here from the definition); a packed
+    record's gap varints decode to the list's indices and its later sections
+    are the list record's; unpack(pack(stream)) is the stream, byte for byte;
+    the packed stream applies, once unpacked, to new."""
+    from oracle import oracle as O
+    for seed in seeds:
+        lay = synth.random_layout(1900 + seed, rate=[0.002, 0.01, 0.03][seed % 3], max_tensors=5,
+                                  max_chunks=4.0)
+        olds, news, co, cn = canon_lists(lay)
+        for mode in (O.MODE_DELTA, O.MODE_RETRY):
+            rc, hdr, d, p = orc.encode(lay.tensors, lay.segments, olds, news, mode=mode | O.ENC_LISTS,
+                                       base_version=7, new_version=8)
+            assert rc == 0
+            rc, ph, pd, pp = orc.pack_stream(lay.tensors, hdr, d, p)
+            assert rc == 0
+            ents, pents = fmt.dirents(d), fmt.dirents(pd)
+            assert len(ents) == len(pents)
+            pos = 0
+            for e, f in zip(ents, pents):
+                assert (e["t"], e["c"], e["K"], e["kind"], e["hi_mode"], e["w"], e["H"]) == \
+                       (f["t"], f["c"], f["K"], f["kind"], f["hi_mode"], f["w"], f["H"])
+                assert f["off"] == pos
+                body = p[e["off"]:e["off"] + e["size"]]
+                pbody = pp[f["off"]:f["off"] + f["size"]]
+                if e["layout"] == 1:
+                    li = body[:2 * e["K"]].view("<u2").astype(np.int64)
+                    vb = sum(len(fmt.leb128(int(g))) for g in np.diff(np.concatenate([[-1], li])) - 1)
+                    want = fmt.pad16(vb) < fmt.pad16(2 * e["K"])
+                    assert (f["layout"] == 2) == want, (seed, e)
+                if f["layout"] == 2:
+                    gi, used = fmt.read_gaps(pbody, e["K"])
+                    assert np.array_equal(gi, body[:2 * e["K"]].view("<u2").astype(np.int64))
+                    assert not pbody[used:fmt.pad16(used)].any()
+                    assert np.array_equal(pbody[fmt.pad16(used):], body[fmt.pad16(2 * e["K"]):])
+                else:
+                    assert np.array_equal(pbody, body)
+                pos += f["size"]
+            assert pos == len(pp)
+            rc, uh, ud, up = orc.unpack_stream(lay.tensors, ph, pd, pp)
+            assert rc == 0 and np.array_equal(uh, hdr) and np.array_equal(ud, d) and np.array_equal(up, p)
+
+
+def pin_unpack_refusals(orc):
+    """Unpack refuses malformed packed streams: a plain (unpacked) header, a
+    nonzero padding byte after the last varint, a varint written longer than
+    it needs, a varint cut off by the section's end, an index past the
+    chunk's elements, a gap section as long as the list it replaces."""
+    from oracle import oracle as O
+    spec = _golden_spec("worked_packed_record.txt")
+    idx = [int(x) for x in spec["indices"].split()]
+    T, old, new, hdr, d, p = _gaps_stream(orc, idx, int(spec["numel"]))
+    rc, ph, pd, pp = orc.pack_stream(T, hdr, d, p)
+    assert rc == 0
+    assert orc.unpack_stream(T, ph, pd, pp)[0] == 0
+    bad_h = ph.copy()
+    bad_h[0:4] = hdr[0:4]
+    assert orc.unpack_stream(T, bad_h, pd, pp)[0] == O.E_FORMAT
+    # the golden section uses all 16 bytes; a smaller list leaves padding
+    idx2 = [0, 1, 2, 3, 4, 5, 6, 7, 9]
+    T2, _o, _n, h2, d2, p2 = _gaps_stream(orc, idx2, 4096)
+    rc, ph2, pd2, pp2 = orc.pack_stream(T2, h2, d2, p2)
+    assert rc == 0 and pd2[15] == 2 and pp2[9] == 0 and pp2[15] == 0   # 9 one-byte varints, 7 padding bytes
+    assert orc.unpack_stream(T2, ph2, pd2, pp2)[0] == 0
+    x = pp2.copy(); x[15] = 1                                   # nonzero padding
+    assert orc.unpack_stream(T2, ph2, pd2, x)[0] == O.E_FORMAT
+    x = pp2.copy(); x[8] |= 0x80; x[9] = 0                      # last varint 01 written as 81 00
+    assert orc.unpack_stream(T2, ph2, pd2, x)[0] == O.E_FORMAT
+    x = pp2.copy(); x[8:16] = 0x80                             # last varint never ends
+    assert orc.unpack_stream(T2, ph2, pd2, x)[0] == O.E_FORMAT
+    x = pp.copy(); x[14:16] = [0xB0, 0x10]                      # last gap 2094 -> 2096: index 4097 >= 4096
+    assert orc.unpack_stream(T, ph, pd, x)[0] == O.E_FORMAT
+    x = pd.copy(); x[24:28] = np.frombuffer(np.uint32(48).tobytes(), np.uint8)   # section as long as the list
+    xp = np.concatenate([pp[:16], np.zeros(16, np.uint8), pp[16:]])
+    xh = ph.copy(); xh[48:56] = np.frombuffer(np.uint64(48).tobytes(), np.uint8)
+    assert orc.unpack_stream(T, xh, x, xp)[0] == O.E_FORMAT
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -5,8 +5,9 @@ wrong word, tie-break, byte plane, transposed strides, chunk size, missing
 dedup, inverted routing, missing padding, partial retry ignoring the flags or
 marking the wrong chunk, index lists off by one or never chosen, the same-group
 check between a chunk's two records skipped, a header field left unwritten,
-tensor-table refusals dropped); the copy is compiled in a temp directory and
-loaded beside the real oracle.  Nothing here touches a GPU.
+tensor-table refusals dropped, gap varints off by one or never ending, packing
+on a size tie, longer varints accepted); the copy is compiled in a temp
+directory and loaded beside the real oracle.  Nothing here touches a GPU.
 """
 import os
 import shutil
@@ -55,6 +56,13 @@ MUTANTS = {
     "xor_on_w4_allowed": ("if (d->route != ORC_ROUTE_OVERWRITE && w == 4) return ORC_E_INVAL;", "(void)0;"),
     "scale_length_unchecked": ("if (s->numel != (d->numel + d->scale_block - 1) / d->scale_block) return ORC_E_INVAL;",
                                "(void)s;"),
+    "gap_written_without_minus_one": ("q += leb_put(payload_out + pos + q, gap);",
+                                      "q += leb_put(payload_out + pos + q, gap + (j ? 1u : 0u));"),
+    "leb128_continuation_on_last": ("p[n++] = (uint8_t)v;", "p[n++] = (uint8_t)(v | 0x80u);"),
+    "pack_on_a_tie": ("if (pad16(vb) < pad16(2 * (uint64_t)e.K)) {\n                uint64_t q = 0;",
+                      "if (pad16(vb) <= pad16(2 * (uint64_t)e.K)) {\n                uint64_t q = 0;"),
+    "unpack_accepts_longer_varints": ("if (q - start > 1 && b == 0) return ORC_E_FORMAT;   /* not minimal */",
+                                      "(void)start;"),
     "list_layout_never": ("return (lists && pad16(2 * K) < pad16((n_c + 7) / 8)) ? ORC_LAYOUT_LIST : ORC_LAYOUT_BITMAP;",
                           "(void)lists; (void)K; (void)n_c; return ORC_LAYOUT_BITMAP;"),
 }
