@@ -335,7 +335,7 @@ def config1_values(lay: Layout, lr: float | None = None, target=0.01, n_flips=64
 # ------------------------------------------------------- config 2 (Llama)
 
 def llama_layout(hidden=4096, layers=32, ffn=14336, n_q=32, n_kv=8, head_dim=128,
-                 vocab=128256, tp=4, rate=0.01, seed=0xDC202602, name="cfg2") -> Layout:
+                 vocab=128256, tp=4, rate=0.01, seed=0xDC202602, name="cfg2", gate_up_group=0) -> Layout:
     """Llama-style dense checkpoint trained with tensor parallelism tp.
 
     Trainer shards per rank r: vocab-parallel embed / lm_head rows; a fused
@@ -343,8 +343,16 @@ def llama_layout(hidden=4096, layers=32, ffn=14336, n_q=32, n_kv=8, head_dim=128
     canonical q/k/v); o_proj row-parallel (input columns split); fused fc1
     [gate_r ; up_r] (output rows split); down_proj row-parallel.  Norms are
     replicated; rank 0 owns them (other replicas are never read).
+
+    gate_up_group > 0: the fused fc1 of each rank interleaves gate and up
+    rows in groups of that many rows ([gate 0..g-1, up 0..g-1, gate g..2g-1,
+    ...]), the physical layout a fused MoE / MLP kernel may want (the
+    humansand "weight teleportation" page, "Working with low-precision RL",
+    pairs gate and up weights in groups of 64); the same tensor table, so
+    the same plan fingerprint.
     """
     assert vocab % tp == 0 and ffn % tp == 0 and n_kv % tp == 0 and hidden % tp == 0
+    assert gate_up_group == 0 or (ffn // tp) % gate_up_group == 0
     assert n_q * head_dim == hidden and n_q % n_kv == 0
     b = _Builder(name, seed)
     thr = rate_thr(rate)
@@ -408,11 +416,22 @@ def llama_layout(hidden=4096, layers=32, ffn=14336, n_q=32, n_kv=8, head_dim=128
         recipe.append((t, "whole", [ln2]))
         tg = b.tensor(p + "mlp.gate_proj.weight", ffn * hidden, 2)
         tu = b.tensor(p + "mlp.up_proj.weight", ffn * hidden, 2)
-        for r in range(tp):
-            b.seg(tg, fc1[r], 0, r * f_r * hidden, [f_r * hidden], [1], [1])
-            b.seg(tu, fc1[r], f_r * hidden, r * f_r * hidden, [f_r * hidden], [1], [1])
-        recipe.append((tg, "cat0", [(fc1[r], 0, f_r, hidden) for r in range(tp)]))
-        recipe.append((tu, "cat0", [(fc1[r], f_r, f_r, hidden) for r in range(tp)]))
+        if gate_up_group:
+            gg = gate_up_group
+            for r in range(tp):
+                # row block j of g rows: gate at fused rows [2gj, 2gj + g), up at [2gj + g, 2g(j + 1))
+                b.seg(tg, fc1[r], 0, r * f_r * hidden, [f_r // gg, gg * hidden], [2 * gg * hidden, 1],
+                      [gg * hidden, 1])
+                b.seg(tu, fc1[r], gg * hidden, r * f_r * hidden, [f_r // gg, gg * hidden], [2 * gg * hidden, 1],
+                      [gg * hidden, 1])
+            recipe.append((tg, "interleave", [(fc1[r], 0, gg, f_r, hidden) for r in range(tp)]))
+            recipe.append((tu, "interleave", [(fc1[r], 1, gg, f_r, hidden) for r in range(tp)]))
+        else:
+            for r in range(tp):
+                b.seg(tg, fc1[r], 0, r * f_r * hidden, [f_r * hidden], [1], [1])
+                b.seg(tu, fc1[r], f_r * hidden, r * f_r * hidden, [f_r * hidden], [1], [1])
+            recipe.append((tg, "cat0", [(fc1[r], 0, f_r, hidden) for r in range(tp)]))
+            recipe.append((tu, "cat0", [(fc1[r], f_r, f_r, hidden) for r in range(tp)]))
         t = b.tensor(p + "mlp.down_proj.weight", hidden * ffn, 2)
         for r in range(tp):
             b.seg(t, down[r], 0, r * f_r, [hidden, f_r], [f_r, 1], [ffn, 1])
@@ -427,7 +446,7 @@ def llama_layout(hidden=4096, layers=32, ffn=14336, n_q=32, n_kv=8, head_dim=128
     def assemble(shards):
         return _assemble(recipe, shards, len(b.tensors))
 
-    return b.build(assemble=assemble, meta={"seed": seed, "rate": rate, "tp": tp})
+    return b.build(assemble=assemble, meta={"seed": seed, "rate": rate, "tp": tp, "gate_up_group": gate_up_group})
 
 
 def _assemble(recipe, shards, n_tensors):
@@ -442,6 +461,9 @@ def _assemble(recipe, shards, n_tensors):
                                 for s, r0, nr, c in parts], 0).reshape(-1)
         elif how == "cat1":        # column blocks: (shard, rows, cols)
             out[t] = torch.cat([shards[s].reshape(rows, c) for s, rows, c in parts], 1).reshape(-1)
+        elif how == "interleave":  # every other group of g rows: (shard, 0 or 1, g, rows, cols) per rank
+            out[t] = torch.cat([shards[s].reshape(rows // g, 2, g, c).select(1, k).reshape(rows, c)
+                                for s, k, g, rows, c in parts], 0).reshape(-1)
         elif how == "stack_sel":   # one matrix out of a stack: (shard, index, rows, cols)
             s, e, rows, c = parts
             out[t] = shards[s].reshape(-1, rows, c)[e].reshape(-1)

@@ -384,6 +384,59 @@ def test_apply_sharded(gh, orc, seed, lists):
     assert torch.equal(rbuf, exp_buf), seed
 
 
+def test_apply_sharded_gate_up_interleaved(gh, orc):
+    """A receiver engine that stores each rank's fused gate/up weight with
+    gate and up rows interleaved in groups of 64 (the physical layout of the
+    humansand "weight teleportation" page, "Working with low-precision RL"),
+    sharded TP=4: the DELTA stream of a TP=4 trainer applied straight into
+    it, and a kill at 50 % healed by the RETRY stream; the receiver shards
+    end byte-identical to the new tensors scattered into the layout (the
+    scatter checked by the oracle's gather), and the layout's own assembly
+    (select every other 64-row group) reads new back."""
+    kw = dict(hidden=256, layers=2, ffn=1024, n_q=8, n_kv=4, head_dim=32, vocab=1000, tp=4, rate=0.03)
+    say("apply sharded, gate/up interleaved in 64-row groups")
+    lay = synth.llama_layout(**kw)
+    lay_r = synth.llama_layout(**kw, gate_up_group=64)
+    olds, news = lay.shards_host(0), lay.shards_host(1)
+    # this layout assembles with torch ops: canonical tensors from the host shards
+    co, cn = ([x.reshape(-1).numpy().view(np.uint8).copy()
+               for x in lay.assemble([torch.from_numpy(np.ascontiguousarray(v).view(np.int16)) for v in vs])]
+              for vs in (olds, news))
+    g = gh.Gpu(lay, olds, news)
+    sb = g.encode(0)
+    hdr, d, _p = g.stream_host(sb)
+    n = len(d) // 32
+    rplan = dcr.dcr_plan_build(lay_r.tensors, [lay_r.shard_bytes(s) for s in range(lay_r.n_shards)],
+                               lay_r.segments)
+    dcr.dcr_plan_upload(rplan, "cuda")
+    assert rplan.info.fingerprint == g.plan.info.fingerprint
+    ws = dcr.workspace(rplan, "cuda")
+    exp_buf, exp_sh = gh.scatter_shards(lay_r, cn)
+    eh = [x.cpu().numpy() for x in exp_sh]
+    for t in range(lay.n_tensors):
+        assert np.array_equal(orc.gather(lay_r.tensors, lay_r.segments, eh, t), cn[t]), t
+    res = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+    rbuf, rsh = gh.scatter_shards(lay_r, co)
+    dcr.dcr_apply_sharded(rplan, rsh, hdr, sb.dir, sb.payload, flags, 0, n, 7, res, ws)
+    torch.cuda.synchronize()
+    r = dcr.apply_result(res)
+    assert int(r["n_applied"]) == n and int(r["n_invalid"]) == 0
+    assert torch.equal(rbuf, exp_buf)
+    got = lay_r.assemble([x.view(torch.int16) for x in rsh])
+    for t in range(lay.n_tensors):
+        assert np.array_equal(got[t].reshape(-1).cpu().numpy().view(np.uint8), cn[t]), lay.tensor_names[t]
+    rbuf, rsh = gh.scatter_shards(lay_r, co)
+    flags.zero_()
+    dcr.dcr_apply_sharded(rplan, rsh, hdr, sb.dir, sb.payload, flags, 0, n // 2, 7, res, ws)
+    rsb = g.encode(1)
+    rh = g.stream_host(rsb)[0]
+    dcr.dcr_apply_overwrite_retry_sharded(rplan, rsh, rh, rsb.dir, rsb.payload, 7, res, ws)
+    torch.cuda.synchronize()
+    assert int(dcr.apply_result(res)["n_invalid"]) == 0
+    assert torch.equal(rbuf, exp_buf)
+
+
 def test_apply_sharded_refuses_overlapping_layout(gh):
     """A receiver layout that maps two canonical elements to one shard
     element cannot be applied into."""
