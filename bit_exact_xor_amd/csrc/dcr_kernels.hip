@@ -28,6 +28,7 @@
 #include <atomic>
 #include <chrono>
 #include <cstring>
+#include <mutex>
 #include <thread>
 #include <string>
 
@@ -1974,6 +1975,38 @@ static uint32_t cu_count() {
     return cached[dev];
 }
 
+// Device memory of the allocation-free encode (dcr_encode_noalloc): its
+// workspace and staging area.  In host code `scratch` names a host-side
+// stand-in, not the device array: its device address, one per GPU, comes
+// from hipGetSymbolAddress with that GPU current, and only that address is
+// handed to kernels and copies.
+static __device__ __align__(256) uint8_t scratch[DCR_NOALLOC_SCRATCH_BYTES];
+static std::atomic<uint8_t*> g_scratch_ptr[64];
+static std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up once per device).
+static int32_t scratch_ptr(uint8_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DCR_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(DCR_E_INVAL, "device index out of range for the scratch table");
+    uint8_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void* q = nullptr;
+            e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !q)
+                return fail(DCR_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+            p = static_cast<uint8_t*>(q);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return DCR_OK;
+}
+
 // benchmark hook: events recorded around the main kernel of each call
 static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 static void mark(bool start, hipStream_t s) {
@@ -2309,6 +2342,29 @@ int32_t dcr_encode(const dcr_plan* plan, const void* const* old_shards, const vo
     return encode_impl(plan, old_shards, new_shards, mode, base_version, new_version, header_dev, dir_dev, dir_cap,
                        payload_dev, payload_cap, result_dev, workspace_dev, ws_bytes, stream, nullptr, nullptr,
                        UINT64_MAX);
+}
+
+int32_t dcr_encode_noalloc(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards,
+                           uint32_t mode, uint64_t base_version, uint64_t new_version, void* header_dev,
+                           void* dir_dev, uint64_t dir_cap, void* payload_dev, uint64_t payload_cap,
+                           dcr_encode_result* result_dev, void* stream) {
+    using namespace dcr;
+    set_error("");
+    if (!plan) return fail(DCR_E_INVAL, "plan is NULL");
+    if (plan->ws_bytes > DCR_NOALLOC_SCRATCH_BYTES)
+        return fail(DCR_E_CAPACITY, "plan workspace of " + std::to_string(plan->ws_bytes) +
+                                        " bytes exceeds the library's scratch of " +
+                                        std::to_string(uint64_t(DCR_NOALLOC_SCRATCH_BYTES)) + " bytes");
+    uint8_t* ws = nullptr;
+    const int32_t rc = scratch_ptr(&ws);
+    if (rc) return rc;
+    // staged when every chunk's slot fits past the workspace, else in order
+    // (windows of a few fix-up blocks would cost more than the look-back)
+    const uint64_t ws_bytes = plan->ws_bytes + plan->max_payload_bytes <= DCR_NOALLOC_SCRATCH_BYTES
+                                  ? uint64_t(DCR_NOALLOC_SCRATCH_BYTES)
+                                  : plan->ws_bytes;
+    return encode_impl(plan, old_shards, new_shards, mode, base_version, new_version, header_dev, dir_dev, dir_cap,
+                       payload_dev, payload_cap, result_dev, ws, ws_bytes, stream, nullptr, nullptr, UINT64_MAX);
 }
 
 int32_t dcr_encode_pipelined(const dcr_plan* plan, const void* const* old_shards, const void* const* new_shards,

@@ -82,6 +82,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dcr_encode.restype = I32
     lib.dcr_encode.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P, U64, P]
     lib.dcr_encode_pipelined.restype = I32
+    lib.dcr_encode_noalloc.restype = I32
+    lib.dcr_encode_noalloc.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P]
     lib.dcr_encode_pipelined.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P, U64, U32, P, U64, P]
     lib.dcr_ready_wait.restype = I32
     lib.dcr_ready_wait.argtypes = [P, U32, U64, P]
@@ -220,6 +222,20 @@ def dcr_encode(plan: Plan, old_shards, new_shards, mode, base_version, new_versi
         mode, base_version, new_version, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload),
         _nbytes(payload), _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_encode")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DCR_NOALLOC_SCRATCH_BYTES
+
+
+def dcr_encode_noalloc(plan: Plan, old_shards, new_shards, mode, base_version, new_version,
+                       header, dir_buf, payload, result, stream=None) -> None:
+    """Enqueue an encode that uses the library's own device scratch array as
+    its workspace (no workspace argument; calls overlapping on one GPU race)."""
+    rc = load_library().dcr_encode_noalloc(
+        plan.handle, _ptrs(old_shards), _ptrs(new_shards),
+        mode, base_version, new_version, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload),
+        _nbytes(payload), _dptr(result), _stream(stream))
+    _check(rc, "dcr_encode_noalloc")
 
 
 def ready_region_bytes(n_slices: int) -> int:

@@ -261,6 +261,31 @@ int32_t dcr_encode(const dcr_plan* plan,
                    dcr_encode_result* result_dev,
                    void* workspace_dev, uint64_t ws_bytes, void* stream);
 
+/* Allocation-free encode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): dcr_encode without a workspace argument.  The workspace and the
+ * staging area live in a device array of the library, DCR_NOALLOC_SCRATCH_BYTES
+ * on each GPU, held from the library's first use on that GPU until the process
+ * ends; its address on the current device is looked up once per device.  The
+ * encode runs staged when workspace_bytes + max_payload_bytes fit the array,
+ * else in order (decoupled look-back, no staging); the stream is the same as
+ * dcr_encode's.  The call allocates nothing (no hipMalloc; on the host only
+ * the error text) and enqueues the same kind of work as dcr_encode.
+ *   Errors: DCR_E_CAPACITY, before anything is enqueued, when the plan's
+ *   workspace_bytes exceed DCR_NOALLOC_SCRATCH_BYTES; otherwise as dcr_encode.
+ *   Concurrency: every call on one GPU uses that GPU's one array, and the
+ *   array keeps the last call's contents (each call clears what it needs
+ *   cleared), so calls that overlap on one GPU (other streams or threads)
+ *   race and must be serialised by the caller.  Other entry points do not
+ *   touch the array. */
+#define DCR_NOALLOC_SCRATCH_BYTES (64u << 20)
+int32_t dcr_encode_noalloc(const dcr_plan* plan,
+                           const void* const* old_shards, const void* const* new_shards,
+                           uint32_t mode, uint64_t base_version, uint64_t new_version,
+                           void* header_dev, void* dir_dev, uint64_t dir_cap,
+                           void* payload_dev, uint64_t payload_cap,
+                           dcr_encode_result* result_dev, void* stream);
+
 /* Pipelined encode (sender side): the trainer starts sending finished parts
  * of the stream while the rest is still being built, so a refit costs about
  * the larger of build and transfer time rather than their sum (ai-feeds

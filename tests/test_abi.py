@@ -164,3 +164,21 @@ def test_plan_chunk_limit():
             with pytest.raises(dcr.DcrError) as e:
                 dcr.dcr_plan_build(T, [numel], S)
             assert e.value.code == dcr.DCR_E_INVAL
+
+
+def test_encode_noalloc_refuses_large_workspace():
+    """dcr_encode_noalloc refuses, before any device work, a plan whose
+    workspace exceeds the library's scratch array (DCR_E_CAPACITY); a plan
+    of 3 M chunks needs about 80 MB of workspace against 64 MiB."""
+    n_chunks = 3_000_000
+    numel = n_chunks * 65536
+    T = np.zeros(1, dtype=synth.TENSOR_DT)
+    T[0] = (numel, 1, 1, -1, 0)
+    S = np.zeros(1, dtype=synth.SEGMENT_DT)
+    S[0] = (0, 0, 1, 0, 0, 0, [numel, 1, 1, 1], [1, 0, 0, 0], [1, 0, 0, 0])
+    p = dcr.dcr_plan_build(T, [numel], S)
+    assert p.info.workspace_bytes > dcr.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(dcr.DcrError) as e:
+        dcr.dcr_encode_noalloc(p, [0x1000], [0x1000], 0, 0, 1, 0x1000, 0x1000, 0x1000, 0x1000, stream=1)
+    assert e.value.code == dcr.DCR_E_CAPACITY
+    assert "scratch" in str(e.value)
