@@ -37,7 +37,7 @@ def _compile(out: str, sources: list[str], extra: list[str] | None = None) -> No
 
 def build(verbose: bool = True) -> None:
     _compile(LIB_DCR, [os.path.join(CSRC, "dcr_plan.cpp"), os.path.join(CSRC, "dcr_kernels.hip"),
-                       os.path.join(CSRC, "dcr_transcode.hip")])
+                       os.path.join(CSRC, "dcr_transcode.hip"), os.path.join(CSRC, "dcr_pack.hip")])
     _compile(LIB_SYNTH, [os.path.join(CSRC, "synth.hip")])
     if verbose:
         print(f"built {LIB_DCR} and {LIB_SYNTH} for {ARCH}")

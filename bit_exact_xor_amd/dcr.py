@@ -82,6 +82,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dcr_encode.restype = I32
     lib.dcr_encode.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P, U64, P]
     lib.dcr_encode_pipelined.restype = I32
+    for fn in (lib.dcr_stream_pack, lib.dcr_stream_unpack):
+        fn.restype = I32
+        fn.argtypes = [P, P, P, P, P, P, U64, P, U64, P, P, U64, P]
     lib.dcr_encode_noalloc.restype = I32
     lib.dcr_encode_noalloc.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P]
     lib.dcr_encode_pipelined.argtypes = [P, P, P, U32, U64, U64, P, P, U64, P, U64, P, P, U64, U32, P, U64, P]
@@ -222,6 +225,34 @@ def dcr_encode(plan: Plan, old_shards, new_shards, mode, base_version, new_versi
         mode, base_version, new_version, _dptr(header), _dptr(dir_buf), _nbytes(dir_buf), _dptr(payload),
         _nbytes(payload), _dptr(result), _dptr(workspace), _nbytes(workspace), _stream(stream))
     _check(rc, "dcr_encode")
+
+
+LAYOUT_GAPS = 2                    # directory entry byte 15, packed streams only
+MAGIC_PACKED = 0x50524344
+
+
+def _transport(fn, what, plan, header, dir_buf, payload, header_out, dir_out, payload_out, result, workspace,
+               stream=None):
+    h = np.ascontiguousarray(np.asarray(header, dtype=np.uint8).reshape(-1)[:64])
+    rc = fn(plan.handle, h.ctypes.data, _dptr(dir_buf), _dptr(payload), _dptr(header_out), _dptr(dir_out),
+            _nbytes(dir_out), _dptr(payload_out), _nbytes(payload_out), _dptr(result), _dptr(workspace),
+            _nbytes(workspace), _stream(stream))
+    _check(rc, what)
+
+
+def dcr_stream_pack(plan: Plan, header, dir_buf, payload, header_out, dir_out, payload_out, result, workspace,
+                    stream=None) -> None:
+    """Enqueue the transport packing of a stream (host header, device
+    buffers) into the output buffers."""
+    _transport(load_library().dcr_stream_pack, "dcr_stream_pack", plan, header, dir_buf, payload, header_out,
+               dir_out, payload_out, result, workspace, stream)
+
+
+def dcr_stream_unpack(plan: Plan, header, dir_buf, payload, header_out, dir_out, payload_out, result, workspace,
+                      stream=None) -> None:
+    """Enqueue the inverse of dcr_stream_pack."""
+    _transport(load_library().dcr_stream_unpack, "dcr_stream_unpack", plan, header, dir_buf, payload, header_out,
+               dir_out, payload_out, result, workspace, stream)
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # DCR_NOALLOC_SCRATCH_BYTES

@@ -85,11 +85,13 @@ enum { DCR_MODE_DELTA = 0, DCR_MODE_RETRY = 1 };
 /* encode option, OR-ed into dcr_encode's mode: index-list layout for records
  * where it is smaller than the bitmap (the stream kind stays mode & 0xFF) */
 enum { DCR_ENC_INDEX_LISTS = 0x100 };
-/* record layouts (byte 15 of a directory entry) */
-enum { DCR_LAYOUT_BITMAP = 0, DCR_LAYOUT_LIST = 1 };
+/* record layouts (byte 15 of a directory entry); DCR_LAYOUT_GAPS only in a
+ * packed stream (dcr_stream_pack) */
+enum { DCR_LAYOUT_BITMAP = 0, DCR_LAYOUT_LIST = 1, DCR_LAYOUT_GAPS = 2 };
 enum { DCR_KIND_XOR = 0, DCR_KIND_OW = 1 };
 enum { DCR_HI_NONE = 0, DCR_HI_SPARSE = 1, DCR_HI_DENSE = 2 };
 #define DCR_MAGIC 0x31524344u          /* "DCR1" */
+#define DCR_MAGIC_PACKED 0x50524344u   /* "DCRP": a packed stream (dcr_stream_pack) */
 #define DCR_FORMAT_VERSION 1u
 #define DCR_CHUNK_BYTES 65536u
 #define DCR_HEADER_BYTES 64u
@@ -487,6 +489,59 @@ int32_t dcr_apply_overwrite_retry_sharded(const dcr_plan* plan, void* const* sha
                                           uint64_t expected_base_version,
                                           dcr_apply_result* result_dev,
                                           void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* Transport packing (sender side, after the encode): the pages compress the
+ * sparse mask stream before it travels (ai-feeds summary "key modules" 3;
+ * humansand "weight teleportation" page, "A strong baseline with
+ * Blackwell-native DE", on codecs for masks that are mostly runs of zeros).
+ * Every index-list record (DCR_ENC_INDEX_LISTS) whose list, written as gap
+ * varints, takes strictly fewer padded bytes gets its first section
+ * replaced: change j's gap is its index minus the previous change's index
+ * minus one (change 0's gap is its index), each gap an unsigned LEB128
+ * varint (seven bits per byte, low group first, the high bit set on every
+ * byte but the last), the varints back to back, zero-padded to 16 bytes;
+ * its entry gets layout DCR_LAYOUT_GAPS and its new offset and size.  Every
+ * other record is copied unchanged.  The output header is the input's with
+ * magic DCR_MAGIC_PACKED and the packed payload size.  A packed stream is a
+ * transport form only: dcr_apply refuses it; dcr_stream_unpack turns it
+ * back into the stream it was made from, byte for byte.
+ *   header         the input stream's header in HOST memory: a plain stream
+ *                  (DCR_MAGIC) of this plan (fingerprint), at most two
+ *                  records per chunk; else DCR_E_FORMAT
+ *   dir_dev, payload_dev            the input stream (device)
+ *   header_out_dev, dir_out_dev, dir_cap, payload_out_dev, payload_cap
+ *                  the output stream (device); dir_cap of at least
+ *                  n_records * 32 bytes (DCR_E_CAPACITY otherwise, before
+ *                  any launch): the output directory also carries
+ *                  per-record scratch during the call
+ *   result_dev     n_records, payload_bytes (the output's size, also when it
+ *                  did not fit) and status: DCR_OK; DCR_E_CAPACITY when
+ *                  payload_cap is smaller; DCR_E_FORMAT when an entry does
+ *                  not describe a record of the format inside the payload,
+ *                  or a list is not strictly ascending below its chunk's
+ *                  elements (the outputs then hold no usable stream)
+ *   workspace_dev, ws_bytes         at least the plan's workspace_bytes */
+int32_t dcr_stream_pack(const dcr_plan* plan, const dcr_stream_header* header,
+                        const void* dir_dev, const void* payload_dev,
+                        void* header_out_dev, void* dir_out_dev, uint64_t dir_cap,
+                        void* payload_out_dev, uint64_t payload_cap,
+                        dcr_encode_result* result_dev,
+                        void* workspace_dev, uint64_t ws_bytes, void* stream);
+
+/* The inverse of dcr_stream_pack (receiver side, before the apply): gap
+ * records back to index lists, every other record copied, header magic back
+ * to DCR_MAGIC.  Arguments as for dcr_stream_pack, with a packed stream's
+ * header (DCR_MAGIC_PACKED).  result->status DCR_E_FORMAT: an entry that does
+ * not describe a record inside the payload or does not start where the
+ * previous one ends; a gap section that is not exactly K minimal varints
+ * (at most three bytes, values below 2^16) followed by zero bytes, or a
+ * last index at or past its chunk's elements. */
+int32_t dcr_stream_unpack(const dcr_plan* plan, const dcr_stream_header* header,
+                          const void* dir_dev, const void* payload_dev,
+                          void* header_out_dev, void* dir_out_dev, uint64_t dir_cap,
+                          void* payload_out_dev, uint64_t payload_cap,
+                          dcr_encode_result* result_dev,
+                          void* workspace_dev, uint64_t ws_bytes, void* stream);
 
 /* Benchmark hook.  While set (both non-NULL), every encode, apply or retry
  * call made on this host thread records `start` on its stream just before its
