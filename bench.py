@@ -215,13 +215,13 @@ def _typed(lay, shards):
 
 def _choose_stage(info, avail):
     """The staging area an encode gets from `avail` bytes: every chunk's slot
-    when it fits, else windows as large as memory allows (at least the
-    plan's window minimum), else none (in-order look-back)."""
+    when it fits, else a compact area as large as memory allows (at least
+    the plan's minimum), else none (in-order look-back)."""
     full = int(info.max_payload_bytes)
     if full <= avail:
         return full, "full"
-    if int(info.window_stage_bytes) <= avail:
-        return max(int(info.window_stage_bytes), avail // (256 << 20) * (256 << 20)), "windowed"
+    if int(info.compact_stage_bytes) <= avail:
+        return max(int(info.compact_stage_bytes), avail // (256 << 20) * (256 << 20)), "compact"
     return 0, "in_order"
 
 
@@ -760,14 +760,14 @@ def workload_extras(key, lay, plan, info, olds, news, olds_t, canon, canon_t, ca
                                          p_bytes, dev, per_op["encode"]["ms"], per_op["apply"]["ms"])
     log(f"{key}: pipelined transfer through pinned host memory: {ex['pipelined']}")
 
-    # staging area sizes: the whole worst case, windows of fix-up blocks in
-    # 4 GiB and 1 GiB, and none (in-order look-back); each stream compared
-    # with the step's
-    sm = {"window_stage_bytes": int(info.window_stage_bytes), "full_stage_bytes": int(info.max_payload_bytes)}
+    # staging area sizes: the whole worst case, compact areas of 4 GiB,
+    # 2 GiB and the plan's minimum, and none (in-order look-back); each
+    # stream compared with the step's
+    sm = {"compact_stage_bytes": int(info.compact_stage_bytes), "full_stage_bytes": int(info.max_payload_bytes)}
     ref = (delta.header.clone(), delta.dir[:32 * n_rec].clone(), delta.payload[:p_bytes].clone())
     news_t = dcr.PtrTable(news)
-    for name, sbytes in (("full", int(info.max_payload_bytes)), ("window_4GiB", 4 << 30), ("window_1GiB", 1 << 30),
-                         ("in_order", 0)):
+    for name, sbytes in (("full", int(info.max_payload_bytes)), ("compact_4GiB", 4 << 30),
+                         ("compact_2GiB", 2 << 30), ("compact_min", int(info.compact_stage_bytes)), ("in_order", 0)):
         wsm = dcr.workspace(plan, dev, stage_bytes=sbytes)
         tm = []
         for _ in range(4):
@@ -780,6 +780,7 @@ def workload_extras(key, lay, plan, info, olds, news, olds_t, canon, canon_t, ca
         same = (torch.equal(delta.header, ref[0]) and torch.equal(delta.dir[:32 * n_rec], ref[1])
                 and torch.equal(delta.payload[:p_bytes], ref[2]))
         sm[name] = {"stage_GB": round(sbytes / 1e9, 3), "encode_ms": round(float(np.median(tm[1:])), 3),
+                    "reencoded_chunks": int(delta.result_host()["n_reencoded"]),
                     "stream_eq": bool(same)}
         del wsm
         torch.cuda.empty_cache()

@@ -41,6 +41,13 @@ constexpr uint32_t kCtrTile = 0, kCtrFix = 1, kCtrChanged = 2, kCtrTotal = 4;
 constexpr uint32_t kCtrBig = 8;
 // partial retry: [10] nonzero if a DELTA directory entry named no chunk
 constexpr uint32_t kCtrBad = 10;
+// The counter area is kCtrBytes long: the uint32 counters above in its first
+// 256 bytes, then the staging claim counters (kStageParts uint64, one per
+// partition of the staging area, at byte kStageCtrOff), then the count of
+// tiles to encode again (uint32 at byte kRedoCtrOff).  All zeroed per encode.
+constexpr uint32_t kCtrBytes = 1024, kStageParts = 64, kStageCtrOff = 256, kRedoCtrOff = 768;
+// a tile whose records found no room in a compact staging area
+constexpr uint64_t kNoClaim = ~uint64_t(0);
 constexpr uint32_t kSmallThreads = 256;             // workgroup of the small-record apply
 constexpr uint32_t kSmallStage = 16384;             // its LDS stage (records up to this size)
 // the small-record apply reads and writes whole 128-byte lines for records
@@ -100,13 +107,13 @@ struct Plan {
     bool shard_disjoint = true;           // no shard element holds two canonical elements
     uint64_t scale_bits = 0;              // total flag bits (multiple of 64)
     uint64_t max_dir_bytes = 0, max_payload_bytes = 0;
-    uint64_t window_stage_bytes = 0;      // slots of the largest fix-up block
+    uint64_t compact_stage_bytes = 0;     // least staging area used compactly
     // device table layout
     uint64_t off_tensors = 0, off_chunks = 0, off_pieces = 0, off_scale_chunks = 0, off_slots = 0, off_slow = 0,
              off_direct[3] = {0, 0, 0}, table_bytes = 0;
     // workspace layout
     uint64_t ws_status = 0, ws_fix = 0, ws_need = 0, ws_counter = 0, ws_old = 0, ws_new = 0, ws_scale = 0, ws_canon = 0,
-             ws_agg = 0, ws_info = 0, ws_big = 0, big_cap = 0, ws_bytes = 0;
+             ws_agg = 0, ws_info = 0, ws_big = 0, big_cap = 0, ws_soff = 0, ws_bytes = 0;
     std::vector<uint8_t> blob;            // host image of the device tables
     void* dev_tables = nullptr;           // bound by dcr_plan_upload
 };

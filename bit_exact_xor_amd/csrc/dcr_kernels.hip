@@ -174,9 +174,13 @@ struct EncodeArgs {
     uint64_t dir_cap;       // bytes
     uint64_t payload_cap;   // bytes
     const uint64_t* need;   // partial retry: one bit per tile, set = encode it (NULL: every tile)
+    uint64_t* soff;         // compact staging: per tile, the staging offset it claimed (or kNoClaim)
+    unsigned long long* stage_ctr;   // compact staging: bytes claimed in each of kStageParts partitions
+    uint64_t part_bytes;    // compact staging: bytes of one partition
     uint32_t n_tiles;
     uint32_t mode;
     uint32_t lists;         // 1: index-list layout allowed for low-density records
+    uint32_t compact;       // 1: tiles claim exactly their records' bytes of the staging area
 };
 
 struct EncodeShared {
@@ -189,6 +193,7 @@ struct EncodeShared {
     uint64_t pnew[kMaxCachedPieces];
     uint64_t scan[2 * 3 * (kThreads / 64) + 3];
     uint64_t excl;
+    uint64_t claim;
     uint32_t next;
 };
 
@@ -586,9 +591,9 @@ __device__ __forceinline__ TileSums scan_tile(EncodeShared& S, uint64_t (&cnt)[3
 // elements that fall in the window into LDS (zeroed first: the zero padding),
 // then the window leaves as 128-bit stores.  ONE: the records fit in one
 // window (no range checks).
-template <int W, bool ONE>
-__device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint32_t w0, uint32_t total,
-                                             uint32_t bm, const uint32_t (&meta)[kVecsPerThread],
+template <int W, bool ONE, bool COMPACT>
+__device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint8_t* cbase, uint32_t w0,
+                                             uint32_t total, uint32_t bm, const uint32_t (&meta)[kVecsPerThread],
                                              const uint64_t (&cnt)[3], const TileSums& t, const RecLayout& L) {
     constexpr uint32_t V = 16 / W;
     const uint32_t tid = threadIdx.x;
@@ -709,6 +714,13 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
         }
     }
     __syncthreads();
+    // compact staging: the offset the tile claimed (published by the first
+    // barrier of the window); no room: nothing is copied out
+    if constexpr (COMPACT) {
+        const uint64_t cl = S.claim;
+        if (cl == kNoClaim) return;   // uniform
+        out = cbase + cl;
+    }
     const uint32_t n = ONE ? total : uint32_t(umin64(kWinBytes, total - w0));
     for (uint32_t q = opaque_tid(); q < n / 16; q += kThreads)
         reinterpret_cast<v4u*>(out + w0)[q] = reinterpret_cast<const v4u*>(win)[q];
@@ -717,14 +729,32 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
 // Write a tile's records (XOR record, then overwrite record) at out: change
 // bitmaps (LSB first), byte planes of the changed elements in element order,
 // zero padding to 16 bytes, assembled in LDS one window at a time.
-template <int W>
-__device__ __forceinline__ void write_tile(EncodeShared& S, uint8_t* out, uint32_t n_c,
-                                           const uint32_t (&meta)[kVecsPerThread], const uint64_t (&cnt)[3],
-                                           const TileSums& t, const RecLayout& L) {
+// Compact staging (compact set): the records go to the offset thread 0
+// claims first in its workgroup's partition of the staging area (one atomic
+// add on one of kStageParts counters, so no single address takes every
+// tile's atomic); the claim is recorded for the fix-up, and a claim past the
+// partition's end (kNoClaim) writes nothing: the fix-up lists the tile to be
+// encoded again at its place.  The atomic's latency overlaps the window's
+// zeroing; the offset is read from LDS only when the window is copied out.
+template <int W, bool COMPACT>
+__device__ __forceinline__ void write_tile(const EncodeArgs& a, EncodeShared& S, uint8_t* out, uint32_t tile,
+                                           uint32_t n_c, const uint32_t (&meta)[kVecsPerThread],
+                                           const uint64_t (&cnt)[3], const TileSums& t, const RecLayout& L) {
     const uint32_t bm = dpad16((n_c + 7) / 8);
     const uint32_t total = L.size_x + L.size_o;
+    uint8_t* cbase = nullptr;
+    if constexpr (COMPACT) {
+        if (threadIdx.x == 0) {
+            const uint32_t part = blockIdx.x & (kStageParts - 1);
+            const uint64_t o = atomicAdd(a.stage_ctr + part, (unsigned long long)total);
+            const uint64_t cl = o + total <= a.part_bytes ? uint64_t(part) * a.part_bytes + o : kNoClaim;
+            a.soff[tile] = cl;
+            S.claim = cl;
+        }
+        cbase = a.stage;
+    }
     if (total <= kWinBytes) {
-        write_window<W, true>(S, out, 0, total, bm, meta, cnt, t, L);
+        write_window<W, true, COMPACT>(S, out, cbase, 0, total, bm, meta, cnt, t, L);
         return;
     }
 #pragma nounroll
@@ -738,8 +768,13 @@ __device__ __forceinline__ void write_tile(EncodeShared& S, uint8_t* out, uint32
         cc[1] = cnt[1];
         cc[2] = cnt[2];
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(cc[0]), "+v"(cc[1]), "+v"(cc[2]));
-        write_window<W, false>(S, out, w0, total, bm, m, cc, t, L);
+        write_window<W, false, COMPACT>(S, out, cbase, w0, total, bm, m, cc, t, L);
         __syncthreads();
+    }
+    if constexpr (COMPACT) {
+        const uint64_t cl = S.claim;
+        if (cl == kNoClaim) return;   // uniform
+        out = cbase + cl;
     }
     // index lists of records spanning several windows: the windows left their
     // bytes zero; each thread stores its changes' indices over them (the
@@ -823,7 +858,7 @@ __device__ __forceinline__ void inorder_tile(const EncodeArgs& a, EncodeShared& 
     const uint64_t P = (S.excl & kP16Mask) << 4;
     const uint64_t bytes = (agg & kP16Mask) << 4;
     if ((R + nrec) * DCR_DIRENT_BYTES > a.dir_cap || P + bytes > a.payload_cap) return;   // uniform
-    write_tile<W>(S, a.payload + P, c.n_c, meta, cnt, t, L);
+    write_tile<W, false>(a, S, a.payload + P, tile, c.n_c, meta, cnt, t, L);
     if (tid < nrec) put_dirent(a.dir, R + tid, tid, c.tensor, c.chunk_idx, W, L, t.Kx, t.Ko, P);
 }
 
@@ -865,7 +900,26 @@ __device__ __forceinline__ void staged_tile(const EncodeArgs& a, EncodeShared& S
         a.tile_agg[c.tile] = agg;
         a.tile_info[c.tile] = tile_counts(t);
     }
-    if (agg) write_tile<W>(S, a.stage + a.slots[c.tile], c.n_c, meta, cnt, t, L);
+    if (!agg) return;
+    if (a.compact) write_tile<W, true>(a, S, nullptr, c.tile, c.n_c, meta, cnt, t, L);
+    else write_tile<W, false>(a, S, a.stage + a.slots[c.tile], c.tile, c.n_c, meta, cnt, t, L);
+}
+
+// A tile encoded again, straight to its place in the payload (compact
+// staging found no room for it in the first pass): the same records, no
+// aggregates published.
+template <int W>
+__device__ __forceinline__ void redo_tile(const EncodeArgs& a, EncodeShared& S, const TileCtx& c, uint8_t* out) {
+    const uint32_t owm = ow_mask<W>(a, c);
+    v4u lo[kVecsPerThread], ln[kVecsPerThread];
+    if (c.fast) load_fast(c, lo, ln);
+    else gather_tile<W>(a, S, c, lo, ln);
+    uint32_t meta[kVecsPerThread];
+    uint64_t cnt[3];
+    digest_tile<W>(S, owm, lo, ln, meta, cnt);
+    const TileSums t = scan_tile(S, cnt);
+    const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx, a.lists);
+    if (t.Kx || t.Ko) write_tile<W, false>(a, S, out, c.tile, c.n_c, meta, cnt, t, L);
 }
 
 // Staged encode of the tiles that are not direct (pieces that split
@@ -925,7 +979,7 @@ __device__ __forceinline__ void prefetch_direct(const EncodeArgs& a, EncodeShare
 // Staged encode of the direct tiles of W-byte elements (the staging area
 // holds every chunk's slot): one workgroup per list entry; nothing waits on
 // another workgroup.
-template <int W, bool LISTS>
+template <int W, bool LISTS, bool COMPACT>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_direct_kernel(
     EncodeArgs a, const uint32_t* list, uint32_t n_list) {
     __shared__ EncodeShared S;
@@ -951,7 +1005,26 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         a.tile_agg[c.tile] = agg;
         a.tile_info[c.tile] = tile_counts(t);
     }
-    if (agg) write_tile<W>(S, out, c.n_c, meta, cnt, t, L);
+    if (agg) write_tile<W, COMPACT>(a, S, out, c.tile, c.n_c, meta, cnt, t, L);
+}
+
+// Compact staging, after the fix-up: the tiles whose records found no room
+// in the staging area, encoded again straight to the payload offset the
+// fix-up stored for them.  A persistent grid over the fix-up's list (its
+// length read once; every workgroup leaves when the list is done).
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_redo_kernel(
+    EncodeArgs a, const uint32_t* redo, const uint32_t* redo_count) {
+    __shared__ EncodeShared S;
+    const uint32_t n = sgpr(*redo_count);
+    for (uint32_t i = blockIdx.x; i < n; i += gridDim.x) {
+        const uint32_t tile = sgpr(redo[i]);
+        const TileCtx c = tile_ctx(a, tile);
+        uint8_t* out = a.payload + uniform_load(a.soff + tile);
+        if (c.w == 2) redo_tile<2>(a, S, c, out);
+        else if (c.w == 1) redo_tile<1>(a, S, c, out);
+        else redo_tile<4>(a, S, c, out);
+        __syncthreads();
+    }
 }
 
 // Encode fix-up: one workgroup of 256 threads per kFixTiles consecutive
@@ -967,6 +1040,9 @@ struct FixArgs {
     const uint64_t* tile_info;
     const uint64_t* slots;
     const uint64_t* need;      // partial retry: wanted-chunk bits (others count as empty), else NULL
+    uint64_t* soff;            // compact staging: per-tile staging offsets (kNoClaim: encode again)
+    uint32_t* redo;            // compact staging: the tiles to encode again
+    uint32_t* redo_count;
     uint64_t* fix_status;
     uint32_t* counter;
     const uint8_t* stage;
@@ -978,6 +1054,7 @@ struct FixArgs {
     uint32_t n_blocks;
     uint32_t staged;
     uint32_t lists;
+    uint32_t compact;
 };
 
 __global__ __launch_bounds__(256) void encode_fixup_kernel(FixArgs a) {
@@ -1041,18 +1118,27 @@ __global__ __launch_bounds__(256) void encode_fixup_kernel(FixArgs a) {
         const uint32_t nrec = uint32_t(ag >> kRecShift);
         const uint64_t bytes = (ag & kP16Mask) << 4;
         if ((R + nrec) * DCR_DIRENT_BYTES > a.dir_cap || P + bytes > a.payload_cap) continue;
-        const v4u* src = reinterpret_cast<const v4u*>(a.stage + a.slots[tile]);
-        v4u* dst = reinterpret_cast<v4u*>(a.payload + P);
-        const uint32_t nv = uint32_t(bytes >> 4);
-        uint32_t j = lane;
-        for (; j + 192 < nv; j += 256) {
-            const v4u q0 = src[j], q1 = src[j + 64], q2 = src[j + 128], q3 = src[j + 192];
-            dst[j] = q0;
-            dst[j + 64] = q1;
-            dst[j + 128] = q2;
-            dst[j + 192] = q3;
+        const uint64_t so = a.compact ? a.soff[tile] : a.slots[tile];
+        if (so == kNoClaim) {
+            // no room in the staging area: encoded again at P after this pass
+            if (lane == 0) {
+                a.redo[atomicAdd(a.redo_count, 1u)] = tile;
+                a.soff[tile] = P;
+            }
+        } else {
+            const v4u* src = reinterpret_cast<const v4u*>(a.stage + so);
+            v4u* dst = reinterpret_cast<v4u*>(a.payload + P);
+            const uint32_t nv = uint32_t(bytes >> 4);
+            uint32_t j = lane;
+            for (; j + 192 < nv; j += 256) {
+                const v4u q0 = src[j], q1 = src[j + 64], q2 = src[j + 128], q3 = src[j + 192];
+                dst[j] = q0;
+                dst[j + 64] = q1;
+                dst[j + 128] = q2;
+                dst[j + 192] = q3;
+            }
+            for (; j < nv; j += 64) dst[j] = src[j];
         }
-        for (; j < nv; j += 64) dst[j] = src[j];
         if (lane < nrec) {
             const DevChunk ch = a.chunks[tile];
             const DevTensor td = a.tensors[ch.tensor];
@@ -1135,7 +1221,7 @@ __global__ void encode_finalize_kernel(const uint32_t* counter, uint32_t mode, u
     uint4* r = reinterpret_cast<uint4*>(res);
     r[0] = make_uint4(uint32_t(nrec), uint32_t(nrec >> 32), uint32_t(pbytes), uint32_t(pbytes >> 32));
     const int32_t st = bad ? DCR_E_FORMAT : (fits ? DCR_OK : DCR_E_CAPACITY);
-    r[1] = make_uint4(uint32_t(changed), uint32_t(changed >> 32), uint32_t(st), 0u);
+    r[1] = make_uint4(uint32_t(changed), uint32_t(changed >> 32), uint32_t(st), counter[kRedoCtrOff / 4]);
 }
 
 // Ready watermark of a sliced encode: after slice k's fix-up blocks (the last
@@ -2193,21 +2279,20 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
         hipLaunchKernelGGL(scale_flags_kernel, dim3(uint32_t(p.scale_chunks.size())), dim3(256), 0, s, tensors,
                            chunks, pieces, tab<uint32_t>(p, p.off_scale_chunks), old_sh, new_sh, scale_flags);
     uint32_t* counter = reinterpret_cast<uint32_t*>(ws + p.ws_counter);
-    // bytes past the plan's workspace: staging area.  It is used whole when
-    // it holds every chunk's slot (max_payload_bytes).  A smaller one that
-    // holds the slots of any single fix-up block is used in windows: runs of
-    // whole fix-up blocks whose slots fit, each window's tiles and fix-up
-    // launched before the next window reuses the area (stream order), with
-    // the staging base moved back by the window's first slot offset (the
-    // fix-up block counter and look-back carry over between launches).
-    // Anything smaller: the in-order encode, no staging.
+    // bytes past the plan's workspace: staging area.  When it holds every
+    // chunk's worst-case slot (max_payload_bytes), each tile writes to its
+    // own fixed slot.  A smaller one of at least compact_stage_bytes is used
+    // compactly: it is cut into kStageParts partitions, and each tile with
+    // records claims exactly their bytes in its workgroup's partition with one
+    // atomic add; a tile that finds no room writes nothing, and after the
+    // fix-up (which knows every offset) it is encoded again straight to its
+    // place.  Anything smaller (or a sliced encode without the whole area):
+    // the in-order encode, no staging.
     uint8_t* stage = ws + p.ws_bytes;
     const uint64_t stage_bytes = ws_bytes - p.ws_bytes;
-    const uint32_t n_blocks = (n_tiles + kFixTiles - 1) / kFixTiles;
-    auto slot_end = [&](uint32_t t1) { return t1 < n_tiles ? p.slots[t1] : p.max_payload_bytes; };
     const bool full = stage_bytes >= p.max_payload_bytes;
-    const bool windowed = !full && !n_slices && n_tiles && stage_bytes >= p.window_stage_bytes;
-    const uint32_t staged = (full || windowed) ? 1u : 0u;
+    const bool compact = !full && !n_slices && n_tiles && stage_bytes >= p.compact_stage_bytes;
+    const uint32_t staged = (full || compact) ? 1u : 0u;
     EncodeArgs a;
     a.tensors = tensors;
     a.chunks = chunks;
@@ -2226,9 +2311,13 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
     a.dir_cap = dir_cap;
     a.payload_cap = payload_cap;
     a.need = partial ? need : nullptr;
+    a.soff = reinterpret_cast<uint64_t*>(ws + p.ws_soff);
+    a.stage_ctr = reinterpret_cast<unsigned long long*>(ws + p.ws_counter + kStageCtrOff);
+    a.part_bytes = (stage_bytes / kStageParts) & ~uint64_t(15);
     a.n_tiles = n_tiles;
     a.mode = mode;
     a.lists = lists;
+    a.compact = compact ? 1u : 0u;
     FixArgs f;
     f.tensors = tensors;
     f.chunks = chunks;
@@ -2236,6 +2325,9 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
     f.tile_info = a.tile_info;
     f.slots = a.slots;
     f.need = a.need;
+    f.soff = a.soff;
+    f.redo = reinterpret_cast<uint32_t*>(ws + p.ws_status);   // the tile look-back status is unused when staged
+    f.redo_count = reinterpret_cast<uint32_t*>(ws + p.ws_counter + kRedoCtrOff);
     f.fix_status = reinterpret_cast<uint64_t*>(ws + p.ws_fix);
     f.counter = counter;
     f.stage = stage;
@@ -2247,6 +2339,29 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
     f.n_blocks = (n_tiles + kFixTiles - 1) / kFixTiles;
     f.staged = staged;
     f.lists = lists;
+    f.compact = a.compact;
+    // one direct tile kernel: width index i (1-, 2-, 4-byte), index lists,
+    // compact staging
+    auto launch_direct = [&](int i, bool li, bool co, uint32_t n, const uint32_t* list) {
+#define DCR_DIRECT(W_, L_, C_) \
+    hipLaunchKernelGGL((encode_direct_kernel<W_, L_, C_>), dim3(n), dim3(kThreads), 0, s, a, list, n)
+        const int key = i * 4 + (li ? 2 : 0) + (co ? 1 : 0);
+        switch (key) {
+            case 0: DCR_DIRECT(1, false, false); break;
+            case 1: DCR_DIRECT(1, false, true); break;
+            case 2: DCR_DIRECT(1, true, false); break;
+            case 3: DCR_DIRECT(1, true, true); break;
+            case 4: DCR_DIRECT(2, false, false); break;
+            case 5: DCR_DIRECT(2, false, true); break;
+            case 6: DCR_DIRECT(2, true, false); break;
+            case 7: DCR_DIRECT(2, true, true); break;
+            case 8: DCR_DIRECT(4, false, false); break;
+            case 9: DCR_DIRECT(4, false, true); break;
+            case 10: DCR_DIRECT(4, true, false); break;
+            default: DCR_DIRECT(4, true, true); break;
+        }
+#undef DCR_DIRECT
+    };
     // Tiles [t0, t1): in a staged launch the direct tiles of each element
     // width, then the others (any order: every tile has its own slot); the
     // lists hold tile ids in ascending order, so a range of tiles is a range
@@ -2261,15 +2376,7 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
                 const uint32_t n = uint32_t(std::lower_bound(L.begin(), L.end(), t1) - L.begin()) - lo;
                 if (!n) continue;
                 const uint32_t* list = tab<uint32_t>(p, p.off_direct[i]) + lo;
-                if (lists) {
-                    if (i == 0) hipLaunchKernelGGL((encode_direct_kernel<1, true>), dim3(n), dim3(kThreads), 0, s, a, list, n);
-                    else if (i == 1) hipLaunchKernelGGL((encode_direct_kernel<2, true>), dim3(n), dim3(kThreads), 0, s, a, list, n);
-                    else hipLaunchKernelGGL((encode_direct_kernel<4, true>), dim3(n), dim3(kThreads), 0, s, a, list, n);
-                } else {
-                    if (i == 0) hipLaunchKernelGGL((encode_direct_kernel<1, false>), dim3(n), dim3(kThreads), 0, s, a, list, n);
-                    else if (i == 1) hipLaunchKernelGGL((encode_direct_kernel<2, false>), dim3(n), dim3(kThreads), 0, s, a, list, n);
-                    else hipLaunchKernelGGL((encode_direct_kernel<4, false>), dim3(n), dim3(kThreads), 0, s, a, list, n);
-                }
+                launch_direct(i, lists != 0, compact, n, list);
             }
         } else if (t1 > t0) {
             hipLaunchKernelGGL(encode_kernel, dim3(t1 - t0), dim3(kThreads), 0, s, a);
@@ -2293,21 +2400,12 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
                            p.fingerprint, dir_cap, payload_cap, static_cast<uint8_t*>(header_dev), result_dev);
     };
     if (!n_slices) {
-        if (n_tiles && !windowed) {
+        if (n_tiles) {
             run_tiles(0, n_tiles, true);
             run_fix(0, f.n_blocks);
-        } else if (n_tiles) {
-            for (uint32_t b0 = 0; b0 < n_blocks;) {
-                const uint32_t t0 = b0 * kFixTiles;
-                uint32_t b1 = b0 + 1;
-                while (b1 < n_blocks && slot_end(std::min((b1 + 1) * kFixTiles, n_tiles)) - p.slots[t0] <= stage_bytes)
-                    b1++;
-                a.stage = stage - p.slots[t0];
-                f.stage = a.stage;
-                run_tiles(t0, std::min(b1 * kFixTiles, n_tiles), false);
-                run_fix(b0, b1);
-                b0 = b1;
-            }
+            if (compact)
+                hipLaunchKernelGGL(encode_redo_kernel, dim3(std::min<uint32_t>(n_tiles, 2 * cu_count())),
+                                   dim3(kThreads), 0, s, a, f.redo, f.redo_count);
         }
         finalize();
     } else {

@@ -466,7 +466,7 @@ __global__ void pk_finish_kernel(const unsigned long long* ctr, dcr_stream_heade
     r.payload_bytes = total;
     r.n_changed = 0;
     r.status = bad ? DCR_E_FORMAT : (total > payload_cap ? DCR_E_CAPACITY : DCR_OK);
-    r.reserved = 0;
+    r.n_reencoded = 0;
     *res = r;
 }
 

@@ -250,13 +250,10 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
         P.canonical_bytes += d.numel * w;
         if (d.route == DCR_ROUTE_BLOCK_SCALED) is_scale_used[d.scale_tensor] = 1;
     }
-    // the staging bytes of the largest fix-up block (kFixTiles consecutive
-    // chunks): the least staging area the encode can run in windows with
-    for (uint64_t t0 = 0; t0 < P.slots.size(); t0 += kFixTiles) {
-        const uint64_t t1 = std::min<uint64_t>(t0 + kFixTiles, P.slots.size());
-        const uint64_t end = t1 < P.slots.size() ? P.slots[t1] : P.max_payload_bytes;
-        P.window_stage_bytes = std::max(P.window_stage_bytes, end - P.slots[t0]);
-    }
+    // the least staging area the encode uses compactly: 1/16 of the worst
+    // case (about 4 KiB a chunk of 2-byte elements, the records of a chunk
+    // with ~1 % of its elements changed), and 16 bytes a partition at least
+    P.compact_stage_bytes = std::max<uint64_t>(pad16(P.max_payload_bytes / 16), uint64_t(kStageParts) * 16);
     // per-block "scale changed" flag bits, one bit per element of each gating scale tensor
     std::vector<uint64_t> bit_off(nT, 0);
     for (uint32_t s = 0; s < nT; s++) {
@@ -322,19 +319,19 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
         if (!P.direct[i].empty())
             std::memcpy(P.blob.data() + P.off_direct[i], P.direct[i].data(), P.direct[i].size() * sizeof(uint32_t));
 
-    // workspace: tile look-back status | fix-up look-back status | partial
+    // workspace: tile look-back status (a staged encode keeps its list of
+    // tiles to encode again there) | fix-up look-back status | partial
     // retry's wanted-chunk bits | counters | shard pointers | scale flags |
     // canonical pointers | per-tile aggregates | per-tile change counts |
-    // apply's list of deferred large records.  Everything before the shard
-    // pointers is zeroed at the start of an encode.  Bytes past ws_bytes are
-    // the optional staging area of encode (used when it holds every chunk's
-    // slot).
+    // apply's list of deferred large records | per-tile staging offsets.
+    // Everything before the shard pointers is zeroed at the start of an
+    // encode.  Bytes past ws_bytes are the optional staging area of encode.
     const uint64_t n_tiles = P.chunks.size();
     P.ws_status = 0;
     P.ws_fix = pad256(n_tiles * 8);
     P.ws_need = pad256(P.ws_fix + (n_tiles + kFixTiles - 1) / kFixTiles * 8);
     P.ws_counter = pad256(P.ws_need + (n_tiles + 63) / 64 * 8);
-    P.ws_old = P.ws_counter + 256;
+    P.ws_old = P.ws_counter + kCtrBytes;
     P.ws_new = pad256(P.ws_old + uint64_t(nS) * 8);
     P.ws_scale = pad256(P.ws_new + uint64_t(nS) * 8);
     P.ws_canon = pad256(P.ws_scale + P.scale_bits / 8);
@@ -342,7 +339,8 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     P.ws_info = pad256(P.ws_agg + n_tiles * 8);
     P.big_cap = P.max_dir_bytes / DCR_DIRENT_BYTES;
     P.ws_big = pad256(P.ws_info + n_tiles * 8);
-    P.ws_bytes = pad256(P.ws_big + P.big_cap * 4);
+    P.ws_soff = pad256(P.ws_big + P.big_cap * 4);
+    P.ws_bytes = pad256(P.ws_soff + n_tiles * 8);
     return DCR_OK;
 }
 
@@ -387,7 +385,7 @@ int32_t dcr_plan_query(const dcr_plan* p, dcr_plan_info* out) {
     out->max_payload_bytes = p->max_payload_bytes;
     out->fingerprint = p->fingerprint;
     out->canonical_bytes = p->canonical_bytes;
-    out->window_stage_bytes = p->window_stage_bytes;
+    out->compact_stage_bytes = p->compact_stage_bytes;
     return DCR_OK;
 }
 

@@ -39,7 +39,7 @@ STREAM_HEADER = np.dtype([("magic", "<u4"), ("format_version", "<u2"), ("stream_
                           ("new_version", "<u8"), ("plan_fingerprint", "<u8"), ("n_records", "<u8"),
                           ("payload_bytes", "<u8"), ("reserved1", "<u8")])
 ENCODE_RESULT = np.dtype([("n_records", "<u8"), ("payload_bytes", "<u8"), ("n_changed", "<u8"),
-                          ("status", "<i4"), ("reserved", "<u4")])
+                          ("status", "<i4"), ("n_reencoded", "<u4")])
 APPLY_RESULT = np.dtype([("n_applied", "<u8"), ("n_skipped", "<u8"), ("n_invalid", "<u8"),
                          ("first_invalid", "<u8")])
 assert TENSOR_DESC.itemsize == 24 and SEGMENT.itemsize == 128 and STREAM_HEADER.itemsize == 64
@@ -49,7 +49,7 @@ assert ENCODE_RESULT.itemsize == 32 and APPLY_RESULT.itemsize == 32
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "n_tensors", "n_shards", "n_chunks", "n_pieces", "table_bytes", "workspace_bytes",
-        "max_dir_bytes", "max_payload_bytes", "fingerprint", "canonical_bytes", "window_stage_bytes")]
+        "max_dir_bytes", "max_payload_bytes", "fingerprint", "canonical_bytes", "compact_stage_bytes")]
 
 
 class DcrError(RuntimeError):

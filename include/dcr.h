@@ -144,9 +144,10 @@ typedef struct {
                                    the size of encode's staging area          */
     uint64_t fingerprint;       /* FNV-1a-64 of the serialised tensor table       */
     uint64_t canonical_bytes;   /* sum of numel * elem_bytes                      */
-    uint64_t window_stage_bytes; /* the least staging area dcr_encode runs in
-                                   windows with (the worst-case slots of the
-                                   largest run of 256 consecutive chunks)     */
+    uint64_t compact_stage_bytes; /* the least staging area dcr_encode uses
+                                   compactly: 1/16 of max_payload_bytes
+                                   (16-byte aligned, at least 1 KiB); below
+                                   it the encode runs in order                */
 } dcr_plan_info;
 
 /* Stream header, 64 bytes (the first bytes of every stream). */
@@ -173,7 +174,9 @@ typedef struct {
                                    was too small: grow the buffers and encode again;
                                    DCR_E_FORMAT from dcr_encode_retry_partial if the
                                    DELTA directory names a chunk the plan lacks */
-    uint32_t reserved;
+    uint32_t n_reencoded;       /* chunks encoded a second time because a compact
+                                   staging area had no room left for them (0 with
+                                   a full staging area or none) */
 } dcr_encode_result;
 
 /* Written by dcr_apply / dcr_apply_overwrite_retry in device memory.  32 bytes. */
@@ -242,15 +245,22 @@ void dcr_plan_destroy(dcr_plan* plan);
  *   workspace_dev, ws_bytes    at least workspace_bytes of device memory.
  *                  The excess past workspace_bytes is a staging area.  With
  *                  at least max_payload_bytes of it, each chunk writes its
- *                  records to a slot of its own at once and a second pass
- *                  moves them into place, so no chunk waits for another.
- *                  With less, but at least window_stage_bytes (the slots of
- *                  any 256 consecutive chunks; dcr_encode_pipelined excepted),
- *                  the same runs in windows of whole blocks whose slots fit,
- *                  one after the other on the stream.  With less than that,
- *                  each chunk waits until every earlier chunk has published
- *                  its sizes (decoupled look-back) and writes in place.  All
- *                  give the same stream.
+ *                  records to a slot of its own (sized for its worst case)
+ *                  at once and a second pass moves them into place, so no
+ *                  chunk waits for another.  With less, but at least
+ *                  compact_stage_bytes (dcr_encode_pipelined excepted), the
+ *                  area is used compactly: it is cut into 64 partitions and
+ *                  each chunk claims exactly its records' bytes in one of
+ *                  them (one atomic add); a chunk that finds no room is
+ *                  encoded again, straight to its place, after the offsets
+ *                  are known.  An area a little larger than the stream's
+ *                  payload runs at nearly the speed of the whole worst case;
+ *                  one far below it encodes most chunks twice, slower than
+ *                  in order (size the area from the last stream's
+ *                  payload_bytes).  With less than compact_stage_bytes, or
+ *                  none, each chunk waits until every earlier
+ *                  chunk has published its sizes (decoupled look-back) and
+ *                  writes in place.  All give the same stream.
  * Records are written in (tensor, chunk, kind) order with contiguous 16-byte
  * aligned payload offsets.  If a buffer is too small, result->status becomes
  * DCR_E_CAPACITY with the required totals; the buffers then hold no usable
@@ -545,13 +555,13 @@ int32_t dcr_stream_unpack(const dcr_plan* plan, const dcr_stream_header* header,
 
 /* Benchmark hook.  While set (both non-NULL), every encode, apply or retry
  * call made on this host thread records `start` on its stream just before its
- * main kernel (the encode tile kernel, or the apply kernel) and `stop` just
+ * main kernel (the encode tile kernels, or the apply kernel) and `stop` just
  * after it, so that hipEventElapsedTime gives that kernel's duration alone.
  * The events are hipEvent_t handles the caller created; NULL, NULL turns the
- * hook off.  An encode that runs in windows (a staging area below
- * max_payload_bytes but at least window_stage_bytes) or in slices
- * (dcr_encode_pipelined) has no single main kernel and records neither
- * event.  Never fails. */
+ * hook off.  An encode that runs in slices (dcr_encode_pipelined) has no
+ * single main kernel and records neither event; with a compact staging area
+ * the chunks encoded again after the fix-up are outside the events.  Never
+ * fails. */
 void dcr_set_kernel_events(void* start, void* stop);
 
 /* Message of the last error on this thread ("" if none). */

@@ -126,22 +126,23 @@ def test_ready_wait_host_logic():
     assert e.value.code == dcr.DCR_E_INVAL
 
 
-def test_window_stage_bytes():
-    """window_stage_bytes is the worst-case staging of the largest run of 256
-    consecutive chunks: for one 4096x4096 BF16 tensor (512 full chunks, each
-    at most a 4 KiB bitmap plus two 32 KiB planes) exactly 256 x 69 632
-    bytes, half of max_payload_bytes; for a plan of fewer than 256 chunks,
-    all of max_payload_bytes."""
+def test_compact_stage_bytes():
+    """max_payload_bytes is every chunk's worst-case records (one 4096x4096
+    BF16 tensor: 512 full chunks, each at most a 4 KiB bitmap plus two 32 KiB
+    planes, 512 x 69 632 bytes); compact_stage_bytes is 1/16 of it, 16-byte
+    aligned, and never below 1 KiB (16 bytes for each of 64 partitions)."""
     from bit_exact_xor_amd import dcr, synth
     lay = synth.config1_layout()
     plan = dcr.dcr_plan_build(lay.tensors, [lay.shard_bytes(s) for s in range(lay.n_shards)], lay.segments)
     assert plan.info.n_chunks == 512
-    assert plan.info.window_stage_bytes == 256 * (4096 + 2 * 32768)
-    assert plan.info.max_payload_bytes == 2 * plan.info.window_stage_bytes
-    small = synth.config1_layout(512, 512)
+    assert plan.info.max_payload_bytes == 512 * (4096 + 2 * 32768)
+    assert plan.info.compact_stage_bytes == 32 * (4096 + 2 * 32768)
+    small = synth.config1_layout(40, 40)
     p2 = dcr.dcr_plan_build(small.tensors, [small.shard_bytes(s) for s in range(small.n_shards)], small.segments)
-    assert p2.info.n_chunks < 256
-    assert p2.info.window_stage_bytes == p2.info.max_payload_bytes
+    assert p2.info.n_chunks == 1
+    # 1600 elements: 208-byte bitmap, two 1600-byte planes -> 3408; /16 = 213
+    assert p2.info.max_payload_bytes == 3408
+    assert p2.info.compact_stage_bytes == 1024
 
 
 def test_plan_chunk_limit():

@@ -811,28 +811,36 @@ def test_graph_replay(gh, orc):
     del graph
 
 
-def test_windowed_staging(gh, orc):
+def test_compact_staging(gh, orc):
     """A staging area smaller than every chunk's slot but at least
-    window_stage_bytes runs the staged encode in windows of whole fix-up
-    blocks: on config 1's tensor (512 chunks, two blocks) with the smallest
-    such area, one a little larger, and one just short of the full worst
-    case, the DELTA and RETRY streams equal the oracle's, byte for byte."""
+    compact_stage_bytes is used compactly (each chunk claims its records'
+    bytes in one of 64 partitions; a chunk that finds no room is encoded
+    again at its place after the fix-up).  On config 1's tensor (512 chunks)
+    with the smallest such area, one 16 bytes larger, one twice the stream's
+    payload and one just short of the full worst case, the DELTA and RETRY
+    streams equal the oracle's byte for byte; from twice the payload up no
+    chunk is encoded twice, and with a full area none ever is."""
     lay = synth.config1_layout()
     old, new, _lr, _pos = synth.config1_values(lay, lr=synth.CFG1_LR)
     g = gh.Gpu(lay, [old], [new])
     info = g.plan.info
-    win, full = int(info.window_stage_bytes), int(info.max_payload_bytes)
-    say("windowed staging", win, full)
+    win, full = int(info.compact_stage_bytes), int(info.max_payload_bytes)
     assert 0 < win < full
     for mode in (0, 1):
         exp = oracle_stream(orc, lay, [old], [new], mode)
-        for stage in (win, win + 16, full - 16):
-            assert_same_stream(g.stream_host(g.encode(mode, stage=stage)), exp, f"mode {mode} stage {stage}")
-    # the index-list layout and the partial retry take the same windows
+        pb = len(exp[2])
+        for stage in (win, win + 16, 2 * pb, full - 16, full):
+            sb = g.encode(mode, stage=stage)
+            assert_same_stream(g.stream_host(sb), exp, f"mode {mode} stage {stage}")
+            re = int(sb.result_host()["n_reencoded"])
+            say("compact staging", mode, stage, pb, re)
+            if stage >= 2 * pb:
+                assert re == 0, (mode, stage)
+    # the index-list layout and the partial retry stage the same way
     rc, lh, ld, lp = orc.encode(lay.tensors, lay.segments, [old], [new], mode=dcr.ENC_INDEX_LISTS,
                                 base_version=7, new_version=8)
     assert rc == 0
-    assert_same_stream(g.stream_host(g.encode(dcr.ENC_INDEX_LISTS, stage=win)), (lh, ld, lp), "lists, window")
+    assert_same_stream(g.stream_host(g.encode(dcr.ENC_INDEX_LISTS, stage=win)), (lh, ld, lp), "lists, compact")
     sb = g.encode(0)
     hdr, d, _p = g.stream_host(sb)
     n = len(d) // 32
@@ -843,4 +851,32 @@ def test_windowed_staging(gh, orc):
                                                base_version=7, new_version=8)
     assert rc == 0
     assert_same_stream(g.stream_host(g.encode_retry_partial(hdr, sb, flags, stage=win)), (eh, ed, ep),
-                       "partial retry, window")
+                       "partial retry, compact")
+
+
+@pytest.mark.parametrize("frac", [1.0, 0.6, 0.3])
+def test_compact_staging_overflow(gh, orc, frac):
+    """Compact staging with too little room: config 1's tensor (512 chunks)
+    with a fraction `frac` of its elements changed in random bits (records
+    near their worst case at 1.0) and the smallest compact area, so that
+    chunks find their partition full and are encoded again after the
+    fix-up.  DELTA, RETRY and index-list streams equal the oracle's byte for
+    byte, and the count of chunks encoded again is nonzero whenever the
+    stream's payload exceeds the area."""
+    lay = synth.config1_layout()
+    old, _new, _lr, _pos = synth.config1_values(lay, lr=synth.CFG1_LR)
+    rng = np.random.default_rng(int(frac * 1000) + 17)
+    x = rng.integers(1, 1 << 16, old.size, dtype=np.uint16)
+    x[rng.random(old.size) >= frac] = 0
+    new = old ^ x
+    g = gh.Gpu(lay, [old], [new])
+    win = int(g.plan.info.compact_stage_bytes)
+    for mode in (0, 1, dcr.ENC_INDEX_LISTS):
+        exp = oracle_stream(orc, lay, [old], [new], mode)
+        sb = g.encode(mode, stage=win)
+        r = sb.result_host()
+        say("compact overflow", frac, mode, int(r["payload_bytes"]), win, int(r["n_reencoded"]))
+        assert_same_stream(g.stream_host(sb), exp, f"frac {frac} mode {mode}")
+        if int(r["payload_bytes"]) > win:
+            assert int(r["n_reencoded"]) > 0
+        assert int(r["n_reencoded"]) <= 512
