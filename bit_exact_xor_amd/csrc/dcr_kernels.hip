@@ -1603,16 +1603,22 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 // at group 16t (its bitmap bits are contiguous, so one scan of per-thread
 // change counts ranks every change).  Records that do not fit go to the
 // large-record kernel.
+constexpr uint32_t kLinesPerChunk = kChunkBytes / 128;
 struct SmallShared {
     alignas(16) uint8_t stage[kSmallStage];
     uint32_t pres_pre[kSmallThreads];   // SPARSE: set presence bits before each 32-bit word
     uint32_t jpre[kSmallThreads];       // line mode: changes before each thread's bitmap slice
+    uint8_t whole[kLinesPerChunk];      // line mode: lines that may be read and written whole
+    uint8_t other[kLinesPerChunk];      // line mode beside another record: lines that record marks
     uint64_t scan[kSmallThreads / 64];
     uint32_t ent[8];
     uint32_t state;                     // 0 invalid, 1 skip, 2 apply, 3 deferred
     uint32_t n_c;
     uint32_t bad;
-    uint32_t solo;                      // no other record of this call names the same chunk
+    uint32_t solo;                      // 1: no other record of this call names the same chunk;
+                                        // 2: one other does, a bitmap record at sib_off (below)
+    uint64_t sib_off;                   // payload offset of that other record
+    uint32_t sib;                       // line mode beside it (its lines flagged in `other`)
     uint32_t mfirst, mnp, mdirect;      // receiver layout (as in ApplyShared)
     uint32_t mstart[kMaxCachedPieces];
     uint64_t maddr[kMaxCachedPieces];
@@ -1733,7 +1739,6 @@ __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, 
     constexpr uint32_t GM = (V == 16) ? 0xFFFFu : ((1u << V) - 1u);
     const uint32_t tid = threadIdx.x;
     const uint32_t n_groups = (n_c + V - 1) / V;
-    const uint32_t whole_lines = n_c / (LG * V);
     for (uint32_t k0 = 0; k0 < GT; k0 += KB) {
         v4u v[KB];
         uint32_t gb[KB], st[KB];   // change bits; 0 skip, 1 whole line, 2 group alone
@@ -1760,7 +1765,10 @@ __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, 
                     touched = lb != 0;
                     b = (lb >> (4 * q)) & GM;
                 }
-                if (touched) s_ = L < whole_lines ? 1u : (b ? 2u : 0u);
+                // a line that may not be written whole (the chunk's other
+                // record marks it, or it passes the chunk's end): this
+                // record's groups alone
+                if (touched) s_ = S.whole[L] ? 1u : (b ? 2u : 0u);
             }
             st[kk] = s_;
             gb[kk] = b;
@@ -1798,7 +1806,7 @@ __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, 
 }
 
 template <int W>
-__device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t r, uint32_t n_c) {
+__device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t r, uint32_t n_c) {
     constexpr uint32_t V = 16 / W;                        // elements (= bitmap bits) per group
     constexpr uint32_t E = kChunkBytes / W;
     constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;  // groups per thread (16)
@@ -1817,9 +1825,27 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     const uint32_t pres = lo + dpad16(K);
     const uint32_t hi = hm == DCR_HI_SPARSE ? pres + dpad16((K + 7) / 8) : pres;
 
-    // stage the record
+    // stage the record; for line mode beside the chunk's other record, flag
+    // the lines that record's bitmap marks (V bitmap bytes per line)
     const uint4* src = reinterpret_cast<const uint4*>(a.payload + off);
     for (uint32_t q = tid; q < sz / 16; q += kSmallThreads) reinterpret_cast<uint4*>(S.stage)[q] = src[q];
+    if (S.sib) {
+        const uint4* ssrc = reinterpret_cast<const uint4*>(a.payload + S.sib_off);
+        for (uint32_t q = tid; q < bm / 16; q += kSmallThreads) {
+            const uint4 v = ssrc[q];
+            if constexpr (W == 2) {
+                S.other[2 * q] = (v.x | v.y) != 0;
+                S.other[2 * q + 1] = (v.z | v.w) != 0;
+            } else if constexpr (W == 1) {
+                S.other[q] = (v.x | v.y | v.z | v.w) != 0;
+            } else {
+                S.other[4 * q] = v.x != 0;
+                S.other[4 * q + 1] = v.y != 0;
+                S.other[4 * q + 2] = v.z != 0;
+                S.other[4 * q + 3] = v.w != 0;
+            }
+        }
+    }
     if (tid == 0) S.bad = 0;
     map_table<W>(a, S);
     __syncthreads();
@@ -1906,18 +1932,20 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     uint8_t* dst = a.sharded ? nullptr : a.canon[t] + uint64_t(c) * E * W;
     const uint32_t pk = dpad16(K);
     const bool is_xor = kind == DCR_KIND_XOR;
-    // Line mode for records dense enough that most lines hold a change, when
-    // no other writer can touch the same 128-byte lines: the record is the
-    // only one of this call for its chunk (the other record a chunk may have
-    // sits next to it in the directory; one applied by another call or by
-    // the large-record kernel does not run concurrently), and the chunk is
-    // canonical at a 128-byte aligned address (lines past the chunk's
-    // elements are never written whole).
+    // Line mode for records dense enough that most lines hold a change:
+    // touched 128-byte lines are read and written whole.  Only lines no
+    // other writer touches are written whole: the record is the only one of
+    // this call for its chunk, or the chunk's other record (next to it in the
+    // directory; records of a chunk mark disjoint groups) has its bitmap
+    // staged, and lines it marks take the group-by-group update instead.  A
+    // record applied by another call or by the large-record kernel does not
+    // run concurrently.  The chunk is canonical at a 128-byte aligned
+    // address (lines past the chunk's elements are never written whole).
     // A list record's bitmap is rebuilt past the record in the stage (each
     // thread stores its checked slice whole, so a slice that straddles the
     // bitmap's end needs room for all of it), when it fits.
     const uint32_t bmo = layout == DCR_LAYOUT_LIST ? dpad16(sz) : 0u;
-    const bool line_mode = !a.sharded && S.solo && bmo + bm + BB <= kSmallStage &&
+    const bool line_mode = !a.sharded && (S.solo == 1 || S.sib) && bmo + bm + BB <= kSmallStage &&
                            uint64_t(K) * kLineDensity >= n_c && (reinterpret_cast<uintptr_t>(dst) & 127u) == 0;
     if (line_mode) {
         S.jpre[tid] = j;
@@ -1925,6 +1953,11 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
 #pragma unroll
             for (uint32_t i = 0; i < NW; i++) reinterpret_cast<uint32_t*>(S.stage + bmo + b0)[i] = bw[i];
         }
+        // lines that may be written whole: inside the chunk's elements and
+        // unmarked by the other record
+        const uint32_t whole_lines = n_c / (8 * V), sib = S.sib;
+        for (uint32_t L = tid; L < kLinesPerChunk; L += kSmallThreads)
+            S.whole[L] = L < whole_lines && !(sib && S.other[L]);
         __syncthreads();
         apply_lines<W>(S, dst, n_c, lo, hi, pres, pk, hm, is_xor, bmo);
         __syncthreads();
@@ -1974,7 +2007,51 @@ __device__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t 
     if (tid == 0 && !a.retry) a.flags[r] = 1;   // visible with the writes at kernel completion
 }
 
-__global__ __launch_bounds__(kSmallThreads) void apply_small_kernel(ApplyArgs a) {
+// Thread 0 of a small-record workgroup: the other records of this call for
+// the record's chunk (t, c), whose entries are adjacent in the directory
+// (the XOR record first).  solo 1: none.  solo 2: exactly one, a bitmap
+// record of the other kind whose bitmap lies inside the payload, at
+// sib_off (if that record is malformed it is refused and writes nothing).
+// solo 0: anything else.  pv / nx: the first halves of the neighbouring
+// entries, de: this record's entry.  Values only (no reference to LDS or
+// to a private array), so that every access keeps its address space.
+struct Neighbours {
+    uint32_t solo;
+    uint64_t sib_off;
+};
+__device__ __forceinline__ Neighbours chunk_neighbours(const uint4* de, uint64_t r, uint64_t first, uint64_t end,
+                                                       uint64_t payload_bytes, uint32_t t, uint32_t c, uint32_t kind,
+                                                       uint32_t n_c, bool has_prev, bool has_next, uint4 pv, uint4 nx) {
+    Neighbours o{0u, 0};
+    const bool sp = has_prev && pv.x == t && pv.y == c;
+    const bool sn = has_next && nx.x == t && nx.y == c;
+    if (!sp && !sn) {
+        o.solo = 1u;
+        return o;
+    }
+    if (sp && sn) return o;
+    const uint32_t ow = sp ? pv.w : nx.w;
+    const uint32_t xk = sp ? (ow & 0xFF) : kind, ok = sp ? kind : (ow & 0xFF);
+    if (xk != DCR_KIND_XOR || ok != DCR_KIND_OW || (ow >> 24) != DCR_LAYOUT_BITMAP) return o;
+    // the entry past the other record names another chunk
+    if (sp ? r >= first + 2 : r + 2 < end) {
+        const uint4 far = sp ? de[-4] : de[4];
+        if (far.x == t && far.y == c) return o;
+    }
+    const uint4 o1 = sp ? de[-1] : de[3];
+    const uint64_t off = uint64_t(o1.x) | (uint64_t(o1.y) << 32);
+    const uint64_t bm = dpad16((n_c + 7) / 8);
+    if ((off & 15u) != 0 || off > payload_bytes || bm > payload_bytes - off) return o;
+    o.solo = 2u;
+    o.sib_off = off;
+    return o;
+}
+
+// Seven workgroups per compute unit: a small record's time is mostly the
+// latency of its dependent loads (entry, record, lines), so more resident
+// workgroups pay for the few registers spilled to reach them.
+__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(7, 8))) void apply_small_kernel(
+    ApplyArgs a) {
     __shared__ SmallShared S;
     const uint64_t r = a.first + blockIdx.x;
     uint32_t n_c = 0;
@@ -1999,8 +2076,13 @@ __global__ __launch_bounds__(kSmallThreads) void apply_small_kernel(ApplyArgs a)
             st = fits ? 2 : 3;
             if (!fits) a.big_list[atomicAdd(a.big_count, 1u)] = uint32_t(r - a.first);
             else map_chunk(a, S, e[0], e[1]);
-            S.solo = (!has_prev || pv.x != e[0] || pv.y != e[1]) && (!has_next || nx.x != e[0] || nx.y != e[1]) ? 1u
-                                                                                                                : 0u;
+            const Neighbours nb = chunk_neighbours(de, r, a.first, a.first + gridDim.x, a.payload_bytes, e[0], e[1],
+                                                   e[3] & 0xFF, n_c, has_prev, has_next, pv, nx);
+            S.solo = nb.solo;
+            S.sib_off = nb.sib_off;
+            // line mode beside the other record, when this one is dense
+            // enough for line mode
+            S.sib = nb.solo == 2 && !a.sharded && uint64_t(K) * kLineDensity >= n_c ? 1u : 0u;
         }
         S.state = st;
         S.n_c = n_c;

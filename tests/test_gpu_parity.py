@@ -672,12 +672,16 @@ def _line_mode_layout(seed):
     sides of its threshold, ragged last chunks and groups, 1-byte and 2-byte
     elements, overwrite routes, and block-scaled tensors whose scale blocks
     are (64 BF16 = one 128-byte line) and are not (8 BF16) whole lines, and
-    one whose block (96 BF16) is not a power of two."""
+    one whose block (96 BF16) is not a power of two.  Block-scaled chunks
+    hold an XOR and an overwrite record: dense XOR with sparse and with
+    dense overwrite blocks (both records in line mode, each writing whole
+    only the lines the other leaves alone), and a 1-byte chunk whose XOR
+    record is too large for the small-record stage."""
     rng = np.random.default_rng(seed)
     b = synth._Builder("lines", seed)
     olds, news = [], []
 
-    def add(numel, w, rate, route=synth.ROUTE_AFFINE_XOR, scale_block=0):
+    def add(numel, w, rate, route=synth.ROUTE_AFFINE_XOR, scale_block=0, scale_rate=0.3):
         dt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[w]
         st = -1
         if route == synth.ROUTE_BLOCK_SCALED:
@@ -687,7 +691,7 @@ def _line_mode_layout(seed):
             b.seg(st, s, 0, 0, [ns], [1], [1])
             so = rng.integers(0, 1 << 32, size=ns, dtype=np.uint64).astype(np.uint32)
             sn = so.copy()
-            hit = rng.random(ns) < 0.3
+            hit = rng.random(ns) < scale_rate
             sn[hit] ^= 1
             olds.append(so)
             news.append(sn)
@@ -709,6 +713,10 @@ def _line_mode_layout(seed):
     add(50000, 2, 0.05, synth.ROUTE_BLOCK_SCALED, 64)    # blocks of one line: line path
     add(70000, 2, 0.05, synth.ROUTE_BLOCK_SCALED, 96)    # blocks of 12 groups (not a power of two)
     add(1000, 2, 0.2)
+    add(3 * 32768, 2, 0.05, synth.ROUTE_BLOCK_SCALED, 64, 0.03)    # dense XOR, sparse overwrite blocks
+    add(3 * 32768, 2, 0.1, synth.ROUTE_BLOCK_SCALED, 64, 0.3)      # both dense enough for line mode
+    add(2 * 32768, 2, 0.3, synth.ROUTE_BLOCK_SCALED, 64, 0.02)     # XOR record past the small stage
+    add(2 * 65536, 1, 0.2, synth.ROUTE_BLOCK_SCALED, 128, 0.05)    # 1-byte elements, both records
     lay = b.build()
     lay.values = (olds, news)
     return lay, olds, news
@@ -719,7 +727,9 @@ def test_apply_line_mode_edges(gh, orc, align):
     """Apply and retry give the new tensors bit for bit when the canonical
     tensors are packed at 16-byte offsets (no 128-byte aligned chunk: group
     path, neighbours sharing lines) and at 256-byte offsets (line path for
-    the dense records); the streams equal the oracle's."""
+    the dense records); the streams equal the oracle's.  The index-list
+    stream (sparse records as lists: no line mode beside them) applies to
+    new too."""
     lay, olds, news = _line_mode_layout(11)
     say("line-mode edges, canonical alignment", align)
     g = gh.Gpu(lay, olds, news)
@@ -736,6 +746,15 @@ def test_apply_line_mode_edges(gh, orc, align):
     assert int(r["n_applied"]) == n and int(r["n_invalid"]) == 0
     for v, e in zip(gh.host(canon), news):
         assert np.array_equal(v, e.view(np.uint8)), "apply"
+    lsb = g.encode(dcr.ENC_INDEX_LISTS)
+    lh, ld, _lp = g.stream_host(lsb)
+    nl = len(ld) // 32
+    buf, canon = g.canon_alloc(olds, align=align)
+    lflags = torch.zeros(max(nl, 1), dtype=torch.uint8, device="cuda")
+    r = g.apply(canon, lh, lsb, lflags)
+    assert int(r["n_applied"]) == nl and int(r["n_invalid"]) == 0
+    for v, e in zip(gh.host(canon), news):
+        assert np.array_equal(v, e.view(np.uint8)), "apply, index lists"
     # kill at half the records from old, then the overwrite retry
     buf, canon = g.canon_alloc(olds, align=align)
     flags.zero_()
@@ -746,6 +765,71 @@ def test_apply_line_mode_edges(gh, orc, align):
     assert int(r["n_invalid"]) == 0
     for v, e in zip(gh.host(canon), news):
         assert np.array_equal(v, e.view(np.uint8)), "retry"
+
+
+@pytest.mark.parametrize("align", [16, 256])
+def test_apply_pairs(gh, orc, align):
+    """Chunks with an XOR and an overwrite record (block-scaled tensors):
+    the two records' workgroups run at once, each writing whole only the
+    lines the other record leaves alone.  Each case equals the oracle's
+    apply from the same state and flags, byte for byte:
+    every record fresh; the overwrite records of some pairs and the XOR
+    records of others already flagged (skipped); the XOR record of one pair
+    and the overwrite record of another corrupted (refused, while the other
+    record of the pair applies); and calls split between the two records of
+    a pair.  Canonical tensors at 16-byte offsets (group path) and at
+    256-byte offsets (line mode)."""
+    lay, olds, news = _line_mode_layout(11)
+    say("apply pairs, canonical alignment", align)
+    g = gh.Gpu(lay, olds, news)
+    sb = g.encode(0)
+    hdr, d, p = g.stream_host(sb)
+    ents = fmt.dirents(d)
+    n = len(ents)
+    pairs = [i for i in range(n - 1) if (ents[i]["t"], ents[i]["c"]) == (ents[i + 1]["t"], ents[i + 1]["c"])
+             and ents[i]["w"] == 2]
+    assert len(pairs) >= 10, len(pairs)
+    co = [np.ascontiguousarray(x).view(np.uint8).reshape(-1).copy() for x in olds]
+
+    def check(what, flags0, payload=None, calls=((0, None),), refused=()):
+        # the oracle refuses a whole stream with a bad record: its expected
+        # state skips the refused records instead (flagged beforehand)
+        if payload is not None:
+            sb.payload[:len(payload)].copy_(torch.from_numpy(payload))
+        buf, canon = g.canon_alloc(co, align=align)
+        fl = torch.from_numpy(flags0.copy()).cuda()
+        res = [g.apply(canon, hdr, sb, fl, f0, cnt) for f0, cnt in calls]
+        W = [x.copy() for x in co]
+        fo = flags0.copy()
+        fo[list(refused)] = 1
+        for f0, cnt in calls:
+            assert orc.apply(lay.tensors, W, hdr, d, p, fo, f0, cnt, expected_base_version=7) == 0
+        fo[list(refused)] = 0
+        got = gh.host(canon)
+        for t in range(lay.n_tensors):
+            assert np.array_equal(got[t], W[t]), (what, t)
+        assert np.array_equal(fl.cpu().numpy(), fo), what
+        if payload is not None:
+            sb.payload[:len(p)].copy_(torch.from_numpy(p))
+        return res
+
+    zero = np.zeros(n, np.uint8)
+    res = check("fresh", zero)
+    assert int(res[0]["n_applied"]) == n and int(res[0]["n_invalid"]) == 0
+    f = zero.copy()
+    for i in pairs[0::3]:
+        f[i + 1] = 1
+    for i in pairs[1::3]:
+        f[i] = 1
+    res = check("flagged", f)
+    assert int(res[0]["n_skipped"]) == int(f.sum())
+    bad = p.copy()
+    bad[ents[pairs[0]]["off"]] ^= 0x01           # an XOR record's bitmap: popcount no longer K
+    bad[ents[pairs[1] + 1]["off"]] ^= 0x01       # an overwrite record's bitmap
+    res = check("corrupt", zero, payload=bad, refused=(pairs[0], pairs[1] + 1))
+    assert int(res[0]["n_invalid"]) == 2 and int(res[0]["first_invalid"]) == pairs[0]
+    i = pairs[len(pairs) // 2]
+    check("split", zero, calls=((0, i + 1), (i + 1, n - i - 1)))
 
 
 def test_graph_replay(gh, orc):
