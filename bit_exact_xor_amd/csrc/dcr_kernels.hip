@@ -71,17 +71,43 @@ __device__ __forceinline__ uint64_t wave_sum(uint64_t x) {
     return x;
 }
 
+// Inclusive wave64 scan of a 32-bit value by DPP lane moves (no LDS): the
+// three preceding lanes' original values within each row of 16, then the
+// partial sums 4 and 8 lanes back (banks past the first), then the last lane
+// of row 0 broadcast into rows 1 and 3 and the last lane of row 1 into rows
+// 2 and 3.  Lanes a move leaves out add nothing.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x) {
+    const uint32_t x0 = x;
+    x += __builtin_amdgcn_update_dpp(0u, x0, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x0, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x0, 0x113, 0xf, 0xf, true);   // row_shr:3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xe, false);   // row_shr:4, banks 1-3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xc, false);   // row_shr:8, banks 2-3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
+    return x;
+}
+
+// The same over a 64-bit value whose two 32-bit halves never carry into each
+// other: packed 16-bit counts whose workgroup sums stay below 65536, or a
+// plain count whose sum stays below 2^32.
+__device__ __forceinline__ uint64_t wave_incl_scan_halves(uint64_t x) {
+    return uint64_t(wave_incl_scan_dpp(uint32_t(x))) | (uint64_t(wave_incl_scan_dpp(uint32_t(x >> 32))) << 32);
+}
+
 // Exclusive workgroup scan of N packed 64-bit values; totals returned in tot.
-// Uses sh[2 * N * 16 + N] of LDS; ends with a barrier so sh may be reused.
-// The first wave scans the 16 wave totals, so that each thread reads back
-// just two values per scanned quantity.
+// Each value's halves are scanned apart (wave_incl_scan_halves), so every
+// caller's values keep their sums inside each 32-bit half.  Uses
+// sh[2 * N * 16 + N] of LDS; ends with a barrier so sh may be reused.  The
+// first wave scans the 16 wave totals, so that each thread reads back just
+// two values per scanned quantity.
 template <int N>
 __device__ __forceinline__ void block_excl_scan(uint64_t (&v)[N], uint64_t (&tot)[N], uint64_t* sh) {
     constexpr uint32_t NW = kThreads / 64;
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
     uint64_t inc[N];
 #pragma unroll
-    for (int i = 0; i < N; i++) inc[i] = wave_incl_scan(v[i], lane);
+    for (int i = 0; i < N; i++) inc[i] = wave_incl_scan_halves(v[i]);
     if (lane == 63) {
 #pragma unroll
         for (int i = 0; i < N; i++) sh[i * NW + wave] = inc[i];
@@ -91,7 +117,7 @@ __device__ __forceinline__ void block_excl_scan(uint64_t (&v)[N], uint64_t (&tot
 #pragma unroll
         for (int i = 0; i < N; i++) {
             const uint64_t t = lane < NW ? sh[i * NW + lane] : 0;
-            const uint64_t ti = wave_incl_scan(t, lane);
+            const uint64_t ti = wave_incl_scan_halves(t);
             if (lane < NW) sh[N * NW + i * NW + lane] = ti - t;      // exclusive wave prefix
             if (lane == NW - 1) sh[2 * N * NW + i] = ti;            // total
         }
@@ -1624,10 +1650,11 @@ struct SmallShared {
     uint64_t maddr[kMaxCachedPieces];
 };
 
-// Exclusive scan of one value per thread over a kSmallThreads workgroup.
+// Exclusive scan of one count per thread over a kSmallThreads workgroup (the
+// workgroup's sum stays below 2^32: changes of one chunk).
 __device__ __forceinline__ uint64_t small_excl_scan(uint64_t v, uint64_t& total, uint64_t* sh) {
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-    const uint64_t inc = wave_incl_scan(v, lane);
+    const uint64_t inc = wave_incl_scan_halves(v);
     if (lane == 63) sh[wave] = inc;
     __syncthreads();
     uint64_t pre = 0, tot = 0;
