@@ -1037,7 +1037,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 // Compact staging, after the fix-up: the tiles whose records found no room
 // in the staging area, encoded again straight to the payload offset the
 // fix-up stored for them.  A persistent grid over the fix-up's list (its
-// length read once; every workgroup leaves when the list is done).
+// length read once; every workgroup leaves when the list is done), one
+// launch per element width, each encoding the listed tiles of its width
+// (so each width's code is compiled on its own, free of register spills).
+template <int W>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_redo_kernel(
     EncodeArgs a, const uint32_t* redo, const uint32_t* redo_count) {
     __shared__ EncodeShared S;
@@ -1045,10 +1048,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     for (uint32_t i = blockIdx.x; i < n; i += gridDim.x) {
         const uint32_t tile = sgpr(redo[i]);
         const TileCtx c = tile_ctx(a, tile);
+        if (c.w != W) continue;   // uniform
         uint8_t* out = a.payload + uniform_load(a.soff + tile);
-        if (c.w == 2) redo_tile<2>(a, S, c, out);
-        else if (c.w == 1) redo_tile<1>(a, S, c, out);
-        else redo_tile<4>(a, S, c, out);
+        redo_tile<W>(a, S, c, out);
         __syncthreads();
     }
 }
@@ -2512,9 +2514,12 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
         if (n_tiles) {
             run_tiles(0, n_tiles, true);
             run_fix(0, f.n_blocks);
-            if (compact)
-                hipLaunchKernelGGL(encode_redo_kernel, dim3(std::min<uint32_t>(n_tiles, 2 * cu_count())),
-                                   dim3(kThreads), 0, s, a, f.redo, f.redo_count);
+            if (compact) {
+                const dim3 g(std::min<uint32_t>(n_tiles, 2 * cu_count()));
+                hipLaunchKernelGGL(encode_redo_kernel<2>, g, dim3(kThreads), 0, s, a, f.redo, f.redo_count);
+                hipLaunchKernelGGL(encode_redo_kernel<1>, g, dim3(kThreads), 0, s, a, f.redo, f.redo_count);
+                hipLaunchKernelGGL(encode_redo_kernel<4>, g, dim3(kThreads), 0, s, a, f.redo, f.redo_count);
+            }
         }
         finalize();
     } else {
@@ -2566,7 +2571,8 @@ int32_t dcr_encode_noalloc(const dcr_plan* plan, const void* const* old_shards, 
     const int32_t rc = scratch_ptr(&ws);
     if (rc) return rc;
     // staged when every chunk's slot fits past the workspace, else in order
-    // (windows of a few fix-up blocks would cost more than the look-back)
+    // (a compact area of what is left could be far below a large stream's
+    // size, and would then encode most chunks twice)
     const uint64_t ws_bytes = plan->ws_bytes + plan->max_payload_bytes <= DCR_NOALLOC_SCRATCH_BYTES
                                   ? uint64_t(DCR_NOALLOC_SCRATCH_BYTES)
                                   : plan->ws_bytes;
