@@ -747,9 +747,18 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
         if (cl == kNoClaim) return;   // uniform
         out = cbase + cl;
     }
+    // non-temporal 128-bit stores: the records are read back only after the
+    // whole grid (by the fix-up, or by the stream's consumer).  Index lists
+    // of records spanning several windows are stored over these bytes after
+    // the last window: plain stores then, ordered by the barrier in between.
     const uint32_t n = ONE ? total : uint32_t(umin64(kWinBytes, total - w0));
-    for (uint32_t q = opaque_tid(); q < n / 16; q += kThreads)
-        reinterpret_cast<v4u*>(out + w0)[q] = reinterpret_cast<const v4u*>(win)[q];
+    if (ONE || !(L.list_x | L.list_o)) {
+        for (uint32_t q = opaque_tid(); q < n / 16; q += kThreads)
+            __builtin_nontemporal_store(reinterpret_cast<const v4u*>(win)[q], reinterpret_cast<v4u*>(out + w0) + q);
+    } else {
+        for (uint32_t q = opaque_tid(); q < n / 16; q += kThreads)
+            reinterpret_cast<v4u*>(out + w0)[q] = reinterpret_cast<const v4u*>(win)[q];
+    }
 }
 
 // Write a tile's records (XOR record, then overwrite record) at out: change
