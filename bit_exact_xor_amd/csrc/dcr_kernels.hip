@@ -1866,7 +1866,9 @@ __device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShar
     // stage the record; for line mode beside the chunk's other record, flag
     // the lines that record's bitmap marks (V bitmap bytes per line)
     const uint4* src = reinterpret_cast<const uint4*>(a.payload + off);
-    for (uint32_t q = tid; q < sz / 16; q += kSmallThreads) reinterpret_cast<uint4*>(S.stage)[q] = src[q];
+    for (uint32_t q = tid; q < sz / 16; q += kSmallThreads)   // read once: non-temporal
+        reinterpret_cast<v4u*>(S.stage)[q] =
+            __builtin_nontemporal_load(reinterpret_cast<gv4p>(reinterpret_cast<uintptr_t>(src)) + q);
     if (S.sib) {
         const uint4* ssrc = reinterpret_cast<const uint4*>(a.payload + S.sib_off);
         for (uint32_t q = tid; q < bm / 16; q += kSmallThreads) {
