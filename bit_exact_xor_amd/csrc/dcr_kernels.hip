@@ -1203,6 +1203,43 @@ __global__ __launch_bounds__(256) void scale_flags_kernel(const DevTensor* tenso
     const uint32_t n_c = uint32_t(umin64(E, td.numel - c0));
     const DevPiece* pc = pieces + ch.first_piece;
     const uint32_t lane = threadIdx.x & 63u;
+    if ((ch.n_pieces & kPiecesMask) == 1 && (n_c & 3u) == 0) {
+        // one piece: each lane compares four consecutive scales with two
+        // 128-bit loads; a wave covers 256 scales, four flag words, whose
+        // bits come from four ballots (scale 4l + i is bit i of lane l's
+        // nibble) spread so that lane l's nibble lands at bits 4l .. 4l + 3
+        const uint64_t so = reinterpret_cast<uint64_t>(old_sh[pc[0].shard]) + (pc[0].shard_elem_off - pc[0].canon_start) * 4;
+        const uint64_t sn = reinterpret_cast<uint64_t>(new_sh[pc[0].shard]) + (pc[0].shard_elem_off - pc[0].canon_start) * 4;
+        if (((so | sn) & 15u) == 0) {
+            auto spread4 = [](uint64_t x) {   // bit i of a 16-bit value to bit 4i
+                x &= 0xFFFFu;
+                x = (x | (x << 24)) & 0x000000FF000000FFull;
+                x = (x | (x << 12)) & 0x000F000F000F000Full;
+                x = (x | (x << 6)) & 0x0303030303030303ull;
+                x = (x | (x << 3)) & 0x1111111111111111ull;
+                return x;
+            };
+            for (uint32_t e0 = (threadIdx.x & ~63u) * 4; e0 < n_c; e0 += 1024) {
+                const uint32_t e = e0 + 4 * lane;
+                uint32_t nib = 0;
+                if (e < n_c) {
+                    const v4u o = __builtin_nontemporal_load(reinterpret_cast<gv4p>(so + uint64_t(e) * 4));
+                    const v4u n = __builtin_nontemporal_load(reinterpret_cast<gv4p>(sn + uint64_t(e) * 4));
+                    nib = uint32_t(o.x != n.x) | (uint32_t(o.y != n.y) << 1) | (uint32_t(o.z != n.z) << 2) |
+                          (uint32_t(o.w != n.w) << 3);
+                }
+                const uint64_t m0 = __ballot(nib & 1u), m1 = __ballot(nib & 2u), m2 = __ballot(nib & 4u),
+                               m3 = __ballot(nib & 8u);
+                if (lane < 4 && e0 + 64 * lane < n_c) {
+                    const uint32_t sh = 16 * lane;
+                    flags[(td.scale_bit_off + c0 + e0 + 64 * lane) >> 6] =
+                        spread4(m0 >> sh) | (spread4(m1 >> sh) << 1) | (spread4(m2 >> sh) << 2) |
+                        (spread4(m3 >> sh) << 3);
+                }
+            }
+            return;
+        }
+    }
     for (uint32_t e0 = (threadIdx.x & ~63u); e0 < n_c; e0 += 256) {
         const uint32_t e = e0 + lane;
         bool changed = false;
