@@ -486,13 +486,17 @@ __device__ __forceinline__ uint32_t ow_mask(const EncodeArgs& a, const TileCtx& 
     const uint64_t gi = c.c0 / V + tid;                   // this thread's first group in the tensor
     uint64_t q = gi / sbg, r = gi % sbg;
     const uint64_t sq = kThreads / sbg, sr = kThreads % sbg;
-    uint32_t m = 0;
+    // the flag words of the thread's groups, loaded together (a group past
+    // the chunk's elements reads the tensor's first flag word and is masked)
+    uint64_t fw[kVecsPerThread];
+    uint32_t sh[kVecsPerThread], in = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kVecsPerThread; k++) {
-        if ((tid + k * kThreads) * V < c.n_c) {
-            const uint64_t bit = c.scale_bit_off + q;
-            m |= uint32_t((a.scale_flags[bit >> 6] >> (bit & 63)) & 1u) << k;
-        }
+        const bool ok = (tid + k * kThreads) * V < c.n_c;
+        const uint64_t bit = c.scale_bit_off + (ok ? q : 0);
+        fw[k] = a.scale_flags[bit >> 6];
+        sh[k] = uint32_t(bit & 63);
+        in |= ok ? 1u << k : 0u;
         q += sq;
         r += sr;
         if (r >= sbg) {
@@ -500,7 +504,10 @@ __device__ __forceinline__ uint32_t ow_mask(const EncodeArgs& a, const TileCtx& 
             q++;
         }
     }
-    return m;
+    uint32_t m = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kVecsPerThread; k++) m |= uint32_t((fw[k] >> sh[k]) & 1u) << k;
+    return m & in;
 }
 
 // 1 in each 16-bit half of the result iff that half of d is nonzero (one
@@ -863,10 +870,10 @@ __device__ __forceinline__ void skip_tile(const EncodeArgs& a, uint32_t tile, bo
 template <int W>
 __device__ __forceinline__ void inorder_tile(const EncodeArgs& a, EncodeShared& S, const TileCtx& c) {
     const uint32_t tid = threadIdx.x;
-    const uint32_t owm = ow_mask<W>(a, c);
     v4u lo[kVecsPerThread], ln[kVecsPerThread];
     if (c.fast) load_fast(c, lo, ln);
     else gather_tile<W>(a, S, c, lo, ln);
+    const uint32_t owm = ow_mask<W>(a, c);   // after the tile's loads are issued
     uint32_t meta[kVecsPerThread];
     uint64_t cnt[3];
     digest_tile<W>(S, owm, lo, ln, meta, cnt);
@@ -921,10 +928,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 template <int W>
 __device__ __forceinline__ void staged_tile(const EncodeArgs& a, EncodeShared& S, const TileCtx& c) {
     const uint32_t tid = threadIdx.x;
-    const uint32_t owm = ow_mask<W>(a, c);
     v4u lo[kVecsPerThread], ln[kVecsPerThread];
     if (c.fast) load_fast(c, lo, ln);
     else gather_tile<W>(a, S, c, lo, ln);
+    const uint32_t owm = ow_mask<W>(a, c);   // after the tile's loads are issued
     uint32_t meta[kVecsPerThread];
     uint64_t cnt[3];
     digest_tile<W>(S, owm, lo, ln, meta, cnt);
@@ -945,10 +952,10 @@ __device__ __forceinline__ void staged_tile(const EncodeArgs& a, EncodeShared& S
 // aggregates published.
 template <int W>
 __device__ __forceinline__ void redo_tile(const EncodeArgs& a, EncodeShared& S, const TileCtx& c, uint8_t* out) {
-    const uint32_t owm = ow_mask<W>(a, c);
     v4u lo[kVecsPerThread], ln[kVecsPerThread];
     if (c.fast) load_fast(c, lo, ln);
     else gather_tile<W>(a, S, c, lo, ln);
+    const uint32_t owm = ow_mask<W>(a, c);   // after the tile's loads are issued
     uint32_t meta[kVecsPerThread];
     uint64_t cnt[3];
     digest_tile<W>(S, owm, lo, ln, meta, cnt);
@@ -1025,9 +1032,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     // the slot's address is uniform: read it before this workgroup stores
     // anything, into scalar registers
     uint8_t* const out = a.stage + uniform_load(a.slots + c.tile);
-    const uint32_t owm = ow_mask<W>(a, c);
     v4u o[kVecsPerThread], n[kVecsPerThread];
     prefetch_direct(a, S, c, o, n);
+    // the tile's loads are in flight: its routing flags next (loaded before,
+    // their waits held the tile's loads back)
+    const uint32_t owm = ow_mask<W>(a, c);
     uint32_t meta[kVecsPerThread];
     uint64_t cnt[3];
     digest_tile<W>(S, owm, o, n, meta, cnt);
@@ -1692,6 +1701,7 @@ struct SmallShared {
     uint32_t solo;                      // 1: no other record of this call names the same chunk;
                                         // 2: one other does, a bitmap record at sib_off (below)
     uint64_t sib_off;                   // payload offset of that other record
+    uint64_t dst;                       // canonical layout: the chunk's first byte
     uint32_t sib;                       // line mode beside it (its lines flagged in `other`)
     uint32_t mfirst, mnp, mdirect;      // receiver layout (as in ApplyShared)
     uint32_t mstart[kMaxCachedPieces];
@@ -1883,14 +1893,13 @@ __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, 
 template <int W>
 __device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t r, uint32_t n_c) {
     constexpr uint32_t V = 16 / W;                        // elements (= bitmap bits) per group
-    constexpr uint32_t E = kChunkBytes / W;
     constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;  // groups per thread (16)
     constexpr uint32_t BB = GT * V / 8;                   // bitmap bytes per thread (8, 16 or 32)
     constexpr uint32_t NW = BB / 4;                       // ... in 32-bit words
     constexpr uint32_t GPW = 32 / V;                      // groups per bitmap word
     constexpr uint32_t GM = (V == 16) ? 0xFFFFu : ((1u << V) - 1u);
     const uint32_t tid = threadIdx.x;
-    const uint32_t t = S.ent[0], c = S.ent[1], K = S.ent[2];
+    const uint32_t K = S.ent[2];
     const uint32_t kind = S.ent[3] & 0xFF, hm = (S.ent[3] >> 8) & 0xFF;
     const uint64_t off = uint64_t(S.ent[4]) | (uint64_t(S.ent[5]) << 32);
     const uint32_t sz = S.ent[6], H = S.ent[7];
@@ -2006,7 +2015,7 @@ __device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShar
     __syncthreads();
     if (S.bad) return;   // refused before any write
 
-    uint8_t* dst = a.sharded ? nullptr : a.canon[t] + uint64_t(c) * E * W;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(S.dst);
     const uint32_t pk = dpad16(K);
     const bool is_xor = kind == DCR_KIND_XOR;
     // Line mode for records dense enough that most lines hold a change:
@@ -2140,12 +2149,17 @@ __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(7
         const bool has_prev = r > a.first, has_next = r + 1 < a.first + gridDim.x;
         const uint4 pv = has_prev ? de[-2] : make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0, 0);
         const uint4 nx = has_next ? de[2] : make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0, 0);
+        // the dedup flag, and the canonical tensor's address (needed by the
+        // writes), loaded with the entry and with the tensor's descriptor
+        // rather than one after the other
+        const uint8_t done = a.retry ? uint8_t(0) : a.flags[r];
+        const uint8_t* cbase = (!a.sharded && e0.x < a.n_tensors) ? a.canon[e0.x] : nullptr;
         uint32_t e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
         for (int i = 0; i < 8; i++) S.ent[i] = e[i];
         uint32_t st;
         if (!entry_ok(a, e, n_c)) {
             st = 0;
-        } else if (!a.retry && a.flags[r]) {
+        } else if (done) {
             st = 1;
         } else {
             const uint32_t K = e[2], hm = (e[3] >> 8) & 0xFF;
@@ -2160,6 +2174,7 @@ __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(7
             // line mode beside the other record, when this one is dense
             // enough for line mode
             S.sib = nb.solo == 2 && !a.sharded && uint64_t(K) * kLineDensity >= n_c ? 1u : 0u;
+            S.dst = cbase ? reinterpret_cast<uint64_t>(cbase) + uint64_t(e[1]) * kChunkBytes : 0;
         }
         S.state = st;
         S.n_c = n_c;
