@@ -1328,14 +1328,25 @@ def measure_ceiling(buf, dev, reps=3, rmw=None):
     return out
 
 
-def _src_sha256():
-    """SHA-256 over the kernel sources the counters depend on (the kernels and
-    the constants they are built with)."""
+def _code_text(text):
+    """C++ source text without its comments and with its blank space collapsed:
+    what the compiler sees of it (the sources hold no comment markers inside
+    string literals)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def _src_sha256(paths=None):
+    """SHA-256 over the code of the kernel sources the counters depend on (the
+    kernels and the constants they are built with): an edit to a comment
+    leaves the measured kernels, and so the hash, unchanged."""
     import hashlib
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+    for path in (paths or KERNEL_SRCS):
+        with open(path) as f:
+            h.update(_code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -475,7 +475,8 @@ __device__ __forceinline__ void gather_tile(const EncodeArgs& a, EncodeShared& S
 // Per-k routing bits of this thread's groups (1 = overwrite record).  A
 // block-scaled group goes to the overwrite record iff the fp32 scale of its
 // block changed (a group never straddles blocks: scale_block is a multiple
-// of the group's element count).  Computed before the tile's loads are issued.
+// of the group's element count).  Called once the tile's own loads are in
+// flight; its flag loads are issued together.
 template <int W>
 __device__ __forceinline__ uint32_t ow_mask(const EncodeArgs& a, const TileCtx& c) {
     constexpr uint32_t V = 16 / W;

@@ -38,3 +38,18 @@ def test_touched_rejects_unaligned_offsets():
     x = torch.zeros(32, dtype=torch.uint8)
     with pytest.raises(AssertionError):
         bench._touched([x], [x], torch.zeros(4, dtype=torch.uint8), [16])
+
+
+def test_source_hash_ignores_comments_only(tmp_path):
+    """The hash that ties a committed counter summary to the kernel sources:
+    unchanged by comment and layout edits, changed by any edit to the code."""
+    import bench
+    base = "// header\nint f(int x) { /* note */ return x + 1; }  // tail\n"
+    p = tmp_path / "k.hip"
+    p.write_text(base)
+    h0 = bench._src_sha256([str(p)])
+    p.write_text("// other header\n\nint f(int x) {\n    /* changed note */\n    return x + 1;\n}\n")
+    assert bench._src_sha256([str(p)]) == h0
+    p.write_text(base.replace("x + 1", "x + 2"))
+    assert bench._src_sha256([str(p)]) != h0
+    assert bench._code_text(base) == "int f(int x) { return x + 1; }"
