@@ -1692,13 +1692,19 @@ struct SmallShared {
     alignas(16) uint8_t stage[kSmallStage];
     uint32_t pres_pre[kSmallThreads];   // SPARSE: set presence bits before each 32-bit word
     uint32_t jpre[kSmallThreads];       // line mode: changes before each thread's bitmap slice
+    uint32_t jpre2[kSmallThreads];      // ... of a fused pair's overwrite record
     uint8_t whole[kLinesPerChunk];      // line mode: lines that may be read and written whole
     uint8_t other[kLinesPerChunk];      // line mode beside another record: lines that record marks
     uint64_t scan[kSmallThreads / 64];
     uint32_t ent[8];
-    uint32_t state;                     // 0 invalid, 1 skip, 2 apply, 3 deferred
+    uint32_t ent2[8];                   // fused pair: the overwrite record's entry
+    uint32_t state;                     // 0 invalid, 1 skip, 2 apply, 3 deferred, 4 left to the pair's XOR record
     uint32_t n_c;
     uint32_t bad;
+    uint32_t bad2;                      // fused pair: the overwrite record is malformed
+    uint32_t fused;                     // 1: the overwrite record at rec + 1 is applied here too
+    uint32_t pskip;                     // 1: the other record of this record's pair is skipped (flagged)
+    uint64_t rec;                       // the record this workgroup applies
     uint32_t solo;                      // 1: no other record of this call names the same chunk;
                                         // 2: one other does, a bitmap record at sib_off (below)
     uint64_t sib_off;                   // payload offset of that other record
@@ -1812,11 +1818,15 @@ __device__ __forceinline__ void patch_elems(uint8_t* dst, uint32_t g, uint32_t b
 // the ragged one element by element).  Needs S.jpre: the changes before each
 // thread's 16-group bitmap slice, and the record's change bitmap in the
 // stage at byte bmo (0 for a bitmap record; a list record's bitmap is
-// rebuilt past the record).
+// rebuilt past the record).  pair: a fused pair, whose overwrite record is
+// staged at bmo2 (bitmap, then its byte planes from lo2, pk2 apart) with its
+// slice prefixes in S.jpre2; a line touched by either record is written
+// whole, each group patched from the record that marks it.
 template <int W>
 __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, uint32_t n_c, uint32_t lo,
                                             uint32_t hi, uint32_t pres, uint32_t pk, uint32_t hm, bool is_xor,
-                                            uint32_t bmo) {
+                                            uint32_t bmo, bool pair, uint32_t bmo2, uint32_t lo2, uint32_t pk2,
+                                            uint32_t hm2) {
     constexpr uint32_t V = 16 / W;                        // change bits per group
     constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;  // groups per bitmap slice (16)
     constexpr uint32_t BB = GT * V / 8;                   // bitmap bytes per slice
@@ -1825,31 +1835,59 @@ __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, 
     constexpr uint32_t GM = (V == 16) ? 0xFFFFu : ((1u << V) - 1u);
     const uint32_t tid = threadIdx.x;
     const uint32_t n_groups = (n_c + V - 1) / V;
+    // a line's change bits in the bitmap at stage offset b (bits past n_c
+    // were refused, so they are zero); the group's own bits in gbits
+    auto line_bits = [&](uint32_t b, uint32_t L, uint32_t q, uint32_t& gbits) {
+        bool touched;
+        if constexpr (W == 2) {
+            const uint64_t lb = *reinterpret_cast<const uint64_t*>(S.stage + b + 8 * L);
+            touched = lb != 0;
+            gbits = uint32_t(lb >> (8 * q)) & GM;
+        } else if constexpr (W == 1) {
+            const uint4 lb = *reinterpret_cast<const uint4*>(S.stage + b + 16 * L);
+            touched = (lb.x | lb.y | lb.z | lb.w) != 0;
+            const uint32_t wv = (q & 4u) ? ((q & 2u) ? lb.w : lb.z) : ((q & 2u) ? lb.y : lb.x);
+            gbits = (wv >> (16 * (q & 1u))) & GM;
+        } else {
+            const uint32_t lb = *reinterpret_cast<const uint32_t*>(S.stage + b + 4 * L);
+            touched = lb != 0;
+            gbits = (lb >> (4 * q)) & GM;
+        }
+        return touched;
+    };
+    // record index of group g's first change: the changes before its slice
+    // plus those of the slice's earlier groups
+    auto first_index = [&](uint32_t b, uint32_t pre, uint32_t g) {
+        const uint32_t sl = g / GT, nb = (g % GT) * V;
+        uint32_t j = pre;
+#pragma unroll
+        for (uint32_t i = 0; i < BB / 4; i++) {
+            const uint32_t wd = *reinterpret_cast<const uint32_t*>(S.stage + b + sl * BB + 4 * i);
+            const uint32_t m = nb >= 32 * (i + 1) ? 0xFFFFFFFFu : (nb <= 32 * i ? 0u : ((1u << (nb - 32 * i)) - 1u));
+            j += __popc(wd & m);
+        }
+        return j;
+    };
     for (uint32_t k0 = 0; k0 < GT; k0 += KB) {
         v4u v[KB];
         uint32_t gb[KB], st[KB];   // change bits; 0 skip, 1 whole line, 2 group alone
+        uint32_t ob = 0;           // a fused pair: which of the KB groups are the overwrite record's
 #pragma unroll
         for (uint32_t kk = 0; kk < KB; kk++) {
             const uint32_t g = (k0 + kk) * kSmallThreads + tid;
             const uint32_t L = g / LG, q = g % LG;
             uint32_t s_ = 0, b = 0;
             if (g < n_groups) {
-                // the line's change bits (inside the bitmap section: bits past
-                // n_c were refused, so they are zero)
-                bool touched;
-                if constexpr (W == 2) {
-                    const uint64_t lb = *reinterpret_cast<const uint64_t*>(S.stage + bmo + 8 * L);
-                    touched = lb != 0;
-                    b = uint32_t(lb >> (8 * q)) & GM;
-                } else if constexpr (W == 1) {
-                    const uint4 lb = *reinterpret_cast<const uint4*>(S.stage + bmo + 16 * L);
-                    touched = (lb.x | lb.y | lb.z | lb.w) != 0;
-                    const uint32_t wv = (q & 4u) ? ((q & 2u) ? lb.w : lb.z) : ((q & 2u) ? lb.y : lb.x);
-                    b = (wv >> (16 * (q & 1u))) & GM;
-                } else {
-                    const uint32_t lb = *reinterpret_cast<const uint32_t*>(S.stage + bmo + 4 * L);
-                    touched = lb != 0;
-                    b = (lb >> (4 * q)) & GM;
+                bool touched = line_bits(bmo, L, q, b);
+                if (pair) {
+                    // the pair's groups are disjoint: a group is the XOR
+                    // record's, the overwrite record's or neither's
+                    uint32_t b2;
+                    touched |= line_bits(bmo2, L, q, b2);
+                    if (b2) {
+                        b = b2;
+                        ob |= 1u << kk;
+                    }
                 }
                 // a line that may not be written whole (the chunk's other
                 // record marks it, or it passes the chunk's end): this
@@ -1864,118 +1902,46 @@ __device__ __forceinline__ void apply_lines(const SmallShared& S, uint8_t* dst, 
         for (uint32_t kk = 0; kk < KB; kk++) {
             if (!st[kk]) continue;
             const uint32_t g = (k0 + kk) * kSmallThreads + tid;
+            const bool ow2 = (ob >> kk) & 1u;
+            const bool x = ow2 ? false : is_xor;
             uint64_t val0 = 0, val1 = 0, msk0 = 0, msk1 = 0;
             if (gb[kk]) {
-                // record index of the group's first change: the changes before
-                // its slice plus those of the slice's earlier groups
-                const uint32_t sl = g / GT, nb = (g % GT) * V;
-                uint32_t j = S.jpre[sl];
-#pragma unroll
-                for (uint32_t i = 0; i < BB / 4; i++) {
-                    const uint32_t wd = *reinterpret_cast<const uint32_t*>(S.stage + bmo + sl * BB + 4 * i);
-                    const uint32_t m = nb >= 32 * (i + 1) ? 0xFFFFFFFFu
-                                                           : (nb <= 32 * i ? 0u : ((1u << (nb - 32 * i)) - 1u));
-                    j += __popc(wd & m);
+                if (ow2) {
+                    uint32_t j = first_index(bmo2, S.jpre2[g / GT], g);
+                    group_value<W>(S, gb[kk], j, lo2, lo2 + pk2, lo2 + pk2, pk2, hm2, false, val0, val1, msk0,
+                                   msk1);
+                } else {
+                    uint32_t j = first_index(bmo, S.jpre[g / GT], g);
+                    group_value<W>(S, gb[kk], j, lo, hi, pres, pk, hm, is_xor, val0, val1, msk0, msk1);
                 }
-                group_value<W>(S, gb[kk], j, lo, hi, pres, pk, hm, is_xor, val0, val1, msk0, msk1);
             }
             uint8_t* gp = dst + uint64_t(g) * 16;
             if (st[kk] == 1) {
-                *reinterpret_cast<v4u*>(gp) = gb[kk] ? patch16(v[kk], is_xor, val0, val1, msk0, msk1) : v[kk];
+                *reinterpret_cast<v4u*>(gp) = gb[kk] ? patch16(v[kk], x, val0, val1, msk0, msk1) : v[kk];
             } else if ((g + 1) * V <= n_c) {
-                *reinterpret_cast<v4u*>(gp) = patch16(*reinterpret_cast<const v4u*>(gp), is_xor, val0, val1, msk0, msk1);
+                *reinterpret_cast<v4u*>(gp) = patch16(*reinterpret_cast<const v4u*>(gp), x, val0, val1, msk0, msk1);
             } else {
-                patch_elems<W>(dst, g, gb[kk], n_c, is_xor, val0, val1);
+                patch_elems<W>(dst, g, gb[kk], n_c, x, val0, val1);
             }
         }
     }
 }
 
-template <int W>
-__device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t r, uint32_t n_c) {
-    constexpr uint32_t V = 16 / W;                        // elements (= bitmap bits) per group
-    constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;  // groups per thread (16)
-    constexpr uint32_t BB = GT * V / 8;                   // bitmap bytes per thread (8, 16 or 32)
-    constexpr uint32_t NW = BB / 4;                       // ... in 32-bit words
-    constexpr uint32_t GPW = 32 / V;                      // groups per bitmap word
-    constexpr uint32_t GM = (V == 16) ? 0xFFFFu : ((1u << V) - 1u);
-    const uint32_t tid = threadIdx.x;
-    const uint32_t K = S.ent[2];
-    const uint32_t kind = S.ent[3] & 0xFF, hm = (S.ent[3] >> 8) & 0xFF;
-    const uint64_t off = uint64_t(S.ent[4]) | (uint64_t(S.ent[5]) << 32);
-    const uint32_t sz = S.ent[6], H = S.ent[7];
-    const uint32_t bm = dpad16((n_c + 7) / 8);
-    const uint32_t layout = S.ent[3] >> 24;   // bitmap or index list (checked by entry_ok)
-    const uint32_t lo = layout == DCR_LAYOUT_LIST ? dpad16(2 * K) : bm;
-    const uint32_t pres = lo + dpad16(K);
-    const uint32_t hi = hm == DCR_HI_SPARSE ? pres + dpad16((K + 7) / 8) : pres;
-
-    // stage the record; for line mode beside the chunk's other record, flag
-    // the lines that record's bitmap marks (V bitmap bytes per line)
-    const uint4* src = reinterpret_cast<const uint4*>(a.payload + off);
-    for (uint32_t q = tid; q < sz / 16; q += kSmallThreads)   // read once: non-temporal
-        reinterpret_cast<v4u*>(S.stage)[q] =
-            __builtin_nontemporal_load(reinterpret_cast<gv4p>(reinterpret_cast<uintptr_t>(src)) + q);
-    if (S.sib) {
-        const uint4* ssrc = reinterpret_cast<const uint4*>(a.payload + S.sib_off);
-        for (uint32_t q = tid; q < bm / 16; q += kSmallThreads) {
-            const uint4 v = ssrc[q];
-            if constexpr (W == 2) {
-                S.other[2 * q] = (v.x | v.y) != 0;
-                S.other[2 * q + 1] = (v.z | v.w) != 0;
-            } else if constexpr (W == 1) {
-                S.other[q] = (v.x | v.y | v.z | v.w) != 0;
-            } else {
-                S.other[4 * q] = v.x != 0;
-                S.other[4 * q + 1] = v.y != 0;
-                S.other[4 * q + 2] = v.z != 0;
-                S.other[4 * q + 3] = v.w != 0;
-            }
-        }
-    }
-    if (tid == 0) S.bad = 0;
-    map_table<W>(a, S);
-    __syncthreads();
-
-    // this thread's bitmap words (bytes at or past bm are other sections: 0);
-    // nothing may be set at or past n_c
-    uint32_t bw[NW];
-    uint32_t cnt = 0;
-    bool bad = false;
-    const uint32_t b0 = tid * BB;
-    // the thread's bitmap slice as whole 64- / 128-bit LDS reads (word reads
-    // at this stride would collide on the banks)
-    uint32_t raw[NW];
-    if (layout == DCR_LAYOUT_LIST) {
-        // the thread's elements [e_lo, e_lo + 8 BB): find the first listed
-        // index at or past e_lo, then set the bits of the indices below the
-        // end; the list must ascend strictly (checked pairwise across the
-        // workgroup); bits past n_c are refused below
-        const uint16_t* lst = reinterpret_cast<const uint16_t*>(S.stage);
-        const uint32_t e_lo = b0 * 8, e_hi = e_lo + BB * 8;
-        uint32_t l = 0, h = K;
-        while (l < h) {
-            const uint32_t m = (l + h) >> 1;
-            if (lst[m] < e_lo) l = m + 1;
-            else h = m;
-        }
-#pragma unroll
-        for (uint32_t i = 0; i < NW; i++) raw[i] = 0;
-        for (uint32_t j = l; j < K && lst[j] < e_hi; j++) {
-            const uint32_t e = lst[j] - e_lo;
-#pragma unroll
-            for (uint32_t i = 0; i < NW; i++) raw[i] |= (e >> 5) == i ? (1u << (e & 31u)) : 0u;
-        }
-        for (uint32_t j = tid; j + 1 < K; j += kSmallThreads)
-            if (lst[j] >= lst[j + 1]) bad = true;
-    } else if constexpr (NW == 2) {
-        const uint2 v = b0 < bm ? *reinterpret_cast<const uint2*>(S.stage + b0) : make_uint2(0, 0);
+// A thread's slice of a staged bitmap (bytes [b0, b0 + 4 NW) of the bitmap
+// at stage offset base, bm bytes long; bytes at or past bm are other
+// sections: read as 0), as whole 64- / 128-bit LDS reads (word reads at
+// this stride would collide on the banks).
+template <uint32_t NW>
+__device__ __forceinline__ void bitmap_slice(const SmallShared& S, uint32_t base, uint32_t b0, uint32_t bm,
+                                             uint32_t (&raw)[NW]) {
+    if constexpr (NW == 2) {
+        const uint2 v = b0 < bm ? *reinterpret_cast<const uint2*>(S.stage + base + b0) : make_uint2(0, 0);
         raw[0] = v.x;
         raw[1] = v.y;
     } else {
 #pragma unroll
         for (uint32_t h = 0; h < NW / 4; h++) {
-            const uint4 v = b0 + 16 * h < bm ? *reinterpret_cast<const uint4*>(S.stage + b0 + 16 * h)
+            const uint4 v = b0 + 16 * h < bm ? *reinterpret_cast<const uint4*>(S.stage + base + b0 + 16 * h)
                                              : make_uint4(0, 0, 0, 0);
             raw[4 * h] = v.x;
             raw[4 * h + 1] = v.y;
@@ -1983,76 +1949,35 @@ __device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShar
             raw[4 * h + 3] = v.w;
         }
     }
+}
+
+// Nothing may be set at or past n_c: such bits make the record bad and are
+// dropped.  Returns the slice's change count.
+template <uint32_t NW>
+__device__ __forceinline__ uint32_t checked_slice(uint32_t (&x)[NW], uint32_t b0, uint32_t n_c, bool& bad) {
+    uint32_t cnt = 0;
 #pragma unroll
     for (uint32_t i = 0; i < NW; i++) {
-        const uint32_t byte = b0 + 4 * i;
-        uint32_t x = raw[i];
-        const uint32_t e0 = byte * 8;
+        const uint32_t e0 = (b0 + 4 * i) * 8;
         const uint32_t valid = e0 >= n_c ? 0u : (n_c - e0 >= 32 ? 0xFFFFFFFFu : ((1u << (n_c - e0)) - 1u));
-        if (x & ~valid) bad = true;
-        x &= valid;
-        bw[i] = x;
-        cnt += __popc(x);
+        if (x[i] & ~valid) bad = true;
+        x[i] &= valid;
+        cnt += __popc(x[i]);
     }
-    // SPARSE: presence words (one per thread), their prefix counts and H
-    const uint32_t n_pw = dpad16((K + 7) / 8) / 4;
-    uint32_t pword = 0;
-    if (hm == DCR_HI_SPARSE && tid < n_pw) {
-        pword = reinterpret_cast<const uint32_t*>(S.stage + pres)[tid];
-        const uint32_t pb = tid * 32;
-        const uint32_t vmask = pb >= K ? 0u : (K - pb >= 32 ? 0xFFFFFFFFu : ((1u << (K - pb)) - 1u));
-        if (pword & ~vmask) bad = true;
-    }
-    uint64_t total;
-    uint32_t j = uint32_t(small_excl_scan(cnt, total, S.scan));
-    if (hm == DCR_HI_SPARSE) {
-        uint64_t ptot;
-        const uint32_t pp = uint32_t(small_excl_scan(__popc(pword), ptot, S.scan));
-        if (tid < n_pw) S.pres_pre[tid] = pp;
-        if (tid == 0 && ptot != H) bad = true;
-    }
-    if (tid == 0 && total != K) bad = true;
-    if (bad) atomicOr(&S.bad, 1u);
-    __syncthreads();
-    if (S.bad) return;   // refused before any write
+    return cnt;
+}
 
-    uint8_t* dst = reinterpret_cast<uint8_t*>(S.dst);
-    const uint32_t pk = dpad16(K);
-    const bool is_xor = kind == DCR_KIND_XOR;
-    // Line mode for records dense enough that most lines hold a change:
-    // touched 128-byte lines are read and written whole.  Only lines no
-    // other writer touches are written whole: the record is the only one of
-    // this call for its chunk, or the chunk's other record (next to it in the
-    // directory; records of a chunk mark disjoint groups) has its bitmap
-    // staged, and lines it marks take the group-by-group update instead.  A
-    // record applied by another call or by the large-record kernel does not
-    // run concurrently.  The chunk is canonical at a 128-byte aligned
-    // address (lines past the chunk's elements are never written whole).
-    // A list record's bitmap is rebuilt past the record in the stage (each
-    // thread stores its checked slice whole, so a slice that straddles the
-    // bitmap's end needs room for all of it), when it fits.
-    const uint32_t bmo = layout == DCR_LAYOUT_LIST ? dpad16(sz) : 0u;
-    const bool line_mode = !a.sharded && (S.solo == 1 || S.sib) && bmo + bm + BB <= kSmallStage &&
-                           uint64_t(K) * kLineDensity >= n_c && (reinterpret_cast<uintptr_t>(dst) & 127u) == 0;
-    if (line_mode) {
-        S.jpre[tid] = j;
-        if (layout == DCR_LAYOUT_LIST && b0 < bm) {
-#pragma unroll
-            for (uint32_t i = 0; i < NW; i++) reinterpret_cast<uint32_t*>(S.stage + bmo + b0)[i] = bw[i];
-        }
-        // lines that may be written whole: inside the chunk's elements and
-        // unmarked by the other record
-        const uint32_t whole_lines = n_c / (8 * V), sib = S.sib;
-        for (uint32_t L = tid; L < kLinesPerChunk; L += kSmallThreads)
-            S.whole[L] = L < whole_lines && !(sib && S.other[L]);
-        __syncthreads();
-        apply_lines<W>(S, dst, n_c, lo, hi, pres, pk, hm, is_xor, bmo);
-        __syncthreads();
-        if (tid == 0 && !a.retry) a.flags[r] = 1;   // visible with the writes at kernel completion
-        return;
-    }
-
-    // read-modify-write of every touched 16-byte group, in element order
+// Read-modify-write of every 16-byte group a thread's bitmap slice bw marks,
+// in element order; j = the record index of the slice's first change.  The
+// record's sections sit at stage offsets lo / pres / hi.
+template <int W, uint32_t NW>
+__device__ __forceinline__ void apply_groups(const ApplyArgs& a, const SmallShared& S, uint8_t* dst, uint32_t n_c,
+                                             const uint32_t (&bw)[NW], uint32_t j, uint32_t lo, uint32_t hi,
+                                             uint32_t pres, uint32_t pk, uint32_t hm, bool is_xor) {
+    constexpr uint32_t V = 16 / W;
+    constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;
+    constexpr uint32_t GPW = 32 / V;
+    constexpr uint32_t GM = (V == 16) ? 0xFFFFu : ((1u << V) - 1u);
 #pragma unroll
     for (uint32_t wi = 0; wi < NW; wi++) {
         uint32_t wv = bw[wi];
@@ -2060,7 +1985,7 @@ __device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShar
             const uint32_t gi = uint32_t(__ffs(wv) - 1) / V;
             uint32_t b = (wv >> (gi * V)) & GM;
             wv &= ~(GM << (gi * V));
-            const uint32_t g = tid * GT + wi * GPW + gi;
+            const uint32_t g = threadIdx.x * GT + wi * GPW + gi;
             uint64_t val0, val1, msk0, msk1;
             const uint32_t bcopy = b;
             group_value<W>(S, b, j, lo, hi, pres, pk, hm, is_xor, val0, val1, msk0, msk1);
@@ -2090,8 +2015,182 @@ __device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShar
             }
         }
     }
+}
+
+template <int W, bool PAIRS>
+__device__ __forceinline__ void apply_small_record(const ApplyArgs& a, SmallShared& S, uint64_t r, uint32_t n_c) {
+    constexpr uint32_t V = 16 / W;                        // elements (= bitmap bits) per group
+    constexpr uint32_t GT = kVecsPerChunk / kSmallThreads;  // groups per thread (16)
+    constexpr uint32_t BB = GT * V / 8;                   // bitmap bytes per thread (8, 16 or 32)
+    constexpr uint32_t NW = BB / 4;                       // ... in 32-bit words
+    const uint32_t tid = threadIdx.x;
+    const uint32_t K = S.ent[2];
+    const uint32_t kind = S.ent[3] & 0xFF, hm = (S.ent[3] >> 8) & 0xFF;
+    const uint64_t off = uint64_t(S.ent[4]) | (uint64_t(S.ent[5]) << 32);
+    const uint32_t sz = S.ent[6], H = S.ent[7];
+    const uint32_t bm = dpad16((n_c + 7) / 8);
+    const uint32_t layout = S.ent[3] >> 24;   // bitmap or index list (checked by entry_ok)
+    const uint32_t lo = layout == DCR_LAYOUT_LIST ? dpad16(2 * K) : bm;
+    const uint32_t pres = lo + dpad16(K);
+    const uint32_t hi = hm == DCR_HI_SPARSE ? pres + dpad16((K + 7) / 8) : pres;
+
+    // stage the record (and a fused pair's overwrite record right after it);
+    // for line mode beside the chunk's other record, flag the lines that
+    // record's bitmap marks (V bitmap bytes per line)
+    const uint4* src = reinterpret_cast<const uint4*>(a.payload + off);
+    for (uint32_t q = tid; q < sz / 16; q += kSmallThreads)   // read once: non-temporal
+        reinterpret_cast<v4u*>(S.stage)[q] =
+            __builtin_nontemporal_load(reinterpret_cast<gv4p>(reinterpret_cast<uintptr_t>(src)) + q);
+    const uint32_t fused = PAIRS ? S.fused : 0u;
+    if (fused) {
+        const uint64_t off2 = uint64_t(S.ent2[4]) | (uint64_t(S.ent2[5]) << 32);
+        const uint4* src2 = reinterpret_cast<const uint4*>(a.payload + off2);
+        for (uint32_t q = tid; q < S.ent2[6] / 16; q += kSmallThreads)
+            reinterpret_cast<v4u*>(S.stage + sz)[q] =
+                __builtin_nontemporal_load(reinterpret_cast<gv4p>(reinterpret_cast<uintptr_t>(src2)) + q);
+    }
+    if (S.sib) {
+        const uint4* ssrc = reinterpret_cast<const uint4*>(a.payload + S.sib_off);
+        for (uint32_t q = tid; q < bm / 16; q += kSmallThreads) {
+            const uint4 v = ssrc[q];
+            if constexpr (W == 2) {
+                S.other[2 * q] = (v.x | v.y) != 0;
+                S.other[2 * q + 1] = (v.z | v.w) != 0;
+            } else if constexpr (W == 1) {
+                S.other[q] = (v.x | v.y | v.z | v.w) != 0;
+            } else {
+                S.other[4 * q] = v.x != 0;
+                S.other[4 * q + 1] = v.y != 0;
+                S.other[4 * q + 2] = v.z != 0;
+                S.other[4 * q + 3] = v.w != 0;
+            }
+        }
+    }
+    if (tid == 0) S.bad = S.bad2 = 0;
+    map_table<W>(a, S);
     __syncthreads();
-    if (tid == 0 && !a.retry) a.flags[r] = 1;   // visible with the writes at kernel completion
+
+    // this thread's bitmap words; nothing may be set at or past n_c
+    bool bad = false;
+    const uint32_t b0 = tid * BB;
+    uint32_t bw[NW];
+    if (layout == DCR_LAYOUT_LIST) {
+        // the thread's elements [e_lo, e_lo + 8 BB): find the first listed
+        // index at or past e_lo, then set the bits of the indices below the
+        // end; the list must ascend strictly (checked pairwise across the
+        // workgroup); bits past n_c are refused below
+        const uint16_t* lst = reinterpret_cast<const uint16_t*>(S.stage);
+        const uint32_t e_lo = b0 * 8, e_hi = e_lo + BB * 8;
+        uint32_t l = 0, h = K;
+        while (l < h) {
+            const uint32_t m = (l + h) >> 1;
+            if (lst[m] < e_lo) l = m + 1;
+            else h = m;
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < NW; i++) bw[i] = 0;
+        for (uint32_t j = l; j < K && lst[j] < e_hi; j++) {
+            const uint32_t e = lst[j] - e_lo;
+#pragma unroll
+            for (uint32_t i = 0; i < NW; i++) bw[i] |= (e >> 5) == i ? (1u << (e & 31u)) : 0u;
+        }
+        for (uint32_t j = tid; j + 1 < K; j += kSmallThreads)
+            if (lst[j] >= lst[j + 1]) bad = true;
+    } else {
+        bitmap_slice<NW>(S, 0, b0, bm, bw);
+    }
+    const uint32_t cnt = checked_slice<NW>(bw, b0, n_c, bad);
+    // a fused pair's overwrite record (bitmap layout, staged at sz): its own
+    // slice and checks
+    uint32_t bw2[NW];
+    bool bad2 = false;
+#pragma unroll
+    for (uint32_t i = 0; i < NW; i++) bw2[i] = 0;
+    if (fused) bitmap_slice<NW>(S, sz, b0, bm, bw2);
+    const uint32_t cnt2 = checked_slice<NW>(bw2, b0, n_c, bad2);
+    // SPARSE: presence words (one per thread), their prefix counts and H
+    const uint32_t n_pw = dpad16((K + 7) / 8) / 4;
+    uint32_t pword = 0;
+    if (hm == DCR_HI_SPARSE && tid < n_pw) {
+        pword = reinterpret_cast<const uint32_t*>(S.stage + pres)[tid];
+        const uint32_t pb = tid * 32;
+        const uint32_t vmask = pb >= K ? 0u : (K - pb >= 32 ? 0xFFFFFFFFu : ((1u << (K - pb)) - 1u));
+        if (pword & ~vmask) bad = true;
+    }
+    // both records' counts in one scan, as the two 32-bit halves (a chunk's
+    // changes stay far below 2^32)
+    uint64_t total;
+    const uint64_t jj = small_excl_scan(uint64_t(cnt) | (uint64_t(cnt2) << 32), total, S.scan);
+    const uint32_t j = uint32_t(jj), j2 = uint32_t(jj >> 32);
+    if (hm == DCR_HI_SPARSE) {
+        uint64_t ptot;
+        const uint32_t pp = uint32_t(small_excl_scan(__popc(pword), ptot, S.scan));
+        if (tid < n_pw) S.pres_pre[tid] = pp;
+        if (tid == 0 && ptot != H) bad = true;
+    }
+    if (tid == 0 && uint32_t(total) != K) bad = true;
+    if (tid == 0 && fused && uint32_t(total >> 32) != S.ent2[2]) bad2 = true;
+    if (bad) atomicOr(&S.bad, 1u);
+    if (bad2) atomicOr(&S.bad2, 1u);
+    __syncthreads();
+    // a malformed record is refused before any write of its own
+    const bool ok = S.bad == 0, ok2 = fused && S.bad2 == 0;
+    if (!ok && !ok2) return;
+
+    uint8_t* dst = reinterpret_cast<uint8_t*>(S.dst);
+    // a fused pair's overwrite record (the format keeps a chunk's two
+    // records to disjoint 16-byte groups): its sections in the stage
+    const uint32_t K2 = S.ent2[2], hm2 = (S.ent2[3] >> 8) & 0xFF;
+    const uint32_t lo2 = sz + bm, pk2 = dpad16(K2);
+    if (!ok) {
+        // this record refused: the overwrite record alone
+        apply_groups<W, NW>(a, S, dst, n_c, bw2, j2, lo2, lo2 + pk2, lo2 + pk2, pk2, hm2, false);
+        __syncthreads();
+        if (tid == 0) a.flags[r + 1] = 1;   // never a retry
+        return;
+    }
+    const uint32_t pk = dpad16(K);
+    const bool is_xor = kind == DCR_KIND_XOR;
+    // Line mode for records dense enough that most lines hold a change:
+    // touched 128-byte lines are read and written whole.  Only lines no
+    // other writer touches are written whole: the record is the only one of
+    // this call for its chunk, or the chunk's other record (next to it in the
+    // directory; records of a chunk mark disjoint groups) has its bitmap
+    // staged, and lines it marks take the group-by-group update instead.  A
+    // record applied by another call or by the large-record kernel does not
+    // run concurrently.  The chunk is canonical at a 128-byte aligned
+    // address (lines past the chunk's elements are never written whole).
+    // A list record's bitmap is rebuilt past the record in the stage (each
+    // thread stores its checked slice whole, so a slice that straddles the
+    // bitmap's end needs room for all of it), when it fits.
+    // A fused pair's two records are both this workgroup's: every touched
+    // line may be written whole, each group patched from its own record.
+    const uint32_t bmo = layout == DCR_LAYOUT_LIST ? dpad16(sz) : 0u;
+    const bool line_mode = !a.sharded && (S.solo == 1 || S.sib || fused) && bmo + bm + BB <= kSmallStage &&
+                           uint64_t(K) * kLineDensity >= n_c && (reinterpret_cast<uintptr_t>(dst) & 127u) == 0;
+    if (!line_mode && ok2) apply_groups<W, NW>(a, S, dst, n_c, bw2, j2, lo2, lo2 + pk2, lo2 + pk2, pk2, hm2, false);
+    if (line_mode) {
+        S.jpre[tid] = j;
+        S.jpre2[tid] = j2;
+        if (layout == DCR_LAYOUT_LIST && b0 < bm) {
+#pragma unroll
+            for (uint32_t i = 0; i < NW; i++) reinterpret_cast<uint32_t*>(S.stage + bmo + b0)[i] = bw[i];
+        }
+        // lines that may be written whole: inside the chunk's elements and
+        // unmarked by the other record
+        const uint32_t whole_lines = n_c / (8 * V), sib = S.sib;
+        for (uint32_t L = tid; L < kLinesPerChunk; L += kSmallThreads)
+            S.whole[L] = L < whole_lines && !(sib && S.other[L]);
+        __syncthreads();
+        apply_lines<W>(S, dst, n_c, lo, hi, pres, pk, hm, is_xor, bmo, ok2, sz, lo2, pk2, hm2);
+    } else {
+        apply_groups<W, NW>(a, S, dst, n_c, bw, j, lo, hi, pres, pk, hm, is_xor);
+    }
+    __syncthreads();
+    if (tid == 0 && !a.retry) {   // visible with the writes at kernel completion
+        a.flags[r] = 1;
+        if (ok2) a.flags[r + 1] = 1;
+    }
 }
 
 // Thread 0 of a small-record workgroup: the other records of this call for
@@ -2134,9 +2233,62 @@ __device__ __forceinline__ Neighbours chunk_neighbours(const uint4* de, uint64_t
     return o;
 }
 
+// Thread 0 of a small-record workgroup: whether its record belongs to a
+// fused pair, a chunk's XOR record and, next in the directory, its overwrite
+// record, both in bitmap layout, structurally valid, staged together within
+// kSmallStage, with no other record of this call for the chunk, in a
+// canonical-layout apply.  The XOR record's workgroup applies both (and
+// owns both records' flags and counts); the overwrite record's workgroup
+// does nothing.  Both reach the same answer from the same entries.  e: the
+// record's entry (already checked); pv / nx: the first halves of the
+// previous / next entries (when they exist).  Returns 1 for the XOR record
+// of a fused pair, with its partner's entry in e2; 2 for the overwrite
+// record; 0 otherwise.
+__device__ __forceinline__ uint32_t pair_role(const ApplyArgs& a, const uint4* de, uint64_t r, const uint32_t (&e)[8],
+                                              bool has_prev, bool has_next, uint4 pv, uint4 nx, uint32_t (&e2)[8]) {
+    if (a.sharded || a.retry) return 0;
+    const uint64_t end = a.first + gridDim.x;
+    const uint32_t t = e[0], c = e[1];
+    const bool is_xor = (e[3] & 0xFF) == DCR_KIND_XOR;
+    uint32_t x[8], o[8];
+    if (is_xor) {
+        if (!has_next || nx.x != t || nx.y != c) return 0;
+        if (has_prev && pv.x == t && pv.y == c) return 0;
+        if (r + 2 < end) {
+            const uint4 f = de[4];
+            if (f.x == t && f.y == c) return 0;
+        }
+        const uint4 n1 = de[3];
+        const uint32_t oo[8] = {nx.x, nx.y, nx.z, nx.w, n1.x, n1.y, n1.z, n1.w};
+        for (int i = 0; i < 8; i++) x[i] = e[i], o[i] = oo[i];
+    } else {
+        if (!has_prev || pv.x != t || pv.y != c) return 0;
+        if (has_next && nx.x == t && nx.y == c) return 0;
+        if (r >= a.first + 2) {
+            const uint4 f = de[-4];
+            if (f.x == t && f.y == c) return 0;
+        }
+        const uint4 p1 = de[-1];
+        const uint32_t xx[8] = {pv.x, pv.y, pv.z, pv.w, p1.x, p1.y, p1.z, p1.w};
+        for (int i = 0; i < 8; i++) x[i] = xx[i], o[i] = e[i];
+    }
+    if ((x[3] & 0xFF) != DCR_KIND_XOR || (o[3] & 0xFF) != DCR_KIND_OW) return 0;
+    if ((x[3] >> 24) != DCR_LAYOUT_BITMAP || (o[3] >> 24) != DCR_LAYOUT_BITMAP) return 0;
+    uint32_t nx_c, no_c;
+    if (!entry_ok(a, x, nx_c) || !entry_ok(a, o, no_c)) return 0;
+    if (uint64_t(x[6]) + o[6] > kSmallStage) return 0;
+    const uint32_t Kx = x[2], hmx = (x[3] >> 8) & 0xFF;
+    if (hmx == DCR_HI_SPARSE && dpad16((Kx + 7) / 8) / 4 > kSmallThreads) return 0;
+    for (int i = 0; i < 8; i++) e2[i] = o[i];
+    return is_xor ? 1u : 2u;
+}
+
 // Seven workgroups per compute unit: a small record's time is mostly the
 // latency of its dependent loads (entry, record, lines), so more resident
-// workgroups pay for the few registers spilled to reach them.
+// workgroups pay for the few registers spilled to reach them.  PAIRS: fused
+// pairs are looked for (an apply; a retry's stream holds overwrite records
+// only, and its build of the kernel carries none of the pair code).
+template <bool PAIRS>
 __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(7, 8))) void apply_small_kernel(
     ApplyArgs a) {
     __shared__ SmallShared S;
@@ -2156,17 +2308,41 @@ __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(7
         const uint8_t done = a.retry ? uint8_t(0) : a.flags[r];
         const uint8_t* cbase = (!a.sharded && e0.x < a.n_tensors) ? a.canon[e0.x] : nullptr;
         uint32_t e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+        uint32_t e2[8];
+        uint32_t st, fused = 0, pskip = 0;
+        uint64_t rec = r;
+        const bool valid = entry_ok(a, e, n_c);
+        const uint32_t role = PAIRS && valid ? pair_role(a, de, r, e, has_prev, has_next, pv, nx, e2) : 0u;
+        if (role == 1) {
+            // the XOR record of a fused pair: both records' dedup flags decide
+            // which of the two this workgroup applies
+            const bool done2 = a.flags[r + 1] != 0;
+            if (done && done2) {
+                pskip = 1;
+            } else if (done) {
+                // only the overwrite record, alone
+                pskip = 1;
+                rec = r + 1;
+                for (int i = 0; i < 8; i++) e[i] = e2[i];
+            } else if (done2) {
+                pskip = 1;
+            } else {
+                fused = 1;
+                for (int i = 0; i < 8; i++) S.ent2[i] = e2[i];
+            }
+        }
         for (int i = 0; i < 8; i++) S.ent[i] = e[i];
-        uint32_t st;
-        if (!entry_ok(a, e, n_c)) {
+        if (!valid) {
             st = 0;
-        } else if (done) {
+        } else if (role == 2) {
+            st = 4;
+        } else if (done && rec == r) {
             st = 1;
         } else {
             const uint32_t K = e[2], hm = (e[3] >> 8) & 0xFF;
             const bool fits = e[6] <= kSmallStage && (hm != DCR_HI_SPARSE || dpad16((K + 7) / 8) / 4 <= kSmallThreads);
             st = fits ? 2 : 3;
-            if (!fits) a.big_list[atomicAdd(a.big_count, 1u)] = uint32_t(r - a.first);
+            if (!fits) a.big_list[atomicAdd(a.big_count, 1u)] = uint32_t(rec - a.first);
             else map_chunk(a, S, e[0], e[1]);
             const Neighbours nb = chunk_neighbours(de, r, a.first, a.first + gridDim.x, a.payload_bytes, e[0], e[1],
                                                    e[3] & 0xFF, n_c, has_prev, has_next, pv, nx);
@@ -2175,29 +2351,39 @@ __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(7
             // line mode beside the other record, when this one is dense
             // enough for line mode
             S.sib = nb.solo == 2 && !a.sharded && uint64_t(K) * kLineDensity >= n_c ? 1u : 0u;
+            if (rec != r) S.solo = S.sib = 0;   // a pair's overwrite record alone: the group path
+            if (fused) S.sib = 0;               // both of the pair's records are this workgroup's
             S.dst = cbase ? reinterpret_cast<uint64_t>(cbase) + uint64_t(e[1]) * kChunkBytes : 0;
         }
         S.state = st;
         S.n_c = n_c;
+        S.fused = fused;
+        S.pskip = pskip;
+        S.rec = rec;
     }
     __syncthreads();
     const uint32_t st = S.state;
     n_c = S.n_c;
-    if (st == 3) return;
-    if (st == 1) {
-        if (threadIdx.x == 0) atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_skipped), 1ull);
-        return;
-    }
+    if (st >= 3) return;   // deferred, or applied by its pair's XOR record
+    const uint64_t rec = S.rec;
+    if (threadIdx.x == 0 && (S.pskip || st == 1))
+        atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_skipped),
+                  (unsigned long long)((st == 1 ? 1u : 0u) + S.pskip));
+    if (st == 1) return;
     if (st == 2) {
         const uint32_t w = (S.ent[3] >> 16) & 0xFF;
-        if (w == 2) apply_small_record<2>(a, S, r, n_c);
-        else if (w == 1) apply_small_record<1>(a, S, r, n_c);
-        else apply_small_record<4>(a, S, r, n_c);
+        if (w == 2) apply_small_record<2, PAIRS>(a, S, rec, n_c);
+        else if (w == 1) apply_small_record<1, PAIRS>(a, S, rec, n_c);
+        else apply_small_record<4, PAIRS>(a, S, rec, n_c);
+        if (threadIdx.x == 0 && PAIRS && S.fused && S.bad2) {
+            atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_invalid), 1ull);
+            atomicMin(reinterpret_cast<unsigned long long*>(&a.result->first_invalid), (unsigned long long)(rec + 1));
+        }
         if (!S.bad) return;
     }
     if (threadIdx.x == 0) {
         atomicAdd(reinterpret_cast<unsigned long long*>(&a.result->n_invalid), 1ull);
-        atomicMin(reinterpret_cast<unsigned long long*>(&a.result->first_invalid), (unsigned long long)r);
+        atomicMin(reinterpret_cast<unsigned long long*>(&a.result->first_invalid), (unsigned long long)rec);
     }
 }
 
@@ -2361,7 +2547,8 @@ static int32_t launch_apply(const dcr_plan* plan, void* const* canon, const dcr_
         mark(true, s);
         if (n <= p.big_cap) {
             // small records with many per compute unit; the rest deferred
-            hipLaunchKernelGGL(apply_small_kernel, dim3(uint32_t(n)), dim3(kSmallThreads), 0, s, a);
+            if (a.retry) hipLaunchKernelGGL(apply_small_kernel<false>, dim3(uint32_t(n)), dim3(kSmallThreads), 0, s, a);
+            else hipLaunchKernelGGL(apply_small_kernel<true>, dim3(uint32_t(n)), dim3(kSmallThreads), 0, s, a);
             hipLaunchKernelGGL(apply_big_kernel, dim3(uint32_t(std::min<uint64_t>(n, 2 * cu_count()))), dim3(kThreads),
                                0, s, a);
         } else {

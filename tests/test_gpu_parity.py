@@ -769,13 +769,14 @@ def test_apply_line_mode_edges(gh, orc, align):
 
 @pytest.mark.parametrize("align", [16, 256])
 def test_apply_pairs(gh, orc, align):
-    """Chunks with an XOR and an overwrite record (block-scaled tensors):
-    the two records' workgroups run at once, each writing whole only the
-    lines the other record leaves alone.  Each case equals the oracle's
-    apply from the same state and flags, byte for byte:
-    every record fresh; the overwrite records of some pairs and the XOR
-    records of others already flagged (skipped); the XOR record of one pair
-    and the overwrite record of another corrupted (refused, while the other
+    """Chunks with an XOR and an overwrite record (block-scaled tensors): the
+    XOR record's workgroup applies both (the overwrite record's groups, then
+    its own, whole lines only where the overwrite record marks none).  Each
+    case equals the oracle's apply from the same state and flags, byte for
+    byte, with the same counts: every record fresh; the overwrite records of
+    some pairs, the XOR records of others and both records of others already
+    flagged (skipped); the XOR record of one pair, the overwrite record of
+    another and both records of a third corrupted (refused, while the other
     record of the pair applies); and calls split between the two records of
     a pair.  Canonical tensors at 16-byte offsets (group path) and at
     256-byte offsets (line mode)."""
@@ -821,13 +822,20 @@ def test_apply_pairs(gh, orc, align):
         f[i + 1] = 1
     for i in pairs[1::3]:
         f[i] = 1
+    for i in pairs[2::6]:
+        f[i] = f[i + 1] = 1
     res = check("flagged", f)
     assert int(res[0]["n_skipped"]) == int(f.sum())
+    assert int(res[0]["n_applied"]) == n - int(f.sum())
     bad = p.copy()
     bad[ents[pairs[0]]["off"]] ^= 0x01           # an XOR record's bitmap: popcount no longer K
     bad[ents[pairs[1] + 1]["off"]] ^= 0x01       # an overwrite record's bitmap
-    res = check("corrupt", zero, payload=bad, refused=(pairs[0], pairs[1] + 1))
-    assert int(res[0]["n_invalid"]) == 2 and int(res[0]["first_invalid"]) == pairs[0]
+    bad[ents[pairs[2]]["off"]] ^= 0x01           # both records of a third pair
+    bad[ents[pairs[2] + 1]["off"]] ^= 0x01
+    refused = (pairs[0], pairs[1] + 1, pairs[2], pairs[2] + 1)
+    res = check("corrupt", zero, payload=bad, refused=refused)
+    assert int(res[0]["n_invalid"]) == 4 and int(res[0]["first_invalid"]) == pairs[0]
+    assert int(res[0]["n_applied"]) == n - 4
     i = pairs[len(pairs) // 2]
     check("split", zero, calls=((0, i + 1), (i + 1, n - i - 1)))
 
