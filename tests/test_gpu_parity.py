@@ -792,11 +792,13 @@ def test_apply_pairs(gh, orc, align):
     assert len(pairs) >= 10, len(pairs)
     co = [np.ascontiguousarray(x).view(np.uint8).reshape(-1).copy() for x in olds]
 
-    def check(what, flags0, payload=None, calls=((0, None),), refused=()):
+    def check(what, flags0, payload=None, calls=((0, None),), refused=(), dirb=None):
         # the oracle refuses a whole stream with a bad record: its expected
         # state skips the refused records instead (flagged beforehand)
         if payload is not None:
             sb.payload[:len(payload)].copy_(torch.from_numpy(payload))
+        if dirb is not None:
+            sb.dir[:len(dirb)].copy_(torch.from_numpy(dirb))
         buf, canon = g.canon_alloc(co, align=align)
         fl = torch.from_numpy(flags0.copy()).cuda()
         res = [g.apply(canon, hdr, sb, fl, f0, cnt) for f0, cnt in calls]
@@ -812,6 +814,8 @@ def test_apply_pairs(gh, orc, align):
         assert np.array_equal(fl.cpu().numpy(), fo), what
         if payload is not None:
             sb.payload[:len(p)].copy_(torch.from_numpy(p))
+        if dirb is not None:
+            sb.dir[:len(d)].copy_(torch.from_numpy(d))
         return res
 
     zero = np.zeros(n, np.uint8)
@@ -836,6 +840,16 @@ def test_apply_pairs(gh, orc, align):
     res = check("corrupt", zero, payload=bad, refused=refused)
     assert int(res[0]["n_invalid"]) == 4 and int(res[0]["first_invalid"]) == pairs[0]
     assert int(res[0]["n_applied"]) == n - 4
+    # a directory entry of a pair that fails its structural checks (K one
+    # too many): not a fused pair, that record refused by its own workgroup
+    # and the other record applied by its own
+    bad_dir = d.copy()
+    for i in (pairs[3] + 1, pairs[4]):
+        k = bad_dir[32 * i + 8:32 * i + 12].view("<u4")
+        k[0] += 1
+    res = check("bad entries", zero, dirb=bad_dir, refused=(pairs[3] + 1, pairs[4]))
+    assert int(res[0]["n_invalid"]) == 2 and int(res[0]["first_invalid"]) == pairs[3] + 1
+    assert int(res[0]["n_applied"]) == n - 2
     i = pairs[len(pairs) // 2]
     check("split", zero, calls=((0, i + 1), (i + 1, n - i - 1)))
 
