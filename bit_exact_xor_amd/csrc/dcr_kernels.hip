@@ -907,7 +907,10 @@ __device__ __forceinline__ void inorder_tile(const EncodeArgs& a, EncodeShared& 
 
 // In-order encode (no staging area): one workgroup per tile, tiles claimed
 // in increasing order from a counter, so every tile a look-back waits on
-// belongs to a workgroup that is already running.
+// belongs to a workgroup that is already running.  ONE_W: every tile of the
+// plan has elements of ONE_W bytes (only that width's code is built, free of
+// the register spills the three widths together cause); 0: any width.
+template <int ONE_W>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_kernel(EncodeArgs a) {
     __shared__ EncodeShared S;
     if (threadIdx.x == 0) S.next = atomicAdd(a.counter + kCtrTile, 1u);
@@ -919,9 +922,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         return;
     }
     const TileCtx c = tile_ctx(a, tile);
-    if (c.w == 2) inorder_tile<2>(a, S, c);
-    else if (c.w == 1) inorder_tile<1>(a, S, c);
-    else inorder_tile<4>(a, S, c);
+    if constexpr (ONE_W != 0) {
+        inorder_tile<ONE_W>(a, S, c);
+    } else {
+        if (c.w == 2) inorder_tile<2>(a, S, c);
+        else if (c.w == 1) inorder_tile<1>(a, S, c);
+        else inorder_tile<4>(a, S, c);
+    }
 }
 
 // Staged encode of one tile of W-byte elements: write the records to the
@@ -2741,7 +2748,11 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
                 launch_direct(i, lists != 0, compact, n, list);
             }
         } else if (t1 > t0) {
-            hipLaunchKernelGGL(encode_kernel, dim3(t1 - t0), dim3(kThreads), 0, s, a);
+            const dim3 g(t1 - t0);
+            if (p.one_width == 2) hipLaunchKernelGGL(encode_kernel<2>, g, dim3(kThreads), 0, s, a);
+            else if (p.one_width == 1) hipLaunchKernelGGL(encode_kernel<1>, g, dim3(kThreads), 0, s, a);
+            else if (p.one_width == 4) hipLaunchKernelGGL(encode_kernel<4>, g, dim3(kThreads), 0, s, a);
+            else hipLaunchKernelGGL(encode_kernel<0>, g, dim3(kThreads), 0, s, a);
         }
         if (timed) mark(false, s);
         if (staged) {

@@ -158,6 +158,7 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     uint64_t seg_pos = 0;
     std::vector<Run> runs;
     std::vector<uint8_t> is_scale_used(nT, 0);
+    uint32_t widths = 0;   // the element widths of the chunks, OR-ed
     for (uint32_t t = 0; t < nT; t++) {
         const dcr_tensor_desc& d = T[t];
         const uint32_t w = d.elem_bytes;
@@ -234,6 +235,7 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
                 P.slow.push_back(uint32_t(P.chunks.size()));
             }
             P.chunks.push_back(ch);
+            widths |= w;
             // worst-case stream sizes (DELTA or RETRY, whichever is larger)
             const uint64_t n_c = c1 - c0, nb = pad16((n_c + 7) / 8);
             uint64_t worst = nb + w * pad16(n_c);                       // one dense record
@@ -254,6 +256,8 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     // case (about 4 KiB a chunk of 2-byte elements, the records of a chunk
     // with ~1 % of its elements changed), and 16 bytes a partition at least
     P.compact_stage_bytes = std::max<uint64_t>(pad16(P.max_payload_bytes / 16), uint64_t(kStageParts) * 16);
+    // widths are 1, 2 or 4: one bit each
+    P.one_width = (widths == 1 || widths == 2 || widths == 4) ? widths : 0;
     // per-block "scale changed" flag bits, one bit per element of each gating scale tensor
     std::vector<uint64_t> bit_off(nT, 0);
     for (uint32_t s = 0; s < nT; s++) {
