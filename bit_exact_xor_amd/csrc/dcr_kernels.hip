@@ -219,7 +219,7 @@ struct EncodeShared {
     uint64_t pnew[kMaxCachedPieces];
     uint64_t scan[2 * 3 * (kThreads / 64) + 3];
     uint64_t excl;
-    uint64_t claim;
+    uint64_t claim;   // compact staging: the claimed offset; in order: the records' address (0: no room)
     uint32_t next;
 };
 
@@ -625,8 +625,8 @@ __device__ __forceinline__ TileSums scan_tile(EncodeShared& S, uint64_t (&cnt)[3
 // elements that fall in the window into LDS (zeroed first: the zero padding),
 // then the window leaves as 128-bit stores.  ONE: the records fit in one
 // window (no range checks).
-template <int W, bool ONE, bool COMPACT>
-__device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint8_t* cbase, uint32_t w0,
+template <int W, bool ONE, class Dest>
+__device__ __forceinline__ void write_window(EncodeShared& S, const Dest& dest, uint32_t w0,
                                              uint32_t total, uint32_t bm, const uint32_t (&meta)[kVecsPerThread],
                                              const uint64_t (&cnt)[3], const TileSums& t, const RecLayout& L) {
     constexpr uint32_t V = 16 / W;
@@ -748,12 +748,11 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
         }
     }
     __syncthreads();
-    // compact staging: the offset the tile claimed (published by the first
-    // barrier of the window); no room: nothing is copied out
-    if constexpr (COMPACT) {
-        const uint64_t cl = S.claim;
-        if (cl == kNoClaim) return;   // uniform
-        out = cbase + cl;
+    // where the window goes, decided now by every thread (uniform); nowhere:
+    // nothing is copied out
+    uint8_t* const out = dest.at(S, w0);
+    if constexpr (Dest::kMaySkip) {
+        if (!out) return;
     }
     // non-temporal 128-bit stores: the records are read back only after the
     // whole grid (by the fix-up, or by the stream's consumer).  Index lists
@@ -769,24 +768,29 @@ __device__ __forceinline__ void write_window(EncodeShared& S, uint8_t* out, uint
     }
 }
 
-// Write a tile's records (XOR record, then overwrite record) at out: change
-// bitmaps (LSB first), byte planes of the changed elements in element order,
-// zero padding to 16 bytes, assembled in LDS one window at a time.
-// Compact staging (compact set): the records go to the offset thread 0
-// claims first in its workgroup's partition of the staging area (one atomic
-// add on one of kStageParts counters, so no single address takes every
-// tile's atomic); the claim is recorded for the fix-up, and a claim past the
-// partition's end (kNoClaim) writes nothing: the fix-up lists the tile to be
-// encoded again at its place.  The atomic's latency overlaps the window's
-// zeroing; the offset is read from LDS only when the window is copied out.
-template <int W, bool COMPACT>
-__device__ __forceinline__ void write_tile(const EncodeArgs& a, EncodeShared& S, uint8_t* out, uint32_t tile,
-                                           uint32_t n_c, const uint32_t (&meta)[kVecsPerThread],
-                                           const uint64_t (&cnt)[3], const TileSums& t, const RecLayout& L) {
-    const uint32_t bm = dpad16((n_c + 7) / 8);
-    const uint32_t total = L.size_x + L.size_o;
-    uint8_t* cbase = nullptr;
-    if constexpr (COMPACT) {
+// Where a tile's records go.  The record writer calls begin() (every
+// thread) before the first window and at(S, w0) (every thread, uniform
+// result) once a window's bytes are in LDS; with kMaySkip, nullptr means
+// nowhere: nothing is copied out.
+struct SlotDest {   // a fixed address: the tile's staging slot or its place in the payload
+    static constexpr bool kMaySkip = false;
+    uint8_t* out;
+    __device__ __forceinline__ void begin(EncodeShared&) const {}
+    __device__ __forceinline__ uint8_t* at(EncodeShared&, uint32_t) const { return out; }
+};
+
+// Compact staging: the records go to the offset thread 0 claims first in its
+// workgroup's partition of the staging area (one atomic add on one of
+// kStageParts counters, so no single address takes every tile's atomic); the
+// claim is recorded for the fix-up, and a claim past the partition's end
+// (kNoClaim) writes nothing: the fix-up lists the tile to be encoded again at
+// its place.  The atomic's latency overlaps the window's zeroing; the offset
+// is read from LDS (published by the window's barrier) when it is copied out.
+struct CompactDest {
+    static constexpr bool kMaySkip = true;
+    const EncodeArgs& a;
+    uint32_t tile, total;
+    __device__ __forceinline__ void begin(EncodeShared& S) const {
         if (threadIdx.x == 0) {
             const uint32_t part = blockIdx.x & (kStageParts - 1);
             const uint64_t o = atomicAdd(a.stage_ctr + part, (unsigned long long)total);
@@ -794,10 +798,56 @@ __device__ __forceinline__ void write_tile(const EncodeArgs& a, EncodeShared& S,
             a.soff[tile] = cl;
             S.claim = cl;
         }
-        cbase = a.stage;
     }
+    __device__ __forceinline__ uint8_t* at(EncodeShared& S, uint32_t) const {
+        const uint64_t cl = S.claim;
+        return cl == kNoClaim ? nullptr : a.stage + cl;
+    }
+};
+
+// In order: the tile's place in the payload, from the decoupled look-back,
+// run by wave 0 once the first window is in LDS (the wait for predecessors
+// that have not yet published overlaps the window's assembly); S.excl holds
+// the tile's exclusive prefix, and nullptr means the records do not fit the
+// caller's buffers (nothing written).
+struct LookBackDest {
+    static constexpr bool kMaySkip = true;
+    const EncodeArgs& a;
+    uint32_t tile;
+    uint64_t agg;
+    __device__ __forceinline__ void begin(EncodeShared&) const {}
+    __device__ __forceinline__ uint8_t* at(EncodeShared& S, uint32_t w0) const {
+        if (w0 == 0) {
+            if (threadIdx.x < 64) {
+                const uint64_t excl = look_back(a.status, tile, threadIdx.x);
+                if (threadIdx.x == 0) {
+                    if (tile > 0) st_status(a.status + tile, ((excl + agg) << kValShift) | kFlagIncl);
+                    S.excl = excl;
+                    const uint64_t R = excl >> kRecShift, P = (excl & kP16Mask) << 4;
+                    const bool fits = (R + (agg >> kRecShift)) * DCR_DIRENT_BYTES <= a.dir_cap &&
+                                      P + ((agg & kP16Mask) << 4) <= a.payload_cap;
+                    S.claim = fits ? reinterpret_cast<uint64_t>(a.payload) + P : 0;
+                }
+            }
+            __syncthreads();
+        }
+        return reinterpret_cast<uint8_t*>(S.claim);
+    }
+};
+
+// Write a tile's records (XOR record, then overwrite record) where dest
+// says: change bitmaps (LSB first), byte planes of the changed elements in
+// element order, zero padding to 16 bytes, assembled in LDS one window at a
+// time.
+template <int W, class Dest>
+__device__ __forceinline__ void write_tile(EncodeShared& S, const Dest& dest, uint32_t n_c,
+                                           const uint32_t (&meta)[kVecsPerThread], const uint64_t (&cnt)[3],
+                                           const TileSums& t, const RecLayout& L) {
+    const uint32_t bm = dpad16((n_c + 7) / 8);
+    const uint32_t total = L.size_x + L.size_o;
+    dest.begin(S);
     if (total <= kWinBytes) {
-        write_window<W, true, COMPACT>(S, out, cbase, 0, total, bm, meta, cnt, t, L);
+        write_window<W, true>(S, dest, 0, total, bm, meta, cnt, t, L);
         return;
     }
 #pragma nounroll
@@ -811,13 +861,12 @@ __device__ __forceinline__ void write_tile(const EncodeArgs& a, EncodeShared& S,
         cc[1] = cnt[1];
         cc[2] = cnt[2];
         asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(cc[0]), "+v"(cc[1]), "+v"(cc[2]));
-        write_window<W, false, COMPACT>(S, out, cbase, w0, total, bm, m, cc, t, L);
+        write_window<W, false>(S, dest, w0, total, bm, m, cc, t, L);
         __syncthreads();
     }
-    if constexpr (COMPACT) {
-        const uint64_t cl = S.claim;
-        if (cl == kNoClaim) return;   // uniform
-        out = cbase + cl;
+    uint8_t* const out = dest.at(S, total);
+    if constexpr (Dest::kMaySkip) {
+        if (!out) return;   // uniform
     }
     // index lists of records spanning several windows: the windows left their
     // bytes zero; each thread stores its changes' indices over them (the
@@ -866,8 +915,9 @@ __device__ __forceinline__ void skip_tile(const EncodeArgs& a, uint32_t tile, bo
 }
 
 // In-order encode of one tile of W-byte elements (no staging area): publish
-// the aggregate, look back for the exclusive prefix, write the records and
-// directory entries in place.
+// the aggregate, write the records in place (the look-back for the tile's
+// exclusive prefix runs once the first window is assembled), then the
+// directory entries.
 template <int W>
 __device__ __forceinline__ void inorder_tile(const EncodeArgs& a, EncodeShared& S, const TileCtx& c) {
     const uint32_t tid = threadIdx.x;
@@ -889,19 +939,11 @@ __device__ __forceinline__ void inorder_tile(const EncodeArgs& a, EncodeShared& 
         a.tile_info[tile] = tile_counts(t);
     }
     if (nrec == 0) return;   // uniform; an empty tile's aggregate is all it owes
-    if (tid < 64) {
-        const uint64_t excl = look_back(a.status, tile, tid);
-        if (tid == 0) {
-            if (tile > 0) st_status(a.status + tile, ((excl + agg) << kValShift) | kFlagIncl);
-            S.excl = excl;
-        }
-    }
-    __syncthreads();
+    // the look-back runs once the first window is assembled
+    write_tile<W>(S, LookBackDest{a, tile, agg}, c.n_c, meta, cnt, t, L);
+    if (!S.claim) return;   // uniform: the records do not fit the caller's buffers
     const uint64_t R = S.excl >> kRecShift;
     const uint64_t P = (S.excl & kP16Mask) << 4;
-    const uint64_t bytes = (agg & kP16Mask) << 4;
-    if ((R + nrec) * DCR_DIRENT_BYTES > a.dir_cap || P + bytes > a.payload_cap) return;   // uniform
-    write_tile<W, false>(a, S, a.payload + P, tile, c.n_c, meta, cnt, t, L);
     if (tid < nrec) put_dirent(a.dir, R + tid, tid, c.tensor, c.chunk_idx, W, L, t.Kx, t.Ko, P);
 }
 
@@ -951,8 +993,8 @@ __device__ __forceinline__ void staged_tile(const EncodeArgs& a, EncodeShared& S
         a.tile_info[c.tile] = tile_counts(t);
     }
     if (!agg) return;
-    if (a.compact) write_tile<W, true>(a, S, nullptr, c.tile, c.n_c, meta, cnt, t, L);
-    else write_tile<W, false>(a, S, a.stage + a.slots[c.tile], c.tile, c.n_c, meta, cnt, t, L);
+    if (a.compact) write_tile<W>(S, CompactDest{a, c.tile, L.size_x + L.size_o}, c.n_c, meta, cnt, t, L);
+    else write_tile<W>(S, SlotDest{a.stage + a.slots[c.tile]}, c.n_c, meta, cnt, t, L);
 }
 
 // A tile encoded again, straight to its place in the payload (compact
@@ -969,7 +1011,7 @@ __device__ __forceinline__ void redo_tile(const EncodeArgs& a, EncodeShared& S, 
     digest_tile<W>(S, owm, lo, ln, meta, cnt);
     const TileSums t = scan_tile(S, cnt);
     const RecLayout L = rec_layout(W, c.n_c, t.Kx, t.Ko, t.Hx, a.lists);
-    if (t.Kx || t.Ko) write_tile<W, false>(a, S, out, c.tile, c.n_c, meta, cnt, t, L);
+    if (t.Kx || t.Ko) write_tile<W>(S, SlotDest{out}, c.n_c, meta, cnt, t, L);
 }
 
 // Staged encode of the tiles that are not direct (pieces that split
@@ -1057,7 +1099,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         a.tile_agg[c.tile] = agg;
         a.tile_info[c.tile] = tile_counts(t);
     }
-    if (agg) write_tile<W, COMPACT>(a, S, out, c.tile, c.n_c, meta, cnt, t, L);
+    if (!agg) return;   // uniform
+    if constexpr (COMPACT) write_tile<W>(S, CompactDest{a, c.tile, L.size_x + L.size_o}, c.n_c, meta, cnt, t, L);
+    else write_tile<W>(S, SlotDest{out}, c.n_c, meta, cnt, t, L);
 }
 
 // Compact staging, after the fix-up: the tiles whose records found no room
