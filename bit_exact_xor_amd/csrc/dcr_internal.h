@@ -116,7 +116,7 @@ struct Plan {
              ws_agg = 0, ws_info = 0, ws_big = 0, big_cap = 0, ws_soff = 0, ws_bytes = 0;
     std::vector<uint8_t> blob;            // host image of the device tables
     void* dev_tables = nullptr;           // bound by dcr_plan_upload
-    uint32_t one_width = 0;               // the element width of every chunk when they share one, else 0
+    uint32_t widths = 0;                  // the element widths of the chunks, OR-ed (1 | 2 | 4)
 };
 
 void set_error(const std::string& msg);

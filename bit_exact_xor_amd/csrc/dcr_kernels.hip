@@ -949,10 +949,10 @@ __device__ __forceinline__ void inorder_tile(const EncodeArgs& a, EncodeShared& 
 
 // In-order encode (no staging area): one workgroup per tile, tiles claimed
 // in increasing order from a counter, so every tile a look-back waits on
-// belongs to a workgroup that is already running.  ONE_W: every tile of the
-// plan has elements of ONE_W bytes (only that width's code is built, free of
-// the register spills the three widths together cause); 0: any width.
-template <int ONE_W>
+// belongs to a workgroup that is already running.  WIDTHS: the element
+// widths of the plan's tiles (1 | 2 | 4): only their code is built (the
+// three together spill heavily).
+template <int WIDTHS>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void encode_kernel(EncodeArgs a) {
     __shared__ EncodeShared S;
     if (threadIdx.x == 0) S.next = atomicAdd(a.counter + kCtrTile, 1u);
@@ -964,12 +964,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         return;
     }
     const TileCtx c = tile_ctx(a, tile);
-    if constexpr (ONE_W != 0) {
-        inorder_tile<ONE_W>(a, S, c);
+    if constexpr (WIDTHS == 1 || WIDTHS == 2 || WIDTHS == 4) {
+        inorder_tile<WIDTHS>(a, S, c);
     } else {
-        if (c.w == 2) inorder_tile<2>(a, S, c);
-        else if (c.w == 1) inorder_tile<1>(a, S, c);
-        else inorder_tile<4>(a, S, c);
+        if ((WIDTHS & 2) && c.w == 2) inorder_tile<2>(a, S, c);
+        else if ((WIDTHS & 1) && c.w == 1) inorder_tile<1>(a, S, c);
+        else if (WIDTHS & 4) inorder_tile<4>(a, S, c);
     }
 }
 
@@ -2792,11 +2792,16 @@ static int32_t encode_impl(const dcr_plan* plan, const void* const* old_shards, 
                 launch_direct(i, lists != 0, compact, n, list);
             }
         } else if (t1 > t0) {
-            const dim3 g(t1 - t0);
-            if (p.one_width == 2) hipLaunchKernelGGL(encode_kernel<2>, g, dim3(kThreads), 0, s, a);
-            else if (p.one_width == 1) hipLaunchKernelGGL(encode_kernel<1>, g, dim3(kThreads), 0, s, a);
-            else if (p.one_width == 4) hipLaunchKernelGGL(encode_kernel<4>, g, dim3(kThreads), 0, s, a);
-            else hipLaunchKernelGGL(encode_kernel<0>, g, dim3(kThreads), 0, s, a);
+            const dim3 g(t1 - t0), b(kThreads);
+            switch (p.widths) {
+                case 1: hipLaunchKernelGGL(encode_kernel<1>, g, b, 0, s, a); break;
+                case 2: hipLaunchKernelGGL(encode_kernel<2>, g, b, 0, s, a); break;
+                case 3: hipLaunchKernelGGL(encode_kernel<3>, g, b, 0, s, a); break;
+                case 4: hipLaunchKernelGGL(encode_kernel<4>, g, b, 0, s, a); break;
+                case 5: hipLaunchKernelGGL(encode_kernel<5>, g, b, 0, s, a); break;
+                case 6: hipLaunchKernelGGL(encode_kernel<6>, g, b, 0, s, a); break;
+                default: hipLaunchKernelGGL(encode_kernel<7>, g, b, 0, s, a); break;
+            }
         }
         if (timed) mark(false, s);
         if (staged) {

@@ -256,8 +256,7 @@ static int32_t build(const dcr_tensor_desc* T, uint32_t nT, const uint64_t* shar
     // case (about 4 KiB a chunk of 2-byte elements, the records of a chunk
     // with ~1 % of its elements changed), and 16 bytes a partition at least
     P.compact_stage_bytes = std::max<uint64_t>(pad16(P.max_payload_bytes / 16), uint64_t(kStageParts) * 16);
-    // widths are 1, 2 or 4: one bit each
-    P.one_width = (widths == 1 || widths == 2 || widths == 4) ? widths : 0;
+    P.widths = widths;   // 1, 2 or 4: one bit each
     // per-block "scale changed" flag bits, one bit per element of each gating scale tensor
     std::vector<uint64_t> bit_off(nT, 0);
     for (uint32_t s = 0; s < nT; s++) {
