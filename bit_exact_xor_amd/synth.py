@@ -565,7 +565,7 @@ def scatter_canonical_gpu(lay: Layout, canon, device="cuda", fill=0xA5):
 
 
 def random_layout(seed: int, max_tensors=4, max_chunks=3.0, allow_transpose=True,
-                  allow_block_scaled=True, rate=None) -> Layout:
+                  allow_block_scaled=True, rate=None, widths=None) -> Layout:
     """A small random layout with explicit random contents, for property tests.
 
     Tensors are 2-D [rows, cols] with 1- or 2-byte elements (plus fp32 scale
@@ -573,7 +573,9 @@ def random_layout(seed: int, max_tensors=4, max_chunks=3.0, allow_transpose=True
     into uneven row blocks or uneven column blocks over several shards, or
     stored transposed; several tensors may share a shard.  Old contents are
     uniform random bits; a random fraction of elements gets random new bits
-    (sign flips, low-bit and high-bit changes).
+    (sign flips, low-bit and high-bit changes).  widths: element widths
+    given to the tensors in turn (at least one tensor each) instead of the
+    random choice; a 4-byte tensor is an overwrite tensor of its own.
     """
     rng = np.random.default_rng(seed)
     b = _Builder(f"rand{seed}", seed)
@@ -596,11 +598,13 @@ def random_layout(seed: int, max_tensors=4, max_chunks=3.0, allow_transpose=True
         return off, len(shard_parts[s]) - 1
 
     n_t = int(rng.integers(1, max_tensors + 1))
+    if widths is not None:
+        n_t = max(n_t, len(widths))
     canon_vals = []
     pending_fill = []
     shared = {}
     for ti in range(n_t):
-        w = int(rng.choice([1, 2, 2, 2]))
+        w = int(rng.choice([1, 2, 2, 2])) if widths is None else int(widths[ti % len(widths)])
         E = 65536 // w
         numel_target = int(rng.integers(0, int(max_chunks * E) + 2))
         cols = int(rng.choice([1, 3, 8, 24, 100, 129, 256, 1000, 4096]))
@@ -610,6 +614,8 @@ def random_layout(seed: int, max_tensors=4, max_chunks=3.0, allow_transpose=True
         numel = rows * cols
         route = int(rng.choice([ROUTE_AFFINE_XOR, ROUTE_AFFINE_XOR, ROUTE_OVERWRITE,
                                 ROUTE_BLOCK_SCALED if allow_block_scaled else ROUTE_AFFINE_XOR]))
+        if w == 4:
+            route = ROUTE_OVERWRITE
         sb = 0
         if route == ROUTE_BLOCK_SCALED:
             sb = int(rng.choice([16, 32, 128, 256])) if w == 1 else int(rng.choice([8, 64, 128]))
@@ -618,7 +624,7 @@ def random_layout(seed: int, max_tensors=4, max_chunks=3.0, allow_transpose=True
                           else ["whole", "rows", "cols"])
         if numel == 0:
             mode = "whole"
-        dt = {1: np.uint8, 2: np.uint16}[w]
+        dt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[w]
         old = rng.integers(0, 1 << (8 * w), size=numel, dtype=np.uint64).astype(dt)
         canon_vals.append((t, rows, cols, w, old))
         if mode == "whole":
@@ -721,6 +727,27 @@ def random_layout(seed: int, max_tensors=4, max_chunks=3.0, allow_transpose=True
                                            "canon_old": canon_old, "canon_new": canon_new_d})
     lay.values = (olds, news)
     return lay
+
+
+def width_set_layout(ws: int, k: int = 0, rate=None) -> Layout:
+    """A random layout whose non-empty tensors hold exactly the element
+    widths of the bit set ws (1-, 2- and 4-byte elements; a 4-byte tensor
+    also on its own, stored whole, split or transposed): the k-th such
+    layout of the widths option from seed 2300 on (change rate as given,
+    else the layout's own)."""
+    widths = [w for w in (1, 2, 4) if ws & w]
+    found = 0
+    for seed in range(2300, 3300):
+        lay = random_layout(seed, widths=widths, allow_block_scaled=bool(ws & 4), rate=rate)
+        got = 0
+        for t in lay.tensors:
+            if int(t["numel"]):
+                got |= int(t["elem_bytes"])
+        if got == ws:
+            if found == k:
+                return lay
+            found += 1
+    raise ValueError(f"no layout of width set {ws}")
 
 
 def recipes_kind(recipes, t):

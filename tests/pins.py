@@ -114,6 +114,26 @@ def pin_roundtrip_random(orc, seeds=range(12)):
             assert np.array_equal(W[t], cn[t]), (seed, t)
 
 
+def pin_width_sets(orc):
+    """Layouts of every set of element widths, 4-byte overwrite tensors also
+    on their own and split or transposed: both streams decode to the
+    definition, apply gives new and the overwrite retry gives new."""
+    for ws in range(1, 8):
+        lay = synth.width_set_layout(ws)
+        olds, news, co, cn = canon_lists(lay)
+        for mode in (MODE_DELTA, MODE_RETRY):
+            hdr, d, p = encode_ok(orc, lay, olds, news, mode=mode)
+            check_stream_against_definition(lay, co, cn, hdr, d, p, mode)
+            W = [x.copy() for x in co]
+            if mode == MODE_DELTA:
+                flags = np.zeros(max(len(d) // 32, 1), np.uint8)
+                assert orc.apply(lay.tensors, W, hdr, d, p, flags, expected_base_version=7) == 0
+            else:
+                assert orc.retry(lay.tensors, W, hdr, d, p, expected_base_version=7) == 0
+            for t in range(lay.n_tensors):
+                assert np.array_equal(W[t], cn[t]), (ws, mode, t)
+
+
 def pin_xor_involution(orc, seeds=range(4)):
     """Applying a XOR-only stream twice (flags reset) restores old; with the
     flags kept, the second apply is a no-op (dedup)."""

@@ -89,6 +89,37 @@ def test_random_layout_parity(gh, orc, seed):
     assert bool((flags[:n] == 1).all()) if n else True
 
 
+@pytest.mark.parametrize("rate", (None, 0.7))
+@pytest.mark.parametrize("ws", range(1, 8))
+def test_width_set_parity(gh, orc, ws, rate):
+    """The in-order encode has one build per set of element widths a plan
+    holds: a layout of each set (1-, 2- and 4-byte tensors), at its own
+    change rate and at 70 % (records over several LDS windows), both stream
+    kinds, with no staging area, a small one and a full one, against the
+    oracle; the DELTA stream applied and the RETRY stream retried give new."""
+    say("width set", ws, "rate", rate)
+    lay = synth.width_set_layout(ws, rate=rate)
+    olds, news, co, cn = pins.canon_lists(lay)
+    g = gh.Gpu(lay, olds, news)
+    for mode in (0, 1):
+        exp = oracle_stream(orc, lay, olds, news, mode)
+        for stage in stage_sizes(g):
+            sb = g.encode(mode, stage=stage)
+            assert_same_stream(g.stream_host(sb), exp, f"width set {ws} mode {mode} stage {stage}")
+        hdr, d, p = g.stream_host(sb)
+        n = len(d) // 32
+        buf, canon = g.canon_alloc(co)
+        if mode == 0:
+            flags = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+            r = g.apply(canon, hdr, sb, flags)
+        else:
+            r = g.retry(canon, hdr, sb)
+        assert int(r["n_applied"]) == n and int(r["n_invalid"]) == 0, r
+        got = gh.host(canon)
+        for t in range(lay.n_tensors):
+            assert np.array_equal(got[t], cn[t]), (ws, mode, t)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_dedup_involution_retry(gh, orc, seed):
     """Duplicates are skipped; a XOR stream applied twice restores old; the
