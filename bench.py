@@ -1045,11 +1045,46 @@ def pipelined_transfer(plan, lay, olds, news, canon, as_i16, ws, sb, n_rec, p_by
     return out
 
 
+def _pack_roundtrip(plan, sb, hdr, n, pb, ws, dev, reps):
+    """The transport packing of a finished stream and back: packed payload
+    bytes, records by layout (bitmap / list / gap varints), pack and unpack
+    times (median of reps) and the unpacked stream compared with the
+    original byte for byte (its payload buffer poisoned first)."""
+    import torch
+    from bit_exact_xor_amd import dcr
+    ps = dcr.StreamBuffers(plan, dev, dir_bytes=32 * max(n, 1), payload_bytes=max(pb, 16))
+    us = dcr.StreamBuffers(plan, dev, dir_bytes=32 * max(n, 1), payload_bytes=max(pb, 16))
+    us.payload.fill_(0xA5)
+    t = {"pack": [], "unpack": []}
+    for op in ("pack", "unpack"):
+        for _ in range(reps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            if op == "pack":
+                dcr.dcr_stream_pack(plan, hdr, sb.dir, sb.payload, ps.header, ps.dir, ps.payload, ps.result, ws)
+            else:
+                dcr.dcr_stream_unpack(plan, ps.header.cpu().numpy(), ps.dir, ps.payload, us.header, us.dir,
+                                      us.payload, us.result, ws)
+            b_.record()
+            torch.cuda.synchronize()
+            t[op].append(a_.elapsed_time(b_))
+    pr, ur = ps.result_host(), us.result_host()
+    ppb = int(pr["payload_bytes"])
+    layouts = np.bincount(ps.dir[: 32 * n].view(-1, 32)[:, 15].cpu().numpy(), minlength=3) if n else [0, 0, 0]
+    same = (int(pr["status"]) == 0 and int(ur["status"]) == 0 and int(ur["payload_bytes"]) == pb
+            and torch.equal(us.header, sb.header) and torch.equal(us.dir[: 32 * n], sb.dir[: 32 * n])
+            and torch.equal(us.payload[:pb], sb.payload[:pb]))
+    return {"payload_GB": round(ppb / 1e9, 4), "records_by_layout": [int(x) for x in layouts[:3]],
+            "pack_ms": round(float(np.median(t["pack"])), 3), "unpack_ms": round(float(np.median(t["unpack"])), 3),
+            "unpacked_eq_stream": bool(same)}
+
+
 def lists_cfg5(dev, reps=3):
     """Bitmap against index-list streams on config 5's two regions (identity
     layouts: shard i = tensor i, so the old shards are the canonical old
-    tensors): stream bytes, encode and apply times (median of reps), and the
-    weights after an odd number of XOR applies checked against new."""
+    tensors): stream bytes, encode and apply times (median of reps), the
+    weights after an odd number of XOR applies checked against new, and the
+    index-list stream's transport packing and back."""
     import torch
     from bit_exact_xor_amd import dcr, synth
     out = {}
@@ -1097,6 +1132,8 @@ def lists_cfg5(dev, reps=3):
                           "payload_GB": round(int(r["payload_bytes"]) / 1e9, 4),
                           "encode_ms": round(float(np.median(te)), 3), "apply_ms": round(float(np.median(ta)), 3),
                           "apply_eq_new": all(torch.equal(c, x) for c, x in zip(canon, news))}
+            if opt:
+                row[lname]["packed"] = _pack_roundtrip(plan, sb, hdr, n, int(r["payload_bytes"]), ws, dev, reps)
         out[name] = {"canonical_GB": round(cb / 1e9, 3), **row}
         log(f"{name}: {out[name]}")
         del ob, nb, olds, news, cbuf, canon, ws, sb, plan
