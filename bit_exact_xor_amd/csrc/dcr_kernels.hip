@@ -7,21 +7,26 @@
 //   integers (tokendh blog "shard owner": +0/-0 differ) and routes each
 //   16-byte group to XOR or overwrite (ai-feeds "key modules" 2-3).  Change
 //   counts are scanned per workgroup and the records are assembled in LDS and
-//   written with 128-bit stores.  With a staging area (the default), each
-//   tile writes its records to a slot of its own and publishes its record
-//   count and payload size; a fix-up pass scans those sizes (a decoupled
-//   look-back across fix-up blocks of 256 tiles) into directory indices and
-//   payload offsets and moves the records into place.  Without one, each
-//   tile finds its offsets by a decoupled look-back over all earlier tiles
-//   and writes in place.
+//   written with 128-bit stores.  With a staging area holding a slot for
+//   every chunk (the default), each tile writes its records to its slot and
+//   publishes its record count and payload size; a fix-up pass scans those
+//   sizes (a decoupled look-back across fix-up blocks of 256 tiles) into
+//   directory indices and payload offsets and moves the records into place.
+//   With a smaller area, tiles claim exact bytes in partitions of it, and
+//   chunks that find no room are encoded again after the fix-up.  Without
+//   one, each tile finds its offsets by a decoupled look-back over all
+//   earlier tiles, begun once its first record window is assembled, and
+//   writes in place; that kernel is built once per set of element widths.
 // apply (receiver): one workgroup per directory entry.  It checks the entry
 //   and the record bytes before touching anything, stages the record in LDS,
 //   ranks the changes by a workgroup scan of the bitmap, and updates every
 //   touched 16-byte group of the canonical tensor with one 128-bit
 //   read-modify-write: XOR for masks, assignment for overwrites (ai-feeds
-//   "key modules" 4; humansand "Delta update algebra").  Dedup flags make a
-//   duplicate a no-op (tokendh "XOR or overwrite"); the retry ignores them and
-//   overwrites (tokendh "no backup copy").
+//   "key modules" 4; humansand "Delta update algebra").  Dense records read
+//   and write their touched 128-byte lines whole, and a chunk's XOR record
+//   applies the overwrite record next to it in the same pass.  Dedup flags
+//   make a duplicate a no-op (tokendh "XOR or overwrite"); the retry ignores
+//   them and overwrites (tokendh "no backup copy").
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
