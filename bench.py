@@ -481,6 +481,9 @@ def run_workload(key, make, desc, dev, args, headline=False):
         for op in ops:
             per_op[op]["kernel_frac_of_read_ceiling"] = round(
                 per_op[op]["kernel_alg_GBps"] / res["ceiling"]["read_GBps"], 4)
+        for op in ("apply", "retry"):   # against the bare whole-line patch of the same lines
+            per_op[op]["kernel_frac_of_rmw_lines_ceiling"] = round(
+                res["ceiling"]["rmw_lines"]["ms"] / per_op[op]["kernel_ms"], 4)
 
     # every record of both streams against the oracle, and the CPU baseline
     if headline and not args.no_cpu_baseline:
@@ -1362,6 +1365,20 @@ def measure_ceiling(buf, dev, reps=3, rmw=None):
                              "in place in the canonical buffer, no records read; one thread per 16 consecutive "
                              "groups; best of 4 (even: the buffer ends unchanged); line_GBps counts a 128-byte "
                              "line read and written per touched line"}
+        rl = []
+        for _ in range(4):
+            a, b = ev(), ev()
+            a.record()
+            synth.rmw_probe_gpu(cbuf, bits, whole_lines=True)
+            b.record()
+            torch.cuda.synchronize()
+            rl.append(a.elapsed_time(b))
+        ms = min(rl)
+        out["rmw_lines"] = {"ms": round(ms, 4), "lines": n_lines,
+                            "line_GBps": round(2 * LINE * n_lines / (ms * 1e-3) / 1e9, 1),
+                            "how": "the same groups patched with every touched 128-byte line read and written "
+                                   "whole (one thread per 16-byte group; the buffer is 256-byte aligned, so its "
+                                   "lines are the GPU's), no records read; best of 4"}
     return out
 
 

@@ -9,6 +9,8 @@
 // nothing of the delta method itself.  Built into its own library,
 // libdcr_synth.so.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 namespace {
@@ -140,6 +142,25 @@ __global__ __launch_bounds__(256) void rmw_probe_kernel(v4u* buf, const uint16_t
     }
 }
 
+// The same patch with every touched 128-byte line read and written whole
+// (eight 16-byte groups a line, counted from the buffer's start: a 128-byte
+// aligned buffer gives the GPU's own lines), the access pattern of an apply
+// that writes whole lines: one thread per group, the line's eight bits read
+// as one byte; a grid-stride loop over the groups.
+__global__ __launch_bounds__(256) void rmw_lines_probe_kernel(v4u* buf, const uint8_t* bits, uint64_t n16) {
+    const uint64_t stride = uint64_t(gridDim.x) * 256u;
+    const v4u m = {0x00010001u, 0x00800080u, 0x01000100u, 0x80008000u};
+    for (uint64_t g = uint64_t(blockIdx.x) * 256u + threadIdx.x; g < n16; g += stride) {
+        uint32_t lb = bits[g >> 3];
+        const uint64_t l0 = g & ~uint64_t(7);
+        if (n16 - l0 < 8u) lb &= (1u << uint32_t(n16 - l0)) - 1u;
+        if (!lb) continue;
+        v4u v = buf[g];
+        if ((lb >> uint32_t(g & 7u)) & 1u) v ^= m;
+        buf[g] = v;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,6 +206,19 @@ int32_t dcr_synth_rmw_probe(void* buf, uint64_t bytes, const void* bits, void* s
     if (blocks > 0x7FFFFFFFull) return int32_t(hipErrorInvalidValue);
     hipLaunchKernelGGL(rmw_probe_kernel, dim3(uint32_t(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<v4u*>(buf), static_cast<const uint16_t*>(bits), n16);
+    return int32_t(hipGetLastError());
+}
+
+// The same groups patched with each touched 128-byte line (eight groups from
+// the buffer's start) read and written whole.  Same arguments and checks.
+int32_t dcr_synth_rmw_lines_probe(void* buf, uint64_t bytes, const void* bits, void* stream) {
+    if ((reinterpret_cast<uintptr_t>(buf) & 15u) || (bytes & 15u) || (reinterpret_cast<uintptr_t>(bits) & 1u) || !bits)
+        return int32_t(hipErrorInvalidValue);
+    if (bytes == 0) return 0;
+    const uint64_t n16 = bytes / 16, blocks = std::min<uint64_t>((n16 + 255) / 256, uint64_t(1) << 20);
+    hipLaunchKernelGGL(rmw_lines_probe_kernel, dim3(uint32_t(blocks)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<v4u*>(buf), static_cast<const uint8_t*>(bits),
+                       n16);
     return int32_t(hipGetLastError());
 }
 

@@ -815,6 +815,8 @@ def _load_synth():
         lib.dcr_synth_read_probe.argtypes = [P, U64, P, P]
         lib.dcr_synth_rmw_probe.restype = ctypes.c_int32
         lib.dcr_synth_rmw_probe.argtypes = [P, U64, P, P]
+        lib.dcr_synth_rmw_lines_probe.restype = ctypes.c_int32
+        lib.dcr_synth_rmw_lines_probe.argtypes = [P, U64, P, P]
         _synth_lib = lib
     return _synth_lib
 
@@ -865,10 +867,12 @@ def read_probe_gpu(buf, sink, stream=None):
     return n
 
 
-def rmw_probe_gpu(buf, bits, stream=None):
+def rmw_probe_gpu(buf, bits, stream=None, whole_lines=False):
     """XOR a fixed mask into the 16-byte groups of the device tensor `buf`
     whose bits are set in the device bit array `bits` (LSB first, one bit per
-    group; bandwidth probe for the in-place patch pattern)."""
+    group; bandwidth probe for the in-place patch pattern).  whole_lines:
+    every 128-byte line holding a set group (eight groups from the buffer's
+    start) is read and written whole, the other groups unchanged."""
     import torch
     lib = _load_synth()
     if stream is None:
@@ -877,9 +881,10 @@ def rmw_probe_gpu(buf, bits, stream=None):
     groups = n // 16
     if n % 16 or bits.numel() * bits.element_size() < (groups + 15) // 16 * 2:
         raise ValueError("rmw_probe_gpu: buffer not a multiple of 16 bytes, or too few bits")
-    rc = lib.dcr_synth_rmw_probe(buf.data_ptr(), n, bits.data_ptr(), stream or None)
+    fn = lib.dcr_synth_rmw_lines_probe if whole_lines else lib.dcr_synth_rmw_probe
+    rc = fn(buf.data_ptr(), n, bits.data_ptr(), stream or None)
     if rc:
-        raise RuntimeError(f"dcr_synth_rmw_probe failed: {rc}")
+        raise RuntimeError(f"rmw probe failed: {rc}")
 
 
 # ------------------------------------------------- configs 3 / 4 (MoE)

@@ -675,25 +675,29 @@ def test_corrupt_records_refused(gh):
     assert flags[1].item() == 0 and flags[2].item() == 0 and flags[0].item() == 1
 
 
-def test_rmw_probe(gh):
-    """The read-modify-write probe that bench.py times as the apply's ceiling
-    XORs its fixed mask into exactly the flagged 16-byte groups (a ragged
-    last word of bits included), and a second run restores the buffer."""
-    say("rmw probe: 1000 groups, ragged bit word")
+@pytest.mark.parametrize("whole_lines", (False, True))
+@pytest.mark.parametrize("groups", (1000, 1003))
+def test_rmw_probe(gh, groups, whole_lines):
+    """The read-modify-write probes that bench.py times as the apply's
+    ceilings (16-byte groups alone, or every touched 128-byte line whole)
+    XOR their fixed mask into exactly the flagged 16-byte groups (a ragged
+    last word of bits and a ragged last line included), and a second run
+    restores the buffer."""
+    say("rmw probe:", groups, "groups, whole lines" if whole_lines else "groups alone")
     rng = np.random.default_rng(5)
-    groups = 1000
     host = rng.integers(0, 256, size=16 * groups, dtype=np.uint8)
     flags = rng.random(groups) < 0.3
-    bits = np.packbits(np.concatenate([flags, np.ones(1008 - groups, bool)]), bitorder="little")
+    nb = (groups + 15) // 16 * 16
+    bits = np.packbits(np.concatenate([flags, np.ones(nb - groups, bool)]), bitorder="little")
     buf = torch.from_numpy(host.copy()).cuda()
     bdev = torch.from_numpy(bits).cuda()
-    synth.rmw_probe_gpu(buf, bdev)
+    synth.rmw_probe_gpu(buf, bdev, whole_lines=whole_lines)
     torch.cuda.synchronize()
     mask = np.array([0x00010001, 0x00800080, 0x01000100, 0x80008000], dtype="<u4").view(np.uint8)
     exp = host.reshape(groups, 16).copy()
     exp[flags] ^= mask
     assert np.array_equal(buf.cpu().numpy().reshape(groups, 16), exp)
-    synth.rmw_probe_gpu(buf, bdev)
+    synth.rmw_probe_gpu(buf, bdev, whole_lines=whole_lines)
     torch.cuda.synchronize()
     assert np.array_equal(buf.cpu().numpy(), host)
 
