@@ -89,6 +89,42 @@ def test_random_layout_parity(gh, orc, seed):
     assert bool((flags[:n] == 1).all()) if n else True
 
 
+def test_no_changes(gh, orc):
+    """Degenerate inputs: new equal to old (every chunk scanned, no record
+    written) and a plan whose tensors are all empty (no chunk at all): both
+    stream kinds, every staging area, equal to the oracle's empty streams;
+    the empty DELTA stream applied and the empty RETRY stream retried leave
+    the weights as they were."""
+    lay = synth.random_layout(2400, max_tensors=5, max_chunks=4.0)
+    olds, news, co, cn = pins.canon_lists(lay)
+    b = synth._Builder("empty", 1)
+    b.tensor("e0", 0, 2)
+    b.tensor("e1", 0, 1)
+    b.shard(0, 2)
+    empty = b.build()
+    empty.values = ([np.zeros(0, np.uint16)], [np.zeros(0, np.uint16)])
+    cases = (("new = old", lay, olds, co), ("empty plan", empty, empty.values[0], [np.zeros(0, np.uint8)] * 2))
+    for name, L, o, c0 in cases:
+        say("no changes:", name)
+        g = gh.Gpu(L, o, o)
+        for mode in (0, 1):
+            exp = oracle_stream(orc, L, o, o, mode)
+            assert len(exp[1]) == 0 and len(exp[2]) == 0
+            for stage in stage_sizes(g):
+                sb = g.encode(mode, stage=stage)
+                assert_same_stream(g.stream_host(sb), exp, f"{name} mode {mode} stage {stage}")
+            hdr = sb.header.cpu().numpy()
+            buf, canon = g.canon_alloc(c0)
+            if mode == 0:
+                r = g.apply(canon, hdr, sb, torch.zeros(1, dtype=torch.uint8, device="cuda"))
+            else:
+                r = g.retry(canon, hdr, sb)
+            assert int(r["n_applied"]) == 0 and int(r["n_invalid"]) == 0 and int(r["n_skipped"]) == 0, r
+            got = gh.host(canon)
+            for t in range(L.n_tensors):
+                assert np.array_equal(got[t], c0[t]), (name, mode, t)
+
+
 @pytest.mark.parametrize("rate", (None, 0.7))
 @pytest.mark.parametrize("ws", range(1, 8))
 def test_width_set_parity(gh, orc, ws, rate):
